@@ -1,0 +1,219 @@
+/* wsgemv -- batch-1 decode GEMV weight streaming on MI355X (gfx950).
+ *
+ * The operation (emit_qwen38_generate, "Where the speed comes from"): at
+ * batch 1 a decode step is bandwidth-bound; each projection is one GEMV
+ * y = W.x that streams a whole weight matrix against ONE activation vector.
+ * Projections that share an activation are stacked by rows into one matrix
+ * (q/k/v/z, gate+up), so each is one launch (item 1).  Weights are BF16 or
+ * Q8_0 blocks (32 int8 codes + one fp16 scale, llama.cpp style).  The
+ * activation is either quantized to int8 per 32-block, so the inner loop is
+ * an int8 dot product, or kept in f32 and the weights are dequantized in
+ * registers (the "deq" modes 0/1/2 of the same page).  The step ends with
+ * an LM-head GEMV whose argmax stays on the device (item 2; GPU Kernel Lab,
+ * "Decode integration").
+ *
+ * Conventions for every entry point:
+ *  - Every pointer argument is a DEVICE pointer (except the descriptor array
+ *    of wsg_plan_create, which is host memory), allocated and owned by the
+ *    caller.  No entry point allocates or frees device memory, and none
+ *    synchronizes the host with the device, so each can be captured into a
+ *    hipGraph.  Only wsg_plan_create/destroy allocate (host-side graph
+ *    objects).
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *    The return value is a status code, decided BEFORE anything is
+ *    enqueued: on any nonzero status nothing was launched.  WSG_ERR_HIP
+ *    reports a launch that the runtime rejected.  Faults inside a kernel
+ *    surface at the caller's next synchronization, as usual in HIP.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Weight, activation and quantized-activation pointers must be 16-byte
+ *    aligned; f32 outputs and int32 outputs 4-byte aligned.
+ *  - Sizes are int64_t; n and k must each be < 2^31.
+ *  - The library is stateless apart from per-device launch parameters that
+ *    it looks up once; all entry points are thread-safe.
+ */
+#ifndef WSGEMV_H
+#define WSGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The library is built with hidden visibility; everything declared here is
+ * exported. */
+#pragma GCC visibility push(default)
+
+/* ---------------------------------------------------------------- status */
+enum {
+    WSG_OK = 0,
+    WSG_ERR_NULL = 1,      /* a required pointer is NULL */
+    WSG_ERR_SHAPE = 2,     /* n/k out of range, k not a multiple of the block */
+    WSG_ERR_ALIGN = 3,     /* a pointer violates the alignment rule above */
+    WSG_ERR_MODE = 4,      /* unknown activation format / weight type / op */
+    WSG_ERR_WORKSPACE = 5, /* workspace too small */
+    WSG_ERR_HIP = 6,       /* the HIP runtime rejected a call */
+};
+
+/* Activation formats of the Q8_0 GEMV (the deq modes of emit_qwen38_generate):
+ *  WSG_ACT_Q8_0        x is the output of quantize_act_q8_0: int8 dot path.
+ *  WSG_ACT_F32_REQUANT x is f32[k]; each workgroup quantizes it with the same
+ *                      rule and the same bytes as quantize_act_q8_0, then
+ *                      takes the int8 dot path (one launch instead of two).
+ *  WSG_ACT_F32         x is f32[k]: the dequantizing path, no activation
+ *                      quantization error.
+ * deq 0 -> every Q8_0 GEMV uses WSG_ACT_Q8_0 (or _F32_REQUANT);
+ * deq 1 -> the same, except the LM head uses WSG_ACT_F32;
+ * deq 2 -> every Q8_0 GEMV uses WSG_ACT_F32.  BF16 GEMVs always take f32 x. */
+enum { WSG_ACT_Q8_0 = 0, WSG_ACT_F32 = 1, WSG_ACT_F32_REQUANT = 2 };
+
+/* Weight types. */
+enum { WSG_W_BF16 = 0, WSG_W_Q8_0 = 1 };
+
+/* Largest supported k per path (the activation is staged whole in LDS). */
+#define WSG_MAX_K_Q8ACT 57344 /* WSG_ACT_Q8_0 and WSG_ACT_F32_REQUANT */
+#define WSG_MAX_K_F32ACT 36864 /* WSG_ACT_F32 and BF16 weights */
+
+/* Static text for a status code (never NULL). */
+const char* wsg_status_str(int status);
+
+/* Library version, "major.minor.patch". */
+const char* wsg_version(void);
+
+/* ---------------------------------------------------------- Q8_0 layout ---
+ * Canonical interchange (llama.cpp block order): per row, per 32 weights
+ * along k, a 34-byte block {fp16 scale d (little-endian); int8 q[32]};
+ * weight = d * q.
+ *
+ * Device layout ("packed"), produced only by pack_q8_0 or
+ * quantize_q8_0_weights: rows are contiguous, row r at byte
+ * r * q8_0_row_bytes(k).  A row is split into chunks of up to 64 blocks
+ * (2048 weights); a chunk of nb blocks holds
+ *     [nb fp16 scales, zero-padded to a multiple of 16 bytes]
+ *     [first 16 codes of each of its nb blocks, 16 bytes per block]
+ *     [last 16 codes of each of its nb blocks]
+ * so one wave of 64 lanes loads one whole block per lane with two
+ * contiguous 1 KB loads.  Bytes per weight stay 34/32 whenever k % 256 == 0
+ * (otherwise the last chunk carries up to 14 bytes of padding).
+ */
+int64_t q8_0_row_bytes(int64_t k);
+int64_t q8_0_packed_bytes(int64_t n, int64_t k);
+
+/* ------------------------------------------------ offline weight prep ---
+ * Concatenation of projections that share an activation = writing each
+ * projection's rows into consecutive row ranges of one packed matrix:
+ * pass w_packed + row0 * q8_0_row_bytes(k) (resp. out + row0 * k).
+ */
+
+/* Canonical AoS blocks (n rows x k/32 blocks x 34 bytes, any alignment)
+ * -> device layout.  k % 32 == 0. */
+int pack_q8_0(const void* blocks_aos, int64_t n, int64_t k, void* w_packed, hipStream_t stream);
+
+/* Row-major f32 weights [n][k] -> device layout, with the Q8_0 rule:
+ * d = fp16_RNE(max|w| / 127) (IEEE fp32 divide), q = clamp(round half away
+ * from zero of w / float(d), -127, 127) (fp32 divide by the stored scale);
+ * an all-zero block (or one whose scale underflows fp16) stores d = +0,
+ * q = 0.  Non-finite weights are outside the contract.  k % 32 == 0. */
+int quantize_q8_0_weights(const float* w, int64_t n, int64_t k, void* w_packed, hipStream_t stream);
+
+/* f32 -> bf16, round to nearest even, count elements. */
+int convert_bf16(const float* in, int64_t count, uint16_t* out, hipStream_t stream);
+
+/* ------------------------------------------ activation quantization ---
+ * x f32[k] -> planar Q8_0 activation: int8 q[k] at byte 0, then fp16
+ * d[k/32] at byte k (natural order, same rule as quantize_q8_0_weights).
+ * k % 32 == 0.  act_q8_0_bytes(k) = k + k/16. */
+int64_t act_q8_0_bytes(int64_t k);
+int quantize_act_q8_0(const float* x, int64_t k, void* x_q8, hipStream_t stream);
+
+/* ------------------------------------------------------------- GEMVs ---
+ * y[r] = sum_i W[r,i] x[i], f32 accumulation, r < n.  n == 0 is a no-op;
+ * k == 0 writes y = 0.
+ *
+ * gemv_bf16: W row-major bf16 [n][k], k % 8 == 0, k <= WSG_MAX_K_F32ACT;
+ *   x f32[k].  Acceptance: |y - y_ref| <= 2^-10 sum_i |w_i x_i| per row.
+ * gemv_q8_0: W in the device layout; k % 32 == 0.  act_fmt as above.
+ *   debug_block_dots (nullable; WSG_ACT_Q8_0 / _F32_REQUANT only) receives
+ *   the exact int32 block dot products s[r][b] = sum_i qw[r,32b+i] qx[32b+i]
+ *   as int32[n][k/32].  Acceptance: |y - y_ref| <= 1e-4 sum_b |d_w d_x s_b|
+ *   (int8 paths), <= 1e-4 sum_b sum_i |d_w q_i x_i| (f32 path). */
+int gemv_bf16(const uint16_t* w, int64_t n, int64_t k, const float* x, float* y, hipStream_t stream);
+int gemv_q8_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act_fmt, float* y,
+              int32_t* debug_block_dots, hipStream_t stream);
+
+/* ------------------------------------------------- LM head + argmax ---
+ * The LM-head GEMV (as gemv_bf16 / gemv_q8_0, w_type selects) fused with
+ * stage 1 of a two-stage argmax: each workgroup reduces its rows' logits
+ * to one key (value, lowest index among IEEE-equal values, -0 == +0) in
+ * `ws`; stage 2 (one workgroup) writes the winning row index to *idx_out
+ * in device memory.  The library never reads it back.  debug_logits
+ * (nullable) receives the f32 logits.  n >= 1.  ws must hold at least
+ * wsg_argmax_ws_bytes() bytes (8-byte aligned). */
+int64_t wsg_argmax_ws_bytes(void);
+int lm_head_argmax(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt,
+                   void* ws, size_t ws_bytes, int32_t* idx_out, float* debug_logits,
+                   hipStream_t stream);
+
+/* The same two-stage argmax over an f32 vector v[n], n >= 1 (NaN outside
+ * the contract). */
+int argmax_f32(const float* v, int64_t n, void* ws, size_t ws_bytes, int32_t* idx_out,
+               hipStream_t stream);
+
+/* ------------------------------------------------- whole-token plan ---
+ * A sequence of the calls above, captured once into a hipGraph and
+ * replayed with one launch per token (emit_qwen38_generate, "Where the
+ * speed comes from", item 2; qwen3-8b-rtx4080-cutedsl, "CUDA graphs").
+ * Buffers are fixed at capture time: the caller keeps every buffer alive,
+ * at the same address, until wsg_plan_destroy.  Replays reproduce the eager
+ * results bit for bit. */
+enum {
+    WSG_OP_GEMV_BF16 = 0,       /* w, n, k, x (f32), y */
+    WSG_OP_GEMV_Q8_0 = 1,       /* w, n, k, x, act_fmt, y */
+    WSG_OP_QUANTIZE_ACT = 2,    /* x (f32), k, y = x_q8 output (void*) */
+    WSG_OP_LM_HEAD_ARGMAX = 3,  /* w, w_type, n, k, x, act_fmt, ws, ws_bytes, idx_out */
+};
+
+typedef struct {
+    int op;
+    int w_type;
+    int act_fmt;
+    int64_t n;
+    int64_t k;
+    const void* w;
+    const void* x;
+    void* y;
+    void* ws;
+    size_t ws_bytes;
+    int32_t* idx_out;
+} wsg_op_desc;
+
+typedef struct wsg_plan wsg_plan;
+
+/* Validates every descriptor (first failure's status is returned, nothing
+ * captured), then captures them in order.  `stream` is used for capture
+ * only; it must not be capturing already. */
+int wsg_plan_create(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_plan** out);
+int wsg_plan_launch(wsg_plan* plan, hipStream_t stream);
+int wsg_plan_destroy(wsg_plan* plan);
+/* Number of kernel launches one replay makes. */
+int wsg_plan_kernel_count(const wsg_plan* plan);
+
+/* --------------------------------------------------- measurement tools ---
+ * wsg_read_probe: reads `bytes` (multiple of 16) from buf with the same
+ * load width and cache policy as the GEMV weight stream and writes one
+ * float per workgroup to sink[blocks] so the reads are not elided; blocks
+ * <= 0 picks the GEMV's grid size.  wsg_copy_probe: dst[i] = src[i] for
+ * `bytes` (multiple of 16): a kernel of exactly known traffic for
+ * calibrating hardware byte counters. */
+int wsg_read_probe(const void* buf, int64_t bytes, float* sink, int blocks, hipStream_t stream);
+int wsg_copy_probe(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
+#pragma GCC visibility pop
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WSGEMV_H */

@@ -1,0 +1,131 @@
+"""The C-ABI library loads without a GPU, exports every function the header
+declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_streaming_gemv_q8_amd as wsg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wsgemv.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+char\s*\*|int64_t|int)\s+(\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(wsg.LIB_PATH):
+        from weight_streaming_gemv_q8_amd import build
+        build.build()
+    return wsg.lib()
+
+
+def test_header_symbols_are_exported(L):
+    names = _declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(names) == sorted(wsg.EXPORTS)
+
+
+def test_status_strings_and_sizes(L):
+    for s in range(7):
+        assert wsg.status_str(s)
+    assert wsg.status_str(99) == "unknown status"
+    assert wsg.version().count(".") == 2
+    assert wsg.q8_0_row_bytes(5120) == 5440
+    assert wsg.q8_0_row_bytes(17408) == 18496
+    assert wsg.q8_0_row_bytes(32) == 16 + 32  # one block: scale padded to 16
+    assert wsg.q8_0_row_bytes(33) == 0
+    assert wsg.q8_0_packed_bytes(16384, 5120) == 16384 * 5440
+    assert wsg.act_q8_0_bytes(4096) == 4096 + 256
+    assert wsg.argmax_ws_bytes() >= 8 * 256
+
+
+# Every call below must fail validation, so nothing is launched (no GPU here).
+BAD = 0x1001  # a misaligned fake address, never dereferenced
+
+
+def test_gemv_q8_argument_errors(L):
+    A16 = 0x10000
+    cases = [
+        (dict(w=A16, n=4, k=33, x=A16, act=0, y=A16), wsg.ERR_SHAPE),
+        (dict(w=A16, n=-1, k=32, x=A16, act=0, y=A16), wsg.ERR_SHAPE),
+        (dict(w=A16, n=4, k=wsg.MAX_K_Q8ACT + 32, x=A16, act=0, y=A16), wsg.ERR_SHAPE),
+        (dict(w=A16, n=4, k=wsg.MAX_K_F32ACT + 32, x=A16, act=1, y=A16), wsg.ERR_SHAPE),
+        (dict(w=A16, n=2 ** 31, k=32, x=A16, act=0, y=A16), wsg.ERR_SHAPE),
+        (dict(w=None, n=4, k=32, x=A16, act=0, y=A16), wsg.ERR_NULL),
+        (dict(w=A16, n=4, k=32, x=None, act=0, y=A16), wsg.ERR_NULL),
+        (dict(w=A16, n=4, k=32, x=A16, act=0, y=None), wsg.ERR_NULL),
+        (dict(w=BAD, n=4, k=32, x=A16, act=0, y=A16), wsg.ERR_ALIGN),
+        (dict(w=A16, n=4, k=32, x=BAD, act=0, y=A16), wsg.ERR_ALIGN),
+        (dict(w=A16, n=4, k=32, x=A16, act=0, y=0x10002), wsg.ERR_ALIGN),
+        (dict(w=A16, n=4, k=32, x=A16, act=7, y=A16), wsg.ERR_MODE),
+    ]
+    for a, want in cases:
+        got = L.gemv_q8_0(a["w"], a["n"], a["k"], a["x"], a["act"], a["y"], None, None)
+        assert got == want, (a, got, want)
+    # block dots are only defined on the int8 paths
+    assert L.gemv_q8_0(A16, 4, 32, A16, wsg.ACT_F32, A16, A16, None) == wsg.ERR_MODE
+
+
+def test_gemv_bf16_and_quant_argument_errors(L):
+    A16 = 0x10000
+    assert L.gemv_bf16(A16, 4, 12, A16, A16, None) == wsg.ERR_SHAPE
+    assert L.gemv_bf16(A16, 4, wsg.MAX_K_F32ACT + 8, A16, A16, None) == wsg.ERR_SHAPE
+    assert L.gemv_bf16(None, 4, 16, A16, A16, None) == wsg.ERR_NULL
+    assert L.gemv_bf16(BAD, 4, 16, A16, A16, None) == wsg.ERR_ALIGN
+    assert L.quantize_act_q8_0(A16, 40, A16, None) == wsg.ERR_SHAPE
+    assert L.quantize_act_q8_0(None, 64, A16, None) == wsg.ERR_NULL
+    assert L.quantize_act_q8_0(A16, 64, BAD, None) == wsg.ERR_ALIGN
+    assert L.quantize_q8_0_weights(A16, 2, 48, A16, None) == wsg.ERR_SHAPE
+    assert L.pack_q8_0(A16, 2, 64, BAD, None) == wsg.ERR_ALIGN
+    assert L.convert_bf16(None, 10, A16, None) == wsg.ERR_NULL
+
+
+def test_lm_head_and_argmax_argument_errors(L):
+    A16 = 0x10000
+    ws = wsg.argmax_ws_bytes()
+    assert L.lm_head_argmax(A16, 5, 10, 32, A16, 0, A16, ws, A16, None, None) == wsg.ERR_MODE
+    assert L.lm_head_argmax(A16, 1, 0, 32, A16, 0, A16, ws, A16, None, None) == wsg.ERR_SHAPE
+    assert L.lm_head_argmax(A16, 1, 10, 32, A16, 0, A16, 8, A16, None, None) == wsg.ERR_WORKSPACE
+    assert L.lm_head_argmax(A16, 1, 10, 32, A16, 0, A16, ws, None, None, None) == wsg.ERR_NULL
+    assert L.lm_head_argmax(A16, 1, 10, 32, A16, 0, 0x10004, ws, A16, None, None) == wsg.ERR_ALIGN
+    assert L.argmax_f32(A16, 0, A16, ws, A16, None) == wsg.ERR_SHAPE
+    assert L.argmax_f32(A16, 10, A16, 16, A16, None) == wsg.ERR_WORKSPACE
+
+
+def test_plan_rejects_bad_descriptors_before_capture(L):
+    A16 = 0x10000
+    ops = [wsg.op_gemv_q8_0(A16, 4, 33, A16, wsg.ACT_Q8_0, A16)]
+    with pytest.raises(wsg.WsgError) as e:
+        wsg.Plan(ops, stream=0)
+    assert e.value.status == wsg.ERR_SHAPE
+    ops = [wsg.OpDesc(op=9)]
+    with pytest.raises(wsg.WsgError) as e:
+        wsg.Plan(ops, stream=0)
+    assert e.value.status == wsg.ERR_MODE
+    h = ctypes.c_void_p()
+    assert L.wsg_plan_create(None, 1, None, ctypes.byref(h)) == wsg.ERR_NULL
+    assert L.wsg_plan_launch(None, None) == wsg.ERR_NULL
+    assert L.wsg_plan_kernel_count(None) == -1
+
+
+def test_deq_mode_mapping():
+    # emit_qwen38_generate: deq 0 = int8 activations everywhere, 1 = f32 for
+    # the LM head only, 2 = f32 for every Q8_0 GEMV
+    assert wsg.act_fmt_for(0, False) == wsg.ACT_F32_REQUANT
+    assert wsg.act_fmt_for(0, True, fused_requant=False) == wsg.ACT_Q8_0
+    assert wsg.act_fmt_for(1, False) == wsg.ACT_F32_REQUANT
+    assert wsg.act_fmt_for(1, True) == wsg.ACT_F32
+    assert wsg.act_fmt_for(2, False) == wsg.ACT_F32
+    assert wsg.act_fmt_for(2, True) == wsg.ACT_F32
+    with pytest.raises(ValueError):
+        wsg.act_fmt_for(3, False)

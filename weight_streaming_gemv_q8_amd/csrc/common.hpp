@@ -1,0 +1,120 @@
+// Device helpers shared by the wsgemv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wsg {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 32;             // Q8_0 block: 32 weights, one fp16 scale
+constexpr int kChunkBlocks = 64;       // one block per lane of a wave
+constexpr int kChunkWeights = kChunkBlocks * kBlock;  // 2048
+constexpr int kFullChunkBytes = 2 * kChunkBlocks + kChunkWeights;  // 128 scale + 2048 code bytes
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------- Q8_0 layout
+// Bytes of a chunk's scale section: 2 bytes per block, padded to 16.
+__host__ __device__ inline int64_t scale_section_bytes(int64_t nb) { return (2 * nb + 15) & ~int64_t(15); }
+
+__host__ __device__ inline int64_t chunk_count(int64_t k) { return (k / kBlock + kChunkBlocks - 1) / kChunkBlocks; }
+
+__host__ __device__ inline int64_t last_chunk_blocks(int64_t k) {
+    const int64_t nb = k / kBlock;
+    return nb - (chunk_count(k) - 1) * kChunkBlocks;
+}
+
+__host__ __device__ inline int64_t packed_row_bytes(int64_t k) {
+    if (k <= 0) return 0;
+    const int64_t c = chunk_count(k);
+    const int64_t nl = last_chunk_blocks(k);
+    return (c - 1) * kFullChunkBytes + scale_section_bytes(nl) + 32 * nl;
+}
+
+// --------------------------------------------------------------- loads
+// Weight stream loads: 16 bytes per lane, optionally marked non-temporal so
+// the stream does not evict the (re-used) activation from L2.
+template <bool NT>
+__device__ inline int4v load16(const void* p) {
+    if constexpr (NT) {
+        return __builtin_nontemporal_load(reinterpret_cast<const int4v*>(p));
+    } else {
+        return *reinterpret_cast<const int4v*>(p);
+    }
+}
+
+template <bool NT>
+__device__ inline uint16_t load_u16(const void* p) {
+    if constexpr (NT) {
+        return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+    } else {
+        return *reinterpret_cast<const uint16_t*>(p);
+    }
+}
+
+__device__ inline float half_bits_to_float(uint16_t h) {
+    _Float16 f;
+    __builtin_memcpy(&f, &h, 2);
+    return (float)f;
+}
+
+__device__ inline uint16_t float_to_half_bits_rne(float x) {
+    _Float16 f = (_Float16)x;  // v_cvt_f16_f32: round to nearest even
+    uint16_t h;
+    __builtin_memcpy(&h, &f, 2);
+    return h;
+}
+
+// ------------------------------------------------------ Q8_0 block quantizer
+// The Q8_0 rule for one 32-value block, in fp32 as the oracle takes it:
+// d = fp16_RNE(max|v| / 127) (IEEE divide), q_i = clamp(round half away from
+// zero of v_i / float(d), -127, 127) (IEEE divide by the stored scale); a
+// zero scale stores d = +0 and q = 0.
+__device__ inline float q8_round_half_away(float v) {
+    const float t = __builtin_truncf(v);
+    const float frac = v - t;  // exact for |v| < 2^23
+    return (__builtin_fabsf(frac) >= 0.5f) ? t + __builtin_copysignf(1.0f, v) : t;
+}
+
+__device__ inline int8_t q8_code(float v, float d) {
+    float r = q8_round_half_away(v / d);
+    r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
+    return (int8_t)(int)r;
+}
+
+// Scale bits for a block whose largest magnitude is amax.
+__device__ inline uint16_t q8_scale_bits(float amax) { return float_to_half_bits_rne(amax / 127.0f); }
+
+// ------------------------------------------------------- wave reductions
+// Butterfly sums over the 64 lanes of a wave; every lane ends with the same
+// value and the order of additions does not depend on which row is reduced.
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t u = __shfl_xor(v, o, kWave);
+        v = u > v ? u : v;
+    }
+    return v;
+}
+
+// --------------------------------------------------------- argmax keys
+// Order-preserving 64-bit key for (value, index): larger value wins; among
+// IEEE-equal values (-0 == +0 after canonicalization) the lower index wins.
+__device__ inline uint64_t argmax_key(float v, uint32_t idx) {
+    if (v == 0.0f) v = 0.0f;  // -0 -> +0
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t ordered = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)ordered << 32) | (uint64_t)(~idx);
+}
+
+__device__ inline uint32_t argmax_key_index(uint64_t key) { return ~(uint32_t)(key & 0xFFFFFFFFu); }
+
+}  // namespace wsg

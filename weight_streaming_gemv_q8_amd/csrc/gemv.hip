@@ -1,0 +1,742 @@
+// Batch-1 decode GEMV kernels for gfx950: y = W.x streaming a whole weight
+// matrix against one activation vector (emit_qwen38_generate, "Where the
+// speed comes from"; qwen3-8b-rtx4080-cutedsl, "Decode GEMV path"; GPU
+// Kernel Lab, "What we built": split-K, warp-reduced decode GEMV).
+//
+// Mapping (all paths):
+//  * A persistent grid of workgroups of WAVES wave64s.  Each workgroup first
+//    stages the whole activation in LDS, in the order the lanes consume it,
+//    then walks row tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...
+//  * A tile holds WAVES/S rows; S waves share one row and split its chunks
+//    (split-K inside the workgroup: chunk c goes to wave-part c % S).  Each
+//    wave reduces over its 64 lanes with a fixed butterfly, the S partials
+//    meet in LDS and are added in part order, so a row's result does not
+//    depend on where or when it was computed.  No atomics, no cross-workgroup
+//    reduction.
+//  * Lane l of a wave owns block l of every 64-block chunk of a row: with the
+//    device layout it gets the block's 32 codes from two contiguous 1 KB
+//    wave loads (16 bytes per lane) and its scale from one 128-byte load.
+//  * Loads of U chunks are issued before any of them is consumed, so each
+//    lane keeps 2U 16-byte weight loads in flight.
+//  * No MFMA: at batch 1 there is one multiply-add per weight and no reuse.
+#include "common.hpp"
+#include "internal.hpp"
+
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <utility>
+
+namespace wsg {
+namespace {
+
+constexpr int kActQ8 = 0, kActF32 = 1, kActRequant = 2;  // = WSG_ACT_*
+
+// ------------------------------------------------------------------ LDS
+// Layouts of the staged activation (per 2048-weight chunk c, lane l):
+//  int8 paths : int4v q[C][2][64]   (half h of block 64c+l), float dx[C*64]
+//  f32 path   : float4v x[C][8][64] (values 4g..4g+3 of block 64c+l)
+//  bf16 path  : float4v x[C'][2][2][64] over 1024-element chunks:
+//               values 1024c + 512h + 8l + 4j .. +3
+
+__host__ __device__ inline size_t lds_q8act_bytes(int C) { return (size_t)C * (2 * kWave * 16 + kWave * 4); }
+__host__ __device__ inline size_t lds_f32act_bytes(int C) { return (size_t)C * 8 * kWave * 16; }
+__host__ __device__ inline int bf16_chunks(int k) { return (k + 1023) / 1024; }
+__host__ __device__ inline size_t lds_bf16_bytes(int k) { return (size_t)bf16_chunks(k) * 4 * kWave * 16; }
+// tail of the LDS allocation: S partial sums per tile and the argmax keys
+template <int WAVES>
+__host__ __device__ constexpr size_t lds_tail_bytes() {
+    return WAVES * sizeof(float) + WAVES * sizeof(uint64_t) + 16;
+}
+
+// Stage a planar Q8_0 activation (q[k] then fp16 d[k/32]).
+__device__ inline void stage_q8(const void* __restrict__ xin, int k, int C, int4v* lds_q, float* lds_dx) {
+    const int NB = k / kBlock;
+    const int8_t* q = static_cast<const int8_t*>(xin);
+    const uint16_t* d = reinterpret_cast<const uint16_t*>(q + k);
+    // unit u = (c*2 + h)*64 + l  <-  block b = 64c + l, half h
+    for (int u = threadIdx.x; u < C * 2 * kWave; u += blockDim.x) {
+        const int l = u % kWave, ch = u / kWave, h = ch & 1, c = ch >> 1;
+        const int b = c * kWave + l;
+        if (b < NB) lds_q[u] = *reinterpret_cast<const int4v*>(q + (int64_t)b * kBlock + 16 * h);
+    }
+    for (int b = threadIdx.x; b < NB; b += blockDim.x) lds_dx[b] = half_bits_to_float(d[b]);
+}
+
+// Quantize an f32 activation into LDS with the Q8_0 rule (the same device
+// functions and the same bytes as quantize_act_q8_0).
+__device__ inline void stage_requant(const float* __restrict__ x, int k, int4v* lds_q, float* lds_dx) {
+    const int NB = k / kBlock;
+    for (int b = threadIdx.x; b < NB; b += blockDim.x) {
+        float v[32];
+        const float4v* s4 = reinterpret_cast<const float4v*>(x + (int64_t)b * kBlock);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4v t = s4[i];
+            v[4 * i + 0] = t.x;
+            v[4 * i + 1] = t.y;
+            v[4 * i + 2] = t.z;
+            v[4 * i + 3] = t.w;
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+        const float d = half_bits_to_float(q8_scale_bits(amax));
+        int8_t codes[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) codes[i] = (d == 0.0f) ? (int8_t)0 : q8_code(v[i], d);
+        const int c = b / kWave, l = b % kWave;
+        int4v lo, hi;
+        __builtin_memcpy(&lo, codes, 16);
+        __builtin_memcpy(&hi, codes + 16, 16);
+        lds_q[(c * 2 + 0) * kWave + l] = lo;
+        lds_q[(c * 2 + 1) * kWave + l] = hi;
+        lds_dx[b] = d;
+    }
+}
+
+// Stage an f32 activation for the dequantizing path.
+__device__ inline void stage_f32(const float* __restrict__ x, int k, float4v* lds_x) {
+    const int n4 = k / 4;
+    // global float4 index v -> block b = v/8, group g = v%8 -> LDS unit (c*8+g)*64 + l
+    for (int v = threadIdx.x; v < n4; v += blockDim.x) {
+        const int b = v >> 3, g = v & 7, c = b / kWave, l = b % kWave;
+        lds_x[(c * 8 + g) * kWave + l] = reinterpret_cast<const float4v*>(x)[v];
+    }
+}
+
+// Stage an f32 activation for the bf16 path.
+__device__ inline void stage_bf16x(const float* __restrict__ x, int k, float4v* lds_x) {
+    const int n4 = k / 4;
+    // element e = 1024c + 512h + 8l + 4j  <->  float4 index v = e/4
+    for (int v = threadIdx.x; v < n4; v += blockDim.x) {
+        const int e = 4 * v;
+        const int c = e >> 10, h = (e >> 9) & 1, l = (e >> 3) & 63, j = (e >> 2) & 1;
+        lds_x[((c * 2 + h) * 2 + j) * kWave + l] = reinterpret_cast<const float4v*>(x)[v];
+    }
+}
+
+// Epilogue shared by all paths: combine split-K partials in part order,
+// then store y (and/or fold the row into the workgroup's argmax key).
+template <int WAVES, int S, bool ARGMAX>
+__device__ inline void finish_row(float acc, int row, int n, int lane, int wave, float* lds_part, float* y,
+                                  uint64_t& best) {
+    constexpr int GROUPS = WAVES / S;
+    (void)GROUPS;
+    const int part = wave % S;
+    float total = acc;
+    if constexpr (S > 1) {
+        if (lane == 0) lds_part[wave] = acc;
+        __syncthreads();
+        if (part == 0) {
+            total = lds_part[wave];
+#pragma unroll
+            for (int p = 1; p < S; ++p) total += lds_part[wave + p];
+        }
+        __syncthreads();
+    }
+    if (part == 0 && row < n) {
+        if constexpr (ARGMAX) {
+            const uint64_t key = argmax_key(total, (uint32_t)row);
+            best = key > best ? key : best;
+            if (y != nullptr && lane == 0) y[row] = total;
+        } else {
+            if (lane == 0) y[row] = total;
+        }
+    }
+}
+
+template <int WAVES>
+__device__ inline void write_block_key(uint64_t best, int lane, int wave, uint64_t* lds_key, uint64_t* keys) {
+    if (lane == 0) lds_key[wave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t m = lds_key[0];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) m = lds_key[w] > m ? lds_key[w] : m;
+        keys[blockIdx.x] = m;
+    }
+}
+
+// ------------------------------------------------ Q8_0 x int8 (and requant)
+template <int WAVES, int S, int U, int ACT, bool NT, bool DEBUG, bool ARGMAX>
+__global__ void __launch_bounds__(WAVES * kWave)
+q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict__ xin, float* __restrict__ y,
+             int32_t* __restrict__ dots, uint64_t* __restrict__ keys) {
+    static_assert(WAVES % S == 0, "S must divide WAVES");
+    constexpr int GROUPS = WAVES / S;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int C = (int)chunk_count(k);
+    const int NB = k / kBlock;
+    const int nl = NB - (C - 1) * kChunkBlocks;
+    const int sbl = (int)scale_section_bytes(nl);
+    const int64_t row_bytes = packed_row_bytes(k);
+    int4v* lds_q = reinterpret_cast<int4v*>(smem);
+    float* lds_dx = reinterpret_cast<float*>(smem + (size_t)C * 2 * kWave * 16);
+    float* lds_part = reinterpret_cast<float*>(smem + lds_q8act_bytes(C));
+    uint64_t* lds_key = reinterpret_cast<uint64_t*>(smem + ((lds_q8act_bytes(C) + WAVES * 4 + 15) & ~size_t(15)));
+
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int group = wave / S, part = wave % S;
+
+    if constexpr (ACT == kActRequant) {
+        stage_requant(static_cast<const float*>(xin), k, lds_q, lds_dx);
+    } else {
+        stage_q8(xin, k, C, lds_q, lds_dx);
+    }
+    __syncthreads();
+
+    uint64_t best = 0;
+    const int tiles = (n + GROUPS - 1) / GROUPS;
+    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const int row = tile * GROUPS + group;
+        float acc = 0.0f;
+        if (row < n) {
+            const uint8_t* rowp = W + (int64_t)row * row_bytes;
+            for (int c0 = part; c0 < C; c0 += S * U) {
+                int4v a[U], b[U];
+                uint16_t sc[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * S;
+                    a[u] = int4v{0, 0, 0, 0};
+                    b[u] = int4v{0, 0, 0, 0};
+                    sc[u] = 0;
+                    if (c < C) {
+                        const bool last = (c == C - 1);
+                        const int nbc = last ? nl : kChunkBlocks;
+                        const int sb = last ? sbl : 2 * kChunkBlocks;
+                        const uint8_t* cp = rowp + (int64_t)c * kFullChunkBytes;
+                        if (lane < nbc) {
+                            sc[u] = load_u16<NT>(cp + 2 * lane);
+                            a[u] = load16<NT>(cp + sb + 16 * lane);
+                            b[u] = load16<NT>(cp + sb + 16 * nbc + 16 * lane);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * S;
+                    if (c < C) {
+                        const int blk = c * kWave + lane;
+                        if (blk < NB) {
+                            const int4v xa = lds_q[(c * 2 + 0) * kWave + lane];
+                            const int4v xb = lds_q[(c * 2 + 1) * kWave + lane];
+                            int s = 0;
+                            s = __builtin_amdgcn_sdot4(a[u].x, xa.x, s, false);
+                            s = __builtin_amdgcn_sdot4(a[u].y, xa.y, s, false);
+                            s = __builtin_amdgcn_sdot4(a[u].z, xa.z, s, false);
+                            s = __builtin_amdgcn_sdot4(a[u].w, xa.w, s, false);
+                            s = __builtin_amdgcn_sdot4(b[u].x, xb.x, s, false);
+                            s = __builtin_amdgcn_sdot4(b[u].y, xb.y, s, false);
+                            s = __builtin_amdgcn_sdot4(b[u].z, xb.z, s, false);
+                            s = __builtin_amdgcn_sdot4(b[u].w, xb.w, s, false);
+                            if constexpr (DEBUG) dots[(int64_t)row * NB + blk] = s;
+                            const float t = half_bits_to_float(sc[u]) * lds_dx[blk];
+                            acc = __builtin_fmaf(t, (float)s, acc);
+                        }
+                    }
+                }
+            }
+            acc = wave_sum(acc);
+        }
+        finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
+    }
+    if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
+}
+
+// ------------------------------------------------------ Q8_0 x f32 (deq)
+__device__ inline float dot4_i8_f32(int w, float4v x, float acc) {
+    acc = __builtin_fmaf((float)(int8_t)(w & 0xFF), x.x, acc);
+    acc = __builtin_fmaf((float)(int8_t)((w >> 8) & 0xFF), x.y, acc);
+    acc = __builtin_fmaf((float)(int8_t)((w >> 16) & 0xFF), x.z, acc);
+    acc = __builtin_fmaf((float)(int8_t)(w >> 24), x.w, acc);
+    return acc;
+}
+
+template <int WAVES, int S, int U, bool NT, bool ARGMAX>
+__global__ void __launch_bounds__(WAVES * kWave)
+q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restrict__ x, float* __restrict__ y,
+              uint64_t* __restrict__ keys) {
+    static_assert(WAVES % S == 0, "S must divide WAVES");
+    constexpr int GROUPS = WAVES / S;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int C = (int)chunk_count(k);
+    const int NB = k / kBlock;
+    const int nl = NB - (C - 1) * kChunkBlocks;
+    const int sbl = (int)scale_section_bytes(nl);
+    const int64_t row_bytes = packed_row_bytes(k);
+    float4v* lds_x = reinterpret_cast<float4v*>(smem);
+    float* lds_part = reinterpret_cast<float*>(smem + lds_f32act_bytes(C));
+    uint64_t* lds_key = reinterpret_cast<uint64_t*>(smem + ((lds_f32act_bytes(C) + WAVES * 4 + 15) & ~size_t(15)));
+
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int group = wave / S, part = wave % S;
+
+    stage_f32(x, k, lds_x);
+    __syncthreads();
+
+    uint64_t best = 0;
+    const int tiles = (n + GROUPS - 1) / GROUPS;
+    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const int row = tile * GROUPS + group;
+        float acc = 0.0f;
+        if (row < n) {
+            const uint8_t* rowp = W + (int64_t)row * row_bytes;
+            for (int c0 = part; c0 < C; c0 += S * U) {
+                int4v a[U], b[U];
+                uint16_t sc[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * S;
+                    a[u] = int4v{0, 0, 0, 0};
+                    b[u] = int4v{0, 0, 0, 0};
+                    sc[u] = 0;
+                    if (c < C) {
+                        const bool last = (c == C - 1);
+                        const int nbc = last ? nl : kChunkBlocks;
+                        const int sb = last ? sbl : 2 * kChunkBlocks;
+                        const uint8_t* cp = rowp + (int64_t)c * kFullChunkBytes;
+                        if (lane < nbc) {
+                            sc[u] = load_u16<NT>(cp + 2 * lane);
+                            a[u] = load16<NT>(cp + sb + 16 * lane);
+                            b[u] = load16<NT>(cp + sb + 16 * nbc + 16 * lane);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * S;
+                    if (c < C && c * kWave + lane < NB) {
+                        const float4v* xv = lds_x + (size_t)c * 8 * kWave + lane;
+                        float bs = 0.0f;
+                        bs = dot4_i8_f32(a[u].x, xv[0 * kWave], bs);
+                        bs = dot4_i8_f32(a[u].y, xv[1 * kWave], bs);
+                        bs = dot4_i8_f32(a[u].z, xv[2 * kWave], bs);
+                        bs = dot4_i8_f32(a[u].w, xv[3 * kWave], bs);
+                        bs = dot4_i8_f32(b[u].x, xv[4 * kWave], bs);
+                        bs = dot4_i8_f32(b[u].y, xv[5 * kWave], bs);
+                        bs = dot4_i8_f32(b[u].z, xv[6 * kWave], bs);
+                        bs = dot4_i8_f32(b[u].w, xv[7 * kWave], bs);
+                        acc = __builtin_fmaf(half_bits_to_float(sc[u]), bs, acc);
+                    }
+                }
+            }
+            acc = wave_sum(acc);
+        }
+        finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
+    }
+    if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
+}
+
+// ---------------------------------------------------------- BF16 x f32
+__device__ inline float dot_bf16x8(int4v w, float4v x0, float4v x1, float acc) {
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.x << 16), x0.x, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.x & 0xFFFF0000u), x0.y, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.y << 16), x0.z, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.y & 0xFFFF0000u), x0.w, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.z << 16), x1.x, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.z & 0xFFFF0000u), x1.y, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.w << 16), x1.z, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.w & 0xFFFF0000u), x1.w, acc);
+    return acc;
+}
+
+template <int WAVES, int S, int U, bool NT, bool ARGMAX>
+__global__ void __launch_bounds__(WAVES * kWave)
+bf16_kernel(const uint16_t* __restrict__ W, int n, int k, const float* __restrict__ x, float* __restrict__ y,
+            uint64_t* __restrict__ keys) {
+    static_assert(WAVES % S == 0, "S must divide WAVES");
+    constexpr int GROUPS = WAVES / S;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int C = bf16_chunks(k);
+    float4v* lds_x = reinterpret_cast<float4v*>(smem);
+    float* lds_part = reinterpret_cast<float*>(smem + lds_bf16_bytes(k));
+    uint64_t* lds_key = reinterpret_cast<uint64_t*>(smem + ((lds_bf16_bytes(k) + WAVES * 4 + 15) & ~size_t(15)));
+
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int group = wave / S, part = wave % S;
+
+    stage_bf16x(x, k, lds_x);
+    __syncthreads();
+
+    uint64_t best = 0;
+    const int tiles = (n + GROUPS - 1) / GROUPS;
+    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const int row = tile * GROUPS + group;
+        float acc = 0.0f;
+        if (row < n) {
+            const uint16_t* rowp = W + (int64_t)row * k;
+            for (int c0 = part; c0 < C; c0 += S * U) {
+                int4v a[U], b[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * S;
+                    a[u] = int4v{0, 0, 0, 0};
+                    b[u] = int4v{0, 0, 0, 0};
+                    if (c < C) {
+                        const int e0 = c * 1024 + 8 * lane;
+                        if (e0 < k) a[u] = load16<NT>(rowp + e0);
+                        if (e0 + 512 < k) b[u] = load16<NT>(rowp + e0 + 512);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * S;
+                    if (c < C) {
+                        const float4v* xv = lds_x + (size_t)c * 4 * kWave + lane;
+                        // out-of-range lanes hold zero weights and zero-staged x is not
+                        // guaranteed, so guard by element index
+                        const int e0 = c * 1024 + 8 * lane;
+                        if (e0 < k) acc = dot_bf16x8(a[u], xv[0 * kWave], xv[1 * kWave], acc);
+                        if (e0 + 512 < k) acc = dot_bf16x8(b[u], xv[2 * kWave], xv[3 * kWave], acc);
+                    }
+                }
+            }
+            acc = wave_sum(acc);
+        }
+        finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
+    }
+    if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
+}
+
+// ---------------------------------------------------------------- argmax
+__global__ void argmax_stage1_kernel(const float* __restrict__ v, int64_t n, uint64_t* __restrict__ keys) {
+    __shared__ uint64_t lds_key[16];
+    const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+    const int64_t begin = (int64_t)blockIdx.x * per;
+    const int64_t end = begin + per < n ? begin + per : n;
+    uint64_t best = 0;
+    for (int64_t i = begin + threadIdx.x; i < end; i += blockDim.x) {
+        const uint64_t key = argmax_key(v[i], (uint32_t)i);
+        best = key > best ? key : best;
+    }
+    best = wave_max_u64(best);
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    if (lane == 0) lds_key[wave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t m = lds_key[0];
+        for (int w = 1; w < (int)(blockDim.x / kWave); ++w) m = lds_key[w] > m ? lds_key[w] : m;
+        keys[blockIdx.x] = m;
+    }
+}
+
+__global__ void argmax_stage2_kernel(const uint64_t* __restrict__ keys, int count, int32_t* __restrict__ idx_out) {
+    __shared__ uint64_t lds_key[16];
+    uint64_t best = 0;
+    for (int i = threadIdx.x; i < count; i += blockDim.x) best = keys[i] > best ? keys[i] : best;
+    best = wave_max_u64(best);
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    if (lane == 0) lds_key[wave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t m = lds_key[0];
+        for (int w = 1; w < (int)(blockDim.x / kWave); ++w) m = lds_key[w] > m ? lds_key[w] : m;
+        idx_out[0] = (int32_t)argmax_key_index(m);
+    }
+}
+
+// ------------------------------------------------------------- planning
+constexpr int kMaxGrid = 8192;  // keys in the argmax workspace
+
+std::once_flag g_info_once;
+DeviceInfo g_info;
+
+}  // namespace
+
+const DeviceInfo& device_info() {
+    std::call_once(g_info_once, [] {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) g_info.cus = v;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess)
+            g_info.max_lds = v;
+        if (g_info.cus <= 0) g_info.cus = 256;
+        if (g_info.max_lds <= 0) g_info.max_lds = 65536;
+    });
+    return g_info;
+}
+
+namespace {
+
+// Optional tuning overrides, read once from the environment (0 = automatic):
+// WSG_TUNE_SPLITK (1, 2 or 4 waves per row), WSG_TUNE_WG_PER_CU (grid =
+// CUs x this, capped by occupancy).
+int env_int(const char* name) {
+    const char* v = std::getenv(name);
+    return v ? std::atoi(v) : 0;
+}
+
+int tune_splitk() {
+    static const int v = env_int("WSG_TUNE_SPLITK");
+    return v;
+}
+
+int tune_wg_per_cu() {
+    static const int v = env_int("WSG_TUNE_WG_PER_CU");
+    return v;
+}
+
+// Workgroups resident per CU for a kernel with the given dynamic LDS
+// (looked up once per kernel and LDS size).
+template <typename K>
+int resident_per_cu(K kernel, int threads, size_t lds) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, size_t>, int> cache;
+    const void* key = reinterpret_cast<const void*>(kernel);
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({key, lds});
+    if (it != cache.end()) return it->second;
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, key, threads, lds) != hipSuccess || blocks < 1)
+        blocks = 1;
+    cache[{key, lds}] = blocks;
+    return blocks;
+}
+
+int persistent_grid(int tiles, int per_cu) {
+    const int cus = device_info().cus;
+    const int forced = tune_wg_per_cu();
+    if (forced > 0 && forced < per_cu) per_cu = forced;
+    int64_t g = (int64_t)cus * per_cu;
+    if (g > kMaxGrid) g = kMaxGrid;
+    if (g > tiles) g = tiles;
+    if (g > 8) g -= g % 8;  // whole rounds over the 8 XCDs
+    return g < 1 ? 1 : (int)g;
+}
+
+// Split-K factor: when a matrix has few rows per CU and long rows, several
+// waves share a row so that every CU still has enough independent streams.
+int choose_split(int64_t n, int64_t k, int waves) {
+    const int forced = tune_splitk();
+    if ((forced == 1 || forced == 2 || forced == 4) && forced <= waves) return forced;
+    const int64_t rows_per_cu = n / device_info().cus;
+    if (rows_per_cu < 16 && k >= 16384 && waves >= 4) return 4;
+    if (rows_per_cu < 32 && k >= 8192) return 2;
+    return 1;
+}
+
+template <typename K>
+void raise_lds_limit(K kernel, size_t lds) {
+    if (lds > 65536)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+}
+
+template <int WAVES, int S, int ACT, bool DEBUG, bool ARGMAX>
+int launch_q8_i8_s(const void* w, int n, int k, const void* x, float* y, int32_t* dots, uint64_t* keys,
+                   hipStream_t stream, int* grid_out) {
+    constexpr int U = 4;
+    auto kern = q8_i8_kernel<WAVES, S, U, ACT, true, DEBUG, ARGMAX>;
+    const int C = (int)chunk_count(k);
+    const size_t lds = lds_q8act_bytes(C) + lds_tail_bytes<WAVES>();
+    raise_lds_limit(kern, lds);
+    const int tiles = (n + WAVES / S - 1) / (WAVES / S);
+    const int grid = persistent_grid(tiles, resident_per_cu(kern, WAVES * kWave, lds));
+    if (grid_out) *grid_out = grid;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, static_cast<const uint8_t*>(w), n, k,
+                       x, y, dots, keys);
+    return launch_status();
+}
+
+template <int ACT, bool DEBUG, bool ARGMAX>
+int launch_q8_i8(const void* w, int n, int k, const void* x, float* y, int32_t* dots, uint64_t* keys,
+                 hipStream_t stream, int* grid_out) {
+    constexpr int WAVES = 4;
+    switch (choose_split(n, k, WAVES)) {
+        case 1: return launch_q8_i8_s<WAVES, 1, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, grid_out);
+        case 2: return launch_q8_i8_s<WAVES, 2, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, grid_out);
+        default: return launch_q8_i8_s<WAVES, 4, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, grid_out);
+    }
+}
+
+template <int WAVES, int S, bool ARGMAX>
+int launch_q8_f32_s(const void* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
+                    int* grid_out) {
+    constexpr int U = 2;
+    auto kern = q8_f32_kernel<WAVES, S, U, true, ARGMAX>;
+    const int C = (int)chunk_count(k);
+    const size_t lds = lds_f32act_bytes(C) + lds_tail_bytes<WAVES>();
+    raise_lds_limit(kern, lds);
+    const int tiles = (n + WAVES / S - 1) / (WAVES / S);
+    const int grid = persistent_grid(tiles, resident_per_cu(kern, WAVES * kWave, lds));
+    if (grid_out) *grid_out = grid;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, static_cast<const uint8_t*>(w), n, k,
+                       x, y, keys);
+    return launch_status();
+}
+
+template <bool ARGMAX>
+int launch_q8_f32(const void* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
+                  int* grid_out) {
+    constexpr int WAVES = 8;
+    switch (choose_split(n, k, WAVES)) {
+        case 1: return launch_q8_f32_s<WAVES, 1, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
+        case 2: return launch_q8_f32_s<WAVES, 2, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
+        default: return launch_q8_f32_s<WAVES, 4, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
+    }
+}
+
+template <int WAVES, int S, bool ARGMAX>
+int launch_bf16_s(const uint16_t* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
+                  int* grid_out) {
+    constexpr int U = 4;
+    auto kern = bf16_kernel<WAVES, S, U, true, ARGMAX>;
+    const size_t lds = lds_bf16_bytes(k) + lds_tail_bytes<WAVES>();
+    raise_lds_limit(kern, lds);
+    const int tiles = (n + WAVES / S - 1) / (WAVES / S);
+    const int grid = persistent_grid(tiles, resident_per_cu(kern, WAVES * kWave, lds));
+    if (grid_out) *grid_out = grid;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, w, n, k, x, y, keys);
+    return launch_status();
+}
+
+template <bool ARGMAX>
+int launch_bf16(const uint16_t* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
+                int* grid_out) {
+    constexpr int WAVES = 4;
+    switch (choose_split(n, k, WAVES)) {
+        case 1: return launch_bf16_s<WAVES, 1, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
+        case 2: return launch_bf16_s<WAVES, 2, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
+        default: return launch_bf16_s<WAVES, 4, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
+    }
+}
+
+int launch_argmax_stage2(const uint64_t* keys, int count, int32_t* idx_out, hipStream_t stream) {
+    hipLaunchKernelGGL(argmax_stage2_kernel, dim3(1), dim3(1024), 0, stream, keys, count, idx_out);
+    return launch_status();
+}
+
+int check_q8_args(const void* w, int64_t n, int64_t k, const void* x, int act_fmt, const void* out) {
+    if (act_fmt != WSG_ACT_Q8_0 && act_fmt != WSG_ACT_F32 && act_fmt != WSG_ACT_F32_REQUANT) return WSG_ERR_MODE;
+    if (n < 0 || k < 0 || n > kMaxDim || k > kMaxDim || k % kBlock) return WSG_ERR_SHAPE;
+    const int64_t kmax = act_fmt == WSG_ACT_F32 ? WSG_MAX_K_F32ACT : WSG_MAX_K_Q8ACT;
+    if (k > kmax) return WSG_ERR_SHAPE;
+    if (n == 0) return WSG_OK;
+    if (!out) return WSG_ERR_NULL;
+    if (!aligned(out, 4)) return WSG_ERR_ALIGN;
+    if (k == 0) return WSG_OK;
+    if (!w || !x) return WSG_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(x, 16)) return WSG_ERR_ALIGN;
+    return WSG_OK;
+}
+
+int check_bf16_args(const void* w, int64_t n, int64_t k, const void* x, const void* out) {
+    if (n < 0 || k < 0 || n > kMaxDim || k > kMaxDim || k % 8) return WSG_ERR_SHAPE;
+    if (k > WSG_MAX_K_F32ACT) return WSG_ERR_SHAPE;
+    if (n == 0) return WSG_OK;
+    if (!out) return WSG_ERR_NULL;
+    if (!aligned(out, 4)) return WSG_ERR_ALIGN;
+    if (k == 0) return WSG_OK;
+    if (!w || !x) return WSG_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(x, 16)) return WSG_ERR_ALIGN;
+    return WSG_OK;
+}
+
+}  // namespace
+
+// Validation without launching (used by the plan).
+int validate_gemv_q8(const void* w, int64_t n, int64_t k, const void* x, int act_fmt, const void* y) {
+    return check_q8_args(w, n, k, x, act_fmt, y);
+}
+
+int validate_gemv_bf16(const void* w, int64_t n, int64_t k, const void* x, const void* y) {
+    return check_bf16_args(w, n, k, x, y);
+}
+
+int validate_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, const void* ws,
+                     size_t ws_bytes, const void* idx_out) {
+    if (w_type != WSG_W_BF16 && w_type != WSG_W_Q8_0) return WSG_ERR_MODE;
+    if (n < 1) return WSG_ERR_SHAPE;
+    if (!idx_out || !ws) return WSG_ERR_NULL;
+    if (!aligned(ws, 8) || !aligned(idx_out, 4)) return WSG_ERR_ALIGN;
+    if (ws_bytes < (size_t)kMaxGrid * 8) return WSG_ERR_WORKSPACE;
+    // logits pointer is optional: validate the GEMV part with a dummy non-null output
+    const int rc = w_type == WSG_W_BF16 ? check_bf16_args(w, n, k, x, idx_out)
+                                        : check_q8_args(w, n, k, x, act_fmt, idx_out);
+    if (rc != WSG_OK) return rc;
+    if (k == 0) return WSG_ERR_SHAPE;
+    return WSG_OK;
+}
+
+}  // namespace wsg
+
+using namespace wsg;
+
+extern "C" {
+
+int gemv_q8_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act_fmt, float* y,
+              int32_t* debug_block_dots, hipStream_t stream) {
+    int rc = check_q8_args(w_packed, n, k, x, act_fmt, y);
+    if (rc != WSG_OK) return rc;
+    if (debug_block_dots && act_fmt == WSG_ACT_F32) return WSG_ERR_MODE;
+    if (debug_block_dots && !aligned(debug_block_dots, 4)) return WSG_ERR_ALIGN;
+    if (n == 0) return WSG_OK;
+    if (k == 0) return fill_zero_f32(y, n, stream);
+    const int ni = (int)n, ki = (int)k;
+    if (act_fmt == WSG_ACT_F32) return launch_q8_f32<false>(w_packed, ni, ki, static_cast<const float*>(x), y,
+                                                            nullptr, stream, nullptr);
+    if (act_fmt == WSG_ACT_Q8_0) {
+        return debug_block_dots
+                   ? launch_q8_i8<kActQ8, true, false>(w_packed, ni, ki, x, y, debug_block_dots, nullptr, stream,
+                                                       nullptr)
+                   : launch_q8_i8<kActQ8, false, false>(w_packed, ni, ki, x, y, nullptr, nullptr, stream, nullptr);
+    }
+    return debug_block_dots
+               ? launch_q8_i8<kActRequant, true, false>(w_packed, ni, ki, x, y, debug_block_dots, nullptr, stream,
+                                                        nullptr)
+               : launch_q8_i8<kActRequant, false, false>(w_packed, ni, ki, x, y, nullptr, nullptr, stream, nullptr);
+}
+
+int gemv_bf16(const uint16_t* w, int64_t n, int64_t k, const float* x, float* y, hipStream_t stream) {
+    int rc = check_bf16_args(w, n, k, x, y);
+    if (rc != WSG_OK) return rc;
+    if (n == 0) return WSG_OK;
+    if (k == 0) return fill_zero_f32(y, n, stream);
+    return launch_bf16<false>(w, (int)n, (int)k, x, y, nullptr, stream, nullptr);
+}
+
+int64_t wsg_argmax_ws_bytes(void) { return (int64_t)kMaxGrid * 8; }
+
+int lm_head_argmax(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, void* ws,
+                   size_t ws_bytes, int32_t* idx_out, float* debug_logits, hipStream_t stream) {
+    int rc = validate_lm_head(w, w_type, n, k, x, act_fmt, ws, ws_bytes, idx_out);
+    if (rc != WSG_OK) return rc;
+    if (debug_logits && !aligned(debug_logits, 4)) return WSG_ERR_ALIGN;
+    uint64_t* keys = static_cast<uint64_t*>(ws);
+    const int ni = (int)n, ki = (int)k;
+    int grid = 0;
+    if (w_type == WSG_W_BF16) {
+        rc = launch_bf16<true>(static_cast<const uint16_t*>(w), ni, ki, static_cast<const float*>(x), debug_logits,
+                               keys, stream, &grid);
+    } else if (act_fmt == WSG_ACT_F32) {
+        rc = launch_q8_f32<true>(w, ni, ki, static_cast<const float*>(x), debug_logits, keys, stream, &grid);
+    } else if (act_fmt == WSG_ACT_Q8_0) {
+        rc = launch_q8_i8<kActQ8, false, true>(w, ni, ki, x, debug_logits, nullptr, keys, stream, &grid);
+    } else {
+        rc = launch_q8_i8<kActRequant, false, true>(w, ni, ki, x, debug_logits, nullptr, keys, stream, &grid);
+    }
+    if (rc != WSG_OK) return rc;
+    return launch_argmax_stage2(keys, grid, idx_out, stream);
+}
+
+int argmax_f32(const float* v, int64_t n, void* ws, size_t ws_bytes, int32_t* idx_out, hipStream_t stream) {
+    if (n < 1 || n > kMaxDim) return WSG_ERR_SHAPE;
+    if (!v || !ws || !idx_out) return WSG_ERR_NULL;
+    if (!aligned(v, 4) || !aligned(ws, 8) || !aligned(idx_out, 4)) return WSG_ERR_ALIGN;
+    if (ws_bytes < (size_t)kMaxGrid * 8) return WSG_ERR_WORKSPACE;
+    int64_t g = (n + 4095) / 4096;
+    const int64_t cap = (int64_t)device_info().cus * 4;
+    if (g > cap) g = cap;
+    if (g > kMaxGrid) g = kMaxGrid;
+    if (g < 1) g = 1;
+    uint64_t* keys = static_cast<uint64_t*>(ws);
+    hipLaunchKernelGGL(argmax_stage1_kernel, dim3((unsigned)g), dim3(256), 0, stream, v, n, keys);
+    int rc = launch_status();
+    if (rc != WSG_OK) return rc;
+    return launch_argmax_stage2(keys, (int)g, idx_out, stream);
+}
+
+}  // extern "C"
