@@ -1,0 +1,389 @@
+#!/usr/bin/env python3
+"""Bench: the whole-token batch-1 decode GEMV weight stream on one MI355X.
+
+One step = one replay of the captured hipGraph that streams every weight
+matrix of one token once (emit_qwen38_generate, "Where the speed comes
+from": ~27 GB of Q8_0 weights per token, one launch per concatenated
+projection, one graph per token).  Default workload: the 27B-scale Q8_0
+stream (64 layers x qkvz 16384x5120, out 5120x8192, gate+up 34816x5120,
+down 5120x17408), int8 activations (deq 0) quantized inside each GEMV.
+Weights are synthetic (seeded ~N(0, 0.02), quantized on the device) and
+resident in HBM before timing starts.
+
+Prints ONE JSON line: achieved HBM GB/s over the stream (algorithmic weight
+bytes / time), microseconds per token stream, the roofline of the dominant
+GEMV kernel (HIP events around each launch), and the CPU oracle timed on a
+bounded sample on the host.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+GEMV_SOURCES = [os.path.join(ROOT, "weight_streaming_gemv_q8_amd", "csrc", f)
+                for f in ("gemv.hip", "common.hpp")]
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ arithmetic
+# Closed forms used by the pages (pinned in tests/test_bench_metrics.py).
+
+def tokens_per_s(bandwidth_gbps: float, bytes_per_token_gb: float) -> float:
+    """Batch-1 decode rate when the weight stream is the whole cost."""
+    return bandwidth_gbps / bytes_per_token_gb
+
+
+def dequant_op_rate_tflops(bandwidth_gbps: float, bytes_per_weight: float, ops_per_weight: float) -> float:
+    """Float ops per second the dequantizing GEMV form needs at a given stream rate."""
+    return bandwidth_gbps / bytes_per_weight * ops_per_weight / 1000.0
+
+
+def gbps(nbytes: float, seconds: float) -> float:
+    return nbytes / seconds / 1e9
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in GEMV_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(kernel_name: str):
+    """HBM bytes per launch measured by rocprofv3 counters for this kernel
+    (profiles/traffic_*.txt), or None if absent or taken on other sources."""
+    if not os.path.isdir(PROFILES):
+        return None
+    digest = source_digest()
+    for fn in sorted(os.listdir(PROFILES)):
+        if not (fn.startswith("traffic_") and fn.endswith(".txt")):
+            continue
+        kv = {}
+        with open(os.path.join(PROFILES, fn)) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    a, b = line.split(":", 1)
+                    kv[a.strip()] = b.strip()
+        if kv.get("kernel") == kernel_name and kv.get("source_sha256") == digest:
+            try:
+                return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+            except (KeyError, ValueError):
+                return None
+    return None
+
+
+# ------------------------------------------------------------ workload
+
+def build_stream(wl, deq: int, requant: str):
+    import torch
+
+    import synth
+    from synth import workloads as W
+    from weight_streaming_gemv_q8_amd.stream import TokenStream
+
+    shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
+    ts = TokenStream(shapes, wl.layers, wl.wtype, deq=deq, requant=requant)
+    log(f"allocated {ts.weight_bytes_alloc / 1e9:.3f} GB of weights; generating on the device")
+    t0 = time.time()
+
+    def fill(layer, m, part, rows, staging):
+        synth.dev_normal_f32(staging.data_ptr(), wl.seed, W.weight_tensor_id(layer, m, part),
+                             rows * wl.matrices[m].k, W.WEIGHT_SIGMA,
+                             stream=torch.cuda.current_stream().cuda_stream)
+
+    ts.fill_weights(fill)
+    k0 = wl.matrices[0].k
+    xs = [synth.activation(wl.seed, W.activation_tensor_id(l), k0, rms=True) for l in range(wl.layers)]
+    import numpy as np
+    ts.set_inputs(torch.from_numpy(np.stack(xs)).cuda())
+    torch.cuda.synchronize()
+    log(f"weights ready in {time.time() - t0:.1f} s")
+    return ts
+
+
+def kernel_label(wtype: str, act_fmt: int, cfg: dict) -> str:
+    import weight_streaming_gemv_q8_amd as wsg
+    if wtype == "bf16":
+        base = "bf16_kernel"
+    elif act_fmt == wsg.ACT_F32:
+        base = "q8_f32_kernel"
+    else:
+        base = "q8_i8_kernel"
+    act = {wsg.ACT_Q8_0: "q8act", wsg.ACT_F32: "f32act", wsg.ACT_F32_REQUANT: "requant"}[act_fmt]
+    return f"{base}<waves={cfg['waves']},split={cfg['split']},{act}>"
+
+
+def time_per_launch(ts, reps: int = 1):
+    """HIP events around every GEMV launch of the chain (eager, on the
+    current stream); returns per-slot mean seconds."""
+    import torch
+    n = len(ts.slots)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    acc = [0.0] * n
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        for i in range(n):
+            ev[i][0].record()
+            ts.run_slot(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        for i in range(n):
+            acc[i] += ev[i][0].elapsed_time(ev[i][1]) / 1e3
+    return [a / reps for a in acc]
+
+
+def read_ceiling(ts, reps: int = 3) -> float:
+    import torch
+
+    import weight_streaming_gemv_q8_amd as wsg
+    nbytes = ts.weight_bytes_alloc // 16 * 16
+    sink = torch.empty(65536, dtype=torch.float32, device="cuda")
+    wsg.read_probe(ts.weights, nbytes, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        wsg.read_probe(ts.weights, nbytes, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    return gbps(nbytes * reps, e0.elapsed_time(e1) / 1e3)
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(wl, deq: int, budget_s: float) -> dict:
+    """The oracle as it stands, single-threaded, on a bounded sample: the
+    first layer(s) of the same stream, weights generated and quantized on the
+    host beforehand (untimed, as on the GPU), then the chain of GEMVs (with
+    per-call activation quantization at deq 0) repeated until the budget is
+    used.  GB/s of weight stream."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from synth import workloads as W
+
+    layers = []
+    t_setup = time.time()
+    n_layers = 1
+    for l in range(n_layers):
+        mats = []
+        for j, m in enumerate(wl.matrices):
+            w = np.concatenate([synth.normal_f32(wl.seed, W.weight_tensor_id(l, j, p), r * m.k, W.WEIGHT_SIGMA)
+                                .reshape(r, m.k) for p, r in enumerate(m.parts)])
+            if wl.wtype == "q8_0":
+                mats.append(oracle.quantize_q8_0(w))
+            else:
+                mats.append(oracle.f32_to_bf16_rows(w))
+            del w
+        layers.append(mats)
+    xs = [synth.activation(wl.seed, W.activation_tensor_id(l), wl.matrices[0].k, rms=True)
+          for l in range(n_layers)]
+    log(f"cpu baseline: sample of {n_layers} layer(s) prepared in {time.time() - t_setup:.1f} s")
+
+    per_layer_bytes = wl.weight_bytes_per_layer()
+    done_bytes = 0
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        for l, mats in enumerate(layers):
+            x = xs[l]
+            for j, m in enumerate(wl.matrices):
+                xin = x[:m.k].astype(np.float32)
+                if wl.wtype == "bf16":
+                    y, _ = oracle.gemv_bf16(mats[j], xin)
+                elif deq == 2:
+                    y, _ = oracle.gemv_q8_act_f32(mats[j][0], mats[j][1], xin)
+                else:
+                    dx, qx = oracle.quantize_q8_0(xin)
+                    y, _ = oracle.gemv_q8_act_q8(mats[j][0], mats[j][1], dx, qx)
+                x = y
+            done_bytes += per_layer_bytes
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {
+        "value": round(gbps(done_bytes, el), 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"layer 0 of {wl.name} ({per_layer_bytes / 1e6:.1f} MB of weights, "
+                   f"{len(wl.matrices)} GEMVs{', with per-call activation quantization' if wl.wtype == 'q8_0' and deq != 2 else ''}), "
+                   f"{passes} pass(es) in {el:.1f} s, single-threaded fp64 C oracle"),
+    }
+
+
+# ------------------------------------------------------------ main
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense27b_q8_0_64L")
+    ap.add_argument("--deq", type=int, default=0, choices=(0, 1, 2))
+    ap.add_argument("--requant", default="fused", choices=("fused", "separate"))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the deq-2 line and the read ceiling")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU step (see the design notes on "
+              "sharding by output rows); run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import weight_streaming_gemv_q8_amd as wsg
+    from synth import workloads as W
+
+    wl = {w.name: w for w in W.ALL}.get(args.workload)
+    if wl is None or wl.wtype not in ("q8_0", "bf16") or wl.layers < 2:
+        print(f"unknown or non-stream workload {args.workload}; choose one of "
+              f"{[w.name for w in W.ALL if w.wtype in ('q8_0', 'bf16') and w.layers > 1]}", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    wsg.lib()
+
+    ts = build_stream(wl, args.deq, args.requant)
+    alg_bytes = ts.algorithmic_weight_bytes()
+    act_fmt = ts.act_fmt()
+    plan = ts.capture()
+    kernels_per_token = plan.kernel_count
+    log(f"captured plan: {kernels_per_token} kernels per token")
+
+    for _ in range(args.warmup):
+        ts.launch()
+    torch.cuda.synchronize()
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        ts.launch()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / args.steps
+    value = gbps(alg_bytes, sec)
+    log(f"timed {args.steps} steps: {sec * 1e6:.1f} us per token, {value:.1f} GB/s")
+
+    # dominant kernel: group the launches by kernel instantiation
+    per = time_per_launch(ts)
+    groups = {}
+    wtype_code = wsg.W_Q8_0 if wl.wtype == "q8_0" else wsg.W_BF16
+    for s, t in zip(ts.slots, per):
+        cfg = wsg.gemv_config(wtype_code, act_fmt, s.n, s.k)
+        label = kernel_label(wl.wtype, act_fmt, cfg)
+        bpl = s.n * (s.k // 32) * 34 if wl.wtype == "q8_0" else s.n * s.k * 2
+        g = groups.setdefault(label, {"t": 0.0, "bytes": 0, "launches": 0})
+        g["t"] += t
+        g["bytes"] += bpl
+        g["launches"] += 1
+    dom = max(groups, key=lambda k: groups[k]["t"])
+    g = groups[dom]
+    achieved = gbps(g["bytes"] / g["launches"], g["t"] / g["launches"])
+    traffic = read_traffic(dom)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "kernel": dom,
+        "launches_per_token": g["launches"],
+        "bytes_per_launch": g["bytes"] // g["launches"],
+        "us_per_launch": round(g["t"] / g["launches"] * 1e6, 2),
+    }
+    log(f"dominant kernel {dom}: {roofline['us_per_launch']} us/launch, {achieved:.1f} GB/s")
+    kernel_sum = sum(per)
+
+    extras = {}
+    if not args.no_extras:
+        extras["read_ceiling_GBps"] = round(read_ceiling(ts), 1)
+        log(f"read ceiling {extras['read_ceiling_GBps']} GB/s")
+    ts.close()
+
+    if not args.no_extras and wl.wtype == "q8_0" and args.deq != 2:
+        # the same stream with f32 activations (deq 2), same weights
+        ts.deq = 2
+        ts.capture()
+        for _ in range(max(1, args.warmup)):
+            ts.launch()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            ts.launch()
+        e1.record()
+        torch.cuda.synchronize()
+        sec2 = e0.elapsed_time(e1) / 1e3 / args.steps
+        extras["deq2"] = {"us_per_token": round(sec2 * 1e6, 1), "GBps": round(gbps(alg_bytes, sec2), 1),
+                          "frac_of_peak": round(gbps(alg_bytes, sec2) / HBM_PEAK_GBPS, 4)}
+        log(f"deq 2: {sec2 * 1e6:.1f} us per token")
+        ts.close()
+        ts.deq = args.deq
+
+    del ts
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.deq, args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']} GB/s")
+
+    dtype = "bf16xf32" if wl.wtype == "bf16" else ("int8" if act_fmt != wsg.ACT_F32 else "q8_0xf32")
+    out = {
+        "metric": "achieved HBM GB/s (% of peak) and us per full-token batch-1 GEMV stream",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "description": wl.description,
+            "matrices": [f"{m.name} {m.n}x{m.k}" for m in wl.matrices],
+            "layers": wl.layers,
+            "gemvs_per_token": wl.gemvs_per_token(),
+            "weight_bytes_per_token": alg_bytes,
+            "deq": args.deq,
+            "activation_quantization": ("fused into each GEMV" if args.requant == "fused" else "separate launch")
+            if act_fmt != wsg.ACT_F32 else "none (f32 activations)",
+            "kernels_per_token": kernels_per_token,
+        },
+        "us_per_token": round(sec * 1e6, 1),
+        "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+        "tok_per_s_equiv": round(1.0 / sec, 1),
+        "kernel_time_sum_us": round(kernel_sum * 1e6, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    out.update(extras)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

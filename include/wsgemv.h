@@ -144,6 +144,13 @@ int gemv_bf16(const uint16_t* w, int64_t n, int64_t k, const float* x, float* y,
 int gemv_q8_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act_fmt, float* y,
               int32_t* debug_block_dots, hipStream_t stream);
 
+/* Launch configuration a gemv_bf16 / gemv_q8_0 / lm_head_argmax call of this
+ * shape would use on the current device: waves per workgroup, waves that
+ * share one row (split-K factor), workgroups in the grid and dynamic LDS
+ * bytes (outputs nullable).  For tooling; launches nothing. */
+int wsg_gemv_config(int w_type, int act_fmt, int64_t n, int64_t k, int* waves, int* split, int* grid,
+                    int64_t* lds_bytes);
+
 /* ------------------------------------------------- LM head + argmax ---
  * The LM-head GEMV (as gemv_bf16 / gemv_q8_0, w_type selects) fused with
  * stage 1 of a two-stage argmax: each workgroup reduces its rows' logits

@@ -36,7 +36,7 @@ MAX_K_F32ACT = 36864
 EXPORTS = (
     "wsg_status_str", "wsg_version", "q8_0_row_bytes", "q8_0_packed_bytes", "pack_q8_0",
     "quantize_q8_0_weights", "convert_bf16", "act_q8_0_bytes", "quantize_act_q8_0", "gemv_bf16",
-    "gemv_q8_0", "wsg_argmax_ws_bytes", "lm_head_argmax", "argmax_f32", "wsg_plan_create",
+    "gemv_q8_0", "wsg_gemv_config", "wsg_argmax_ws_bytes", "lm_head_argmax", "argmax_f32", "wsg_plan_create",
     "wsg_plan_launch", "wsg_plan_destroy", "wsg_plan_kernel_count", "wsg_read_probe",
     "wsg_copy_probe",
 )
@@ -81,6 +81,8 @@ def lib():
             "quantize_act_q8_0": (i32, [vp, i64, vp, vp]),
             "gemv_bf16": (i32, [vp, i64, i64, vp, vp, vp]),
             "gemv_q8_0": (i32, [vp, i64, i64, vp, i32, vp, vp, vp]),
+            "wsg_gemv_config": (i32, [i32, i32, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                       ctypes.POINTER(i32), ctypes.POINTER(i64)]),
             "wsg_argmax_ws_bytes": (i64, []),
             "lm_head_argmax": (i32, [vp, i32, i64, i64, vp, i32, vp, ctypes.c_size_t, vp, vp, vp]),
             "argmax_f32": (i32, [vp, i64, vp, ctypes.c_size_t, vp, vp]),
@@ -175,6 +177,15 @@ def gemv_bf16(w, n: int, k: int, x, y, stream=None) -> None:
 def gemv_q8_0(w_packed, n: int, k: int, x, act_fmt: int, y, debug_block_dots=None, stream=None) -> None:
     _check("gemv_q8_0", lib().gemv_q8_0(_ptr(w_packed), n, k, _ptr(x), act_fmt, _ptr(y),
                                         _ptr(debug_block_dots), _stream(stream)))
+
+
+def gemv_config(w_type: int, act_fmt: int, n: int, k: int) -> dict:
+    """Launch configuration the library uses for this call shape."""
+    w, s, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    lds = ctypes.c_int64()
+    _check("wsg_gemv_config", lib().wsg_gemv_config(w_type, act_fmt, n, k, ctypes.byref(w), ctypes.byref(s),
+                                                    ctypes.byref(g), ctypes.byref(lds)))
+    return {"waves": w.value, "split": s.value, "grid": g.value, "lds_bytes": lds.value}
 
 
 def lm_head_argmax(w, w_type: int, n: int, k: int, x, act_fmt: int, ws, ws_bytes: int, idx_out,

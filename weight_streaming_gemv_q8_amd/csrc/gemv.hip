@@ -525,9 +525,15 @@ void raise_lds_limit(K kernel, size_t lds) {
                                   (int)lds);
 }
 
+// Launch configuration of one GEMV call (reported by wsg_gemv_config).
+struct LaunchInfo {
+    int waves = 0, split = 0, grid = 0;
+    size_t lds = 0;
+};
+
 template <int WAVES, int S, int ACT, bool DEBUG, bool ARGMAX>
 int launch_q8_i8_s(const void* w, int n, int k, const void* x, float* y, int32_t* dots, uint64_t* keys,
-                   hipStream_t stream, int* grid_out) {
+                   hipStream_t stream, LaunchInfo* info, bool run) {
     constexpr int U = 4;
     auto kern = q8_i8_kernel<WAVES, S, U, ACT, true, DEBUG, ARGMAX>;
     const int C = (int)chunk_count(k);
@@ -535,7 +541,8 @@ int launch_q8_i8_s(const void* w, int n, int k, const void* x, float* y, int32_t
     raise_lds_limit(kern, lds);
     const int tiles = (n + WAVES / S - 1) / (WAVES / S);
     const int grid = persistent_grid(tiles, resident_per_cu(kern, WAVES * kWave, lds));
-    if (grid_out) *grid_out = grid;
+    if (info) *info = LaunchInfo{WAVES, S, grid, lds};
+    if (!run) return WSG_OK;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, static_cast<const uint8_t*>(w), n, k,
                        x, y, dots, keys);
     return launch_status();
@@ -543,18 +550,21 @@ int launch_q8_i8_s(const void* w, int n, int k, const void* x, float* y, int32_t
 
 template <int ACT, bool DEBUG, bool ARGMAX>
 int launch_q8_i8(const void* w, int n, int k, const void* x, float* y, int32_t* dots, uint64_t* keys,
-                 hipStream_t stream, int* grid_out) {
+                 hipStream_t stream, LaunchInfo* info, bool run = true) {
     constexpr int WAVES = 4;
     switch (choose_split(n, k, WAVES)) {
-        case 1: return launch_q8_i8_s<WAVES, 1, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, grid_out);
-        case 2: return launch_q8_i8_s<WAVES, 2, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, grid_out);
-        default: return launch_q8_i8_s<WAVES, 4, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, grid_out);
+        case 1:
+            return launch_q8_i8_s<WAVES, 1, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, info, run);
+        case 2:
+            return launch_q8_i8_s<WAVES, 2, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, info, run);
+        default:
+            return launch_q8_i8_s<WAVES, 4, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, info, run);
     }
 }
 
 template <int WAVES, int S, bool ARGMAX>
 int launch_q8_f32_s(const void* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
-                    int* grid_out) {
+                    LaunchInfo* info, bool run) {
     constexpr int U = 2;
     auto kern = q8_f32_kernel<WAVES, S, U, true, ARGMAX>;
     const int C = (int)chunk_count(k);
@@ -562,7 +572,8 @@ int launch_q8_f32_s(const void* w, int n, int k, const float* x, float* y, uint6
     raise_lds_limit(kern, lds);
     const int tiles = (n + WAVES / S - 1) / (WAVES / S);
     const int grid = persistent_grid(tiles, resident_per_cu(kern, WAVES * kWave, lds));
-    if (grid_out) *grid_out = grid;
+    if (info) *info = LaunchInfo{WAVES, S, grid, lds};
+    if (!run) return WSG_OK;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, static_cast<const uint8_t*>(w), n, k,
                        x, y, keys);
     return launch_status();
@@ -570,37 +581,38 @@ int launch_q8_f32_s(const void* w, int n, int k, const float* x, float* y, uint6
 
 template <bool ARGMAX>
 int launch_q8_f32(const void* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
-                  int* grid_out) {
+                  LaunchInfo* info, bool run = true) {
     constexpr int WAVES = 8;
     switch (choose_split(n, k, WAVES)) {
-        case 1: return launch_q8_f32_s<WAVES, 1, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
-        case 2: return launch_q8_f32_s<WAVES, 2, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
-        default: return launch_q8_f32_s<WAVES, 4, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
+        case 1: return launch_q8_f32_s<WAVES, 1, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
+        case 2: return launch_q8_f32_s<WAVES, 2, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
+        default: return launch_q8_f32_s<WAVES, 4, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
     }
 }
 
 template <int WAVES, int S, bool ARGMAX>
 int launch_bf16_s(const uint16_t* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
-                  int* grid_out) {
+                  LaunchInfo* info, bool run) {
     constexpr int U = 4;
     auto kern = bf16_kernel<WAVES, S, U, true, ARGMAX>;
     const size_t lds = lds_bf16_bytes(k) + lds_tail_bytes<WAVES>();
     raise_lds_limit(kern, lds);
     const int tiles = (n + WAVES / S - 1) / (WAVES / S);
     const int grid = persistent_grid(tiles, resident_per_cu(kern, WAVES * kWave, lds));
-    if (grid_out) *grid_out = grid;
+    if (info) *info = LaunchInfo{WAVES, S, grid, lds};
+    if (!run) return WSG_OK;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, w, n, k, x, y, keys);
     return launch_status();
 }
 
 template <bool ARGMAX>
 int launch_bf16(const uint16_t* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
-                int* grid_out) {
+                LaunchInfo* info, bool run = true) {
     constexpr int WAVES = 4;
     switch (choose_split(n, k, WAVES)) {
-        case 1: return launch_bf16_s<WAVES, 1, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
-        case 2: return launch_bf16_s<WAVES, 2, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
-        default: return launch_bf16_s<WAVES, 4, ARGMAX>(w, n, k, x, y, keys, stream, grid_out);
+        case 1: return launch_bf16_s<WAVES, 1, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
+        case 2: return launch_bf16_s<WAVES, 2, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
+        default: return launch_bf16_s<WAVES, 4, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
     }
 }
 
@@ -700,6 +712,36 @@ int gemv_bf16(const uint16_t* w, int64_t n, int64_t k, const float* x, float* y,
 
 int64_t wsg_argmax_ws_bytes(void) { return (int64_t)kMaxGrid * 8; }
 
+int wsg_gemv_config(int w_type, int act_fmt, int64_t n, int64_t k, int* waves, int* split, int* grid,
+                    int64_t* lds_bytes) {
+    if (w_type != WSG_W_BF16 && w_type != WSG_W_Q8_0) return WSG_ERR_MODE;
+    if (w_type == WSG_W_BF16) act_fmt = WSG_ACT_F32;
+    if (act_fmt != WSG_ACT_Q8_0 && act_fmt != WSG_ACT_F32 && act_fmt != WSG_ACT_F32_REQUANT) return WSG_ERR_MODE;
+    if (n < 1 || k < 1 || n > kMaxDim || k > kMaxDim) return WSG_ERR_SHAPE;
+    if (w_type == WSG_W_BF16 ? (k % 8 || k > WSG_MAX_K_F32ACT)
+                             : (k % kBlock || k > (act_fmt == WSG_ACT_F32 ? WSG_MAX_K_F32ACT : WSG_MAX_K_Q8ACT)))
+        return WSG_ERR_SHAPE;
+    LaunchInfo info;
+    const int ni = (int)n, ki = (int)k;
+    int rc;
+    if (w_type == WSG_W_BF16)
+        rc = launch_bf16<false>(nullptr, ni, ki, nullptr, nullptr, nullptr, nullptr, &info, false);
+    else if (act_fmt == WSG_ACT_F32)
+        rc = launch_q8_f32<false>(nullptr, ni, ki, nullptr, nullptr, nullptr, nullptr, &info, false);
+    else if (act_fmt == WSG_ACT_Q8_0)
+        rc = launch_q8_i8<kActQ8, false, false>(nullptr, ni, ki, nullptr, nullptr, nullptr, nullptr, nullptr, &info,
+                                                false);
+    else
+        rc = launch_q8_i8<kActRequant, false, false>(nullptr, ni, ki, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                     &info, false);
+    if (rc != WSG_OK) return rc;
+    if (waves) *waves = info.waves;
+    if (split) *split = info.split;
+    if (grid) *grid = info.grid;
+    if (lds_bytes) *lds_bytes = (int64_t)info.lds;
+    return WSG_OK;
+}
+
 int lm_head_argmax(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, void* ws,
                    size_t ws_bytes, int32_t* idx_out, float* debug_logits, hipStream_t stream) {
     int rc = validate_lm_head(w, w_type, n, k, x, act_fmt, ws, ws_bytes, idx_out);
@@ -707,19 +749,19 @@ int lm_head_argmax(const void* w, int w_type, int64_t n, int64_t k, const void* 
     if (debug_logits && !aligned(debug_logits, 4)) return WSG_ERR_ALIGN;
     uint64_t* keys = static_cast<uint64_t*>(ws);
     const int ni = (int)n, ki = (int)k;
-    int grid = 0;
+    LaunchInfo info;
     if (w_type == WSG_W_BF16) {
         rc = launch_bf16<true>(static_cast<const uint16_t*>(w), ni, ki, static_cast<const float*>(x), debug_logits,
-                               keys, stream, &grid);
+                               keys, stream, &info);
     } else if (act_fmt == WSG_ACT_F32) {
-        rc = launch_q8_f32<true>(w, ni, ki, static_cast<const float*>(x), debug_logits, keys, stream, &grid);
+        rc = launch_q8_f32<true>(w, ni, ki, static_cast<const float*>(x), debug_logits, keys, stream, &info);
     } else if (act_fmt == WSG_ACT_Q8_0) {
-        rc = launch_q8_i8<kActQ8, false, true>(w, ni, ki, x, debug_logits, nullptr, keys, stream, &grid);
+        rc = launch_q8_i8<kActQ8, false, true>(w, ni, ki, x, debug_logits, nullptr, keys, stream, &info);
     } else {
-        rc = launch_q8_i8<kActRequant, false, true>(w, ni, ki, x, debug_logits, nullptr, keys, stream, &grid);
+        rc = launch_q8_i8<kActRequant, false, true>(w, ni, ki, x, debug_logits, nullptr, keys, stream, &info);
     }
     if (rc != WSG_OK) return rc;
-    return launch_argmax_stage2(keys, grid, idx_out, stream);
+    return launch_argmax_stage2(keys, info.grid, idx_out, stream);
 }
 
 int argmax_f32(const float* v, int64_t n, void* ws, size_t ws_bytes, int32_t* idx_out, hipStream_t stream) {

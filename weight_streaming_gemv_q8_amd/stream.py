@@ -1,0 +1,193 @@
+"""A whole-token batch-1 GEMV chain held resident in HBM, and its captured
+plan (emit_qwen38_generate, "Where the speed comes from": one launch per
+concatenated projection, one graph per token).
+
+Per layer the chain is ``len(shapes)`` GEMVs.  The first reads the layer's
+own input vector; each later GEMV reads the first K entries of the previous
+GEMV's output (the projections' data flow within a layer; the non-GEMV
+operators between them are not part of this path).  Every GEMV writes its
+own output buffer, so all intermediates stay readable after a replay.
+
+Weights live in one allocation; concatenated projections are filled part by
+part into consecutive row ranges.  How the weight values are produced is
+left to the caller (``fill_q8`` / ``fill_bf16`` callbacks that write f32
+rows into a device staging buffer); this module only lays the buffers out
+and drives the library.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Callable, List, Sequence, Tuple
+
+import torch
+
+import weight_streaming_gemv_q8_amd as wsg
+
+ALIGN = 256
+
+
+def _align(v: int, a: int = ALIGN) -> int:
+    return (v + a - 1) // a * a
+
+
+@dataclass(eq=False)
+class GemvSlot:
+    layer: int
+    index: int
+    n: int
+    k: int
+    w_offset: int      # byte offset into the weight allocation
+    w_bytes: int
+    x_ptr: int = 0     # f32 input (layer input or previous output)
+    xq_ptr: int = 0    # quantized-activation buffer (separate-requant mode only)
+    y: torch.Tensor = None
+
+
+class TokenStream:
+    """Buffers of one token's GEMV chain.
+
+    shapes: per-layer list of (rows n, k, parts) with parts the row counts of
+            the stacked projections.
+    wtype:  "q8_0" or "bf16".
+    deq:    0, 1 or 2 (the deq modes); deq 0/1 use int8 activations on every
+            layer GEMV.  BF16 chains ignore it.
+    requant: "fused" (the GEMV quantizes its f32 input itself) or
+            "separate" (a quantize_act_q8_0 launch before each GEMV).
+    """
+
+    def __init__(self, shapes: Sequence[Tuple[int, int, Tuple[int, ...]]], layers: int, wtype: str,
+                 deq: int = 0, requant: str = "fused", device: str = "cuda"):
+        if wtype not in ("q8_0", "bf16"):
+            raise ValueError("wtype must be q8_0 or bf16")
+        if requant not in ("fused", "separate"):
+            raise ValueError("requant must be fused or separate")
+        self.shapes = [(int(n), int(k), tuple(p)) for n, k, p in shapes]
+        self.layers = layers
+        self.wtype = wtype
+        self.deq = deq
+        self.requant = requant
+        self.device = device
+        for j in range(1, len(self.shapes)):
+            if self.shapes[j][1] > self.shapes[j - 1][0]:
+                raise ValueError("a GEMV's k exceeds the previous GEMV's rows")
+
+        self.slots: List[GemvSlot] = []
+        off = 0
+        for layer in range(layers):
+            for j, (n, k, _) in enumerate(self.shapes):
+                wb = wsg.q8_0_packed_bytes(n, k) if wtype == "q8_0" else n * k * 2
+                self.slots.append(GemvSlot(layer, j, n, k, off, wb))
+                off = _align(off + wb)
+        self.weight_bytes_alloc = off
+        self.weights = torch.empty(off, dtype=torch.uint8, device=device)
+        k0 = self.shapes[0][1]
+        self.inputs = torch.empty((layers, k0), dtype=torch.float32, device=device)
+        for s in self.slots:
+            s.y = torch.empty(s.n, dtype=torch.float32, device=device)
+        # chain the inputs
+        for i, s in enumerate(self.slots):
+            if s.index == 0:
+                s.x_ptr = self.inputs[s.layer].data_ptr()
+            else:
+                s.x_ptr = self.slots[i - 1].y.data_ptr()
+        self.xq = None
+        if wtype == "q8_0" and requant == "separate":
+            per = [_align(wsg.act_q8_0_bytes(k)) for _, k, _ in self.shapes]
+            self.xq = torch.empty(layers * sum(per), dtype=torch.uint8, device=device)
+            base = self.xq.data_ptr()
+            for s in self.slots:
+                s.xq_ptr = base
+                base += per[s.index]
+        self.plan = None
+
+    # ------------------------------------------------------------ sizes
+    def algorithmic_weight_bytes(self) -> int:
+        """Weight bytes per token at 34/32 (Q8_0) or 2 (BF16) bytes per weight."""
+        per = 0
+        for n, k, _ in self.shapes:
+            per += n * (k // 32) * 34 if self.wtype == "q8_0" else n * k * 2
+        return per * self.layers
+
+    def act_fmt(self) -> int:
+        if self.wtype == "bf16":
+            return wsg.ACT_F32
+        return wsg.act_fmt_for(self.deq, lm_head=False, fused_requant=(self.requant == "fused"))
+
+    # ------------------------------------------------------------ filling
+    def fill_weights(self, fill_rows: Callable[[int, int, int, int, torch.Tensor], None],
+                     stream=None) -> None:
+        """fill_rows(layer, matrix, part, rows, staging) writes rows x k f32
+        values of one projection part into `staging` (a device tensor); they
+        are then quantized (Q8_0) or rounded (BF16) into the part's row range."""
+        kmax = max(k for _, k, _ in self.shapes)
+        pmax = max(max(p) for _, _, p in self.shapes)
+        staging = torch.empty(pmax * kmax, dtype=torch.float32, device=self.device)
+        base = self.weights.data_ptr()
+        for s in self.slots:
+            _, k, parts = self.shapes[s.index]
+            r0 = 0
+            for pi, rows in enumerate(parts):
+                buf = staging[: rows * k]
+                fill_rows(s.layer, s.index, pi, rows, buf)
+                if self.wtype == "q8_0":
+                    dst = base + s.w_offset + r0 * wsg.q8_0_row_bytes(k)
+                    wsg.quantize_q8_0_weights(buf, rows, k, dst, stream)
+                else:
+                    dst = base + s.w_offset + r0 * k * 2
+                    wsg.convert_bf16(buf, rows * k, dst, stream)
+                r0 += rows
+        torch.cuda.synchronize()
+        del staging
+
+    def set_inputs(self, x_rows: torch.Tensor) -> None:
+        self.inputs.copy_(x_rows)
+
+    # ------------------------------------------------------------ calls
+    def _slot_ops(self, s: GemvSlot) -> List[wsg.OpDesc]:
+        w = self.weights.data_ptr() + s.w_offset
+        if self.wtype == "bf16":
+            return [wsg.op_gemv_bf16(w, s.n, s.k, s.x_ptr, s.y)]
+        fmt = self.act_fmt()
+        if fmt == wsg.ACT_Q8_0:
+            return [wsg.op_quantize_act(s.x_ptr, s.k, s.xq_ptr),
+                    wsg.op_gemv_q8_0(w, s.n, s.k, s.xq_ptr, wsg.ACT_Q8_0, s.y)]
+        return [wsg.op_gemv_q8_0(w, s.n, s.k, s.x_ptr, fmt, s.y)]
+
+    def ops(self) -> List[wsg.OpDesc]:
+        return [op for s in self.slots for op in self._slot_ops(s)]
+
+    def run_slot(self, i: int, stream=None) -> None:
+        """One GEMV of the chain, eagerly: the same calls the plan captured."""
+        for op in self._slot_ops(self.slots[i]):
+            if op.op == wsg.OP_GEMV_BF16:
+                wsg.gemv_bf16(op.w, op.n, op.k, op.x, op.y, stream=stream)
+            elif op.op == wsg.OP_QUANTIZE_ACT:
+                wsg.quantize_act_q8_0(op.x, op.k, op.y, stream=stream)
+            else:
+                wsg.gemv_q8_0(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
+
+    def run_eager(self, stream=None) -> None:
+        for i in range(len(self.slots)):
+            self.run_slot(i, stream)
+
+    def capture(self, stream=None) -> wsg.Plan:
+        if self.plan is not None:
+            self.plan.destroy()
+        self.plan = wsg.Plan(self.ops(), stream=stream)
+        return self.plan
+
+    def launch(self, stream=None) -> None:
+        if self.plan is None:
+            self.capture(stream)
+        self.plan.launch(stream)
+
+    def outputs(self):
+        return [s.y for s in self.slots]
+
+    def weight_ptr(self, i: int) -> int:
+        return self.weights.data_ptr() + self.slots[i].w_offset
+
+    def close(self) -> None:
+        if self.plan is not None:
+            self.plan.destroy()
+            self.plan = None
