@@ -146,6 +146,27 @@ def time_per_launch(ts, reps: int = 1):
     return [a / reps for a in acc]
 
 
+def time_plan(ts, persistent: bool, steps: int, warmup: int):
+    """Capture the token (graph of one node per call, or one persistent
+    kernel) and time `steps` replays with HIP events on the launch stream.
+    Returns (seconds per token, kernels per token)."""
+    import torch
+    plan = ts.capture(persistent=persistent)
+    kernels = plan.kernel_count
+    for _ in range(warmup):
+        ts.launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ts.launch()
+    e1.record()
+    torch.cuda.synchronize()
+    if persistent and plan.error():
+        raise RuntimeError("a barrier of the persistent token kernel timed out: results invalid")
+    return e0.elapsed_time(e1) / 1e3 / steps, kernels
+
+
 def read_ceiling(ts, reps: int = 3) -> float:
     import torch
 
@@ -228,6 +249,35 @@ def cpu_baseline(wl, deq: int, budget_s: float) -> dict:
     }
 
 
+# ------------------------------------------------------------ probes
+
+def run_probe(kind: str, nbytes: int) -> int:
+    import torch
+
+    import weight_streaming_gemv_q8_amd as wsg
+    nbytes = nbytes // 16 * 16
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty(nbytes if kind == "copy" else 16, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(65536, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        if kind == "copy":
+            wsg.copy_probe(src, dst, nbytes)
+        else:
+            wsg.read_probe(src, nbytes, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / 3
+    moved = nbytes * (2 if kind == "copy" else 1)
+    print(json.dumps({"probe": kind, "bytes_read_per_launch": nbytes,
+                      "bytes_written_per_launch": nbytes if kind == "copy" else 0,
+                      "us_per_launch": round(sec * 1e6, 1), "GBps": round(gbps(moved, sec), 1)}), flush=True)
+    return 0
+
+
 # ------------------------------------------------------------ main
 
 def main() -> int:
@@ -238,10 +288,18 @@ def main() -> int:
     ap.add_argument("--workload", default="dense27b_q8_0_64L")
     ap.add_argument("--deq", type=int, default=0, choices=(0, 1, 2))
     ap.add_argument("--requant", default="fused", choices=("fused", "separate"))
+    ap.add_argument("--plan", default="graph", choices=("persistent", "graph"),
+                    help="one resident kernel per token, or a graph node per GEMV")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the deq-2 line and the read ceiling")
+    ap.add_argument("--probe", choices=("copy", "read"),
+                    help="only run the copy (or read) probe over --probe-bytes, 3 launches: a kernel of known "
+                         "traffic for calibrating hardware byte counters")
+    ap.add_argument("--probe-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
+    if args.probe:
+        return run_probe(args.probe, args.probe_bytes)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU step (see the design notes on "
@@ -264,80 +322,70 @@ def main() -> int:
     ts = build_stream(wl, args.deq, args.requant)
     alg_bytes = ts.algorithmic_weight_bytes()
     act_fmt = ts.act_fmt()
-    plan = ts.capture()
-    kernels_per_token = plan.kernel_count
-    log(f"captured plan: {kernels_per_token} kernels per token")
+    persistent = args.plan == "persistent"
+    if persistent and (wl.wtype != "q8_0" or args.requant != "fused"):
+        print("the persistent plan runs Q8_0 streams with fused requantization (or f32 activations)",
+              file=sys.stderr)
+        return 2
 
-    for _ in range(args.warmup):
-        ts.launch()
-    torch.cuda.synchronize()
-
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        ts.launch()
-    e1.record()
-    torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) / 1e3 / args.steps
+    sec, kernels_per_token = time_plan(ts, persistent, args.steps, args.warmup)
     value = gbps(alg_bytes, sec)
-    log(f"timed {args.steps} steps: {sec * 1e6:.1f} us per token, {value:.1f} GB/s")
+    log(f"{args.plan} plan, {kernels_per_token} kernel(s) per token: timed {args.steps} steps: "
+        f"{sec * 1e6:.1f} us per token, {value:.1f} GB/s")
 
-    # dominant kernel: group the launches by kernel instantiation
-    per = time_per_launch(ts)
-    groups = {}
     wtype_code = wsg.W_Q8_0 if wl.wtype == "q8_0" else wsg.W_BF16
-    for s, t in zip(ts.slots, per):
-        cfg = wsg.gemv_config(wtype_code, act_fmt, s.n, s.k)
-        label = kernel_label(wl.wtype, act_fmt, cfg)
-        bpl = s.n * (s.k // 32) * 34 if wl.wtype == "q8_0" else s.n * s.k * 2
-        g = groups.setdefault(label, {"t": 0.0, "bytes": 0, "launches": 0})
-        g["t"] += t
-        g["bytes"] += bpl
-        g["launches"] += 1
-    dom = max(groups, key=lambda k: groups[k]["t"])
-    g = groups[dom]
-    achieved = gbps(g["bytes"] / g["launches"], g["t"] / g["launches"])
-    traffic = read_traffic(dom)
-    roofline = {
-        "bound": "hbm",
-        "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": traffic,
-        "kernel": dom,
-        "launches_per_token": g["launches"],
-        "bytes_per_launch": g["bytes"] // g["launches"],
-        "us_per_launch": round(g["t"] / g["launches"] * 1e6, 2),
-    }
-    log(f"dominant kernel {dom}: {roofline['us_per_launch']} us/launch, {achieved:.1f} GB/s")
-    kernel_sum = sum(per)
+    if persistent:
+        # one launch per token: the dominant kernel is the whole stream
+        roofline = {
+            "bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": read_traffic("stream_kernel"),
+            "kernel": "stream_kernel (whole token, " + ("f32 activations" if act_fmt == wsg.ACT_F32
+                                                        else "int8 activations, fused requantization") + ")",
+            "launches_per_token": 1, "bytes_per_launch": alg_bytes, "us_per_launch": round(sec * 1e6, 1),
+        }
+    else:
+        # group the launches by kernel instantiation; HIP events around each
+        per = time_per_launch(ts)
+        groups = {}
+        for slot, t in zip(ts.slots, per):
+            cfg = wsg.gemv_config(wtype_code, act_fmt, slot.n, slot.k)
+            label = kernel_label(wl.wtype, act_fmt, cfg)
+            bpl = slot.n * (slot.k // 32) * 34 if wl.wtype == "q8_0" else slot.n * slot.k * 2
+            g = groups.setdefault(label, {"t": 0.0, "bytes": 0, "launches": 0})
+            g["t"] += t
+            g["bytes"] += bpl
+            g["launches"] += 1
+        dom = max(groups, key=lambda kk: groups[kk]["t"])
+        g = groups[dom]
+        achieved = gbps(g["bytes"] / g["launches"], g["t"] / g["launches"])
+        roofline = {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": read_traffic(dom), "kernel": dom,
+            "launches_per_token": g["launches"], "bytes_per_launch": g["bytes"] // g["launches"],
+            "us_per_launch": round(g["t"] / g["launches"] * 1e6, 2),
+        }
+    log(f"dominant kernel {roofline['kernel']}: {roofline['us_per_launch']} us/launch, "
+        f"{roofline['achieved']} GB/s")
 
     extras = {}
     if not args.no_extras:
+        other = "graph" if persistent else "persistent"
+        if wl.wtype == "q8_0" and args.requant == "fused":
+            sec_o, k_o = time_plan(ts, not persistent, args.steps, args.warmup)
+            extras[f"{other}_plan"] = {"us_per_token": round(sec_o * 1e6, 1), "GBps": round(gbps(alg_bytes, sec_o), 1),
+                                       "kernels_per_token": k_o}
+            log(f"{other} plan: {sec_o * 1e6:.1f} us per token")
         extras["read_ceiling_GBps"] = round(read_ceiling(ts), 1)
         log(f"read ceiling {extras['read_ceiling_GBps']} GB/s")
+        if wl.wtype == "q8_0" and args.deq != 2:
+            # the same stream with f32 activations (deq 2), same weights
+            ts.deq = 2
+            sec2, _ = time_plan(ts, persistent, args.steps, args.warmup)
+            extras["deq2"] = {"us_per_token": round(sec2 * 1e6, 1), "GBps": round(gbps(alg_bytes, sec2), 1),
+                              "frac_of_peak": round(gbps(alg_bytes, sec2) / HBM_PEAK_GBPS, 4)}
+            log(f"deq 2: {sec2 * 1e6:.1f} us per token")
+            ts.deq = args.deq
     ts.close()
-
-    if not args.no_extras and wl.wtype == "q8_0" and args.deq != 2:
-        # the same stream with f32 activations (deq 2), same weights
-        ts.deq = 2
-        ts.capture()
-        for _ in range(max(1, args.warmup)):
-            ts.launch()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.steps):
-            ts.launch()
-        e1.record()
-        torch.cuda.synchronize()
-        sec2 = e0.elapsed_time(e1) / 1e3 / args.steps
-        extras["deq2"] = {"us_per_token": round(sec2 * 1e6, 1), "GBps": round(gbps(alg_bytes, sec2), 1),
-                          "frac_of_peak": round(gbps(alg_bytes, sec2) / HBM_PEAK_GBPS, 4)}
-        log(f"deq 2: {sec2 * 1e6:.1f} us per token")
-        ts.close()
-        ts.deq = args.deq
 
     del ts
     torch.cuda.empty_cache()
@@ -372,11 +420,11 @@ def main() -> int:
             "activation_quantization": ("fused into each GEMV" if args.requant == "fused" else "separate launch")
             if act_fmt != wsg.ACT_F32 else "none (f32 activations)",
             "kernels_per_token": kernels_per_token,
+            "plan": args.plan,
         },
         "us_per_token": round(sec * 1e6, 1),
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "tok_per_s_equiv": round(1.0 / sec, 1),
-        "kernel_time_sum_us": round(kernel_sum * 1e6, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -144,12 +144,25 @@ int gemv_bf16(const uint16_t* w, int64_t n, int64_t k, const float* x, float* y,
 int gemv_q8_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act_fmt, float* y,
               int32_t* debug_block_dots, hipStream_t stream);
 
-/* Launch configuration a gemv_bf16 / gemv_q8_0 / lm_head_argmax call of this
- * shape would use on the current device: waves per workgroup, waves that
- * share one row (split-K factor), workgroups in the grid and dynamic LDS
- * bytes (outputs nullable).  For tooling; launches nothing. */
-int wsg_gemv_config(int w_type, int act_fmt, int64_t n, int64_t k, int* waves, int* split, int* grid,
-                    int64_t* lds_bytes);
+/* Launch configuration a gemv_bf16 / gemv_q8_0 call of this shape would use
+ * on the current device: waves per workgroup, waves that share one row
+ * (split-K factor), chunks loaded ahead per wave (unroll), workgroups in the
+ * grid and dynamic LDS bytes (outputs nullable).  For tooling; launches
+ * nothing. */
+int wsg_gemv_config(int w_type, int act_fmt, int64_t n, int64_t k, int* waves, int* split, int* unroll,
+                    int* grid, int64_t* lds_bytes);
+
+/* Tuning knobs for measurement sweeps (process-wide; 0 restores the
+ * automatic choice).  WSG_TUNE_SPLITK: waves that share one row (1, 2 or
+ * 4).  WSG_TUNE_WG_PER_CU: cap on workgroups per CU in the persistent grid.
+ * WSG_TUNE_WAVES: waves per workgroup (4, 8 or 16).  WSG_TUNE_UNROLL:
+ * chunks each wave loads ahead (2, 4 or 8; the f32 path 1, 2 or 4).  The
+ * debug and argmax variants keep their default unroll.  Calls already
+ * captured into a plan keep the configuration they were captured with.
+ * Returns WSG_ERR_MODE for an unknown knob, WSG_ERR_SHAPE for a bad
+ * value. */
+enum { WSG_TUNE_SPLITK = 0, WSG_TUNE_WG_PER_CU = 1, WSG_TUNE_WAVES = 2, WSG_TUNE_UNROLL = 3 };
+int wsg_tune(int knob, int value);
 
 /* ------------------------------------------------- LM head + argmax ---
  * The LM-head GEMV (as gemv_bf16 / gemv_q8_0, w_type selects) fused with
@@ -204,6 +217,24 @@ typedef struct wsg_plan wsg_plan;
  * only; it must not be capturing already. */
 int wsg_plan_create(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_plan** out);
 int wsg_plan_launch(wsg_plan* plan, hipStream_t stream);
+
+/* Persistent whole-token plan: the same descriptors (Q8_0 GEMVs only, all
+ * with WSG_ACT_F32_REQUANT or all with WSG_ACT_F32; f32 inputs) executed by
+ * ONE kernel
+ * launch per replay, captured as a one-node hipGraph.  Every workgroup stays
+ * resident for the whole token; a grid-wide barrier separates an op from the
+ * earlier ops whose output it reads (or whose buffers it overwrites), and
+ * each workgroup requests the next matrix's weights before it waits there,
+ * so the weight stream does not drain between GEMVs.  Results equal the
+ * eager calls' to the same tolerances (the split-K factor per op may
+ * differ).  The plan owns a small device allocation (descriptor table and
+ * barrier state).  A barrier wait that exceeds its spin limit makes the
+ * kernel give up rather than hang; wsg_plan_error reports it. */
+int wsg_plan_create_persistent(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_plan** out);
+
+/* *flag = 1 if a persistent plan's barrier ever timed out (its outputs are
+ * then invalid), else 0.  Synchronizes the device. */
+int wsg_plan_error(wsg_plan* plan, int* flag);
 int wsg_plan_destroy(wsg_plan* plan);
 /* Number of kernel launches one replay makes. */
 int wsg_plan_kernel_count(const wsg_plan* plan);

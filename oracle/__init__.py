@@ -52,6 +52,8 @@ def lib():
                    "orc_bf16_to_f64_array"):
             getattr(L, nm).restype = None
             getattr(L, nm).argtypes = [vp, i64, vp]
+        L.orc_q8_code_array.restype = None
+        L.orc_q8_code_array.argtypes = [vp, vp, i64, vp]
         L.orc_quantize_q8_0.restype = ctypes.c_int
         L.orc_quantize_q8_0.argtypes = [vp, i64, i64, vp, vp]
         L.orc_gemv_q8_act_q8.restype = ctypes.c_int
@@ -112,6 +114,17 @@ def quantize_q8_0(x: np.ndarray):
     if rc != 0:
         raise ValueError(f"orc_quantize_q8_0 failed ({rc})")
     return d, q
+
+
+def q8_codes(v, d16) -> np.ndarray:
+    """Per-value Q8_0 codes against given fp16 scales (the quantizer's inner rule)."""
+    v = _c(v, np.float32)
+    d16 = _c(d16, np.uint16)
+    assert v.shape == d16.shape
+    out = np.empty(v.shape, dtype=np.int8)
+    if v.size:
+        lib().orc_q8_code_array(v.ctypes.data, d16.ctypes.data, v.size, out.ctypes.data)
+    return out
 
 
 # ------------------------------------------------------------------ O3-O5

@@ -150,6 +150,9 @@ double orc_bf16_to_f64(uint16_t h) {
 }
 
 /* Element-wise array forms of the two encoders and decoders. */
+int orc_q8_code(float v, uint16_t d16);
+void orc_q8_code_array(const float* v, const uint16_t* d16, int64_t n, int8_t* out);
+
 void orc_f32_to_f16_array(const float* x, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_f16(x[i]);
 }
@@ -167,7 +170,22 @@ void orc_bf16_to_f64_array(const uint16_t* h, int64_t n, double* out) {
 }
 
 /* ------------------------------------------------------------------ O2 --
- * Q8_0 block quantizer, for weights (offline) and activations (per call).
+ * One Q8_0 code: the fp32 quotient v / d (IEEE divide by the stored fp16
+ * scale), rounded half away from zero, clamped to [-127, 127].  d16 must be
+ * a positive finite fp16 value. */
+int orc_q8_code(float v, uint16_t d16) {
+    float df = (float)orc_f16_to_f64(d16); /* exact */
+    float r = roundf(v / df);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int)r;
+}
+
+void orc_q8_code_array(const float* v, const uint16_t* d16, int64_t n, int8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = (int8_t)orc_q8_code(v[i], d16[i]);
+}
+
+/* Q8_0 block quantizer, for weights (offline) and activations (per call).
  * rows x k floats, k % 32 == 0; writes d[rows][k/32] (fp16 bits) and
  * q[rows][k].  Returns 0, or -1 on a bad shape, -2 on a non-finite input
  * or an fp16 scale overflow (both outside the contract).
@@ -195,12 +213,7 @@ int orc_quantize_q8_0(const float* x, int64_t rows, int64_t k, uint16_t* d, int8
                 continue;
             }
             d[r * nb + b] = d16;
-            for (int i = 0; i < 32; ++i) {
-                float v = roundf(xb[i] / df); /* fp32 divide, half away from zero */
-                if (v > 127.0f) v = 127.0f;
-                if (v < -127.0f) v = -127.0f;
-                qb[i] = (int8_t)v;
-            }
+            for (int i = 0; i < 32; ++i) qb[i] = (int8_t)orc_q8_code(xb[i], d16);
         }
     }
     return 0;

@@ -62,6 +62,42 @@ def test_replay_equals_eager_q8(gpu_lib, deq, requant):
     ts.close()
 
 
+@pytest.mark.parametrize("wl_name,layers,deq", [("qwen3_8b_q8_0_36L", 3, 0), ("qwen3_8b_q8_0_36L", 2, 2),
+                                                ("dense27b_q8_0_64L", 2, 0), ("dense27b_q8_0_64L", 2, 2)])
+def test_persistent_replay_equals_eager(gpu_lib, wl_name, layers, deq):
+    """The whole token in one resident kernel: the same rows reduced in the
+    same order as the eager calls, so every output is bit-identical, on two
+    replays, and no barrier timed out."""
+    wl = {w.name: w for w in W.ALL}[wl_name]
+    ts, _ = _stream(wl, layers, deq=deq)
+    ts.run_eager()
+    eager = _snapshot(ts)
+    for y in ts.outputs():
+        y.fill_(np.nan)
+    plan = ts.capture(persistent=True)
+    assert plan.kernel_count == 1
+    ts.launch()
+    first = _snapshot(ts)
+    for y in ts.outputs():
+        y.fill_(np.nan)
+    ts.launch()
+    second = _snapshot(ts)
+    assert not plan.error()
+    for i, (a, b, c) in enumerate(zip(eager, first, second)):
+        assert np.array_equal(a, b), f"slot {i}: persistent differs from eager"
+        assert np.array_equal(b, c), f"slot {i}: replays differ"
+    ts.close()
+
+
+def test_persistent_plan_rejects_unsupported_ops(gpu_lib):
+    wsg = gpu_lib
+    ts, _ = _stream(W.QWEN3_0P6B_BF16, 1)
+    with pytest.raises(wsg.WsgError) as e:
+        ts.capture(persistent=True)
+    assert e.value.status == wsg.ERR_MODE
+    ts.close()
+
+
 def test_replay_equals_eager_bf16(gpu_lib):
     ts, _ = _stream(W.QWEN3_0P6B_BF16, 3)
     ts.run_eager()

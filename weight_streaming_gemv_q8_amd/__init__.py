@@ -36,8 +36,9 @@ MAX_K_F32ACT = 36864
 EXPORTS = (
     "wsg_status_str", "wsg_version", "q8_0_row_bytes", "q8_0_packed_bytes", "pack_q8_0",
     "quantize_q8_0_weights", "convert_bf16", "act_q8_0_bytes", "quantize_act_q8_0", "gemv_bf16",
-    "gemv_q8_0", "wsg_gemv_config", "wsg_argmax_ws_bytes", "lm_head_argmax", "argmax_f32", "wsg_plan_create",
-    "wsg_plan_launch", "wsg_plan_destroy", "wsg_plan_kernel_count", "wsg_read_probe",
+    "gemv_q8_0", "wsg_gemv_config", "wsg_tune", "wsg_argmax_ws_bytes", "lm_head_argmax", "argmax_f32", "wsg_plan_create",
+    "wsg_plan_launch", "wsg_plan_create_persistent", "wsg_plan_error", "wsg_plan_destroy", "wsg_plan_kernel_count",
+    "wsg_read_probe",
     "wsg_copy_probe",
 )
 
@@ -82,12 +83,15 @@ def lib():
             "gemv_bf16": (i32, [vp, i64, i64, vp, vp, vp]),
             "gemv_q8_0": (i32, [vp, i64, i64, vp, i32, vp, vp, vp]),
             "wsg_gemv_config": (i32, [i32, i32, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
-                                       ctypes.POINTER(i32), ctypes.POINTER(i64)]),
+                                       ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i64)]),
+            "wsg_tune": (i32, [i32, i32]),
             "wsg_argmax_ws_bytes": (i64, []),
             "lm_head_argmax": (i32, [vp, i32, i64, i64, vp, i32, vp, ctypes.c_size_t, vp, vp, vp]),
             "argmax_f32": (i32, [vp, i64, vp, ctypes.c_size_t, vp, vp]),
             "wsg_plan_create": (i32, [ctypes.POINTER(OpDesc), i32, vp, ctypes.POINTER(vp)]),
             "wsg_plan_launch": (i32, [vp, vp]),
+            "wsg_plan_create_persistent": (i32, [ctypes.POINTER(OpDesc), i32, vp, ctypes.POINTER(vp)]),
+            "wsg_plan_error": (i32, [vp, ctypes.POINTER(i32)]),
             "wsg_plan_destroy": (i32, [vp]),
             "wsg_plan_kernel_count": (i32, [vp]),
             "wsg_read_probe": (i32, [vp, i64, vp, i32, vp]),
@@ -181,11 +185,19 @@ def gemv_q8_0(w_packed, n: int, k: int, x, act_fmt: int, y, debug_block_dots=Non
 
 def gemv_config(w_type: int, act_fmt: int, n: int, k: int) -> dict:
     """Launch configuration the library uses for this call shape."""
-    w, s, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    w, s, u, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     lds = ctypes.c_int64()
     _check("wsg_gemv_config", lib().wsg_gemv_config(w_type, act_fmt, n, k, ctypes.byref(w), ctypes.byref(s),
-                                                    ctypes.byref(g), ctypes.byref(lds)))
-    return {"waves": w.value, "split": s.value, "grid": g.value, "lds_bytes": lds.value}
+                                                    ctypes.byref(u), ctypes.byref(g), ctypes.byref(lds)))
+    return {"waves": w.value, "split": s.value, "unroll": u.value, "grid": g.value, "lds_bytes": lds.value}
+
+
+TUNE_SPLITK, TUNE_WG_PER_CU, TUNE_WAVES, TUNE_UNROLL = 0, 1, 2, 3
+
+
+def tune(knob: int, value: int) -> None:
+    """Process-wide launch-configuration override for sweeps (0 = automatic)."""
+    _check("wsg_tune", lib().wsg_tune(knob, value))
 
 
 def lm_head_argmax(w, w_type: int, n: int, k: int, x, act_fmt: int, ws, ws_bytes: int, idx_out,
@@ -219,14 +231,23 @@ def op_lm_head_argmax(w, w_type, n, k, x, act_fmt, ws, ws_bytes, idx_out, debug_
 
 
 class Plan:
-    """A captured whole-token sequence of calls (hipGraph), replayed by launch()."""
+    """A captured whole-token sequence of calls (hipGraph), replayed by launch().
+    persistent=True runs the whole sequence in one resident kernel launch."""
 
-    def __init__(self, ops: Sequence[OpDesc], stream=None):
+    def __init__(self, ops: Sequence[OpDesc], stream=None, persistent: bool = False):
         arr = (OpDesc * len(ops))(*ops)
         h = ctypes.c_void_p()
-        _check("wsg_plan_create", lib().wsg_plan_create(arr, len(ops), _stream(stream), ctypes.byref(h)))
+        fn = "wsg_plan_create_persistent" if persistent else "wsg_plan_create"
+        _check(fn, getattr(lib(), fn)(arr, len(ops), _stream(stream), ctypes.byref(h)))
         self._h = h
         self.n_ops = len(ops)
+        self.persistent = persistent
+
+    def error(self) -> bool:
+        """True if a persistent plan's barrier timed out (outputs invalid); synchronizes."""
+        f = ctypes.c_int()
+        _check("wsg_plan_error", lib().wsg_plan_error(self._h, ctypes.byref(f)))
+        return bool(f.value)
 
     @property
     def kernel_count(self) -> int:

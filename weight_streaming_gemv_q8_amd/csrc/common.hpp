@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "q8rule.hpp"
+
 namespace wsg {
 
 constexpr int kWave = 64;
@@ -36,6 +38,29 @@ __host__ __device__ inline int64_t packed_row_bytes(int64_t k) {
 // --------------------------------------------------------------- loads
 // Weight stream loads: 16 bytes per lane, optionally marked non-temporal so
 // the stream does not evict the (re-used) activation from L2.
+// A pointer known to address global memory: loads through it compile to
+// global_* instructions even when the pointer itself was read from memory.
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+
+template <bool NT>
+__device__ inline int4v load16(gptr<void> p) {
+    if constexpr (NT) {
+        return __builtin_nontemporal_load(reinterpret_cast<gptr<int4v>>(p));
+    } else {
+        return *reinterpret_cast<gptr<int4v>>(p);
+    }
+}
+
+template <bool NT>
+__device__ inline uint16_t load_u16(gptr<void> p) {
+    if constexpr (NT) {
+        return __builtin_nontemporal_load(reinterpret_cast<gptr<uint16_t>>(p));
+    } else {
+        return *reinterpret_cast<gptr<uint16_t>>(p);
+    }
+}
+
 template <bool NT>
 __device__ inline int4v load16(const void* p) {
     if constexpr (NT) {
@@ -70,22 +95,32 @@ __device__ inline uint16_t float_to_half_bits_rne(float x) {
 // ------------------------------------------------------ Q8_0 block quantizer
 // The Q8_0 rule for one 32-value block, in fp32 as the oracle takes it:
 // d = fp16_RNE(max|v| / 127) (IEEE divide), q_i = clamp(round half away from
-// zero of v_i / float(d), -127, 127) (IEEE divide by the stored scale); a
-// zero scale stores d = +0 and q = 0.
-__device__ inline float q8_round_half_away(float v) {
-    const float t = __builtin_truncf(v);
-    const float frac = v - t;  // exact for |v| < 2^23
-    return (__builtin_fabsf(frac) >= 0.5f) ? t + __builtin_copysignf(1.0f, v) : t;
-}
-
-__device__ inline int8_t q8_code(float v, float d) {
-    float r = q8_round_half_away(v / d);
-    r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
-    return (int8_t)(int)r;
-}
-
-// Scale bits for a block whose largest magnitude is amax.
+// zero of v_i / float(d), -127, 127) (IEEE divide by the stored scale,
+// decided without a per-value divide by q8_code_exact); a zero scale stores
+// d = +0 and q = 0.  Returns the scale bits.
 __device__ inline uint16_t q8_scale_bits(float amax) { return float_to_half_bits_rne(amax / 127.0f); }
+
+__device__ inline uint16_t q8_quantize_block_bits(const float* v, int8_t* q) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    const uint16_t d16 = q8_scale_bits(amax);
+    const float d = half_bits_to_float(d16);
+    if (d == 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) q[i] = 0;
+        return 0;
+    }
+    const float r = 1.0f / d;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) q[i] = (int8_t)q8_code_exact(v[i], d, r);
+    return d16;
+}
+
+// The same, returning float(d) (0 for a zero block).
+__device__ inline float q8_quantize_block(const float* v, int8_t* q) {
+    return half_bits_to_float(q8_quantize_block_bits(v, q));
+}
 
 // ------------------------------------------------------- wave reductions
 // Butterfly sums over the 64 lanes of a wave; every lane ends with the same

@@ -20,9 +20,12 @@
 //    lane keeps 2U 16-byte weight loads in flight.
 //  * No MFMA: at batch 1 there is one multiply-add per weight and no reuse.
 #include "common.hpp"
+#include "gemv_device.hpp"
 #include "internal.hpp"
 
+#include <atomic>
 #include <cstdlib>
+#include <type_traits>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -30,141 +33,13 @@
 namespace wsg {
 namespace {
 
-constexpr int kActQ8 = 0, kActF32 = 1, kActRequant = 2;  // = WSG_ACT_*
-
-// ------------------------------------------------------------------ LDS
-// Layouts of the staged activation (per 2048-weight chunk c, lane l):
-//  int8 paths : int4v q[C][2][64]   (half h of block 64c+l), float dx[C*64]
-//  f32 path   : float4v x[C][8][64] (values 4g..4g+3 of block 64c+l)
-//  bf16 path  : float4v x[C'][2][2][64] over 1024-element chunks:
-//               values 1024c + 512h + 8l + 4j .. +3
-
-__host__ __device__ inline size_t lds_q8act_bytes(int C) { return (size_t)C * (2 * kWave * 16 + kWave * 4); }
-__host__ __device__ inline size_t lds_f32act_bytes(int C) { return (size_t)C * 8 * kWave * 16; }
-__host__ __device__ inline int bf16_chunks(int k) { return (k + 1023) / 1024; }
-__host__ __device__ inline size_t lds_bf16_bytes(int k) { return (size_t)bf16_chunks(k) * 4 * kWave * 16; }
-// tail of the LDS allocation: S partial sums per tile and the argmax keys
-template <int WAVES>
-__host__ __device__ constexpr size_t lds_tail_bytes() {
-    return WAVES * sizeof(float) + WAVES * sizeof(uint64_t) + 16;
-}
-
-// Stage a planar Q8_0 activation (q[k] then fp16 d[k/32]).
-__device__ inline void stage_q8(const void* __restrict__ xin, int k, int C, int4v* lds_q, float* lds_dx) {
-    const int NB = k / kBlock;
-    const int8_t* q = static_cast<const int8_t*>(xin);
-    const uint16_t* d = reinterpret_cast<const uint16_t*>(q + k);
-    // unit u = (c*2 + h)*64 + l  <-  block b = 64c + l, half h
-    for (int u = threadIdx.x; u < C * 2 * kWave; u += blockDim.x) {
-        const int l = u % kWave, ch = u / kWave, h = ch & 1, c = ch >> 1;
-        const int b = c * kWave + l;
-        if (b < NB) lds_q[u] = *reinterpret_cast<const int4v*>(q + (int64_t)b * kBlock + 16 * h);
-    }
-    for (int b = threadIdx.x; b < NB; b += blockDim.x) lds_dx[b] = half_bits_to_float(d[b]);
-}
-
-// Quantize an f32 activation into LDS with the Q8_0 rule (the same device
-// functions and the same bytes as quantize_act_q8_0).
-__device__ inline void stage_requant(const float* __restrict__ x, int k, int4v* lds_q, float* lds_dx) {
-    const int NB = k / kBlock;
-    for (int b = threadIdx.x; b < NB; b += blockDim.x) {
-        float v[32];
-        const float4v* s4 = reinterpret_cast<const float4v*>(x + (int64_t)b * kBlock);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4v t = s4[i];
-            v[4 * i + 0] = t.x;
-            v[4 * i + 1] = t.y;
-            v[4 * i + 2] = t.z;
-            v[4 * i + 3] = t.w;
-        }
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-        const float d = half_bits_to_float(q8_scale_bits(amax));
-        int8_t codes[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) codes[i] = (d == 0.0f) ? (int8_t)0 : q8_code(v[i], d);
-        const int c = b / kWave, l = b % kWave;
-        int4v lo, hi;
-        __builtin_memcpy(&lo, codes, 16);
-        __builtin_memcpy(&hi, codes + 16, 16);
-        lds_q[(c * 2 + 0) * kWave + l] = lo;
-        lds_q[(c * 2 + 1) * kWave + l] = hi;
-        lds_dx[b] = d;
-    }
-}
-
-// Stage an f32 activation for the dequantizing path.
-__device__ inline void stage_f32(const float* __restrict__ x, int k, float4v* lds_x) {
-    const int n4 = k / 4;
-    // global float4 index v -> block b = v/8, group g = v%8 -> LDS unit (c*8+g)*64 + l
-    for (int v = threadIdx.x; v < n4; v += blockDim.x) {
-        const int b = v >> 3, g = v & 7, c = b / kWave, l = b % kWave;
-        lds_x[(c * 8 + g) * kWave + l] = reinterpret_cast<const float4v*>(x)[v];
-    }
-}
-
-// Stage an f32 activation for the bf16 path.
-__device__ inline void stage_bf16x(const float* __restrict__ x, int k, float4v* lds_x) {
-    const int n4 = k / 4;
-    // element e = 1024c + 512h + 8l + 4j  <->  float4 index v = e/4
-    for (int v = threadIdx.x; v < n4; v += blockDim.x) {
-        const int e = 4 * v;
-        const int c = e >> 10, h = (e >> 9) & 1, l = (e >> 3) & 63, j = (e >> 2) & 1;
-        lds_x[((c * 2 + h) * 2 + j) * kWave + l] = reinterpret_cast<const float4v*>(x)[v];
-    }
-}
-
-// Epilogue shared by all paths: combine split-K partials in part order,
-// then store y (and/or fold the row into the workgroup's argmax key).
-template <int WAVES, int S, bool ARGMAX>
-__device__ inline void finish_row(float acc, int row, int n, int lane, int wave, float* lds_part, float* y,
-                                  uint64_t& best) {
-    constexpr int GROUPS = WAVES / S;
-    (void)GROUPS;
-    const int part = wave % S;
-    float total = acc;
-    if constexpr (S > 1) {
-        if (lane == 0) lds_part[wave] = acc;
-        __syncthreads();
-        if (part == 0) {
-            total = lds_part[wave];
-#pragma unroll
-            for (int p = 1; p < S; ++p) total += lds_part[wave + p];
-        }
-        __syncthreads();
-    }
-    if (part == 0 && row < n) {
-        if constexpr (ARGMAX) {
-            const uint64_t key = argmax_key(total, (uint32_t)row);
-            best = key > best ? key : best;
-            if (y != nullptr && lane == 0) y[row] = total;
-        } else {
-            if (lane == 0) y[row] = total;
-        }
-    }
-}
-
-template <int WAVES>
-__device__ inline void write_block_key(uint64_t best, int lane, int wave, uint64_t* lds_key, uint64_t* keys) {
-    if (lane == 0) lds_key[wave] = best;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t m = lds_key[0];
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) m = lds_key[w] > m ? lds_key[w] : m;
-        keys[blockIdx.x] = m;
-    }
-}
-
 // ------------------------------------------------ Q8_0 x int8 (and requant)
 template <int WAVES, int S, int U, int ACT, bool NT, bool DEBUG, bool ARGMAX>
-__global__ void __launch_bounds__(WAVES * kWave)
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict__ xin, float* __restrict__ y,
              int32_t* __restrict__ dots, uint64_t* __restrict__ keys) {
     static_assert(WAVES % S == 0, "S must divide WAVES");
-    constexpr int GROUPS = WAVES / S;
+    static_assert(NT, "the weight stream is always loaded non-temporally");
     extern __shared__ __align__(16) uint8_t smem[];
     const int C = (int)chunk_count(k);
     const int NB = k / kBlock;
@@ -175,91 +50,45 @@ q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
     float* lds_dx = reinterpret_cast<float*>(smem + (size_t)C * 2 * kWave * 16);
     float* lds_part = reinterpret_cast<float*>(smem + lds_q8act_bytes(C));
     uint64_t* lds_key = reinterpret_cast<uint64_t*>(smem + ((lds_q8act_bytes(C) + WAVES * 4 + 15) & ~size_t(15)));
+    const int lane = threadIdx.x % kWave;
 
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int group = wave / S, part = wave % S;
+    const Sched sc(C, S, U, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
+    auto load = [&](Q8Regs<U>& r, int row, int m) { q8_load<U>(r, W, row_bytes, sc, nl, sbl, row, m); };
+    auto compute = [&](const Q8Regs<U>& r, int row, int m, float& acc) {
+        q8_i8_item<U, DEBUG>(r, sc, m, NB, lds_q, lds_dx, row, dots, acc);
+    };
 
+    Q8Regs<U> cur;
     if constexpr (ACT == kActRequant) {
-        stage_requant(static_cast<const float*>(xin), k, lds_q, lds_dx);
+        StageRequant<1> st;
+        st.issue(xin, k, C);
+        __builtin_amdgcn_sched_barrier(0);
+        if (sc.tiles_wg > 0 && sc.ipt > 0 && sc.row(0) < n) load(cur, sc.row(0), 0);
+        __builtin_amdgcn_sched_barrier(0);
+        st.commit(xin, k, C, lds_q, lds_dx);
     } else {
-        stage_q8(xin, k, C, lds_q, lds_dx);
+        StageQ8<4> st;
+        st.issue(xin, k, C);
+        __builtin_amdgcn_sched_barrier(0);
+        if (sc.tiles_wg > 0 && sc.ipt > 0 && sc.row(0) < n) load(cur, sc.row(0), 0);
+        __builtin_amdgcn_sched_barrier(0);
+        st.commit(xin, k, C, lds_q, lds_dx);
     }
     __syncthreads();
-
     uint64_t best = 0;
-    const int tiles = (n + GROUPS - 1) / GROUPS;
-    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const int row = tile * GROUPS + group;
-        float acc = 0.0f;
-        if (row < n) {
-            const uint8_t* rowp = W + (int64_t)row * row_bytes;
-            for (int c0 = part; c0 < C; c0 += S * U) {
-                int4v a[U], b[U];
-                uint16_t sc[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + u * S;
-                    a[u] = int4v{0, 0, 0, 0};
-                    b[u] = int4v{0, 0, 0, 0};
-                    sc[u] = 0;
-                    if (c < C) {
-                        const bool last = (c == C - 1);
-                        const int nbc = last ? nl : kChunkBlocks;
-                        const int sb = last ? sbl : 2 * kChunkBlocks;
-                        const uint8_t* cp = rowp + (int64_t)c * kFullChunkBytes;
-                        if (lane < nbc) {
-                            sc[u] = load_u16<NT>(cp + 2 * lane);
-                            a[u] = load16<NT>(cp + sb + 16 * lane);
-                            b[u] = load16<NT>(cp + sb + 16 * nbc + 16 * lane);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + u * S;
-                    if (c < C) {
-                        const int blk = c * kWave + lane;
-                        if (blk < NB) {
-                            const int4v xa = lds_q[(c * 2 + 0) * kWave + lane];
-                            const int4v xb = lds_q[(c * 2 + 1) * kWave + lane];
-                            int s = 0;
-                            s = __builtin_amdgcn_sdot4(a[u].x, xa.x, s, false);
-                            s = __builtin_amdgcn_sdot4(a[u].y, xa.y, s, false);
-                            s = __builtin_amdgcn_sdot4(a[u].z, xa.z, s, false);
-                            s = __builtin_amdgcn_sdot4(a[u].w, xa.w, s, false);
-                            s = __builtin_amdgcn_sdot4(b[u].x, xb.x, s, false);
-                            s = __builtin_amdgcn_sdot4(b[u].y, xb.y, s, false);
-                            s = __builtin_amdgcn_sdot4(b[u].z, xb.z, s, false);
-                            s = __builtin_amdgcn_sdot4(b[u].w, xb.w, s, false);
-                            if constexpr (DEBUG) dots[(int64_t)row * NB + blk] = s;
-                            const float t = half_bits_to_float(sc[u]) * lds_dx[blk];
-                            acc = __builtin_fmaf(t, (float)s, acc);
-                        }
-                    }
-                }
-            }
-            acc = wave_sum(acc);
-        }
+    const int wave = threadIdx.x / kWave;
+    row_loop(sc, cur, load, compute, [&](float acc, int row, bool) {
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
-    }
+    });
     if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
 }
 
-// ------------------------------------------------------ Q8_0 x f32 (deq)
-__device__ inline float dot4_i8_f32(int w, float4v x, float acc) {
-    acc = __builtin_fmaf((float)(int8_t)(w & 0xFF), x.x, acc);
-    acc = __builtin_fmaf((float)(int8_t)((w >> 8) & 0xFF), x.y, acc);
-    acc = __builtin_fmaf((float)(int8_t)((w >> 16) & 0xFF), x.z, acc);
-    acc = __builtin_fmaf((float)(int8_t)(w >> 24), x.w, acc);
-    return acc;
-}
-
 template <int WAVES, int S, int U, bool NT, bool ARGMAX>
-__global__ void __launch_bounds__(WAVES * kWave)
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restrict__ x, float* __restrict__ y,
               uint64_t* __restrict__ keys) {
     static_assert(WAVES % S == 0, "S must divide WAVES");
-    constexpr int GROUPS = WAVES / S;
+    static_assert(NT, "the weight stream is always loaded non-temporally");
     extern __shared__ __align__(16) uint8_t smem[];
     const int C = (int)chunk_count(k);
     const int NB = k / kBlock;
@@ -269,134 +98,87 @@ q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restri
     float4v* lds_x = reinterpret_cast<float4v*>(smem);
     float* lds_part = reinterpret_cast<float*>(smem + lds_f32act_bytes(C));
     uint64_t* lds_key = reinterpret_cast<uint64_t*>(smem + ((lds_f32act_bytes(C) + WAVES * 4 + 15) & ~size_t(15)));
+    const int lane = threadIdx.x % kWave;
 
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int group = wave / S, part = wave % S;
+    const Sched sc(C, S, U, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
+    auto load = [&](Q8Regs<U>& r, int row, int m) { q8_load<U>(r, W, row_bytes, sc, nl, sbl, row, m); };
+    auto compute = [&](const Q8Regs<U>& r, int, int m, float& acc) { q8_f32_item<U>(r, sc, m, NB, lds_x, acc); };
 
-    stage_f32(x, k, lds_x);
+    Q8Regs<U> cur;
+    StageF32<4> st;
+    st.issue(x, k);
+    __builtin_amdgcn_sched_barrier(0);
+    if (sc.tiles_wg > 0 && sc.ipt > 0 && sc.row(0) < n) load(cur, sc.row(0), 0);
+    __builtin_amdgcn_sched_barrier(0);
+    st.commit(x, k, lds_x);
     __syncthreads();
-
     uint64_t best = 0;
-    const int tiles = (n + GROUPS - 1) / GROUPS;
-    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const int row = tile * GROUPS + group;
-        float acc = 0.0f;
-        if (row < n) {
-            const uint8_t* rowp = W + (int64_t)row * row_bytes;
-            for (int c0 = part; c0 < C; c0 += S * U) {
-                int4v a[U], b[U];
-                uint16_t sc[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + u * S;
-                    a[u] = int4v{0, 0, 0, 0};
-                    b[u] = int4v{0, 0, 0, 0};
-                    sc[u] = 0;
-                    if (c < C) {
-                        const bool last = (c == C - 1);
-                        const int nbc = last ? nl : kChunkBlocks;
-                        const int sb = last ? sbl : 2 * kChunkBlocks;
-                        const uint8_t* cp = rowp + (int64_t)c * kFullChunkBytes;
-                        if (lane < nbc) {
-                            sc[u] = load_u16<NT>(cp + 2 * lane);
-                            a[u] = load16<NT>(cp + sb + 16 * lane);
-                            b[u] = load16<NT>(cp + sb + 16 * nbc + 16 * lane);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + u * S;
-                    if (c < C && c * kWave + lane < NB) {
-                        const float4v* xv = lds_x + (size_t)c * 8 * kWave + lane;
-                        float bs = 0.0f;
-                        bs = dot4_i8_f32(a[u].x, xv[0 * kWave], bs);
-                        bs = dot4_i8_f32(a[u].y, xv[1 * kWave], bs);
-                        bs = dot4_i8_f32(a[u].z, xv[2 * kWave], bs);
-                        bs = dot4_i8_f32(a[u].w, xv[3 * kWave], bs);
-                        bs = dot4_i8_f32(b[u].x, xv[4 * kWave], bs);
-                        bs = dot4_i8_f32(b[u].y, xv[5 * kWave], bs);
-                        bs = dot4_i8_f32(b[u].z, xv[6 * kWave], bs);
-                        bs = dot4_i8_f32(b[u].w, xv[7 * kWave], bs);
-                        acc = __builtin_fmaf(half_bits_to_float(sc[u]), bs, acc);
-                    }
-                }
-            }
-            acc = wave_sum(acc);
-        }
+    const int wave = threadIdx.x / kWave;
+    row_loop(sc, cur, load, compute, [&](float acc, int row, bool) {
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
-    }
+    });
     if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
 }
 
-// ---------------------------------------------------------- BF16 x f32
-__device__ inline float dot_bf16x8(int4v w, float4v x0, float4v x1, float acc) {
-    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.x << 16), x0.x, acc);
-    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.x & 0xFFFF0000u), x0.y, acc);
-    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.y << 16), x0.z, acc);
-    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.y & 0xFFFF0000u), x0.w, acc);
-    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.z << 16), x1.x, acc);
-    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.z & 0xFFFF0000u), x1.y, acc);
-    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.w << 16), x1.z, acc);
-    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.w & 0xFFFF0000u), x1.w, acc);
-    return acc;
-}
-
 template <int WAVES, int S, int U, bool NT, bool ARGMAX>
-__global__ void __launch_bounds__(WAVES * kWave)
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 bf16_kernel(const uint16_t* __restrict__ W, int n, int k, const float* __restrict__ x, float* __restrict__ y,
             uint64_t* __restrict__ keys) {
     static_assert(WAVES % S == 0, "S must divide WAVES");
-    constexpr int GROUPS = WAVES / S;
+    static_assert(NT, "the weight stream is always loaded non-temporally");
     extern __shared__ __align__(16) uint8_t smem[];
     const int C = bf16_chunks(k);
     float4v* lds_x = reinterpret_cast<float4v*>(smem);
     float* lds_part = reinterpret_cast<float*>(smem + lds_bf16_bytes(k));
     uint64_t* lds_key = reinterpret_cast<uint64_t*>(smem + ((lds_bf16_bytes(k) + WAVES * 4 + 15) & ~size_t(15)));
+    const int lane = threadIdx.x % kWave;
 
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int group = wave / S, part = wave % S;
-
-    stage_bf16x(x, k, lds_x);
-    __syncthreads();
-
-    uint64_t best = 0;
-    const int tiles = (n + GROUPS - 1) / GROUPS;
-    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const int row = tile * GROUPS + group;
-        float acc = 0.0f;
-        if (row < n) {
-            const uint16_t* rowp = W + (int64_t)row * k;
-            for (int c0 = part; c0 < C; c0 += S * U) {
-                int4v a[U], b[U];
+    const Sched sc(C, S, U, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
+    auto load = [&](Bf16Regs<U>& r, int row, int m) {
+        const uint16_t* rowp = W + (int64_t)row * k;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + u * S;
-                    a[u] = int4v{0, 0, 0, 0};
-                    b[u] = int4v{0, 0, 0, 0};
-                    if (c < C) {
-                        const int e0 = c * 1024 + 8 * lane;
-                        if (e0 < k) a[u] = load16<NT>(rowp + e0);
-                        if (e0 + 512 < k) b[u] = load16<NT>(rowp + e0 + 512);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + u * S;
-                    if (c < C) {
-                        const float4v* xv = lds_x + (size_t)c * 4 * kWave + lane;
-                        // out-of-range lanes hold zero weights and zero-staged x is not
-                        // guaranteed, so guard by element index
-                        const int e0 = c * 1024 + 8 * lane;
-                        if (e0 < k) acc = dot_bf16x8(a[u], xv[0 * kWave], xv[1 * kWave], acc);
-                        if (e0 + 512 < k) acc = dot_bf16x8(b[u], xv[2 * kWave], xv[3 * kWave], acc);
-                    }
-                }
+        for (int u = 0; u < U; ++u) {
+            const int c = sc.chunk(m, u);
+            if (c < C) {
+                // lanes past the end of a ragged row re-read its last 8
+                // elements (not divergent); compute skips them
+                const int e0 = c * 1024 + 8 * lane;
+                const int ea = e0 < k ? e0 : k - 8;
+                const int eb = e0 + 512 < k ? e0 + 512 : k - 8;
+                r.a[u] = load16<true>(rowp + ea);
+                r.b[u] = load16<true>(rowp + eb);
             }
-            acc = wave_sum(acc);
         }
+    };
+    auto compute = [&](const Bf16Regs<U>& r, int, int m, float& acc) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = sc.chunk(m, u);
+            if (c < C) {
+                const float4v* xv = lds_x + (size_t)c * 4 * kWave + lane;
+                const int e0 = c * 1024 + 8 * lane;
+                int4v wa = r.a[u], wb = r.b[u];
+                opaque(wa);
+                opaque(wb);
+                if (e0 < k) acc = dot_bf16x8(wa, xv[0 * kWave], xv[1 * kWave], acc);
+                if (e0 + 512 < k) acc = dot_bf16x8(wb, xv[2 * kWave], xv[3 * kWave], acc);
+            }
+        }
+    };
+
+    Bf16Regs<U> cur;
+    StageBf16x<4> st;
+    st.issue(x, k);
+    __builtin_amdgcn_sched_barrier(0);
+    if (sc.tiles_wg > 0 && sc.ipt > 0 && sc.row(0) < n) load(cur, sc.row(0), 0);
+    __builtin_amdgcn_sched_barrier(0);
+    st.commit(x, k, lds_x);
+    __syncthreads();
+    uint64_t best = 0;
+    const int wave = threadIdx.x / kWave;
+    row_loop(sc, cur, load, compute, [&](float acc, int row, bool) {
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
-    }
+    });
     if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
 }
 
@@ -461,21 +243,46 @@ const DeviceInfo& device_info() {
 
 namespace {
 
-// Optional tuning overrides, read once from the environment (0 = automatic):
-// WSG_TUNE_SPLITK (1, 2 or 4 waves per row), WSG_TUNE_WG_PER_CU (grid =
-// CUs x this, capped by occupancy).
+// Tuning overrides (0 = automatic): waves per row (split-K) and workgroups
+// per CU.  Initialized from WSG_TUNE_SPLITK / WSG_TUNE_WG_PER_CU, changed at
+// run time through wsg_tune().
 int env_int(const char* name) {
     const char* v = std::getenv(name);
     return v ? std::atoi(v) : 0;
 }
 
+std::atomic<int> g_tune_splitk{-1};
+std::atomic<int> g_tune_wg_per_cu{-1};
+std::atomic<int> g_tune_waves{-1};
+std::atomic<int> g_tune_unroll{-1};
+
+int tune_read(std::atomic<int>& slot, const char* env) {
+    int v = slot.load(std::memory_order_relaxed);
+    if (v < 0) {
+        v = env_int(env);
+        slot.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+int tune_waves() { return tune_read(g_tune_waves, "WSG_TUNE_WAVES"); }
+int tune_unroll() { return tune_read(g_tune_unroll, "WSG_TUNE_UNROLL"); }
+
 int tune_splitk() {
-    static const int v = env_int("WSG_TUNE_SPLITK");
+    int v = g_tune_splitk.load(std::memory_order_relaxed);
+    if (v < 0) {
+        v = env_int("WSG_TUNE_SPLITK");
+        g_tune_splitk.store(v, std::memory_order_relaxed);
+    }
     return v;
 }
 
 int tune_wg_per_cu() {
-    static const int v = env_int("WSG_TUNE_WG_PER_CU");
+    int v = g_tune_wg_per_cu.load(std::memory_order_relaxed);
+    if (v < 0) {
+        v = env_int("WSG_TUNE_WG_PER_CU");
+        g_tune_wg_per_cu.store(v, std::memory_order_relaxed);
+    }
     return v;
 }
 
@@ -496,26 +303,19 @@ int resident_per_cu(K kernel, int threads, size_t lds) {
     return blocks;
 }
 
+// Persistent grid: at most (CUs x resident workgroups) workgroups, sized so
+// that every workgroup walks the same number of row tiles (the last one at
+// most as many).  A workgroup streams only a few GB/s, so one extra tile on
+// some workgroups would stretch the whole launch by a tile's duration.
 int persistent_grid(int tiles, int per_cu) {
     const int cus = device_info().cus;
     const int forced = tune_wg_per_cu();
     if (forced > 0 && forced < per_cu) per_cu = forced;
-    int64_t g = (int64_t)cus * per_cu;
-    if (g > kMaxGrid) g = kMaxGrid;
-    if (g > tiles) g = tiles;
-    if (g > 8) g -= g % 8;  // whole rounds over the 8 XCDs
-    return g < 1 ? 1 : (int)g;
-}
-
-// Split-K factor: when a matrix has few rows per CU and long rows, several
-// waves share a row so that every CU still has enough independent streams.
-int choose_split(int64_t n, int64_t k, int waves) {
-    const int forced = tune_splitk();
-    if ((forced == 1 || forced == 2 || forced == 4) && forced <= waves) return forced;
-    const int64_t rows_per_cu = n / device_info().cus;
-    if (rows_per_cu < 16 && k >= 16384 && waves >= 4) return 4;
-    if (rows_per_cu < 32 && k >= 8192) return 2;
-    return 1;
+    int64_t gmax = (int64_t)cus * per_cu;
+    if (gmax > kMaxGrid) gmax = kMaxGrid;
+    if (tiles <= gmax) return tiles < 1 ? 1 : tiles;
+    const int64_t rounds = (tiles + gmax - 1) / gmax;
+    return (int)((tiles + rounds - 1) / rounds);
 }
 
 template <typename K>
@@ -527,92 +327,154 @@ void raise_lds_limit(K kernel, size_t lds) {
 
 // Launch configuration of one GEMV call (reported by wsg_gemv_config).
 struct LaunchInfo {
-    int waves = 0, split = 0, grid = 0;
+    int waves = 0, split = 0, unroll = 0, grid = 0;
     size_t lds = 0;
 };
 
-template <int WAVES, int S, int ACT, bool DEBUG, bool ARGMAX>
-int launch_q8_i8_s(const void* w, int n, int k, const void* x, float* y, int32_t* dots, uint64_t* keys,
-                   hipStream_t stream, LaunchInfo* info, bool run) {
-    constexpr int U = 4;
-    auto kern = q8_i8_kernel<WAVES, S, U, ACT, true, DEBUG, ARGMAX>;
-    const int C = (int)chunk_count(k);
-    const size_t lds = lds_q8act_bytes(C) + lds_tail_bytes<WAVES>();
-    raise_lds_limit(kern, lds);
-    const int tiles = (n + WAVES / S - 1) / (WAVES / S);
-    const int grid = persistent_grid(tiles, resident_per_cu(kern, WAVES * kWave, lds));
-    if (info) *info = LaunchInfo{WAVES, S, grid, lds};
-    if (!run) return WSG_OK;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, static_cast<const uint8_t*>(w), n, k,
-                       x, y, dots, keys);
-    return launch_status();
+enum Path { kPathI8 = 0, kPathF32 = 1, kPathBf16 = 2 };
+
+// Default configuration per path and shape; tuning knobs override it.
+struct Cfg {
+    int waves, split, unroll;
+};
+
+Cfg choose_cfg(Path path, int64_t n, int64_t k) {
+    Cfg c;
+    const int64_t rows_per_cu = n / device_info().cus;
+    // measured on the 27B-stream shapes: 8-wave workgroups for tall
+    // matrices; 16-wave workgroups (one per CU, a quarter of the staging
+    // traffic) when there are few rows per CU, and 4 waves per row when the
+    // rows are also long
+    c.waves = rows_per_cu < 32 ? 16 : 8;
+    c.unroll = path == kPathF32 ? 1 : 4;
+    c.split = 1;
+    if (rows_per_cu < 32 && k >= 16384) c.split = 4;
+    else if (rows_per_cu < 8 && k >= 4096) c.split = 4;
+    else if (rows_per_cu < 8 && k >= 2048) c.split = 2;
+    const int tw = tune_waves(), ts = tune_splitk(), tu = tune_unroll();
+    if (tw == 4 || tw == 8 || tw == 16) c.waves = tw;
+    if (ts == 1 || ts == 2 || ts == 4) c.split = ts;
+    if (tu == 1 || tu == 2 || tu == 4 || tu == 8) c.unroll = tu;
+    if (c.split > c.waves) c.split = c.waves;
+    return c;
 }
 
-template <int ACT, bool DEBUG, bool ARGMAX>
-int launch_q8_i8(const void* w, int n, int k, const void* x, float* y, int32_t* dots, uint64_t* keys,
-                 hipStream_t stream, LaunchInfo* info, bool run = true) {
-    constexpr int WAVES = 4;
-    switch (choose_split(n, k, WAVES)) {
-        case 1:
-            return launch_q8_i8_s<WAVES, 1, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, info, run);
-        case 2:
-            return launch_q8_i8_s<WAVES, 2, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, info, run);
-        default:
-            return launch_q8_i8_s<WAVES, 4, ACT, DEBUG, ARGMAX>(w, n, k, x, y, dots, keys, stream, info, run);
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Calls f(IC<waves>, IC<split>) for the compiled (waves, split) pairs.
+template <typename F>
+int dispatch_ws(int waves, int split, F&& f) {
+    auto by_split = [&](auto W) -> int {
+        switch (split) {
+            case 2: return f(W, IC<2>{});
+            case 4: return f(W, IC<4>{});
+            default: return f(W, IC<1>{});
+        }
+    };
+    switch (waves) {
+        case 8: return by_split(IC<8>{});
+        case 16: return by_split(IC<16>{});
+        default: return by_split(IC<4>{});
     }
 }
 
-template <int WAVES, int S, bool ARGMAX>
-int launch_q8_f32_s(const void* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
-                    LaunchInfo* info, bool run) {
-    constexpr int U = 2;
-    auto kern = q8_f32_kernel<WAVES, S, U, true, ARGMAX>;
-    const int C = (int)chunk_count(k);
-    const size_t lds = lds_f32act_bytes(C) + lds_tail_bytes<WAVES>();
+// Calls f(IC<waves>, IC<split>, IC<unroll>) with unroll from {2, 4} (int8
+// and bf16 paths); the f32 path always loads one chunk ahead (deeper unrolls
+// exceed 128 VGPRs and spill).
+template <bool F32, typename F>
+int dispatch_wsu(int waves, int split, int unroll, F&& f) {
+    return dispatch_ws(waves, split, [&](auto W, auto S) -> int {
+        if constexpr (F32) {
+            (void)unroll;
+            return f(W, S, IC<1>{});
+        } else {
+            if (unroll <= 2) return f(W, S, IC<2>{});
+            return f(W, S, IC<4>{});
+        }
+    });
+}
+
+// Grid, LDS and (optionally) the launch of one kernel instantiation.
+template <int WAVES, int S, typename K, typename... Args>
+int launch_kernel(K kern, size_t lds, int n, LaunchInfo* info, int unroll, bool run, hipStream_t stream,
+                  Args... args) {
     raise_lds_limit(kern, lds);
     const int tiles = (n + WAVES / S - 1) / (WAVES / S);
     const int grid = persistent_grid(tiles, resident_per_cu(kern, WAVES * kWave, lds));
-    if (info) *info = LaunchInfo{WAVES, S, grid, lds};
+    if (info) *info = LaunchInfo{WAVES, S, unroll, grid, lds};
     if (!run) return WSG_OK;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, static_cast<const uint8_t*>(w), n, k,
-                       x, y, keys);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, args...);
     return launch_status();
+}
+
+// The debug and argmax instantiations use the default unroll (it does not
+// change the order of additions, so their results match the plain kernel).
+template <int ACT, bool DEBUG, bool ARGMAX>
+int launch_q8_i8(const void* w, int n, int k, const void* x, float* y, int32_t* dots, uint64_t* keys,
+                 hipStream_t stream, LaunchInfo* info, bool run = true) {
+    const Cfg c = choose_cfg(kPathI8, n, k);
+    const size_t lds_act = lds_q8act_bytes((int)chunk_count(k));
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    if constexpr (DEBUG || ARGMAX) {
+        return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
+            constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
+            auto kern = q8_i8_kernel<Wv, Sv, 4, ACT, true, DEBUG, ARGMAX>;
+            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, 4, run, stream, wp, n, k,
+                                         x, y, dots, keys);
+        });
+    } else {
+        return dispatch_wsu<false>(c.waves, c.split, c.unroll, [&](auto W, auto S, auto U) -> int {
+            constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value, Uv = decltype(U)::value;
+            auto kern = q8_i8_kernel<Wv, Sv, Uv, ACT, true, false, false>;
+            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, Uv, run, stream, wp, n, k,
+                                         x, y, dots, keys);
+        });
+    }
 }
 
 template <bool ARGMAX>
 int launch_q8_f32(const void* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
                   LaunchInfo* info, bool run = true) {
-    constexpr int WAVES = 8;
-    switch (choose_split(n, k, WAVES)) {
-        case 1: return launch_q8_f32_s<WAVES, 1, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
-        case 2: return launch_q8_f32_s<WAVES, 2, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
-        default: return launch_q8_f32_s<WAVES, 4, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
+    const Cfg c = choose_cfg(kPathF32, n, k);
+    const size_t lds_act = lds_f32act_bytes((int)chunk_count(k));
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    if constexpr (ARGMAX) {
+        return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
+            constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
+            auto kern = q8_f32_kernel<Wv, Sv, 1, true, true>;
+            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, 1, run, stream, wp, n, k,
+                                         x, y, keys);
+        });
+    } else {
+        return dispatch_wsu<true>(c.waves, c.split, c.unroll, [&](auto W, auto S, auto U) -> int {
+            constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value, Uv = decltype(U)::value;
+            auto kern = q8_f32_kernel<Wv, Sv, Uv, true, false>;
+            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, Uv, run, stream, wp, n, k,
+                                         x, y, keys);
+        });
     }
-}
-
-template <int WAVES, int S, bool ARGMAX>
-int launch_bf16_s(const uint16_t* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
-                  LaunchInfo* info, bool run) {
-    constexpr int U = 4;
-    auto kern = bf16_kernel<WAVES, S, U, true, ARGMAX>;
-    const size_t lds = lds_bf16_bytes(k) + lds_tail_bytes<WAVES>();
-    raise_lds_limit(kern, lds);
-    const int tiles = (n + WAVES / S - 1) / (WAVES / S);
-    const int grid = persistent_grid(tiles, resident_per_cu(kern, WAVES * kWave, lds));
-    if (info) *info = LaunchInfo{WAVES, S, grid, lds};
-    if (!run) return WSG_OK;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, w, n, k, x, y, keys);
-    return launch_status();
 }
 
 template <bool ARGMAX>
 int launch_bf16(const uint16_t* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
                 LaunchInfo* info, bool run = true) {
-    constexpr int WAVES = 4;
-    switch (choose_split(n, k, WAVES)) {
-        case 1: return launch_bf16_s<WAVES, 1, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
-        case 2: return launch_bf16_s<WAVES, 2, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
-        default: return launch_bf16_s<WAVES, 4, ARGMAX>(w, n, k, x, y, keys, stream, info, run);
+    const Cfg c = choose_cfg(kPathBf16, n, k);
+    const size_t lds_act = lds_bf16_bytes(k);
+    if constexpr (ARGMAX) {
+        return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
+            constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
+            auto kern = bf16_kernel<Wv, Sv, 2, true, true>;
+            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, 2, run, stream, w, n, k, x,
+                                         y, keys);
+        });
+    } else {
+        return dispatch_wsu<false>(c.waves, c.split, c.unroll, [&](auto W, auto S, auto U) -> int {
+            constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value, Uv = decltype(U)::value;
+            auto kern = bf16_kernel<Wv, Sv, Uv, true, false>;
+            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, Uv, run, stream, w, n, k, x,
+                                         y, keys);
+        });
     }
 }
 
@@ -648,6 +510,8 @@ int check_bf16_args(const void* w, int64_t n, int64_t k, const void* x, const vo
 }
 
 }  // namespace
+
+int gemv_split(bool f32_act, int64_t n, int64_t k) { return choose_cfg(f32_act ? kPathF32 : kPathI8, n, k).split; }
 
 // Validation without launching (used by the plan).
 int validate_gemv_q8(const void* w, int64_t n, int64_t k, const void* x, int act_fmt, const void* y) {
@@ -712,8 +576,30 @@ int gemv_bf16(const uint16_t* w, int64_t n, int64_t k, const float* x, float* y,
 
 int64_t wsg_argmax_ws_bytes(void) { return (int64_t)kMaxGrid * 8; }
 
-int wsg_gemv_config(int w_type, int act_fmt, int64_t n, int64_t k, int* waves, int* split, int* grid,
-                    int64_t* lds_bytes) {
+int wsg_tune(int knob, int value) {
+    if (value < 0) return WSG_ERR_SHAPE;
+    switch (knob) {
+        case WSG_TUNE_SPLITK:
+            if (value != 0 && value != 1 && value != 2 && value != 4) return WSG_ERR_SHAPE;
+            g_tune_splitk.store(value);
+            return WSG_OK;
+        case WSG_TUNE_WG_PER_CU:
+            g_tune_wg_per_cu.store(value);
+            return WSG_OK;
+        case WSG_TUNE_WAVES:
+            if (value != 0 && value != 4 && value != 8 && value != 16) return WSG_ERR_SHAPE;
+            g_tune_waves.store(value);
+            return WSG_OK;
+        case WSG_TUNE_UNROLL:
+            if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8) return WSG_ERR_SHAPE;
+            g_tune_unroll.store(value);
+            return WSG_OK;
+        default: return WSG_ERR_MODE;
+    }
+}
+
+int wsg_gemv_config(int w_type, int act_fmt, int64_t n, int64_t k, int* waves, int* split, int* unroll,
+                    int* grid, int64_t* lds_bytes) {
     if (w_type != WSG_W_BF16 && w_type != WSG_W_Q8_0) return WSG_ERR_MODE;
     if (w_type == WSG_W_BF16) act_fmt = WSG_ACT_F32;
     if (act_fmt != WSG_ACT_Q8_0 && act_fmt != WSG_ACT_F32 && act_fmt != WSG_ACT_F32_REQUANT) return WSG_ERR_MODE;
@@ -737,6 +623,7 @@ int wsg_gemv_config(int w_type, int act_fmt, int64_t n, int64_t k, int* waves, i
     if (rc != WSG_OK) return rc;
     if (waves) *waves = info.waves;
     if (split) *split = info.split;
+    if (unroll) *unroll = info.unroll;
     if (grid) *grid = info.grid;
     if (lds_bytes) *lds_bytes = (int64_t)info.lds;
     return WSG_OK;

@@ -1,0 +1,425 @@
+// Device building blocks of the GEMV kernels (gfx950, wave64): the work
+// schedule, the pipelined row loop, weight-item loads, activation staging in
+// LDS and the per-item dot products.  Included by gemv.hip and stream.hip;
+// everything here is internal to each translation unit.
+#pragma once
+
+#include "common.hpp"
+
+namespace wsg {
+namespace {
+
+constexpr int kActQ8 = 0, kActF32 = 1, kActRequant = 2;  // = WSG_ACT_*
+
+// ------------------------------------------------------------------ LDS
+// Layouts of the staged activation (per 2048-weight chunk c, lane l):
+//  int8 paths : int4v q[C][2][64]   (half h of block 64c+l), float dx[C*64]
+//  f32 path   : float4v x[C][8][64] (values 4g..4g+3 of block 64c+l)
+//  bf16 path  : float4v x[C'][2][2][64] over 1024-element chunks:
+//               values 1024c + 512h + 8l + 4j .. +3
+
+__host__ __device__ inline size_t lds_q8act_bytes(int C) { return (size_t)C * (2 * kWave * 16 + kWave * 4); }
+__host__ __device__ inline size_t lds_f32act_bytes(int C) { return (size_t)C * 8 * kWave * 16; }
+__host__ __device__ inline int bf16_chunks(int k) { return (k + 1023) / 1024; }
+__host__ __device__ inline size_t lds_bf16_bytes(int k) { return (size_t)bf16_chunks(k) * 4 * kWave * 16; }
+// tail of the LDS allocation: S partial sums per tile and the argmax keys
+template <int WAVES>
+__host__ __device__ constexpr size_t lds_tail_bytes() {
+    return WAVES * sizeof(float) + WAVES * sizeof(uint64_t) + 16;
+}
+
+// --------------------------------------------------------- work schedule
+// A workgroup walks row tiles t = blockIdx.x + j * gridDim.x.  Wave w owns
+// row t * GROUPS + w / S of each tile and the chunks c = p, p + S, ... of it
+// (p = w % S).  Its work is a flat sequence of items (tile j, item m); item m
+// covers U of its chunks.  Loads of item i+1 are issued before item i is
+// consumed, and the loads of the first item before the activation staging
+// completes, so HBM sees requests from the first cycles of the launch.
+struct Sched {
+    int C, S, U, part, group, groups, n, tiles_wg, ipt;
+    __device__ Sched(int C_, int S_, int U_, int waves, int n_, int tiles) {
+        C = C_;
+        S = S_;
+        U = U_;
+        const int wave = threadIdx.x / kWave;
+        part = wave % S;
+        group = wave / S;
+        groups = waves / S;
+        n = n_;
+        tiles_wg = blockIdx.x < (unsigned)tiles ? (tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+        const int count = part < C ? (C - part + S - 1) / S : 0;
+        ipt = (count + U - 1) / U;
+    }
+    __device__ int row(int j) const { return ((int)blockIdx.x + j * (int)gridDim.x) * groups + group; }
+    // chunk of slot u in item m
+    __device__ int chunk(int m, int u) const { return part + S * (m * U + u); }
+};
+
+// Epilogue shared by all paths: combine split-K partials in part order,
+// then store y (and/or fold the row into the workgroup's argmax key).
+template <int WAVES, int S, bool ARGMAX>
+__device__ inline void finish_row(float acc, int row, int n, int lane, int wave, float* lds_part, float* y,
+                                  uint64_t& best) {
+    const int part = wave % S;
+    float total = acc;
+    if constexpr (S > 1) {
+        if (lane == 0) lds_part[wave] = acc;
+        __syncthreads();
+        if (part == 0) {
+            total = lds_part[wave];
+#pragma unroll
+            for (int p = 1; p < S; ++p) total += lds_part[wave + p];
+        }
+        __syncthreads();
+    }
+    if (part == 0 && row < n) {
+        if constexpr (ARGMAX) {
+            const uint64_t key = argmax_key(total, (uint32_t)row);
+            best = key > best ? key : best;
+            if (y != nullptr && lane == 0) y[row] = total;
+        } else {
+            if (lane == 0) y[row] = total;
+        }
+    }
+}
+
+template <int WAVES>
+__device__ inline void write_block_key(uint64_t best, int lane, int wave, uint64_t* lds_key, uint64_t* keys) {
+    if (lane == 0) lds_key[wave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t m = lds_key[0];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) m = lds_key[w] > m ? lds_key[w] : m;
+        keys[blockIdx.x] = m;
+    }
+}
+
+// The pipelined row loop shared by all paths.  `a` holds the wave's first
+// item (loaded by the caller before staging).  Items alternate between two
+// register sets, so the loads of item i+1 are in flight while item i is
+// consumed and no loaded register is ever copied (a copy would force a wait
+// for its load).  load(regs, row, m) issues an item's loads;
+// compute(regs, row, m, acc) consumes it; finish(acc, row, valid) ends a
+// tile (every wave calls it once per tile, as split-K needs).
+template <typename Regs, typename LoadF, typename ComputeF, typename FinishF>
+__device__ inline void row_loop(const Sched& sc, Regs& a, LoadF&& load, ComputeF&& compute, FinishF&& finish) {
+    if (sc.ipt == 0) {
+        for (int j = 0; j < sc.tiles_wg; ++j) finish(0.0f, sc.row(j), false);
+        return;
+    }
+    Regs b;
+    float acc = 0.0f;
+    int j = 0, m = 0;  // current item
+    auto step = [&](Regs& cur, Regs& nxt) {
+        const int jn = (m + 1 < sc.ipt) ? j : j + 1;
+        const int mn = (m + 1 < sc.ipt) ? m + 1 : 0;
+        if (jn < sc.tiles_wg) {
+            const int rown = sc.row(jn);
+            if (rown < sc.n) load(nxt, rown, mn);
+        }
+        const int row = sc.row(j);
+        const bool valid = row < sc.n;
+        if (valid) compute(cur, row, m, acc);
+        if (m == sc.ipt - 1) {
+            if (valid) acc = wave_sum(acc);
+            finish(acc, row, valid);
+            acc = 0.0f;
+        }
+        j = jn;
+        m = mn;
+    };
+    while (j < sc.tiles_wg) {
+        step(a, b);
+        if (j >= sc.tiles_wg) break;
+        step(b, a);
+    }
+}
+
+// ------------------------------------------------------ Q8_0 weight items
+template <int U>
+struct Q8Regs {
+    int4v a[U], b[U];
+    uint16_t sc[U];
+};
+
+// P: const uint8_t* (a kernel argument, known global) or gptr<uint8_t> (a
+// pointer read from a descriptor).
+template <int U, typename P>
+__device__ inline void q8_load(Q8Regs<U>& r, P W, int64_t row_bytes, const Sched& sc, int nl, int sbl, int row,
+                               int m) {
+    const int lane = threadIdx.x % kWave;
+    const P rowp = W + (int64_t)row * row_bytes;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = sc.chunk(m, u);
+        // slots past the last chunk load nothing (a wave-uniform branch);
+        // lanes past a ragged chunk's last block re-read its last block (the
+        // same cache lines), so the loads are not divergent; compute skips
+        // both
+        if (c < sc.C) {
+            const bool last = (c == sc.C - 1);
+            const int nbc = last ? nl : kChunkBlocks;
+            const int sb = last ? sbl : 2 * kChunkBlocks;
+            const int l = lane < nbc ? lane : nbc - 1;
+            const P cp = rowp + (int64_t)c * kFullChunkBytes;
+            r.sc[u] = load_u16<true>(cp + 2 * l);
+            r.a[u] = load16<true>(cp + sb + 16 * l);
+            r.b[u] = load16<true>(cp + sb + 16 * nbc + 16 * l);
+        }
+    }
+}
+
+// ------------------------------------------------------ activation staging
+// Each path stages the activation in LDS in two steps: issue() puts this
+// thread's first NR units in registers (before the weight prefetch, so
+// waiting for them does not wait for the weights), commit() writes them and
+// any remaining units to LDS.
+
+// Planar Q8_0 activation (q[k] then fp16 d[k/32]) -> LDS int4v q[C][2][64]
+// (half h of block 64c+l) and float dx[C*64].
+template <int NR>
+struct StageQ8 {
+    int4v q[NR];
+    uint16_t d[NR];
+    __device__ void issue(const void* __restrict__ xin, int k, int C) {
+        const int NB = k / kBlock;
+        const int8_t* qx = static_cast<const int8_t*>(xin);
+        const uint16_t* dx = reinterpret_cast<const uint16_t*>(qx + k);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int u = threadIdx.x + i * blockDim.x;
+            const int l = u % kWave, ch = u / kWave, h = ch & 1, c = ch >> 1;
+            const int b = c * kWave + l;
+            if (u < C * 2 * kWave && b < NB) q[i] = *reinterpret_cast<const int4v*>(qx + (int64_t)b * kBlock + 16 * h);
+            const int bd = threadIdx.x + i * blockDim.x;
+            if (bd < NB) d[i] = dx[bd];
+        }
+    }
+    __device__ void commit(const void* __restrict__ xin, int k, int C, int4v* lds_q, float* lds_dx) {
+        const int NB = k / kBlock;
+        const int8_t* qx = static_cast<const int8_t*>(xin);
+        const uint16_t* dx = reinterpret_cast<const uint16_t*>(qx + k);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int u = threadIdx.x + i * blockDim.x;
+            const int l = u % kWave, c = (u / kWave) >> 1;
+            if (u < C * 2 * kWave && c * kWave + l < NB) lds_q[u] = q[i];
+            const int bd = threadIdx.x + i * blockDim.x;
+            if (bd < NB) lds_dx[bd] = half_bits_to_float(d[i]);
+        }
+        for (int u = threadIdx.x + NR * blockDim.x; u < C * 2 * kWave; u += blockDim.x) {
+            const int l = u % kWave, ch = u / kWave, h = ch & 1, c = ch >> 1;
+            const int b = c * kWave + l;
+            if (b < NB) lds_q[u] = *reinterpret_cast<const int4v*>(qx + (int64_t)b * kBlock + 16 * h);
+        }
+        for (int b = threadIdx.x + NR * blockDim.x; b < NB; b += blockDim.x) lds_dx[b] = half_bits_to_float(dx[b]);
+    }
+};
+
+// f32 activation quantized with the Q8_0 rule into the same LDS layout (the
+// same device functions and bytes as quantize_act_q8_0).  A unit is one
+// 32-value block.
+__device__ inline void requant_block_to_lds(const float4v* v4, int b, int4v* lds_q, float* lds_dx) {
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[4 * i + 0] = v4[i].x;
+        v[4 * i + 1] = v4[i].y;
+        v[4 * i + 2] = v4[i].z;
+        v[4 * i + 3] = v4[i].w;
+    }
+    int8_t codes[32];
+    const float d = q8_quantize_block(v, codes);
+    const int c = b / kWave, l = b % kWave;
+    int4v lo, hi;
+    __builtin_memcpy(&lo, codes, 16);
+    __builtin_memcpy(&hi, codes + 16, 16);
+    lds_q[(c * 2 + 0) * kWave + l] = lo;
+    lds_q[(c * 2 + 1) * kWave + l] = hi;
+    lds_dx[b] = d;
+}
+
+template <int NR>
+struct StageRequant {
+    float4v v[NR][8];
+    __device__ void issue(const void* __restrict__ xin, int k, int) {
+        const int NB = k / kBlock;
+        const float4v* x4 = static_cast<const float4v*>(xin);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int b = threadIdx.x + i * blockDim.x;
+            if (b < NB) {
+#pragma unroll
+                for (int g = 0; g < 8; ++g) v[i][g] = x4[b * 8 + g];
+            }
+        }
+    }
+    __device__ void commit(const void* __restrict__ xin, int k, int, int4v* lds_q, float* lds_dx) {
+        const int NB = k / kBlock;
+        const float4v* x4 = static_cast<const float4v*>(xin);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int b = threadIdx.x + i * blockDim.x;
+            if (b < NB) requant_block_to_lds(v[i], b, lds_q, lds_dx);
+        }
+        for (int b = threadIdx.x + NR * blockDim.x; b < NB; b += blockDim.x) {
+            float4v t[8];
+#pragma unroll
+            for (int g = 0; g < 8; ++g) t[g] = x4[b * 8 + g];
+            requant_block_to_lds(t, b, lds_q, lds_dx);
+        }
+    }
+};
+
+// f32 activation for the dequantizing path: float4 v (values 4v..4v+3, block
+// b = v/8, group g = v%8) -> LDS float4v x[C][8][64] at (c*8+g)*64 + l.
+template <int NR>
+struct StageF32 {
+    float4v v[NR];
+    __device__ static int slot(int u) {
+        const int b = u >> 3, g = u & 7, c = b / kWave, l = b % kWave;
+        return (c * 8 + g) * kWave + l;
+    }
+    __device__ void issue(const float* __restrict__ x, int k) {
+        const float4v* x4 = reinterpret_cast<const float4v*>(x);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int u = threadIdx.x + i * blockDim.x;
+            if (u < k / 4) v[i] = x4[u];
+        }
+    }
+    __device__ void commit(const float* __restrict__ x, int k, float4v* lds_x) {
+        const float4v* x4 = reinterpret_cast<const float4v*>(x);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int u = threadIdx.x + i * blockDim.x;
+            if (u < k / 4) lds_x[slot(u)] = v[i];
+        }
+        for (int u = threadIdx.x + NR * blockDim.x; u < k / 4; u += blockDim.x) lds_x[slot(u)] = x4[u];
+    }
+};
+
+// f32 activation for the bf16 path: element e = 1024c + 512h + 8l + 4j ->
+// LDS float4v x[C'][2][2][64] at ((c*2+h)*2+j)*64 + l.
+template <int NR>
+struct StageBf16x {
+    float4v v[NR];
+    __device__ static int slot(int u) {
+        const int e = 4 * u;
+        const int c = e >> 10, h = (e >> 9) & 1, l = (e >> 3) & 63, j = (e >> 2) & 1;
+        return ((c * 2 + h) * 2 + j) * kWave + l;
+    }
+    __device__ void issue(const float* __restrict__ x, int k) {
+        const float4v* x4 = reinterpret_cast<const float4v*>(x);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int u = threadIdx.x + i * blockDim.x;
+            if (u < k / 4) v[i] = x4[u];
+        }
+    }
+    __device__ void commit(const float* __restrict__ x, int k, float4v* lds_x) {
+        const float4v* x4 = reinterpret_cast<const float4v*>(x);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int u = threadIdx.x + i * blockDim.x;
+            if (u < k / 4) lds_x[slot(u)] = v[i];
+        }
+        for (int u = threadIdx.x + NR * blockDim.x; u < k / 4; u += blockDim.x) lds_x[slot(u)] = x4[u];
+    }
+};
+
+// ------------------------------------------------------ Q8_0 x f32 (deq)
+__device__ inline float dot4_i8_f32(int w, float4v x, float acc) {
+    acc = __builtin_fmaf((float)(int8_t)(w & 0xFF), x.x, acc);
+    acc = __builtin_fmaf((float)(int8_t)((w >> 8) & 0xFF), x.y, acc);
+    acc = __builtin_fmaf((float)(int8_t)((w >> 16) & 0xFF), x.z, acc);
+    acc = __builtin_fmaf((float)(int8_t)(w >> 24), x.w, acc);
+    return acc;
+}
+
+// ---------------------------------------------------------- BF16 x f32
+__device__ inline float dot_bf16x8(int4v w, float4v x0, float4v x1, float acc) {
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.x << 16), x0.x, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.x & 0xFFFF0000u), x0.y, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.y << 16), x0.z, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.y & 0xFFFF0000u), x0.w, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.z << 16), x1.x, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.z & 0xFFFF0000u), x1.y, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.w << 16), x1.z, acc);
+    acc = __builtin_fmaf(__uint_as_float((uint32_t)w.w & 0xFFFF0000u), x1.w, acc);
+    return acc;
+}
+
+template <int U>
+struct Bf16Regs {
+    int4v a[U], b[U];
+};
+
+// Makes a loaded value opaque to the optimizer at its point of use, so that
+// byte or half extraction is not folded back into the (conditional) block
+// that issued the load -- there it would force an immediate wait for the
+// load and defeat the pipelining.
+__device__ inline void opaque(int4v& v) { asm volatile("" : "+v"(v)); }
+
+// ------------------------------------------------------- item compute
+// One item of the int8 path: U chunks, one 32-weight block per lane each;
+// s = exact int32 block dot (8 x v_dot4), acc += (d_w * d_x) * s.
+template <int U, bool DEBUG>
+__device__ inline void q8_i8_item(const Q8Regs<U>& r, const Sched& sc, int m, int NB, const int4v* lds_q,
+                                  const float* lds_dx, int row, int32_t* dots, float& acc) {
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = sc.chunk(m, u);
+        const int blk = c * kWave + lane;
+        if (c < sc.C && blk < NB) {
+            const int4v xa = lds_q[(c * 2 + 0) * kWave + lane];
+            const int4v xb = lds_q[(c * 2 + 1) * kWave + lane];
+            int s = 0;
+            s = __builtin_amdgcn_sdot4(r.a[u].x, xa.x, s, false);
+            s = __builtin_amdgcn_sdot4(r.a[u].y, xa.y, s, false);
+            s = __builtin_amdgcn_sdot4(r.a[u].z, xa.z, s, false);
+            s = __builtin_amdgcn_sdot4(r.a[u].w, xa.w, s, false);
+            s = __builtin_amdgcn_sdot4(r.b[u].x, xb.x, s, false);
+            s = __builtin_amdgcn_sdot4(r.b[u].y, xb.y, s, false);
+            s = __builtin_amdgcn_sdot4(r.b[u].z, xb.z, s, false);
+            s = __builtin_amdgcn_sdot4(r.b[u].w, xb.w, s, false);
+            if constexpr (DEBUG) dots[(int64_t)row * NB + blk] = s;
+            const float t = half_bits_to_float(r.sc[u]) * lds_dx[blk];
+            acc = __builtin_fmaf(t, (float)s, acc);
+        }
+    }
+    (void)row;
+    (void)dots;
+}
+
+// One item of the dequantizing path: acc += d_w * sum_i q_i x_i per block.
+template <int U>
+__device__ inline void q8_f32_item(const Q8Regs<U>& r, const Sched& sc, int m, int NB, const float4v* lds_x,
+                                   float& acc) {
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = sc.chunk(m, u);
+        if (c < sc.C && c * kWave + lane < NB) {
+            const float4v* xv = lds_x + (size_t)c * 8 * kWave + lane;
+            int4v wa = r.a[u], wb = r.b[u];
+            opaque(wa);
+            opaque(wb);
+            float bs = 0.0f;
+            bs = dot4_i8_f32(wa.x, xv[0 * kWave], bs);
+            bs = dot4_i8_f32(wa.y, xv[1 * kWave], bs);
+            bs = dot4_i8_f32(wa.z, xv[2 * kWave], bs);
+            bs = dot4_i8_f32(wa.w, xv[3 * kWave], bs);
+            bs = dot4_i8_f32(wb.x, xv[4 * kWave], bs);
+            bs = dot4_i8_f32(wb.y, xv[5 * kWave], bs);
+            bs = dot4_i8_f32(wb.z, xv[6 * kWave], bs);
+            bs = dot4_i8_f32(wb.w, xv[7 * kWave], bs);
+            acc = __builtin_fmaf(half_bits_to_float(r.sc[u]), bs, acc);
+        }
+    }
+}
+
+}  // namespace
+}  // namespace wsg

@@ -22,6 +22,10 @@ struct DeviceInfo {
 };
 const DeviceInfo& device_info();
 
+// Waves per row the Q8_0 GEMV uses for this shape (the persistent kernel
+// uses the same, so its rows are reduced in the same order).
+int gemv_split(bool f32_act, int64_t n, int64_t k);
+
 // Writes y[0..n) = 0 (the empty sum for k == 0).
 int fill_zero_f32(float* y, int64_t n, hipStream_t stream);
 

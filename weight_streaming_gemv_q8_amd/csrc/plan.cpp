@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "internal.hpp"
+#include "stream.hpp"
 #include "wsgemv.h"
 
 namespace wsg {
@@ -24,6 +25,9 @@ struct wsg_plan {
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     int kernels = 0;
+    // persistent plans: device descriptor table and barrier state {count, gen, err}
+    void* ops_dev = nullptr;
+    uint32_t* bar_dev = nullptr;
 };
 
 namespace {
@@ -58,20 +62,9 @@ int enqueue_op(const wsg_op_desc& d, hipStream_t s) {
     }
 }
 
-}  // namespace
-
-extern "C" {
-
-int wsg_plan_create(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_plan** out) {
-    if (!ops || !out) return WSG_ERR_NULL;
-    *out = nullptr;
-    if (n_ops <= 0) return WSG_ERR_SHAPE;
-    for (int i = 0; i < n_ops; ++i) {
-        const int rc = validate_op(ops[i]);
-        if (rc != WSG_OK) return rc;
-    }
-    (void)wsg::device_info();  // per-device lookups happen before capture
-
+// Capture `enqueue(cap_stream)` into an instantiated graph held by `p`.
+template <typename F>
+int capture_into(wsg_plan* p, hipStream_t stream, F&& enqueue) {
     hipStream_t cap = stream;
     bool own = false;
     if (cap == nullptr) {
@@ -87,8 +80,7 @@ int wsg_plan_create(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_p
         if (own) (void)hipStreamDestroy(cap);
         return WSG_ERR_HIP;
     }
-    int rc = WSG_OK;
-    for (int i = 0; i < n_ops && rc == WSG_OK; ++i) rc = enqueue_op(ops[i], cap);
+    const int rc = enqueue(cap);
     hipGraph_t graph = nullptr;
     const hipError_t end = hipStreamEndCapture(cap, &graph);
     if (own) (void)hipStreamDestroy(cap);
@@ -112,15 +104,136 @@ int wsg_plan_create(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_p
             }
         }
     }
-    wsg_plan* p = new (std::nothrow) wsg_plan;
-    if (!p) {
-        (void)hipGraphExecDestroy(exec);
-        (void)hipGraphDestroy(graph);
-        return WSG_ERR_HIP;
-    }
     p->graph = graph;
     p->exec = exec;
     p->kernels = kernels;
+    return WSG_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+    bool overlaps(const Range& o) const { return lo < o.hi && o.lo < hi; }
+};
+
+void release(wsg_plan* p) {
+    if (p->exec) (void)hipGraphExecDestroy(p->exec);
+    if (p->graph) (void)hipGraphDestroy(p->graph);
+    if (p->ops_dev) (void)hipFree(p->ops_dev);
+    if (p->bar_dev) (void)hipFree(p->bar_dev);
+    delete p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wsg_plan_create_persistent(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_plan** out) {
+    if (!ops || !out) return WSG_ERR_NULL;
+    *out = nullptr;
+    if (n_ops <= 0 || n_ops >= 4096) return WSG_ERR_SHAPE;  // barrier epochs are numbered per launch
+    std::vector<wsg::StreamOp> table(n_ops);
+    std::vector<Range> reads, writes;  // accessed since the last barrier
+    int max_k = 0;
+    const bool f32 = ops[0].act_fmt == WSG_ACT_F32;
+    for (int i = 0; i < n_ops; ++i) {
+        const wsg_op_desc& d = ops[i];
+        if (d.op != WSG_OP_GEMV_Q8_0) return WSG_ERR_MODE;
+        if (d.act_fmt != WSG_ACT_F32_REQUANT && d.act_fmt != WSG_ACT_F32) return WSG_ERR_MODE;
+        if ((d.act_fmt == WSG_ACT_F32) != f32) return WSG_ERR_MODE;  // one activation format per plan
+        int rc = wsg::validate_gemv_q8(d.w, d.n, d.k, d.x, d.act_fmt, d.y);
+        if (rc != WSG_OK) return rc;
+        if (d.n < 1 || d.k < 32) return WSG_ERR_SHAPE;
+        const Range rx{reinterpret_cast<uintptr_t>(d.x), reinterpret_cast<uintptr_t>(d.x) + 4 * (uintptr_t)d.k};
+        const Range ry{reinterpret_cast<uintptr_t>(d.y), reinterpret_cast<uintptr_t>(d.y) + 4 * (uintptr_t)d.n};
+        bool dep = false;
+        for (const Range& w : writes) dep = dep || w.overlaps(rx) || w.overlaps(ry);
+        for (const Range& r : reads) dep = dep || r.overlaps(ry);
+        if (dep) {
+            reads.clear();
+            writes.clear();
+        }
+        reads.push_back(rx);
+        writes.push_back(ry);
+        wsg::StreamOp& t = table[i];
+        t.w = static_cast<const uint8_t*>(d.w);
+        t.x = static_cast<const float*>(d.x);
+        t.y = static_cast<float*>(d.y);
+        t.n = (int32_t)d.n;
+        t.k = (int32_t)d.k;
+        t.act = d.act_fmt;
+        t.split = wsg::stream_split(f32, d.n, d.k);
+        t.barrier = dep ? 1 : 0;
+        t.pad = 0;
+        if (d.k > max_k) max_k = (int)d.k;
+    }
+    int waves = 0, grid = 0;
+    size_t lds = 0;
+    int rc = wsg::stream_config(max_k, f32, &waves, &grid, &lds);
+    if (rc != WSG_OK) return rc;
+    if ((int64_t)lds > wsg::device_info().max_lds) return WSG_ERR_SHAPE;
+
+    // barrier state: launch counter, release epoch, error flag, one arrival
+    // line per workgroup (128 bytes each)
+    const size_t bar_bytes = (size_t)(3 + grid) * 128;
+    wsg_plan* p = new (std::nothrow) wsg_plan;
+    if (!p) return WSG_ERR_HIP;
+    if (hipMalloc(&p->ops_dev, sizeof(wsg::StreamOp) * n_ops) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void**>(&p->bar_dev), bar_bytes) != hipSuccess) {
+        release(p);
+        return WSG_ERR_HIP;
+    }
+    const std::vector<uint32_t> zero(bar_bytes / 4, 0u);
+    if (hipMemcpy(p->ops_dev, table.data(), sizeof(wsg::StreamOp) * n_ops, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(p->bar_dev, zero.data(), bar_bytes, hipMemcpyHostToDevice) != hipSuccess) {
+        release(p);
+        return WSG_ERR_HIP;
+    }
+    // a wait longer than ~2^22 sleeps (tenths of a second) is a failure
+    const int spin_limit = 1 << 22;
+    const wsg::StreamOp* ops_dev = static_cast<const wsg::StreamOp*>(p->ops_dev);
+    rc = capture_into(p, stream, [&](hipStream_t s) {
+        return wsg::stream_launch(ops_dev, n_ops, f32, p->bar_dev, grid, lds, spin_limit, s);
+    });
+    if (rc != WSG_OK) {
+        release(p);
+        return rc;
+    }
+    *out = p;
+    return WSG_OK;
+}
+
+int wsg_plan_error(wsg_plan* plan, int* flag) {
+    if (!plan || !flag) return WSG_ERR_NULL;
+    *flag = 0;
+    if (!plan->bar_dev) return WSG_OK;
+    uint32_t st[96] = {0};
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(st, plan->bar_dev, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess)
+        return WSG_ERR_HIP;
+    *flag = st[64] != 0 ? 1 : 0;  // the error word of the barrier state
+    return WSG_OK;
+}
+
+int wsg_plan_create(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_plan** out) {
+    if (!ops || !out) return WSG_ERR_NULL;
+    *out = nullptr;
+    if (n_ops <= 0) return WSG_ERR_SHAPE;
+    for (int i = 0; i < n_ops; ++i) {
+        const int rc = validate_op(ops[i]);
+        if (rc != WSG_OK) return rc;
+    }
+    (void)wsg::device_info();  // per-device lookups happen before capture
+    wsg_plan* p = new (std::nothrow) wsg_plan;
+    if (!p) return WSG_ERR_HIP;
+    const int rc = capture_into(p, stream, [&](hipStream_t s) {
+        int r = WSG_OK;
+        for (int i = 0; i < n_ops && r == WSG_OK; ++i) r = enqueue_op(ops[i], s);
+        return r;
+    });
+    if (rc != WSG_OK) {
+        release(p);
+        return rc;
+    }
     *out = p;
     return WSG_OK;
 }
@@ -132,11 +245,8 @@ int wsg_plan_launch(wsg_plan* plan, hipStream_t stream) {
 
 int wsg_plan_destroy(wsg_plan* plan) {
     if (!plan) return WSG_ERR_NULL;
-    int rc = WSG_OK;
-    if (plan->exec && hipGraphExecDestroy(plan->exec) != hipSuccess) rc = WSG_ERR_HIP;
-    if (plan->graph && hipGraphDestroy(plan->graph) != hipSuccess) rc = WSG_ERR_HIP;
-    delete plan;
-    return rc;
+    release(plan);
+    return WSG_OK;
 }
 
 int wsg_plan_kernel_count(const wsg_plan* plan) { return plan ? plan->kernels : -1; }

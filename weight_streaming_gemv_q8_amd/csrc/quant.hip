@@ -23,19 +23,7 @@ __device__ inline uint16_t quantize_block32(const float* __restrict__ src, int8_
         v[4 * i + 2] = t.z;
         v[4 * i + 3] = t.w;
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-    const uint16_t d16 = q8_scale_bits(amax);
-    const float d = half_bits_to_float(d16);
-    if (d == 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) q[i] = 0;
-        return 0;
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) q[i] = q8_code(v[i], d);
-    return d16;
+    return q8_quantize_block_bits(v, q);
 }
 
 __global__ void quantize_act_kernel(const float* __restrict__ x, int nb, int8_t* __restrict__ q,

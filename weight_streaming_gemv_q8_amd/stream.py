@@ -170,10 +170,13 @@ class TokenStream:
         for i in range(len(self.slots)):
             self.run_slot(i, stream)
 
-    def capture(self, stream=None) -> wsg.Plan:
+    def capture(self, stream=None, persistent: bool = False) -> wsg.Plan:
+        """One hipGraph per token: a node per call, or (persistent=True, Q8_0
+        chains with fused requantization or f32 activations) one resident
+        kernel for the whole token."""
         if self.plan is not None:
             self.plan.destroy()
-        self.plan = wsg.Plan(self.ops(), stream=stream)
+        self.plan = wsg.Plan(self.ops(), stream=stream, persistent=persistent)
         return self.plan
 
     def launch(self, stream=None) -> None:
