@@ -30,8 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
-GEMV_SOURCES = [os.path.join(ROOT, "weight_streaming_gemv_q8_amd", "csrc", f)
-                for f in ("gemv.hip", "common.hpp")]
+CSRC = os.path.join(ROOT, "weight_streaming_gemv_q8_amd", "csrc")
 
 
 def log(msg: str) -> None:
@@ -56,10 +55,12 @@ def gbps(nbytes: float, seconds: float) -> float:
 
 
 def source_digest() -> str:
+    """Hash of every kernel source: counters taken on other sources are stale."""
     h = hashlib.sha256()
-    for p in GEMV_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    for fn in sorted(os.listdir(CSRC)):
+        if fn.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(CSRC, fn), "rb") as f:
+                h.update(fn.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -124,7 +125,7 @@ def kernel_label(wtype: str, act_fmt: int, cfg: dict) -> str:
     else:
         base = "q8_i8_kernel"
     act = {wsg.ACT_Q8_0: "q8act", wsg.ACT_F32: "f32act", wsg.ACT_F32_REQUANT: "requant"}[act_fmt]
-    return f"{base}<waves={cfg['waves']},split={cfg['split']},{act}>"
+    return f"{base}<waves={cfg['waves']},split={cfg['split']},unroll={cfg['unroll']},{act}>"
 
 
 def time_per_launch(ts, reps: int = 1):
@@ -278,6 +279,96 @@ def run_probe(kind: str, nbytes: int) -> int:
     return 0
 
 
+# ------------------------------------------------------------ profile summaries
+# rocprofv3 output (CSV) -> short text summaries under profiles/.  Runs on any
+# host; the raw rocprofv3 directories stay out of the repository.
+
+_ACT_NAMES = {"0": "q8act", "1": "f32act", "2": "requant"}
+
+
+def label_from_rocprof(name: str):
+    """Bench label of a kernel from its demangled rocprofv3 name (template
+    arguments), or None for kernels outside the GEMV stream."""
+    import re
+    m = re.search(r"(q8_i8_kernel|q8_f32_kernel|bf16_kernel|stream_kernel)<([^>]*)>", name)
+    if not m:
+        return None
+    kind, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
+    if kind == "q8_i8_kernel":
+        return f"q8_i8_kernel<waves={args[0]},split={args[1]},unroll={args[2]},{_ACT_NAMES[args[3]]}>"
+    if kind in ("q8_f32_kernel", "bf16_kernel"):
+        return f"{kind}<waves={args[0]},split={args[1]},unroll={args[2]},f32act>"
+    return "stream_kernel<" + ",".join(args) + ">"
+
+
+def _read_csv(path: str):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                       workload: str, commands: dict) -> list:
+    """Writes profiles/kernel_stats_<workload>.txt from a --kernel-trace --stats
+    run and profiles/traffic_<kernel>_<workload>.txt per GEMV kernel from two
+    --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter
+    reads for the copy probe of known size.  Returns the files written."""
+    import collections
+    os.makedirs(PROFILES, exist_ok=True)
+    written = []
+    # kernel durations
+    stats = _read_csv(os.path.join(stats_dir, "run_kernel_stats.csv"))
+    path = os.path.join(PROFILES, f"kernel_stats_{workload}.txt")
+    with open(path, "w") as f:
+        f.write(f"# rocprofv3 kernel statistics, {workload}\n# command: {commands['stats']}\n")
+        f.write(f"# {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10} {'pct':>6}  kernel\n")
+        for r in stats:
+            lab = label_from_rocprof(r["Name"]) or r["Name"][:80]
+            f.write(f"  {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                    f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e6:10.3f} "
+                    f"{float(r['Percentage']):6.2f}  {lab}\n")
+    written.append(path)
+
+    def per_kernel(d, counter):
+        agg = collections.defaultdict(list)
+        for r in _read_csv(os.path.join(d, "run_counter_collection.csv")):
+            if r["Counter_Name"] == counter:
+                agg[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)  # KiB -> bytes
+        return agg
+
+    def copy_factor(d, counter, true_bytes):
+        vals = [v for k, v in per_kernel(d, counter).items() if "copy_probe_kernel" in k]
+        if not vals:
+            raise RuntimeError(f"no copy_probe_kernel rows in {d}")
+        got = sum(vals[0]) / len(vals[0])
+        return true_bytes / got, got
+
+    probe_bytes = int(commands.get("probe_bytes", 1 << 30))
+    rf, rgot = copy_factor(copy_fetch_dir, "FETCH_SIZE", probe_bytes)
+    wf, wgot = copy_factor(copy_write_dir, "WRITE_SIZE", probe_bytes)
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    digest = source_digest()
+    for name, vals in fetch.items():
+        lab = label_from_rocprof(name)
+        if lab is None or name not in write:
+            continue
+        fb = sum(vals) / len(vals) * rf
+        wb = sum(write[name]) / len(write[name]) * wf
+        safe = lab.replace("<", "_").replace(">", "").replace(",", "_").replace("=", "")
+        path = os.path.join(PROFILES, f"traffic_{safe}_{workload}.txt")
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic per launch from rocprofv3 counters, {workload}\n")
+            f.write(f"# fetch command: {commands['fetch']}\n# write command: {commands['write']}\n")
+            f.write(f"# calibration commands: {commands['copy_fetch']} ; {commands['copy_write']}\n")
+            f.write(f"# calibration: copy probe of {probe_bytes} B read / {probe_bytes} B written per launch; "
+                    f"FETCH_SIZE reads {rgot:.0f} B (factor {rf:.4f}), WRITE_SIZE reads {wgot:.0f} B "
+                    f"(factor {wf:.4f})\n")
+            f.write(f"kernel: {lab}\nrocprof_name: {name}\nsource_sha256: {digest}\n")
+            f.write(f"launches: {len(vals)}\nfetch_bytes_per_launch: {fb:.0f}\nwrite_bytes_per_launch: {wb:.0f}\n")
+        written.append(path)
+    return written
+
+
 # ------------------------------------------------------------ main
 
 def main() -> int:
@@ -297,9 +388,18 @@ def main() -> int:
                     help="only run the copy (or read) probe over --probe-bytes, 3 launches: a kernel of known "
                          "traffic for calibrating hardware byte counters")
     ap.add_argument("--probe-bytes", type=int, default=1 << 30)
+    ap.add_argument("--summarize", nargs=5, metavar=("STATS", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write profiles/ summaries from rocprofv3 output directories (no GPU needed); "
+                         "the commands that made them are read from STATS/../commands.json")
     args = ap.parse_args()
     if args.probe:
         return run_probe(args.probe, args.probe_bytes)
+    if args.summarize:
+        with open(os.path.join(os.path.dirname(os.path.abspath(args.summarize[0])), "commands.json")) as f:
+            cmds = json.load(f)
+        for p in summarize_profiles(*args.summarize, workload=cmds["workload"], commands=cmds):
+            print(p)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU step (see the design notes on "
