@@ -1,18 +1,21 @@
 #!/usr/bin/env python3
 """Bench: the whole-token batch-1 decode GEMV weight stream on one MI355X.
 
-One step = one replay of the captured hipGraph that streams every weight
-matrix of one token once (emit_qwen38_generate, "Where the speed comes
-from": ~27 GB of Q8_0 weights per token, one launch per concatenated
-projection, one graph per token).  Default workload: the 27B-scale Q8_0
-stream (64 layers x qkvz 16384x5120, out 5120x8192, gate+up 34816x5120,
-down 5120x17408), int8 activations (deq 0) quantized inside each GEMV.
-Weights are synthetic (seeded ~N(0, 0.02), quantized on the device) and
-resident in HBM before timing starts.
+One step = one replay of the captured token: every weight matrix of one
+token streamed once (emit_qwen38_generate, "Where the speed comes from":
+~27 GB of Q8_0 weights per token, one GEMV per concatenated projection, one
+graph per token).  Default plan: the persistent token kernel (one launch,
+captured as a one-node hipGraph); --plan graph replays one graph node per
+GEMV instead.  Default workload: the 27B-scale Q8_0 stream (64 layers x
+qkvz 16384x5120, out 5120x8192, gate+up 34816x5120, down 5120x17408), int8
+activations (deq 0) requantized inside each GEMV.  Weights are synthetic
+(seeded ~N(0, 0.02), quantized on the device) and resident in HBM before
+timing starts.
 
 Prints ONE JSON line: achieved HBM GB/s over the stream (algorithmic weight
 bytes / time), microseconds per token stream, the roofline of the dominant
-GEMV kernel (HIP events around each launch), and the CPU oracle timed on a
+kernel (the token kernel itself, or per GEMV instantiation for the graph
+plan, from HIP events on the launch stream), and the CPU oracle timed on a
 bounded sample on the host.  Progress goes to stderr.
 """
 from __future__ import annotations
@@ -298,7 +301,11 @@ def label_from_rocprof(name: str):
         return f"q8_i8_kernel<waves={args[0]},split={args[1]},unroll={args[2]},{_ACT_NAMES[args[3]]}>"
     if kind in ("q8_f32_kernel", "bf16_kernel"):
         return f"{kind}<waves={args[0]},split={args[1]},unroll={args[2]},f32act>"
-    return "stream_kernel<" + ",".join(args) + ">"
+    return stream_label(int(args[0]), int(args[1]), args[2] == "true")
+
+
+def stream_label(waves: int, unroll: int, f32: bool) -> str:
+    return f"stream_kernel<waves={waves},unroll={unroll},{'f32act' if f32 else 'requant'}>"
 
 
 def _read_csv(path: str):
@@ -379,7 +386,7 @@ def main() -> int:
     ap.add_argument("--workload", default="dense27b_q8_0_64L")
     ap.add_argument("--deq", type=int, default=0, choices=(0, 1, 2))
     ap.add_argument("--requant", default="fused", choices=("fused", "separate"))
-    ap.add_argument("--plan", default="graph", choices=("persistent", "graph"),
+    ap.add_argument("--plan", default="persistent", choices=("persistent", "graph"),
                     help="one resident kernel per token, or a graph node per GEMV")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -395,7 +402,7 @@ def main() -> int:
     if args.probe:
         return run_probe(args.probe, args.probe_bytes)
     if args.summarize:
-        with open(os.path.join(os.path.dirname(os.path.abspath(args.summarize[0])), "commands.json")) as f:
+        with open(os.path.join(os.path.abspath(args.summarize[0]), "commands.json")) as f:
             cmds = json.load(f)
         for p in summarize_profiles(*args.summarize, workload=cmds["workload"], commands=cmds):
             print(p)
@@ -436,11 +443,11 @@ def main() -> int:
     wtype_code = wsg.W_Q8_0 if wl.wtype == "q8_0" else wsg.W_BF16
     if persistent:
         # one launch per token: the dominant kernel is the whole stream
+        label = stream_label(16, 1 if act_fmt == wsg.ACT_F32 else 2, act_fmt == wsg.ACT_F32)
         roofline = {
             "bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": read_traffic("stream_kernel"),
-            "kernel": "stream_kernel (whole token, " + ("f32 activations" if act_fmt == wsg.ACT_F32
-                                                        else "int8 activations, fused requantization") + ")",
+            "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": read_traffic(label),
+            "kernel": label + " (the whole token in one launch)",
             "launches_per_token": 1, "bytes_per_launch": alg_bytes, "us_per_launch": round(sec * 1e6, 1),
         }
     else:

@@ -196,6 +196,13 @@ enum {
     WSG_OP_LM_HEAD_ARGMAX = 3,  /* w, w_type, n, k, x, act_fmt, ws, ws_bytes, idx_out */
 };
 
+/* flags: WSG_OP_AFTER_ALL marks an op that depends on every earlier op of
+ * the plan even where no buffer shows it (in a model, a layer's input is
+ * computed from the previous layer's output by operators outside the plan).
+ * Stream order already serializes the graph plan; the persistent plan makes
+ * such an op wait until the previous op's whole output is written. */
+enum { WSG_OP_AFTER_ALL = 1 };
+
 typedef struct {
     int op;
     int w_type;
@@ -208,6 +215,7 @@ typedef struct {
     void* ws;
     size_t ws_bytes;
     int32_t* idx_out;
+    int flags;
 } wsg_op_desc;
 
 typedef struct wsg_plan wsg_plan;
@@ -220,16 +228,23 @@ int wsg_plan_launch(wsg_plan* plan, hipStream_t stream);
 
 /* Persistent whole-token plan: the same descriptors (Q8_0 GEMVs only, all
  * with WSG_ACT_F32_REQUANT or all with WSG_ACT_F32; f32 inputs) executed by
- * ONE kernel
- * launch per replay, captured as a one-node hipGraph.  Every workgroup stays
- * resident for the whole token; a grid-wide barrier separates an op from the
- * earlier ops whose output it reads (or whose buffers it overwrites), and
- * each workgroup requests the next matrix's weights before it waits there,
- * so the weight stream does not drain between GEMVs.  Results equal the
- * eager calls' to the same tolerances (the split-K factor per op may
- * differ).  The plan owns a small device allocation (descriptor table and
- * barrier state).  A barrier wait that exceeds its spin limit makes the
- * kernel give up rather than hang; wsg_plan_error reports it. */
+ * ONE kernel launch per replay, captured as a one-node hipGraph, with one
+ * 16-wave workgroup per CU resident for the whole token.  Ops are ordered by
+ * their data, not by grid barriers: an op whose x is (a slice of) an earlier
+ * op's y reads each element as soon as its row is written, and a workgroup
+ * requests the next matrix's first weights before it waits for that input,
+ * so the weight stream does not drain between GEMVs.  Hence the plan
+ * requires that each op's x is either wholly inside one earlier op's y or
+ * overlaps no op's y at all, and that no y overlaps another op's y or an
+ * input read from outside the plan (WSG_ERR_MODE otherwise).  Each op
+ * reduces its rows in the same order as the eager call, so results equal
+ * the eager calls' bit for bit.  The plan owns a device allocation: the
+ * descriptor table, a launch counter, an error flag and an 8-byte tagged
+ * copy of every op's output.  A wait that exceeds its spin limit (about a
+ * second) makes the kernel give up rather than hang, every other wait of
+ * that launch stops soon after, and wsg_plan_error reports it; the plan's
+ * results are then invalid and it must be destroyed.  Replays of one plan
+ * must not overlap in time (launch them on one stream). */
 int wsg_plan_create_persistent(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_plan** out);
 
 /* *flag = 1 if a persistent plan's barrier ever timed out (its outputs are

@@ -18,3 +18,11 @@ extern "C" void fast_codes(const float* v, const uint16_t* d16, int64_t n, int8_
         out[i] = (int8_t)wsg::q8_code_exact(v[i], d, r);
     }
 }
+
+extern "C" void fast_split_codes(const float* v, const uint16_t* d16, int64_t n, int8_t* out) {
+    for (int64_t i = 0; i < n; ++i) {
+        const float d = f16_value(d16[i]);
+        const float r = 1.0f / d;
+        out[i] = (int8_t)wsg::q8_code(v[i], d, r);
+    }
+}

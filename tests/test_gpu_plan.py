@@ -9,6 +9,8 @@ fixed-address graph replay checked against eager execution).
   with the error bound propagated through the layer;
 * the first GEMV of every layer reads generator data, so it is checked
   directly against the oracle."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -181,3 +183,39 @@ def test_layer_inputs_match_oracle_int8(gpu_lib):
         y_ref, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
         assert_within(y, y_ref, oracle.q8_tolerance(den), f"layer {layer} qkv")
     ts.close()
+
+
+def test_persistent_plan_rejects_racy_buffers(gpu_lib):
+    """Without grid barriers ops overlap in time, so the persistent plan
+    refuses buffers that would race: an input straddling an earlier output,
+    two outputs that overlap, and an output over an input read from outside
+    the plan."""
+    import torch
+    wsg = gpu_lib
+    n, k = 256, 256
+    w = torch.zeros(n * wsg.q8_0_row_bytes(k), dtype=torch.uint8, device="cuda")
+    buf = torch.zeros(4 * n, dtype=torch.float32, device="cuda")
+    x0 = torch.zeros(k, dtype=torch.float32, device="cuda")
+    fmt = wsg.ACT_F32_REQUANT
+
+    def make(ops):
+        arr = (wsg.OpDesc * len(ops))(*ops)
+        plan = ctypes.c_void_p()
+        return wsg.lib().wsg_plan_create_persistent(arr, len(ops), None, ctypes.byref(plan)), plan
+
+    y0, y1 = buf[0:n], buf[n:2 * n]
+    cases = {
+        "input straddles an output": [wsg.op_gemv_q8_0(w, n, k, x0, fmt, y0),
+                                      wsg.op_gemv_q8_0(w, n, k, buf[n // 2:], fmt, y1)],
+        "outputs overlap": [wsg.op_gemv_q8_0(w, n, k, x0, fmt, y0),
+                            wsg.op_gemv_q8_0(w, n, k, x0, fmt, buf[n // 2:])],
+        "output over an outside input": [wsg.op_gemv_q8_0(w, n, k, y1, fmt, y0),
+                                         wsg.op_gemv_q8_0(w, n, k, x0, fmt, y1)],
+    }
+    for name, ops in cases.items():
+        rc, plan = make(ops)
+        assert rc == wsg.ERR_MODE, name
+    # the legal chain: the second op reads the first op's output
+    rc, plan = make([wsg.op_gemv_q8_0(w, n, k, x0, fmt, y0), wsg.op_gemv_q8_0(w, n, k, y0, fmt, y1)])
+    assert rc == wsg.OK
+    assert wsg.lib().wsg_plan_destroy(plan) == wsg.OK

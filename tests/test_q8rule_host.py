@@ -1,5 +1,6 @@
-"""The HIP library's divide-free Q8_0 code rule (csrc/q8rule.hpp), built for
-the host, gives exactly the oracle's codes (an IEEE fp32 divide by the
+"""The HIP library's divide-free Q8_0 code rules (csrc/q8rule.hpp: the exact
+boundary test, and the branch-free form that defers to it next to a
+boundary), built for the host, give exactly the oracle's codes (an IEEE fp32 divide by the
 stored scale, rounded half away from zero) on random values, on values
 planted at and one ulp around every rounding boundary m + 1/2, and across
 normal and subnormal fp16 scales."""
@@ -16,21 +17,27 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 
 
-@pytest.fixture(scope="module")
-def fast(tmp_path_factory):
+# the GPU compiler may fuse a multiply and an add into one FMA; the rules must
+# hold with and without that contraction
+@pytest.fixture(scope="module", params=[("fast_codes", "off"), ("fast_split_codes", "off"),
+                                        ("fast_codes", "fma"), ("fast_split_codes", "fma")])
+def fast(tmp_path_factory, request):
+    name, contract = request.param
     out = str(tmp_path_factory.mktemp("q8rule") / "libq8rule_host.so")
-    subprocess.run(["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+    flags = ["-ffp-contract=off"] if contract == "off" else ["-ffp-contract=fast", "-mfma"]
+    subprocess.run(["g++", "-std=c++17", "-O2", *flags, "-fno-fast-math", "-fPIC", "-shared",
                     "-I", os.path.join(ROOT, "weight_streaming_gemv_q8_amd", "csrc"),
                     os.path.join(HERE, "cpp", "q8rule_host.cpp"), "-o", out], check=True)
     L = ctypes.CDLL(out)
-    L.fast_codes.restype = None
-    L.fast_codes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    fn = getattr(L, name)
+    fn.restype = None
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
 
     def run(v, d16):
         v = np.ascontiguousarray(v, np.float32)
         d16 = np.ascontiguousarray(d16, np.uint16)
         o = np.empty(v.shape, np.int8)
-        L.fast_codes(v.ctypes.data, d16.ctypes.data, v.size, o.ctypes.data)
+        fn(v.ctypes.data, d16.ctypes.data, v.size, o.ctypes.data)
         return o
     return run
 

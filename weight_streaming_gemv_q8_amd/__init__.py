@@ -28,6 +28,7 @@ ACT_Q8_0, ACT_F32, ACT_F32_REQUANT = 0, 1, 2
 W_BF16, W_Q8_0 = 0, 1
 # plan ops
 OP_GEMV_BF16, OP_GEMV_Q8_0, OP_QUANTIZE_ACT, OP_LM_HEAD_ARGMAX = 0, 1, 2, 3
+OP_AFTER_ALL = 1  # OpDesc.flags: depends on every earlier op of the plan
 
 MAX_K_Q8ACT = 57344
 MAX_K_F32ACT = 36864
@@ -55,6 +56,7 @@ class OpDesc(ctypes.Structure):
         ("n", ctypes.c_int64), ("k", ctypes.c_int64),
         ("w", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("idx_out", ctypes.c_void_p),
+        ("flags", ctypes.c_int),
     ]
 
 

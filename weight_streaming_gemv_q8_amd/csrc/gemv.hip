@@ -338,19 +338,54 @@ struct Cfg {
     int waves, split, unroll;
 };
 
+// Waves per row for a Q8_0 GEMV, chosen so that the persistent token kernel
+// (one 16-wave workgroup per CU, row tiles of 16/S rows dealt round robin)
+// is balanced: cost = tiles per workgroup x the largest share of a row's
+// chunks that one wave reads (the ragged last chunk counts by its blocks),
+// with a 3% premium per doubling of S for the partial-sum exchange.  The
+// eager kernels use the same factor, so both reduce a row in the same order
+// and agree bit for bit.
+int balanced_split(int64_t n, int64_t k) {
+    const int64_t cus = device_info().cus > 0 ? device_info().cus : 1;
+    const int64_t C = chunk_count(k);
+    const double last = (double)last_chunk_blocks(k) / kChunkBlocks;
+    int best = 1;
+    double best_cost = 0.0;
+    for (int S = 1, step = 0; S <= 4; S *= 2, ++step) {
+        const int64_t rows_per_tile = 16 / S;
+        const int64_t tiles = (n + rows_per_tile - 1) / rows_per_tile;
+        const int64_t per_wg = (tiles + cus - 1) / cus;
+        double part_max = 0.0;
+        for (int p = 0; p < S; ++p) {
+            double w = 0.0;
+            for (int64_t c = p; c < C; c += S) w += (c == C - 1) ? last : 1.0;
+            part_max = w > part_max ? w : part_max;
+        }
+        const double cost = (double)per_wg * part_max * (1.0 + 0.03 * step);
+        if (S == 1 || cost < best_cost) {
+            best = S;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 Cfg choose_cfg(Path path, int64_t n, int64_t k) {
     Cfg c;
     const int64_t rows_per_cu = n / device_info().cus;
     // measured on the 27B-stream shapes: 8-wave workgroups for tall
     // matrices; 16-wave workgroups (one per CU, a quarter of the staging
-    // traffic) when there are few rows per CU, and 4 waves per row when the
-    // rows are also long
+    // traffic) when there are few rows per CU
     c.waves = rows_per_cu < 32 ? 16 : 8;
     c.unroll = path == kPathF32 ? 1 : 4;
-    c.split = 1;
-    if (rows_per_cu < 32 && k >= 16384) c.split = 4;
-    else if (rows_per_cu < 8 && k >= 4096) c.split = 4;
-    else if (rows_per_cu < 8 && k >= 2048) c.split = 2;
+    if (path == kPathBf16) {
+        c.split = 1;
+        if (rows_per_cu < 32 && k >= 16384) c.split = 4;
+        else if (rows_per_cu < 8 && k >= 4096) c.split = 4;
+        else if (rows_per_cu < 8 && k >= 2048) c.split = 2;
+    } else {
+        c.split = balanced_split(n, k);
+    }
     const int tw = tune_waves(), ts = tune_splitk(), tu = tune_unroll();
     if (tw == 4 || tw == 8 || tw == 16) c.waves = tw;
     if (ts == 1 || ts == 2 || ts == 4) c.split = ts;

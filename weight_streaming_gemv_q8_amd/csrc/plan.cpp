@@ -25,9 +25,10 @@ struct wsg_plan {
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     int kernels = 0;
-    // persistent plans: device descriptor table and barrier state {count, gen, err}
+    // persistent plans: device descriptor table and barrier state
     void* ops_dev = nullptr;
     uint32_t* bar_dev = nullptr;
+    void* tags_dev = nullptr;  // output copies of every op (two per op, by launch parity)
 };
 
 namespace {
@@ -120,6 +121,7 @@ void release(wsg_plan* p) {
     if (p->graph) (void)hipGraphDestroy(p->graph);
     if (p->ops_dev) (void)hipFree(p->ops_dev);
     if (p->bar_dev) (void)hipFree(p->bar_dev);
+    if (p->tags_dev) (void)hipFree(p->tags_dev);
     delete p;
 }
 
@@ -130,9 +132,12 @@ extern "C" {
 int wsg_plan_create_persistent(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_plan** out) {
     if (!ops || !out) return WSG_ERR_NULL;
     *out = nullptr;
-    if (n_ops <= 0 || n_ops >= 4096) return WSG_ERR_SHAPE;  // barrier epochs are numbered per launch
+    if (n_ops <= 0 || n_ops > 65536) return WSG_ERR_SHAPE;
     std::vector<wsg::StreamOp> table(n_ops);
-    std::vector<Range> reads, writes;  // accessed since the last barrier
+    std::vector<int> producer(n_ops, -1);   // op whose output this op's x is, or -1
+    std::vector<size_t> yc_off(n_ops, 0);   // element offset of each op's output copies
+    std::vector<size_t> yc_stride(n_ops, 0);
+    size_t yc_elems = 0;
     int max_k = 0;
     const bool f32 = ops[0].act_fmt == WSG_ACT_F32;
     for (int i = 0; i < n_ops; ++i) {
@@ -142,28 +147,30 @@ int wsg_plan_create_persistent(const wsg_op_desc* ops, int n_ops, hipStream_t st
         if ((d.act_fmt == WSG_ACT_F32) != f32) return WSG_ERR_MODE;  // one activation format per plan
         int rc = wsg::validate_gemv_q8(d.w, d.n, d.k, d.x, d.act_fmt, d.y);
         if (rc != WSG_OK) return rc;
-        if (d.n < 1 || d.k < 32) return WSG_ERR_SHAPE;
+        if (d.n < 1 || d.k < 32 || d.n > wsg::kMaxDim) return WSG_ERR_SHAPE;
         const Range rx{reinterpret_cast<uintptr_t>(d.x), reinterpret_cast<uintptr_t>(d.x) + 4 * (uintptr_t)d.k};
         const Range ry{reinterpret_cast<uintptr_t>(d.y), reinterpret_cast<uintptr_t>(d.y) + 4 * (uintptr_t)d.n};
-        bool dep = false;
-        for (const Range& w : writes) dep = dep || w.overlaps(rx) || w.overlaps(ry);
-        for (const Range& r : reads) dep = dep || r.overlaps(ry);
-        if (dep) {
-            reads.clear();
-            writes.clear();
+        // Without grid barriers, ops run concurrently with every op that is
+        // not an ancestor, so: the input is either wholly one earlier op's
+        // output (read from its tagged copy, in dataflow order) or untouched
+        // by any output of the plan; and no output may overlap another
+        // output or any input read from outside the plan.
+        for (int p = i - 1; p >= 0 && producer[i] < 0; --p) {
+            const Range yp{reinterpret_cast<uintptr_t>(ops[p].y),
+                           reinterpret_cast<uintptr_t>(ops[p].y) + 4 * (uintptr_t)ops[p].n};
+            if (!yp.overlaps(rx)) continue;
+            if (rx.lo < yp.lo || rx.hi > yp.hi || (rx.lo - yp.lo) % 4) return WSG_ERR_MODE;
+            producer[i] = p;
         }
-        reads.push_back(rx);
-        writes.push_back(ry);
-        wsg::StreamOp& t = table[i];
-        t.w = static_cast<const uint8_t*>(d.w);
-        t.x = static_cast<const float*>(d.x);
-        t.y = static_cast<float*>(d.y);
-        t.n = (int32_t)d.n;
-        t.k = (int32_t)d.k;
-        t.act = d.act_fmt;
-        t.split = wsg::stream_split(f32, d.n, d.k);
-        t.barrier = dep ? 1 : 0;
-        t.pad = 0;
+        for (int p = 0; p < n_ops; ++p) {
+            const Range yp{reinterpret_cast<uintptr_t>(ops[p].y),
+                           reinterpret_cast<uintptr_t>(ops[p].y) + 4 * (uintptr_t)ops[p].n};
+            if (p != i && yp.overlaps(ry)) return WSG_ERR_MODE;
+            if (producer[i] < 0 && yp.overlaps(rx) && p >= i) return WSG_ERR_MODE;
+        }
+        yc_off[i] = yc_elems;
+        yc_stride[i] = ((size_t)d.n + 63) & ~(size_t)63;  // 256-byte aligned copies
+        yc_elems += 2 * yc_stride[i];
         if (d.k > max_k) max_k = (int)d.k;
     }
     int waves = 0, grid = 0;
@@ -172,24 +179,55 @@ int wsg_plan_create_persistent(const wsg_op_desc* ops, int n_ops, hipStream_t st
     if (rc != WSG_OK) return rc;
     if ((int64_t)lds > wsg::device_info().max_lds) return WSG_ERR_SHAPE;
 
-    // barrier state: launch counter, release epoch, error flag, one arrival
-    // line per workgroup (128 bytes each)
-    const size_t bar_bytes = (size_t)(3 + grid) * 128;
+    const size_t state_bytes = wsg::stream_state_bytes();
     wsg_plan* p = new (std::nothrow) wsg_plan;
     if (!p) return WSG_ERR_HIP;
     if (hipMalloc(&p->ops_dev, sizeof(wsg::StreamOp) * n_ops) != hipSuccess ||
-        hipMalloc(reinterpret_cast<void**>(&p->bar_dev), bar_bytes) != hipSuccess) {
+        hipMalloc(reinterpret_cast<void**>(&p->bar_dev), state_bytes) != hipSuccess ||
+        hipMalloc(&p->tags_dev, yc_elems * sizeof(float)) != hipSuccess) {
         release(p);
         return WSG_ERR_HIP;
     }
-    const std::vector<uint32_t> zero(bar_bytes / 4, 0u);
+    float* copies = static_cast<float*>(p->tags_dev);
+    for (int i = 0; i < n_ops; ++i) {
+        const wsg_op_desc& d = ops[i];
+        wsg::StreamOp& t = table[i];
+        t.w = static_cast<const uint8_t*>(d.w);
+        t.x = static_cast<const float*>(d.x);
+        t.xs = nullptr;
+        t.xs_stride = 0;
+        if (producer[i] >= 0) {
+            const int q = producer[i];
+            const size_t off = (reinterpret_cast<uintptr_t>(d.x) - reinterpret_cast<uintptr_t>(ops[q].y)) / 4;
+            t.xs = copies + yc_off[q] + off;
+            t.xs_stride = (int64_t)yc_stride[q];
+        }
+        t.y = static_cast<float*>(d.y);
+        t.ys = copies + yc_off[i];
+        t.ys_stride = (int64_t)yc_stride[i];
+        // an op marked as depending on everything before it waits for the
+        // previous op's whole output (a later reader of it would)
+        const bool after_all = (d.flags & WSG_OP_AFTER_ALL) != 0 && i > 0;
+        t.dep = after_all ? copies + yc_off[i - 1] : nullptr;
+        t.dep_stride = after_all ? (int64_t)yc_stride[i - 1] : 0;
+        t.dep_n = after_all ? (int32_t)ops[i - 1].n : 0;
+        t.n = (int32_t)d.n;
+        t.k = (int32_t)d.k;
+        t.act = d.act_fmt;
+        t.split = wsg::stream_split(f32, d.n, d.k);
+        t.pad = 0;
+    }
+    // the state starts at zero, every output copy at "not written"
     if (hipMemcpy(p->ops_dev, table.data(), sizeof(wsg::StreamOp) * n_ops, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(p->bar_dev, zero.data(), bar_bytes, hipMemcpyHostToDevice) != hipSuccess) {
+        hipMemset(p->bar_dev, 0, state_bytes) != hipSuccess ||
+        hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(p->tags_dev), (int)wsg::kStreamSentinel, yc_elems) !=
+            hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
         release(p);
         return WSG_ERR_HIP;
     }
-    // a wait longer than ~2^22 sleeps (tenths of a second) is a failure
-    const int spin_limit = 1 << 22;
+    // a wait of more than ~2^20 polls (about a second) is a failure
+    const int spin_limit = 1 << 20;
     const wsg::StreamOp* ops_dev = static_cast<const wsg::StreamOp*>(p->ops_dev);
     rc = capture_into(p, stream, [&](hipStream_t s) {
         return wsg::stream_launch(ops_dev, n_ops, f32, p->bar_dev, grid, lds, spin_limit, s);
@@ -206,11 +244,11 @@ int wsg_plan_error(wsg_plan* plan, int* flag) {
     if (!plan || !flag) return WSG_ERR_NULL;
     *flag = 0;
     if (!plan->bar_dev) return WSG_OK;
-    uint32_t st[96] = {0};
+    uint32_t word = 0;
     if (hipDeviceSynchronize() != hipSuccess ||
-        hipMemcpy(st, plan->bar_dev, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess)
+        hipMemcpy(&word, plan->bar_dev + wsg::stream_error_word(), sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
         return WSG_ERR_HIP;
-    *flag = st[64] != 0 ? 1 : 0;  // the error word of the barrier state
+    *flag = word != 0 ? 1 : 0;
     return WSG_OK;
 }
 

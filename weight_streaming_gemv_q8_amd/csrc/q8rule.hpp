@@ -55,4 +55,29 @@ __host__ __device__ inline int q8_code_exact(float v, float d, float r) {
     return v < 0.0f ? -m : m;
 }
 
+// Branch-free form of the same rule for the common case: u = |v| r + 1/2 (one
+// fused multiply-add, so no compiler contraction can change it) and
+// m = floor(u), which equals the rule's code whenever u is at least 4e-5
+// away from an integer (then |v/d| is at least ~4e-5 - 2^-23 away from the
+// boundary m + 1/2, farther than the error of v r).  Otherwise `near` is set
+// and the caller decides the code with q8_code_exact.  Codes at and above the
+// boundary 127.5 clamp to 127 either way, so they never need the exact test.
+__host__ __device__ inline int q8_code_fast(float v, float r, bool& near) {
+    const float u = __builtin_fmaf(__builtin_fabsf(v), r, 0.5f);
+    const float fu = __builtin_floorf(u);
+    const float fr = u - fu;  // exact
+    near = (fr < 4e-5f || fr > 1.0f - 4e-5f) && u < 128.0f;
+    int m = (int)fu;
+    if (m > 127) m = 127;
+    return v < 0.0f ? -m : m;
+}
+
+// The rule as the kernels apply it: the fast form, and the exact decision
+// for values next to a boundary.
+__host__ __device__ inline int q8_code(float v, float d, float r) {
+    bool near;
+    const int q = q8_code_fast(v, r, near);
+    return near ? q8_code_exact(v, d, r) : q;
+}
+
 }  // namespace wsg

@@ -2,17 +2,30 @@
 // Q8_0 GEMVs (emit_qwen38_generate, "Where the speed comes from", items 1-2:
 // the GEMV weight stream is ~90% of a decode step and must not stall between
 // launches).  A launch per GEMV pays a ramp (first requests in flight) and a
-// tail (last workgroups finishing) every time; here every workgroup stays
-// resident, requests the next matrix's first weights as soon as it has
-// finished its rows of the current one (weights do not depend on the
-// activation), and only then waits at a grid-wide barrier for the activation
-// that the next GEMV reads.
+// tail (last workgroups finishing) every time; here one 16-wave workgroup
+// per CU stays resident for the whole token.  When a workgroup has finished
+// its rows of one GEMV it requests the first two items of weights of the
+// next GEMV (weights do not depend on the activation) and only then waits
+// for that GEMV's activation, so the weight stream keeps HBM busy across the
+// wait and the staging of the activation.
 //
-// Barrier: each workgroup posts an arrival epoch in its own cache line,
-// workgroup 0 collects them and posts a release epoch (see below).  A wait
-// that exceeds its spin limit sets an error flag and gives up, so every wave
-// always exits.  The grid never exceeds the number of co-resident
-// workgroups.
+// Dataflow instead of grid barriers: every GEMV output row is also written
+// into a copy that the plan owns, double-buffered by launch parity: the
+// value goes into this launch's buffer and a signalling-NaN sentinel into
+// the other one, which the next launch will fill.  Arithmetic never returns
+// a signalling NaN, so a GEMV whose input is an earlier GEMV's output stages
+// it from the copy and re-reads any element that still holds the sentinel:
+// an element is read only once its row is written, nothing waits for
+// stores to be acknowledged and no counter is shared.  (The buffer a launch
+// reads was reset by the previous launch, which had finished reading the
+// values of the launch before.)  The parity comes from a 64-bit launch
+// counter that every workgroup increments once at start (old value / grid:
+// all workgroups of a launch draw the same number).  Every wait is bounded:
+// on the spin limit a workgroup sets an error flag, and every wait polls
+// that flag now and then, so every wave always exits; the plan reports the
+// flag.  The grid never exceeds the number of co-resident workgroups (one
+// per CU), so a producer is never waiting for a CU that a waiting consumer
+// holds.
 #include "common.hpp"
 #include "gemv_device.hpp"
 #include "internal.hpp"
@@ -21,27 +34,13 @@
 namespace wsg {
 namespace {
 
-constexpr int kStreamWaves = 8;
-
-// Descriptor pointers are read from memory, so the compiler cannot tell they
-// point to global memory and would use flat instructions, which also count
-// against the LDS wait counter: the barrier would then wait for the weight
-// prefetch.  The weight pointer is therefore carried as a global pointer.
-constexpr int kStreamUnroll = 2;
-
-// ------------------------------------------------------------ barrier
-// Device-scope coherence without cache maintenance: outputs that another
-// workgroup reads later are written with device-scope stores (visible at
-// device level once complete) and read with device-scope loads, so no L2
-// write-back or invalidation is needed at a barrier.
-//
-// Barrier state (uint32 words, each group on its own 128-byte line):
-//   st[0]              launch counter (read at start, bumped by workgroup 0 at the end)
-//   st[32]             release epoch, written by workgroup 0
-//   st[64]             error flag
-//   st[96 + 32 * w]    arrival epoch of workgroup w
-// Barrier b of a launch uses epoch = launch * 4096 + b + 1.
-constexpr int kBarRelease = 32, kBarError = 64, kBarArrive = 96, kBarStride = 32;
+constexpr int kStreamWaves = 16;
+constexpr int kStreamUnroll = 2;  // int8 path; the f32 path loads one chunk per item
+// Plan state, in uint32 words (each on its own 128-byte line): a 64-bit
+// launch counter, the error flag.
+constexpr int kStCounter = 0, kStError = 32, kStWords = 64;
+// How often (in polls) a waiting thread also looks at the error flag.
+constexpr int kErrorPollMask = 255;
 
 __device__ inline uint32_t ld_dev(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -50,55 +49,44 @@ __device__ inline void st_dev(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Waits until this wave's outstanding vector-memory operations (its
-// device-scope output stores) have completed.
-__device__ inline void drain_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// Activation pointers are read from the descriptor table; they are carried
+// as global-address-space pointers so that their loads and stores are
+// global (not flat) instructions, which do not count against the LDS wait
+// counter.
+typedef const __attribute__((address_space(1))) float* gcfloat;
+typedef __attribute__((address_space(1))) float* gfloat;
+typedef const __attribute__((address_space(1))) uint64_t* gcu64;
+typedef const __attribute__((address_space(1))) uint32_t* gcu32;
 
-// Arrive: every wave has drained its stores; thread 0 posts the epoch.
-__device__ inline void barrier_arrive(uint32_t* st, uint32_t epoch) {
-    drain_vmem();
-    __syncthreads();
-    if (threadIdx.x == 0) st_dev(st + kBarArrive + kBarStride * blockIdx.x, epoch);
+__device__ inline uint64_t ld_dev64(gcu64 p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// "Not written yet": a signalling NaN, which no arithmetic result can be.
+constexpr uint32_t kSentinel = kStreamSentinel;
+__device__ inline bool ready(float v) { return __float_as_uint(v) != kSentinel; }
+__device__ inline bool ready4(float4v v) { return ready(v.x) && ready(v.y) && ready(v.z) && ready(v.w); }
+
+// One round of a bounded wait: counts a poll, gives up on the spin limit or
+// when another wait has given up (the error flag, looked at now and then).
+// Returns false when the caller must stop waiting.
+__device__ inline bool poll_again(uint32_t* st, int spin_limit, int& spins) {
+    if (++spins >= spin_limit) {
+        st_dev(st + kStError, 1u);
+        return false;
+    }
+    if ((spins & kErrorPollMask) == 0 && ld_dev(st + kStError) != 0u) {
+        spins = spin_limit;  // results are invalid already: stop waiting
+        return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    return true;
 }
 
-// Wait: workgroup 0 collects every arrival (one thread per workgroup) and
-// posts the release; everyone waits for it.  Each poll is bounded.
-__device__ inline void barrier_wait(uint32_t* st, uint32_t epoch, int spin_limit) {
-    if (blockIdx.x == 0) {
-        int spins = 0;  // one budget per thread for all of its flags
-        for (int w = threadIdx.x; w < (int)gridDim.x; w += blockDim.x) {
-            const uint32_t* f = st + kBarArrive + kBarStride * w;
-            while (ld_dev(f) != epoch) {
-                __builtin_amdgcn_s_sleep(1);
-                if (++spins >= spin_limit) {
-                    st_dev(st + kBarError, 1u);
-                    break;
-                }
-            }
-            if (spins >= spin_limit) break;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) st_dev(st + kBarRelease, epoch);
-    }
-    if (threadIdx.x == 0) {
-        int spins = 0;
-        while (ld_dev(st + kBarRelease) != epoch) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins >= spin_limit) {
-                st_dev(st + kBarError, 1u);
-                break;
-            }
-        }
-    }
-    __syncthreads();
-}
-
-// Device-scope loads of an f32 activation written by other workgroups in
-// this launch (8 bytes per load).
-__device__ inline float4v ld_dev_f4(const float* p) {
-    const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-    const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-scope loads of an f32 input written before the launch (8 bytes per
+// load).
+__device__ inline float4v ld_dev_f4(gcfloat p) {
+    const gcu64 q = reinterpret_cast<gcu64>(p);
+    const uint64_t a = ld_dev64(q);
+    const uint64_t b = ld_dev64(q + 1);
     float4v v;
     v.x = __uint_as_float((uint32_t)a);
     v.y = __uint_as_float((uint32_t)(a >> 32));
@@ -107,23 +95,156 @@ __device__ inline float4v ld_dev_f4(const float* p) {
     return v;
 }
 
-// Stage the activation with device-scope loads (requantized, or f32).
-__device__ inline void stage_requant_dev(const float* x, int k, int4v* lds_q, float* lds_dx) {
-    const int NB = k / kBlock;
-    for (int b = threadIdx.x; b < NB; b += blockDim.x) {
-        float4v t[8];
+// ------------------------------------------------------ activation staging
+// Requantized activation (the Q8_0 rule of quantize_act_q8_0) into the LDS
+// layout of the int8 path: four lanes per 32-value block, eight values each;
+// the block maximum meets in a quad reduction, every lane derives the same
+// scale and writes its eight codes (one 8-byte LDS store).
+__device__ inline void requant_unit(const float4v v0, const float4v v1, int u, int4v* lds_q, float* lds_dx) {
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float amax = 0.0f;
 #pragma unroll
-        for (int g = 0; g < 8; ++g) t[g] = ld_dev_f4(x + (int64_t)b * kBlock + 4 * g);
-        requant_block_to_lds(t, b, lds_q, lds_dx);
+    for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    const uint16_t d16 = q8_scale_bits(amax);
+    const float d = half_bits_to_float(d16);
+    uint32_t lo = 0, hi = 0;
+    if (d != 0.0f) {
+        const float r = 1.0f / d;
+        int q[8];
+        bool any_near = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            bool near;
+            q[i] = q8_code_fast(v[i], r, near);
+            any_near |= near;
+        }
+        if (__any(any_near)) {  // rare: a value within 4e-5 of a rounding boundary
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = q8_code(v[i], d, r);
+        }
+        lo = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) | ((uint32_t)(q[2] & 0xFF) << 16) |
+             ((uint32_t)q[3] << 24);
+        hi = (uint32_t)(q[4] & 0xFF) | ((uint32_t)(q[5] & 0xFF) << 8) | ((uint32_t)(q[6] & 0xFF) << 16) |
+             ((uint32_t)q[7] << 24);
+    }
+    const int b = u >> 2, e = u & 3;
+    const int c = b / kWave, l = b % kWave, h = e >> 1;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(lds_q + (c * 2 + h) * kWave + l) + 2 * (e & 1);
+    dst[0] = lo;
+    dst[1] = hi;
+    if (e == 0) lds_dx[b] = d;
+}
+
+// Staging of op inputs.  A unit is eight values (requantized path: four
+// lanes per 32-value block) or four values (f32 path).  Each thread first
+// requests all of its units (up to NR rounds of the workgroup) and then
+// converts them, so the staging costs one round trip when the input is
+// ready.  An input produced in this launch is read from the producer's copy;
+// each round re-requests every group of four values that still holds a
+// sentinel, so a round costs one round trip however many are missing.
+template <int NR, int G>
+__device__ inline void issue_units(gcfloat src, int base, int units, float4v (&v)[NR][G]) {
+    const int T = blockDim.x;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int u = base + threadIdx.x + i * T;
+        if (u < units) {
+#pragma unroll
+            for (int q = 0; q < G; ++q) v[i][q] = ld_dev_f4(src + (int64_t)4 * (G * u + q));
+        }
     }
 }
 
-__device__ inline void stage_f32_dev(const float* x, int k, float4v* lds_x) {
-    for (int u = threadIdx.x; u < k / 4; u += blockDim.x) lds_x[StageF32<1>::slot(u)] = ld_dev_f4(x + 4 * u);
+template <int NR, int G>
+__device__ inline void await_units(gcfloat src, int base, int units, float4v (&v)[NR][G], uint32_t* st,
+                                   int spin_limit, int& spins) {
+    const int T = blockDim.x;
+    for (;;) {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int u = base + threadIdx.x + i * T;
+#pragma unroll
+            for (int q = 0; q < G; ++q) ok = ok && (u >= units || ready4(v[i][q]));
+        }
+        if (ok || !poll_again(st, spin_limit, spins)) return;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int u = base + threadIdx.x + i * T;
+#pragma unroll
+            for (int q = 0; q < G; ++q)
+                if (u < units && !ready4(v[i][q])) v[i][q] = ld_dev_f4(src + (int64_t)4 * (G * u + q));
+        }
+    }
 }
 
-// Split-K epilogue with a run-time split factor.
-__device__ inline void finish_row_rt(float acc, int row, int n, int S, float* lds_part, float* y) {
+// src: the input (an op's own x, or the producer's copy for this launch);
+// produced: whether to wait for sentinels.
+template <int NR>
+__device__ inline void stage_requant(gcfloat src, bool produced, int k, uint32_t* st, int spin_limit,
+                                     int4v* lds_q, float* lds_dx) {
+    const int units = k / 8;
+    const int T = blockDim.x;
+    int spins = 0;
+    for (int base = 0; base < units; base += NR * T) {
+        float4v v[NR][2];
+        issue_units<NR, 2>(src, base, units, v);
+        if (produced) await_units<NR, 2>(src, base, units, v, st, spin_limit, spins);
+        // units = 4 * blocks and T is a multiple of the wave, so the four
+        // lanes of a block are in the same wave and all (in)active together
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int u = base + threadIdx.x + i * T;
+            if (u < units) requant_unit(v[i][0], v[i][1], u, lds_q, lds_dx);
+        }
+    }
+}
+
+template <int NR>
+__device__ inline void stage_f32(gcfloat src, bool produced, int k, uint32_t* st, int spin_limit, float4v* lds_x) {
+    const int units = k / 4;
+    const int T = blockDim.x;
+    int spins = 0;
+    for (int base = 0; base < units; base += NR * T) {
+        float4v v[NR][1];
+        issue_units<NR, 1>(src, base, units, v);
+        if (produced) await_units<NR, 1>(src, base, units, v, st, spin_limit, spins);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int u = base + threadIdx.x + i * T;
+            if (u < units) lds_x[StageF32<1>::slot(u)] = v[i][0];
+        }
+    }
+}
+
+// An op marked as depending on everything before it waits until the
+// previous op's whole output is written in this launch (as a reader of that
+// output would), re-reading the groups that still hold sentinels.
+__device__ inline void wait_range(gcfloat p, int n, uint32_t* st, int spin_limit) {
+    const int units = n / 4;
+    const int T = blockDim.x;
+    int spins = 0;
+    for (int base = 0; base < units; base += 4 * T) {
+        float4v v[4][1];
+        issue_units<4, 1>(p, base, units, v);
+        await_units<4, 1>(p, base, units, v, st, spin_limit, spins);
+    }
+    // the last n % 4 values, one per thread
+    const int i = 4 * units + (int)threadIdx.x;
+    if (i < n) {
+        const gcu32 q = reinterpret_cast<gcu32>(p + i);
+        while (__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kSentinel &&
+               poll_again(st, spin_limit, spins)) {
+        }
+    }
+}
+
+// Split-K epilogue with a run-time split factor: partials meet in LDS in
+// part order (the order of the eager kernels).
+__device__ inline void finish_row_rt(float acc, int row, int n, int S, float* lds_part, gfloat y, gfloat ynow,
+                                     gfloat ynext) {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int part = wave % S;
     float total = acc;
@@ -136,79 +257,182 @@ __device__ inline void finish_row_rt(float acc, int row, int n, int S, float* ld
         }
         __syncthreads();
     }
-    if (part == 0 && row < n && lane == 0)
-        __hip_atomic_store(y + row, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (part == 0 && row < n && lane == 0) {
+        y[row] = total;
+        __hip_atomic_store(ynow + row, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ynext + row, __uint_as_float(kSentinel), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Geometry of one op for this wave (wave-uniform).
+struct OpGeom {
+    gptr<uint8_t> w;
+    gcfloat src;     // staged input: the op's x, or the producer's copy for this launch
+    bool produced;   // src is a producer's copy (wait for sentinels)
+    gfloat y;
+    gfloat ynow, ynext;  // this op's copies: written now / reset for the next launch
+    int n, k, S, C, NB, nl, sbl;
+    int64_t row_bytes;
+};
+
+template <int WAVES>
+__device__ inline OpGeom op_geom(const StreamOp& op, uint32_t parity) {
+    OpGeom g;
+    g.w = (gptr<uint8_t>)op.w;
+    g.produced = op.xs != nullptr;
+    g.src = g.produced ? (gcfloat)(op.xs + parity * op.xs_stride) : (gcfloat)op.x;
+    g.y = (gfloat)op.y;
+    g.ynow = (gfloat)(op.ys + parity * op.ys_stride);
+    g.ynext = (gfloat)(op.ys + (parity ^ 1u) * op.ys_stride);
+    g.n = op.n;
+    g.k = op.k;
+    g.S = op.split;
+    g.C = (int)chunk_count(op.k);
+    g.NB = op.k / kBlock;
+    g.nl = g.NB - (g.C - 1) * kChunkBlocks;
+    g.sbl = (int)scale_section_bytes(g.nl);
+    g.row_bytes = packed_row_bytes(op.k);
+    return g;
+}
+
+template <int WAVES, int U>
+__device__ inline Sched op_sched(const OpGeom& g) {
+    return Sched(g.C, g.S, U, WAVES, g.n, (g.n + WAVES / g.S - 1) / (WAVES / g.S));
+}
+
+// Item i of this wave is (tile i / ipt, item i % ipt).  Loads item 0 into A
+// and item 1 into B, when they exist.
+template <int U>
+__device__ inline void load_first_items(const Sched& sc, const OpGeom& g, Q8Regs<U>& A, Q8Regs<U>& B) {
+    if (sc.ipt == 0 || sc.tiles_wg == 0) return;
+    const int r0 = sc.row(0);
+    if (r0 < g.n) q8_load<U>(A, g.w, g.row_bytes, sc, g.nl, g.sbl, r0, 0);
+    if (sc.ipt > 1) {
+        if (r0 < g.n) q8_load<U>(B, g.w, g.row_bytes, sc, g.nl, g.sbl, r0, 1);
+    } else if (sc.tiles_wg > 1) {
+        const int r1 = sc.row(1);
+        if (r1 < g.n) q8_load<U>(B, g.w, g.row_bytes, sc, g.nl, g.sbl, r1, 0);
+    }
+}
+
+// Runs this wave's items of one op with items 0 and 1 already requested in
+// A and B: item i is consumed from set i % 2, which is then refilled with
+// item i + 2, so one item is always in flight while another is consumed and
+// no loaded register is ever copied.  finish() runs once per tile in every
+// wave (split-K needs that).
+template <int U, typename ComputeF, typename FinishF>
+__device__ inline void run_items(const Sched& sc, const OpGeom& g, Q8Regs<U>& A, Q8Regs<U>& B, ComputeF&& compute,
+                                 FinishF&& finish) {
+    if (sc.ipt == 0) {
+        for (int j = 0; j < sc.tiles_wg; ++j) finish(0.0f, sc.row(j), false);
+        return;
+    }
+    const int total = sc.tiles_wg * sc.ipt;
+    int j = 0, m = 0;  // item being consumed
+    int jl = 0, ml = 0;  // item to request next: i + 2
+    for (int s = 0; s < 2; ++s) {
+        if (++ml == sc.ipt) {
+            ml = 0;
+            ++jl;
+        }
+    }
+    float acc = 0.0f;
+    auto step = [&](Q8Regs<U>& R) {
+        const int row = sc.row(j);
+        const bool valid = row < g.n;
+        if (valid) compute(R, row, m, acc);
+        if (m == sc.ipt - 1) {
+            if (valid) acc = wave_sum(acc);
+            finish(acc, row, valid);
+            acc = 0.0f;
+        }
+        if (jl < sc.tiles_wg) {
+            const int rl = sc.row(jl);
+            if (rl < g.n) q8_load<U>(R, g.w, g.row_bytes, sc, g.nl, g.sbl, rl, ml);
+        }
+        if (++m == sc.ipt) {
+            m = 0;
+            ++j;
+        }
+        if (++ml == sc.ipt) {
+            ml = 0;
+            ++jl;
+        }
+    };
+    for (int i = 0; i < total; i += 2) {
+        step(A);
+        if (i + 1 < total) step(B);
+    }
+}
+
+template <bool F32>
+__device__ inline void stage(const OpGeom& g, uint8_t* smem, uint32_t* st, int spin_limit) {
+    // one round trip for k up to 24576 (requantized) or 20480 (f32) at 16 waves
+    if constexpr (F32) {
+        stage_f32<5>(g.src, g.produced, g.k, st, spin_limit, reinterpret_cast<float4v*>(smem));
+    } else {
+        stage_requant<3>(g.src, g.produced, g.k, st, spin_limit, reinterpret_cast<int4v*>(smem),
+                         reinterpret_cast<float*>(smem + (size_t)g.C * 2 * kWave * 16));
+    }
 }
 
 template <int WAVES, int U, bool F32>
-__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WAVES / 4)))
 stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict__ st, int spin_limit) {
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ uint32_t launch_id;
-    if (threadIdx.x == 0) launch_id = ld_dev(st);
+    __shared__ uint32_t parity_s;
+    if (threadIdx.x == 0) {
+        const uint64_t old = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(st + kStCounter), (uint64_t)1,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        parity_s = (uint32_t)(old / gridDim.x) & 1u;
+    }
     __syncthreads();
-    uint32_t epoch = launch_id * 4096u;
-    for (int j = 0; j < n_ops; ++j) {
-        const StreamOp op = ops[j];
-        const gptr<uint8_t> opw = (gptr<uint8_t>)op.w;
-        const int n = op.n, k = op.k, S = op.split;
-        const int C = (int)chunk_count(k);
-        const int NB = k / kBlock;
-        const int nl = NB - (C - 1) * kChunkBlocks;
-        const int sbl = (int)scale_section_bytes(nl);
-        const int64_t row_bytes = packed_row_bytes(k);
-        const size_t act_bytes = F32 ? lds_f32act_bytes(C) : lds_q8act_bytes(C);
+    const uint32_t parity = parity_s;
+
+    Q8Regs<U> A, B;
+    StreamOp op = ops[0];
+    OpGeom g = op_geom<WAVES>(op, parity);
+    Sched sc = op_sched<WAVES, U>(g);
+    load_first_items<U>(sc, g, A, B);
+    for (int j = 0;;) {
+        if (op.dep) wait_range((gcfloat)(op.dep + parity * op.dep_stride), op.dep_n, st, spin_limit);
+        stage<F32>(g, smem, st, spin_limit);
+        __syncthreads();
+
+        const size_t act_bytes = F32 ? lds_f32act_bytes(g.C) : lds_q8act_bytes(g.C);
         float* lds_part = reinterpret_cast<float*>(smem + act_bytes);
         const float4v* lds_x = reinterpret_cast<const float4v*>(smem);
         const int4v* lds_q = reinterpret_cast<const int4v*>(smem);
-        const float* lds_dx = reinterpret_cast<const float*>(smem + (size_t)C * 2 * kWave * 16);
-
-        const Sched sc(C, S, U, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
-        auto load = [&](Q8Regs<U>& r, int row, int m) { q8_load<U>(r, opw, row_bytes, sc, nl, sbl, row, m); };
-
-        // arrive (outputs drained), request the next matrix's first weights,
-        // then wait for everyone else's outputs
-        Q8Regs<U> cur;
-        if (op.barrier) {
-            ++epoch;
-            barrier_arrive(st, epoch);
-            if (sc.tiles_wg > 0 && sc.ipt > 0 && sc.row(0) < n) load(cur, sc.row(0), 0);
-            barrier_wait(st, epoch, spin_limit);
-        } else {
-            if (sc.tiles_wg > 0 && sc.ipt > 0 && sc.row(0) < n) load(cur, sc.row(0), 0);
-            __syncthreads();  // the previous op's LDS contents are dead
-        }
-
-        if constexpr (F32) {
-            stage_f32_dev(op.x, k, reinterpret_cast<float4v*>(smem));
-        } else {
-            stage_requant_dev(op.x, k, reinterpret_cast<int4v*>(smem),
-                              reinterpret_cast<float*>(smem + (size_t)C * 2 * kWave * 16));
-        }
-        __syncthreads();
-
+        const float* lds_dx = reinterpret_cast<const float*>(smem + (size_t)g.C * 2 * kWave * 16);
         auto compute = [&](const Q8Regs<U>& r, int row, int m, float& acc) {
             if constexpr (F32) {
-                q8_f32_item<U>(r, sc, m, NB, lds_x, acc);
+                q8_f32_item<U>(r, sc, m, g.NB, lds_x, acc);
             } else {
-                q8_i8_item<U, false>(r, sc, m, NB, lds_q, lds_dx, row, nullptr, acc);
+                q8_i8_item<U, false>(r, sc, m, g.NB, lds_q, lds_dx, row, nullptr, acc);
             }
         };
-        row_loop(sc, cur, load, compute,
-                 [&](float acc, int row, bool) { finish_row_rt(acc, row, n, S, lds_part, op.y); });
-    }
-    // the next launch uses fresh epochs; every workgroup read the counter
-    // before its first arrival, and workgroup 0 gets here only after the
-    // last barrier
-    if (blockIdx.x == 0 && threadIdx.x == 0) st_dev(st, launch_id + 1u);
-}
+        run_items<U>(sc, g, A, B, compute, [&](float acc, int row, bool) {
+            finish_row_rt(acc, row, g.n, g.S, lds_part, g.y, g.ynow, g.ynext);
+        });
+        if (++j == n_ops) break;
 
-}  // namespace
+        op = ops[j];
+        g = op_geom<WAVES>(op, parity);
+        sc = op_sched<WAVES, U>(g);
+        load_first_items<U>(sc, g, A, B);
+        __syncthreads();  // the previous op's LDS contents are dead
+    }
+}
 
 template <bool F32>
 const void* stream_kernel_ptr() {
     return reinterpret_cast<const void*>(stream_kernel<kStreamWaves, F32 ? 1 : kStreamUnroll, F32>);
 }
+
+}  // namespace
+
+size_t stream_state_bytes() { return (size_t)kStWords * sizeof(uint32_t); }
+size_t stream_error_word() { return kStError; }
 
 int stream_config(int max_k, bool f32, int* waves, int* grid, size_t* lds) {
     const void* kern = f32 ? stream_kernel_ptr<true>() : stream_kernel_ptr<false>();
@@ -220,27 +444,26 @@ int stream_config(int max_k, bool f32, int* waves, int* grid, size_t* lds) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kStreamWaves * kWave, bytes) != hipSuccess ||
         per_cu < 1)
         return WSG_ERR_HIP;
+    // one workgroup per CU: a 16-wave workgroup at up to 128 VGPRs fills a
+    // CU's register file, so one per CU is always co-resident
     *waves = kStreamWaves;
-    *grid = device_info().cus * per_cu;
+    *grid = device_info().cus;
     *lds = bytes;
     return WSG_OK;
 }
 
-int stream_launch(const StreamOp* ops_dev, int n_ops, bool f32, uint32_t* bar_dev, int grid, size_t lds,
+int stream_launch(const StreamOp* ops_dev, int n_ops, bool f32, uint32_t* state_dev, int grid, size_t lds,
                   int spin_limit, hipStream_t stream) {
     if (f32) {
         hipLaunchKernelGGL((stream_kernel<kStreamWaves, 1, true>), dim3(grid), dim3(kStreamWaves * kWave), lds,
-                           stream, ops_dev, n_ops, bar_dev, spin_limit);
+                           stream, ops_dev, n_ops, state_dev, spin_limit);
     } else {
         hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll, false>), dim3(grid),
-                           dim3(kStreamWaves * kWave), lds, stream, ops_dev, n_ops, bar_dev, spin_limit);
+                           dim3(kStreamWaves * kWave), lds, stream, ops_dev, n_ops, state_dev, spin_limit);
     }
     return launch_status();
 }
 
-int stream_split(bool f32, int64_t n, int64_t k) {
-    const int s = gemv_split(f32, n, k);
-    return s > kStreamWaves ? kStreamWaves : s;
-}
+int stream_split(bool f32, int64_t n, int64_t k) { return gemv_split(f32, n, k); }
 
 }  // namespace wsg

@@ -154,7 +154,18 @@ class TokenStream:
         return [wsg.op_gemv_q8_0(w, s.n, s.k, s.x_ptr, fmt, s.y)]
 
     def ops(self) -> List[wsg.OpDesc]:
-        return [op for s in self.slots for op in self._slot_ops(s)]
+        """The token's calls in order.  A layer's first call is marked as
+        depending on everything before it: in a model its input comes from
+        the previous layer's output (through operators outside this stream),
+        so no plan may start it early."""
+        out = []
+        per_layer = len(self.slots) // self.layers
+        for i, s in enumerate(self.slots):
+            ops = self._slot_ops(s)
+            if i > 0 and i % per_layer == 0:
+                ops[0].flags |= wsg.OP_AFTER_ALL
+            out.extend(ops)
+        return out
 
     def run_slot(self, i: int, stream=None) -> None:
         """One GEMV of the chain, eagerly: the same calls the plan captured."""
