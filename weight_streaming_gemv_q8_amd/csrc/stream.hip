@@ -34,8 +34,15 @@
 namespace wsg {
 namespace {
 
+// One 16-wave workgroup per CU (four waves per SIMD, at most 128 VGPRs
+// each), each wave with a ring of two items of weights: one in flight while
+// the other is consumed.  (Eight waves per CU with a ring of six items keep
+// more bytes in flight but stream ~25% slower: too few waves to hide the
+// latency of the compute's own LDS reads.)
 constexpr int kStreamWaves = 16;
 constexpr int kStreamUnroll = 2;  // int8 path; the f32 path loads one chunk per item
+template <bool F32>
+constexpr int kSets = 2;
 // Plan state, in uint32 words (each on its own 128-byte line): a 64-bit
 // launch counter, the error flag.
 constexpr int kStCounter = 0, kStError = 32, kStWords = 64;
@@ -300,68 +307,71 @@ __device__ inline Sched op_sched(const OpGeom& g) {
     return Sched(g.C, g.S, U, WAVES, g.n, (g.n + WAVES / g.S - 1) / (WAVES / g.S));
 }
 
-// Item i of this wave is (tile i / ipt, item i % ipt).  Loads item 0 into A
-// and item 1 into B, when they exist.
+// Item i of this wave is (tile i / ipt, item i % ipt).
+struct ItemCursor {
+    int j = 0, m = 0;
+    __device__ void next(int ipt) {
+        if (++m == ipt) {
+            m = 0;
+            ++j;
+        }
+    }
+};
+
+// Requests item `it` into R when it exists.
 template <int U>
-__device__ inline void load_first_items(const Sched& sc, const OpGeom& g, Q8Regs<U>& A, Q8Regs<U>& B) {
-    if (sc.ipt == 0 || sc.tiles_wg == 0) return;
-    const int r0 = sc.row(0);
-    if (r0 < g.n) q8_load<U>(A, g.w, g.row_bytes, sc, g.nl, g.sbl, r0, 0);
-    if (sc.ipt > 1) {
-        if (r0 < g.n) q8_load<U>(B, g.w, g.row_bytes, sc, g.nl, g.sbl, r0, 1);
-    } else if (sc.tiles_wg > 1) {
-        const int r1 = sc.row(1);
-        if (r1 < g.n) q8_load<U>(B, g.w, g.row_bytes, sc, g.nl, g.sbl, r1, 0);
+__device__ inline void load_item(const Sched& sc, const OpGeom& g, Q8Regs<U>& R, const ItemCursor& it) {
+    if (it.j < sc.tiles_wg) {
+        const int row = sc.row(it.j);
+        if (row < g.n) q8_load<U>(R, g.w, g.row_bytes, sc, g.nl, g.sbl, row, it.m);
     }
 }
 
-// Runs this wave's items of one op with items 0 and 1 already requested in
-// A and B: item i is consumed from set i % 2, which is then refilled with
-// item i + 2, so one item is always in flight while another is consumed and
-// no loaded register is ever copied.  finish() runs once per tile in every
-// wave (split-K needs that).
-template <int U, typename ComputeF, typename FinishF>
-__device__ inline void run_items(const Sched& sc, const OpGeom& g, Q8Regs<U>& A, Q8Regs<U>& B, ComputeF&& compute,
+// Requests items 0 .. N-1 into R[0 .. N-1].
+template <int N, int U>
+__device__ inline void load_first_items(const Sched& sc, const OpGeom& g, Q8Regs<U> (&R)[N]) {
+    if (sc.ipt == 0) return;
+    ItemCursor it;
+#pragma unroll
+    for (int s = 0; s < N; ++s) {
+        load_item<U>(sc, g, R[s], it);
+        it.next(sc.ipt);
+    }
+}
+
+// Runs this wave's items of one op with items 0 .. N-1 already requested:
+// item i is consumed from set i % N, which is then refilled with item i + N,
+// so N - 1 items stay in flight while one is consumed and no loaded register
+// is ever copied (the ring is unrolled, so every set index is a constant).
+// finish() runs once per tile in every wave (split-K needs that).
+template <int N, int U, typename ComputeF, typename FinishF>
+__device__ inline void run_items(const Sched& sc, const OpGeom& g, Q8Regs<U> (&R)[N], ComputeF&& compute,
                                  FinishF&& finish) {
     if (sc.ipt == 0) {
         for (int j = 0; j < sc.tiles_wg; ++j) finish(0.0f, sc.row(j), false);
         return;
     }
     const int total = sc.tiles_wg * sc.ipt;
-    int j = 0, m = 0;  // item being consumed
-    int jl = 0, ml = 0;  // item to request next: i + 2
-    for (int s = 0; s < 2; ++s) {
-        if (++ml == sc.ipt) {
-            ml = 0;
-            ++jl;
-        }
-    }
+    ItemCursor cur, nxt;
+    for (int s = 0; s < N; ++s) nxt.next(sc.ipt);
     float acc = 0.0f;
-    auto step = [&](Q8Regs<U>& R) {
-        const int row = sc.row(j);
-        const bool valid = row < g.n;
-        if (valid) compute(R, row, m, acc);
-        if (m == sc.ipt - 1) {
-            if (valid) acc = wave_sum(acc);
-            finish(acc, row, valid);
-            acc = 0.0f;
+    for (int i = 0; i < total; i += N) {
+#pragma unroll
+        for (int s = 0; s < N; ++s) {
+            if (i + s < total) {
+                const int row = sc.row(cur.j);
+                const bool valid = row < g.n;
+                if (valid) compute(R[s], row, cur.m, acc);
+                if (cur.m == sc.ipt - 1) {
+                    if (valid) acc = wave_sum(acc);
+                    finish(acc, row, valid);
+                    acc = 0.0f;
+                }
+                load_item<U>(sc, g, R[s], nxt);
+                cur.next(sc.ipt);
+                nxt.next(sc.ipt);
+            }
         }
-        if (jl < sc.tiles_wg) {
-            const int rl = sc.row(jl);
-            if (rl < g.n) q8_load<U>(R, g.w, g.row_bytes, sc, g.nl, g.sbl, rl, ml);
-        }
-        if (++m == sc.ipt) {
-            m = 0;
-            ++j;
-        }
-        if (++ml == sc.ipt) {
-            ml = 0;
-            ++jl;
-        }
-    };
-    for (int i = 0; i < total; i += 2) {
-        step(A);
-        if (i + 1 < total) step(B);
     }
 }
 
@@ -389,11 +399,11 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
     __syncthreads();
     const uint32_t parity = parity_s;
 
-    Q8Regs<U> A, B;
+    Q8Regs<U> R[kSets<F32>];
     StreamOp op = ops[0];
     OpGeom g = op_geom<WAVES>(op, parity);
     Sched sc = op_sched<WAVES, U>(g);
-    load_first_items<U>(sc, g, A, B);
+    load_first_items<kSets<F32>, U>(sc, g, R);
     for (int j = 0;;) {
         if (op.dep) wait_range((gcfloat)(op.dep + parity * op.dep_stride), op.dep_n, st, spin_limit);
         stage<F32>(g, smem, st, spin_limit);
@@ -411,7 +421,7 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
                 q8_i8_item<U, false>(r, sc, m, g.NB, lds_q, lds_dx, row, nullptr, acc);
             }
         };
-        run_items<U>(sc, g, A, B, compute, [&](float acc, int row, bool) {
+        run_items<kSets<F32>, U>(sc, g, R, compute, [&](float acc, int row, bool) {
             finish_row_rt(acc, row, g.n, g.S, lds_part, g.y, g.ynow, g.ynext);
         });
         if (++j == n_ops) break;
@@ -419,7 +429,7 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
         op = ops[j];
         g = op_geom<WAVES>(op, parity);
         sc = op_sched<WAVES, U>(g);
-        load_first_items<U>(sc, g, A, B);
+        load_first_items<kSets<F32>, U>(sc, g, R);
         __syncthreads();  // the previous op's LDS contents are dead
     }
 }
@@ -444,8 +454,7 @@ int stream_config(int max_k, bool f32, int* waves, int* grid, size_t* lds) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kStreamWaves * kWave, bytes) != hipSuccess ||
         per_cu < 1)
         return WSG_ERR_HIP;
-    // one workgroup per CU: a 16-wave workgroup at up to 128 VGPRs fills a
-    // CU's register file, so one per CU is always co-resident
+    // one workgroup per CU (the grid never exceeds what is co-resident)
     *waves = kStreamWaves;
     *grid = device_info().cus;
     *lds = bytes;
