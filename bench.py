@@ -301,11 +301,11 @@ def label_from_rocprof(name: str):
         return f"q8_i8_kernel<waves={args[0]},split={args[1]},unroll={args[2]},{_ACT_NAMES[args[3]]}>"
     if kind in ("q8_f32_kernel", "bf16_kernel"):
         return f"{kind}<waves={args[0]},split={args[1]},unroll={args[2]},f32act>"
-    return stream_label(int(args[0]), int(args[1]), args[2] == "true")
+    return stream_label(int(args[0]), int(args[1]), int(args[2]), args[3] == "true")
 
 
-def stream_label(waves: int, unroll: int, f32: bool) -> str:
-    return f"stream_kernel<waves={waves},unroll={unroll},{'f32act' if f32 else 'requant'}>"
+def stream_label(waves: int, unroll: int, sets: int, f32: bool) -> str:
+    return f"stream_kernel<waves={waves},unroll={unroll},sets={sets},{'f32act' if f32 else 'requant'}>"
 
 
 def _read_csv(path: str):
@@ -443,7 +443,8 @@ def main() -> int:
     wtype_code = wsg.W_Q8_0 if wl.wtype == "q8_0" else wsg.W_BF16
     if persistent:
         # one launch per token: the dominant kernel is the whole stream
-        label = stream_label(16, 1 if act_fmt == wsg.ACT_F32 else 2, act_fmt == wsg.ACT_F32)
+        sc = wsg.stream_config()
+        label = stream_label(sc["waves"], sc["unroll"], sc["sets"], act_fmt == wsg.ACT_F32)
         roofline = {
             "bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": read_traffic(label),

@@ -238,9 +238,11 @@ int wsg_plan_launch(wsg_plan* plan, hipStream_t stream);
  * overlaps no op's y at all, and that no y overlaps another op's y or an
  * input read from outside the plan (WSG_ERR_MODE otherwise).  Each op
  * reduces its rows in the same order as the eager call, so results equal
- * the eager calls' bit for bit.  The plan owns a device allocation: the
- * descriptor table, a launch counter, an error flag and an 8-byte tagged
- * copy of every op's output.  A wait that exceeds its spin limit (about a
+ * the eager calls' bit for bit.  An op may have at most 64 row tiles per
+ * workgroup (rows <= 64 x CUs x 16 / split; 262,144 unsplit rows on 256
+ * CUs), else WSG_ERR_SHAPE.  The plan owns device allocations: the
+ * descriptor table, a launch counter, an error flag and two copies of every
+ * op's output (one per launch parity).  A wait that exceeds its spin limit (about a
  * second) makes the kernel give up rather than hang, every other wait of
  * that launch stops soon after, and wsg_plan_error reports it; the plan's
  * results are then invalid and it must be destroyed.  Replays of one plan
@@ -253,6 +255,10 @@ int wsg_plan_error(wsg_plan* plan, int* flag);
 int wsg_plan_destroy(wsg_plan* plan);
 /* Number of kernel launches one replay makes. */
 int wsg_plan_kernel_count(const wsg_plan* plan);
+/* Shape of the persistent plan's kernel: waves per workgroup, 2048-weight
+ * chunks per weight item and items in flight per wave (outputs nullable).
+ * For tooling; launches nothing. */
+int wsg_stream_config(int* waves, int* unroll, int* sets);
 
 /* --------------------------------------------------- measurement tools ---
  * wsg_read_probe: reads `bytes` (multiple of 16) from buf with the same

@@ -118,6 +118,13 @@ def test_plan_rejects_bad_descriptors_before_capture(L):
     assert L.wsg_plan_kernel_count(None) == -1
 
 
+def test_stream_config_reports_the_kernel_shape():
+    import weight_streaming_gemv_q8_amd as wsg
+    cfg = wsg.stream_config()
+    # 16 waves per CU, and a ring of 1-chunk items that fits 128 VGPRs
+    assert cfg["waves"] == 16 and cfg["unroll"] >= 1 and cfg["sets"] >= 2
+
+
 def test_deq_mode_mapping():
     # emit_qwen38_generate: deq 0 = int8 activations everywhere, 1 = f32 for
     # the LM head only, 2 = f32 for every Q8_0 GEMV

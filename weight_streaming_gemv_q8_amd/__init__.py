@@ -39,7 +39,7 @@ EXPORTS = (
     "quantize_q8_0_weights", "convert_bf16", "act_q8_0_bytes", "quantize_act_q8_0", "gemv_bf16",
     "gemv_q8_0", "wsg_gemv_config", "wsg_tune", "wsg_argmax_ws_bytes", "lm_head_argmax", "argmax_f32", "wsg_plan_create",
     "wsg_plan_launch", "wsg_plan_create_persistent", "wsg_plan_error", "wsg_plan_destroy", "wsg_plan_kernel_count",
-    "wsg_read_probe",
+    "wsg_stream_config", "wsg_read_probe",
     "wsg_copy_probe",
 )
 
@@ -96,6 +96,7 @@ def lib():
             "wsg_plan_error": (i32, [vp, ctypes.POINTER(i32)]),
             "wsg_plan_destroy": (i32, [vp]),
             "wsg_plan_kernel_count": (i32, [vp]),
+            "wsg_stream_config": (i32, [ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "wsg_read_probe": (i32, [vp, i64, vp, i32, vp]),
             "wsg_copy_probe": (i32, [vp, vp, i64, vp]),
         }
@@ -192,6 +193,13 @@ def gemv_config(w_type: int, act_fmt: int, n: int, k: int) -> dict:
     _check("wsg_gemv_config", lib().wsg_gemv_config(w_type, act_fmt, n, k, ctypes.byref(w), ctypes.byref(s),
                                                     ctypes.byref(u), ctypes.byref(g), ctypes.byref(lds)))
     return {"waves": w.value, "split": s.value, "unroll": u.value, "grid": g.value, "lds_bytes": lds.value}
+
+
+def stream_config() -> dict:
+    """Shape of the persistent token kernel."""
+    w, u, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check("wsg_stream_config", lib().wsg_stream_config(ctypes.byref(w), ctypes.byref(u), ctypes.byref(n)))
+    return {"waves": w.value, "unroll": u.value, "sets": n.value}
 
 
 TUNE_SPLITK, TUNE_WG_PER_CU, TUNE_WAVES, TUNE_UNROLL = 0, 1, 2, 3

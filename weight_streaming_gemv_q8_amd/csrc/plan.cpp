@@ -178,6 +178,8 @@ int wsg_plan_create_persistent(const wsg_op_desc* ops, int n_ops, hipStream_t st
     int rc = wsg::stream_config(max_k, f32, &waves, &grid, &lds);
     if (rc != WSG_OK) return rc;
     if ((int64_t)lds > wsg::device_info().max_lds) return WSG_ERR_SHAPE;
+    for (int i = 0; i < n_ops; ++i)
+        if (ops[i].n > wsg::stream_max_rows(wsg::stream_split(f32, ops[i].n, ops[i].k), grid)) return WSG_ERR_SHAPE;
 
     const size_t state_bytes = wsg::stream_state_bytes();
     wsg_plan* p = new (std::nothrow) wsg_plan;
@@ -288,5 +290,14 @@ int wsg_plan_destroy(wsg_plan* plan) {
 }
 
 int wsg_plan_kernel_count(const wsg_plan* plan) { return plan ? plan->kernels : -1; }
+
+int wsg_stream_config(int* waves, int* unroll, int* sets) {
+    int w = 0, u = 0, n = 0;
+    wsg::stream_shape(&w, &u, &n);
+    if (waves) *waves = w;
+    if (unroll) *unroll = u;
+    if (sets) *sets = n;
+    return WSG_OK;
+}
 
 }  // extern "C"

@@ -35,17 +35,22 @@ namespace wsg {
 namespace {
 
 // One 16-wave workgroup per CU (four waves per SIMD, at most 128 VGPRs
-// each), each wave with a ring of two items of weights: one in flight while
-// the other is consumed.  (Eight waves per CU with a ring of six items keep
-// more bytes in flight but stream ~25% slower: too few waves to hide the
-// latency of the compute's own LDS reads.)
+// each), each wave with a ring of three items of one chunk each: two in
+// flight while the third is consumed.  (Eight waves per CU stream ~25%
+// slower: too few waves to hide the latency of the compute's own LDS reads.
+// Deeper rings, or two chunks per item, measured slower: the activation
+// staging at each op start waits for every weight load issued before it,
+// since loads complete in order.)
 constexpr int kStreamWaves = 16;
-constexpr int kStreamUnroll = 2;  // int8 path; the f32 path loads one chunk per item
-template <bool F32>
-constexpr int kSets = 2;
+constexpr int kStreamUnroll = 1;
+constexpr int kStreamSets = 3;
 // Plan state, in uint32 words (each on its own 128-byte line): a 64-bit
-// launch counter, the error flag.
-constexpr int kStCounter = 0, kStError = 32, kStWords = 64;
+// launch counter, the error flag, and 4 KiB that weight loads with nothing
+// to fetch read instead (they stay in the L2 cache).
+constexpr int kStCounter = 0, kStError = 32, kStIdle = 1024, kStWords = 2048;
+// Most row tiles one workgroup takes in one op: the tiles' results wait in
+// LDS until the op's end.
+constexpr int kMaxTiles = 64;
 // How often (in polls) a waiting thread also looks at the error flag.
 constexpr int kErrorPollMask = 255;
 
@@ -248,26 +253,34 @@ __device__ inline void wait_range(gcfloat p, int n, uint32_t* st, int spin_limit
     }
 }
 
-// Split-K epilogue with a run-time split factor: partials meet in LDS in
-// part order (the order of the eager kernels).
-__device__ inline void finish_row_rt(float acc, int row, int n, int S, float* lds_part, gfloat y, gfloat ynow,
-                                     gfloat ynext) {
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int part = wave % S;
-    float total = acc;
-    if (S > 1) {
-        if (lane == 0) lds_part[wave] = acc;
-        __syncthreads();
-        if (part == 0) {
-            total = lds_part[wave];
-            for (int p = 1; p < S; ++p) total += lds_part[wave + p];
+// The results of a workgroup's tiles of one op wait in LDS (res[tile][wave]:
+// the wave's partial sum) until the op's end, so that the row loop issues
+// no stores: on this GPU stores count against the same in-order counter as
+// loads, and a store on some paths of the loop only would leave the
+// compiler unable to tell how many weight loads are still in flight (it
+// would then wait for all of them before every item).
+__device__ inline void keep_tile(float acc, int j, float* lds_res) {
+    if (threadIdx.x % kWave == 0) lds_res[j * (int)(blockDim.x / kWave) + (int)(threadIdx.x / kWave)] = acc;
+}
+
+// After the op's rows (and a barrier): the split-K partials meet in part
+// order (the order of the eager kernels); every row is stored in y and in
+// this launch's copy, and the next launch's copy is reset.
+__device__ inline void flush_tiles(int tiles_wg, int n, int S, const float* lds_res, gfloat y, gfloat ynow,
+                                   gfloat ynext) {
+    const int waves = (int)(blockDim.x / kWave);
+    const int groups = waves / S;
+    for (int i = (int)threadIdx.x; i < tiles_wg * groups; i += (int)blockDim.x) {
+        const int j = i / groups, grp = i % groups;
+        const int row = ((int)blockIdx.x + j * (int)gridDim.x) * groups + grp;
+        if (row < n) {
+            const float* part = lds_res + j * waves + grp * S;
+            float total = part[0];
+            for (int p = 1; p < S; ++p) total += part[p];
+            y[row] = total;
+            __hip_atomic_store(ynow + row, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ynext + row, __uint_as_float(kSentinel), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __syncthreads();
-    }
-    if (part == 0 && row < n && lane == 0) {
-        y[row] = total;
-        __hip_atomic_store(ynow + row, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(ynext + row, __uint_as_float(kSentinel), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -318,24 +331,43 @@ struct ItemCursor {
     }
 };
 
-// Requests item `it` into R when it exists.
+// Requests item `it` into R.  Every call issues the same loads, whether or
+// not the item exists: a slot with nothing to fetch (past the op's items,
+// past the matrix, or past the row's chunks) reads the idle region instead,
+// so every path through the row loop issues the same number of loads and
+// the compiler can wait for exactly one ring set at a time.
 template <int U>
-__device__ inline void load_item(const Sched& sc, const OpGeom& g, Q8Regs<U>& R, const ItemCursor& it) {
-    if (it.j < sc.tiles_wg) {
-        const int row = sc.row(it.j);
-        if (row < g.n) q8_load<U>(R, g.w, g.row_bytes, sc, g.nl, g.sbl, row, it.m);
+__device__ inline void load_item(const Sched& sc, const OpGeom& g, Q8Regs<U>& R, const ItemCursor& it,
+                                 gptr<uint8_t> idle) {
+    const int lane = threadIdx.x % kWave;
+    const int row = it.j < sc.tiles_wg ? sc.row(it.j) : g.n;
+    const bool has_row = row < g.n;
+    const gptr<uint8_t> rowp = g.w + (int64_t)(has_row ? row : 0) * g.row_bytes;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = sc.chunk(it.m, u);
+        const bool real = has_row && c < sc.C;
+        const bool last = (c == sc.C - 1);
+        const int nbc = last ? g.nl : kChunkBlocks;
+        const int sb = last ? g.sbl : 2 * kChunkBlocks;
+        // lanes past a ragged chunk's last block re-read its last block (the
+        // same cache lines); compute skips them
+        const int l = lane < nbc ? lane : nbc - 1;
+        const gptr<uint8_t> cp = real ? rowp + (int64_t)c * kFullChunkBytes : idle;
+        R.sc[u] = load_u16<true>(cp + 2 * l);
+        R.a[u] = load16<true>(cp + sb + 16 * l);
+        R.b[u] = load16<true>(cp + sb + 16 * nbc + 16 * l);
     }
 }
 
 // Requests items 0 .. N-1 into R[0 .. N-1].
 template <int N, int U>
-__device__ inline void load_first_items(const Sched& sc, const OpGeom& g, Q8Regs<U> (&R)[N]) {
-    if (sc.ipt == 0) return;
+__device__ inline void load_first_items(const Sched& sc, const OpGeom& g, Q8Regs<U> (&R)[N], gptr<uint8_t> idle) {
     ItemCursor it;
 #pragma unroll
     for (int s = 0; s < N; ++s) {
-        load_item<U>(sc, g, R[s], it);
-        it.next(sc.ipt);
+        load_item<U>(sc, g, R[s], it, idle);
+        it.next(sc.ipt == 0 ? 1 : sc.ipt);
     }
 }
 
@@ -343,12 +375,13 @@ __device__ inline void load_first_items(const Sched& sc, const OpGeom& g, Q8Regs
 // item i is consumed from set i % N, which is then refilled with item i + N,
 // so N - 1 items stay in flight while one is consumed and no loaded register
 // is ever copied (the ring is unrolled, so every set index is a constant).
-// finish() runs once per tile in every wave (split-K needs that).
-template <int N, int U, typename ComputeF, typename FinishF>
-__device__ inline void run_items(const Sched& sc, const OpGeom& g, Q8Regs<U> (&R)[N], ComputeF&& compute,
-                                 FinishF&& finish) {
+// The loop runs a multiple of N steps and every step issues one item's
+// loads.  keep(acc, tile) runs once per tile in every wave.
+template <int N, int U, typename ComputeF, typename KeepF>
+__device__ inline void run_items(const Sched& sc, const OpGeom& g, Q8Regs<U> (&R)[N], gptr<uint8_t> idle,
+                                 ComputeF&& compute, KeepF&& keep) {
     if (sc.ipt == 0) {
-        for (int j = 0; j < sc.tiles_wg; ++j) finish(0.0f, sc.row(j), false);
+        for (int j = 0; j < sc.tiles_wg; ++j) keep(0.0f, j);
         return;
     }
     const int total = sc.tiles_wg * sc.ipt;
@@ -360,17 +393,15 @@ __device__ inline void run_items(const Sched& sc, const OpGeom& g, Q8Regs<U> (&R
         for (int s = 0; s < N; ++s) {
             if (i + s < total) {
                 const int row = sc.row(cur.j);
-                const bool valid = row < g.n;
-                if (valid) compute(R[s], row, cur.m, acc);
+                if (row < g.n) compute(R[s], row, cur.m, acc);
                 if (cur.m == sc.ipt - 1) {
-                    if (valid) acc = wave_sum(acc);
-                    finish(acc, row, valid);
+                    keep(wave_sum(acc), cur.j);
                     acc = 0.0f;
                 }
-                load_item<U>(sc, g, R[s], nxt);
                 cur.next(sc.ipt);
-                nxt.next(sc.ipt);
             }
+            load_item<U>(sc, g, R[s], nxt, idle);
+            nxt.next(sc.ipt);
         }
     }
 }
@@ -386,7 +417,7 @@ __device__ inline void stage(const OpGeom& g, uint8_t* smem, uint32_t* st, int s
     }
 }
 
-template <int WAVES, int U, bool F32>
+template <int WAVES, int U, int N, bool F32>
 __global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(WAVES / 4)))
 stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict__ st, int spin_limit) {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -399,18 +430,19 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
     __syncthreads();
     const uint32_t parity = parity_s;
 
-    Q8Regs<U> R[kSets<F32>];
+    const gptr<uint8_t> idle = (gptr<uint8_t>)(const uint8_t*)(st + kStIdle);
+    Q8Regs<U> R[N];
     StreamOp op = ops[0];
     OpGeom g = op_geom<WAVES>(op, parity);
     Sched sc = op_sched<WAVES, U>(g);
-    load_first_items<kSets<F32>, U>(sc, g, R);
+    load_first_items<N, U>(sc, g, R, idle);
     for (int j = 0;;) {
         if (op.dep) wait_range((gcfloat)(op.dep + parity * op.dep_stride), op.dep_n, st, spin_limit);
         stage<F32>(g, smem, st, spin_limit);
         __syncthreads();
 
         const size_t act_bytes = F32 ? lds_f32act_bytes(g.C) : lds_q8act_bytes(g.C);
-        float* lds_part = reinterpret_cast<float*>(smem + act_bytes);
+        float* lds_res = reinterpret_cast<float*>(smem + act_bytes);
         const float4v* lds_x = reinterpret_cast<const float4v*>(smem);
         const int4v* lds_q = reinterpret_cast<const int4v*>(smem);
         const float* lds_dx = reinterpret_cast<const float*>(smem + (size_t)g.C * 2 * kWave * 16);
@@ -421,22 +453,21 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
                 q8_i8_item<U, false>(r, sc, m, g.NB, lds_q, lds_dx, row, nullptr, acc);
             }
         };
-        run_items<kSets<F32>, U>(sc, g, R, compute, [&](float acc, int row, bool) {
-            finish_row_rt(acc, row, g.n, g.S, lds_part, g.y, g.ynow, g.ynext);
-        });
+        run_items<N, U>(sc, g, R, idle, compute, [&](float acc, int t) { keep_tile(acc, t, lds_res); });
+        __syncthreads();  // every tile's partial sums are in LDS; the activation is dead
+        flush_tiles(sc.tiles_wg, g.n, g.S, lds_res, g.y, g.ynow, g.ynext);
         if (++j == n_ops) break;
 
         op = ops[j];
         g = op_geom<WAVES>(op, parity);
         sc = op_sched<WAVES, U>(g);
-        load_first_items<kSets<F32>, U>(sc, g, R);
-        __syncthreads();  // the previous op's LDS contents are dead
+        load_first_items<N, U>(sc, g, R, idle);
     }
 }
 
 template <bool F32>
 const void* stream_kernel_ptr() {
-    return reinterpret_cast<const void*>(stream_kernel<kStreamWaves, F32 ? 1 : kStreamUnroll, F32>);
+    return reinterpret_cast<const void*>(stream_kernel<kStreamWaves, kStreamUnroll, kStreamSets, F32>);
 }
 
 }  // namespace
@@ -448,7 +479,7 @@ int stream_config(int max_k, bool f32, int* waves, int* grid, size_t* lds) {
     const void* kern = f32 ? stream_kernel_ptr<true>() : stream_kernel_ptr<false>();
     const int C = (int)chunk_count(max_k);
     const size_t act = f32 ? lds_f32act_bytes(C) : lds_q8act_bytes(C);
-    const size_t bytes = act + kStreamWaves * sizeof(float) + 16;
+    const size_t bytes = act + (size_t)kMaxTiles * kStreamWaves * sizeof(float);
     if (bytes > 65536) (void)hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kStreamWaves * kWave, bytes) != hipSuccess ||
@@ -463,16 +494,20 @@ int stream_config(int max_k, bool f32, int* waves, int* grid, size_t* lds) {
 
 int stream_launch(const StreamOp* ops_dev, int n_ops, bool f32, uint32_t* state_dev, int grid, size_t lds,
                   int spin_limit, hipStream_t stream) {
-    if (f32) {
-        hipLaunchKernelGGL((stream_kernel<kStreamWaves, 1, true>), dim3(grid), dim3(kStreamWaves * kWave), lds,
-                           stream, ops_dev, n_ops, state_dev, spin_limit);
-    } else {
-        hipLaunchKernelGGL((stream_kernel<kStreamWaves, kStreamUnroll, false>), dim3(grid),
-                           dim3(kStreamWaves * kWave), lds, stream, ops_dev, n_ops, state_dev, spin_limit);
-    }
+    const void* kern = f32 ? stream_kernel_ptr<true>() : stream_kernel_ptr<false>();
+    void* args[] = {&ops_dev, &n_ops, &state_dev, &spin_limit};
+    (void)hipLaunchKernel(kern, dim3(grid), dim3(kStreamWaves * kWave), args, lds, stream);
     return launch_status();
 }
 
 int stream_split(bool f32, int64_t n, int64_t k) { return gemv_split(f32, n, k); }
+
+void stream_shape(int* waves, int* unroll, int* sets) {
+    *waves = kStreamWaves;
+    *unroll = kStreamUnroll;
+    *sets = kStreamSets;
+}
+
+int64_t stream_max_rows(int split, int grid) { return (int64_t)kMaxTiles * grid * (kStreamWaves / split); }
 
 }  // namespace wsg

@@ -37,5 +37,10 @@ int stream_config(int max_k, bool f32, int* waves, int* grid, size_t* lds);
 int stream_launch(const StreamOp* ops_dev, int n_ops, bool f32, uint32_t* state_dev, int grid, size_t lds,
                   int spin_limit, hipStream_t stream);
 int stream_split(bool f32, int64_t n, int64_t k);
+// Waves per workgroup, chunks per ring item and ring items per wave.
+void stream_shape(int* waves, int* unroll, int* sets);
+// Most rows one op may have at a split factor and grid (the tiles of a
+// workgroup wait in LDS until the op's end).
+int64_t stream_max_rows(int split, int grid);
 
 }  // namespace wsg
