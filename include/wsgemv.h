@@ -156,8 +156,9 @@ int wsg_gemv_config(int w_type, int act_fmt, int64_t n, int64_t k, int* waves, i
  * automatic choice).  WSG_TUNE_SPLITK: waves that share one row (1, 2 or
  * 4).  WSG_TUNE_WG_PER_CU: cap on workgroups per CU in the persistent grid.
  * WSG_TUNE_WAVES: waves per workgroup (4, 8 or 16).  WSG_TUNE_UNROLL:
- * chunks each wave loads ahead (2, 4 or 8; the f32 path 1, 2 or 4).  The
- * debug and argmax variants keep their default unroll.  Calls already
+ * 2048-weight chunks per weight item (1: three items in each wave's ring;
+ * 2 or 4: two items; the requantizing path at most 2, the f32 path always
+ * 1).  The debug and argmax variants keep the default (1).  Calls already
  * captured into a plan keep the configuration they were captured with.
  * Returns WSG_ERR_MODE for an unknown knob, WSG_ERR_SHAPE for a bad
  * value. */

@@ -16,8 +16,11 @@
 //  * Lane l of a wave owns block l of every 64-block chunk of a row: with the
 //    device layout it gets the block's 32 codes from two contiguous 1 KB
 //    wave loads (16 bytes per lane) and its scale from one 128-byte load.
-//  * Loads of U chunks are issued before any of them is consumed, so each
-//    lane keeps 2U 16-byte weight loads in flight.
+//  * Each wave keeps a ring of weight items (U chunks each: three one-chunk
+//    items by default) in registers: while one item is consumed the others
+//    are in flight.  Every step of the row loop issues the same loads
+//    (absent items read a small idle region), so the compiler waits for one
+//    ring set at a time rather than for every outstanding load.
 //  * No MFMA: at batch 1 there is one multiply-add per weight and no reuse.
 #include "common.hpp"
 #include "gemv_device.hpp"
@@ -32,6 +35,12 @@
 
 namespace wsg {
 namespace {
+
+// Register sets in each wave's ring of weight items of U chunks (one
+// consumed while the others are in flight): three one-chunk items, or two
+// items of two or more chunks.
+template <int U>
+constexpr int kRingSets = U == 1 ? 3 : 2;
 
 // ------------------------------------------------ Q8_0 x int8 (and requant)
 template <int WAVES, int S, int U, int ACT, bool NT, bool DEBUG, bool ARGMAX>
@@ -53,31 +62,32 @@ q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
     const int lane = threadIdx.x % kWave;
 
     const Sched sc(C, S, U, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
-    auto load = [&](Q8Regs<U>& r, int row, int m) { q8_load<U>(r, W, row_bytes, sc, nl, sbl, row, m); };
+    const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
+    auto load = [&](Q8Regs<U>& r, const ItemCursor& it) { q8_load_item<U>(r, Wg, row_bytes, sc, nl, sbl, it); };
     auto compute = [&](const Q8Regs<U>& r, int row, int m, float& acc) {
         q8_i8_item<U, DEBUG>(r, sc, m, NB, lds_q, lds_dx, row, dots, acc);
     };
 
-    Q8Regs<U> cur;
+    Q8Regs<U> R[kRingSets<U>];
     if constexpr (ACT == kActRequant) {
         StageRequant<1> st;
         st.issue(xin, k, C);
         __builtin_amdgcn_sched_barrier(0);
-        if (sc.tiles_wg > 0 && sc.ipt > 0 && sc.row(0) < n) load(cur, sc.row(0), 0);
+        ring_prologue(sc, R, load);
         __builtin_amdgcn_sched_barrier(0);
         st.commit(xin, k, C, lds_q, lds_dx);
     } else {
         StageQ8<4> st;
         st.issue(xin, k, C);
         __builtin_amdgcn_sched_barrier(0);
-        if (sc.tiles_wg > 0 && sc.ipt > 0 && sc.row(0) < n) load(cur, sc.row(0), 0);
+        ring_prologue(sc, R, load);
         __builtin_amdgcn_sched_barrier(0);
         st.commit(xin, k, C, lds_q, lds_dx);
     }
     __syncthreads();
     uint64_t best = 0;
     const int wave = threadIdx.x / kWave;
-    row_loop(sc, cur, load, compute, [&](float acc, int row, bool) {
+    ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool) {
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
     });
     if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
@@ -101,20 +111,21 @@ q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restri
     const int lane = threadIdx.x % kWave;
 
     const Sched sc(C, S, U, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
-    auto load = [&](Q8Regs<U>& r, int row, int m) { q8_load<U>(r, W, row_bytes, sc, nl, sbl, row, m); };
+    const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
+    auto load = [&](Q8Regs<U>& r, const ItemCursor& it) { q8_load_item<U>(r, Wg, row_bytes, sc, nl, sbl, it); };
     auto compute = [&](const Q8Regs<U>& r, int, int m, float& acc) { q8_f32_item<U>(r, sc, m, NB, lds_x, acc); };
 
-    Q8Regs<U> cur;
+    Q8Regs<U> R[kRingSets<U>];
     StageF32<4> st;
     st.issue(x, k);
     __builtin_amdgcn_sched_barrier(0);
-    if (sc.tiles_wg > 0 && sc.ipt > 0 && sc.row(0) < n) load(cur, sc.row(0), 0);
+    ring_prologue(sc, R, load);
     __builtin_amdgcn_sched_barrier(0);
     st.commit(x, k, lds_x);
     __syncthreads();
     uint64_t best = 0;
     const int wave = threadIdx.x / kWave;
-    row_loop(sc, cur, load, compute, [&](float acc, int row, bool) {
+    ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool) {
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
     });
     if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
@@ -134,22 +145,8 @@ bf16_kernel(const uint16_t* __restrict__ W, int n, int k, const float* __restric
     const int lane = threadIdx.x % kWave;
 
     const Sched sc(C, S, U, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
-    auto load = [&](Bf16Regs<U>& r, int row, int m) {
-        const uint16_t* rowp = W + (int64_t)row * k;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = sc.chunk(m, u);
-            if (c < C) {
-                // lanes past the end of a ragged row re-read its last 8
-                // elements (not divergent); compute skips them
-                const int e0 = c * 1024 + 8 * lane;
-                const int ea = e0 < k ? e0 : k - 8;
-                const int eb = e0 + 512 < k ? e0 + 512 : k - 8;
-                r.a[u] = load16<true>(rowp + ea);
-                r.b[u] = load16<true>(rowp + eb);
-            }
-        }
-    };
+    const gptr<uint16_t> Wg = (gptr<uint16_t>)W;
+    auto load = [&](Bf16Regs<U>& r, const ItemCursor& it) { bf16_load_item<U>(r, Wg, k, sc, it); };
     auto compute = [&](const Bf16Regs<U>& r, int, int m, float& acc) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -166,17 +163,17 @@ bf16_kernel(const uint16_t* __restrict__ W, int n, int k, const float* __restric
         }
     };
 
-    Bf16Regs<U> cur;
+    Bf16Regs<U> R[kRingSets<U>];
     StageBf16x<4> st;
     st.issue(x, k);
     __builtin_amdgcn_sched_barrier(0);
-    if (sc.tiles_wg > 0 && sc.ipt > 0 && sc.row(0) < n) load(cur, sc.row(0), 0);
+    ring_prologue(sc, R, load);
     __builtin_amdgcn_sched_barrier(0);
     st.commit(x, k, lds_x);
     __syncthreads();
     uint64_t best = 0;
     const int wave = threadIdx.x / kWave;
-    row_loop(sc, cur, load, compute, [&](float acc, int row, bool) {
+    ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool) {
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
     });
     if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
@@ -377,7 +374,9 @@ Cfg choose_cfg(Path path, int64_t n, int64_t k) {
     // matrices; 16-wave workgroups (one per CU, a quarter of the staging
     // traffic) when there are few rows per CU
     c.waves = rows_per_cu < 32 ? 16 : 8;
-    c.unroll = path == kPathF32 ? 1 : 4;
+    // one-chunk items, three in each wave's ring: measured fastest on every
+    // workload shape once the ring's loads are pipelined
+    c.unroll = 1;
     if (path == kPathBf16) {
         c.split = 1;
         if (rows_per_cu < 32 && k >= 16384) c.split = 4;
@@ -389,7 +388,7 @@ Cfg choose_cfg(Path path, int64_t n, int64_t k) {
     const int tw = tune_waves(), ts = tune_splitk(), tu = tune_unroll();
     if (tw == 4 || tw == 8 || tw == 16) c.waves = tw;
     if (ts == 1 || ts == 2 || ts == 4) c.split = ts;
-    if (tu == 1 || tu == 2 || tu == 4 || tu == 8) c.unroll = tu;
+    if (tu == 1 || tu == 2 || tu == 4) c.unroll = tu;
     if (c.split > c.waves) c.split = c.waves;
     return c;
 }
@@ -414,9 +413,9 @@ int dispatch_ws(int waves, int split, F&& f) {
     }
 }
 
-// Calls f(IC<waves>, IC<split>, IC<unroll>) with unroll from {2, 4} (int8
-// and bf16 paths); the f32 path always loads one chunk ahead (deeper unrolls
-// exceed 128 VGPRs and spill).
+// Calls f(IC<waves>, IC<split>, IC<unroll>) with unroll from {1, 2, 4}
+// (int8 and bf16 paths); the f32 path always loads one-chunk items (deeper
+// unrolls exceed 128 VGPRs and spill).
 template <bool F32, typename F>
 int dispatch_wsu(int waves, int split, int unroll, F&& f) {
     return dispatch_ws(waves, split, [&](auto W, auto S) -> int {
@@ -424,7 +423,8 @@ int dispatch_wsu(int waves, int split, int unroll, F&& f) {
             (void)unroll;
             return f(W, S, IC<1>{});
         } else {
-            if (unroll <= 2) return f(W, S, IC<2>{});
+            if (unroll <= 1) return f(W, S, IC<1>{});
+            if (unroll == 2) return f(W, S, IC<2>{});
             return f(W, S, IC<4>{});
         }
     });
@@ -443,8 +443,9 @@ int launch_kernel(K kern, size_t lds, int n, LaunchInfo* info, int unroll, bool 
     return launch_status();
 }
 
-// The debug and argmax instantiations use the default unroll (it does not
-// change the order of additions, so their results match the plain kernel).
+// The debug and argmax instantiations use the default one-chunk items (the
+// unroll does not change the order of additions, so their results match the
+// plain kernel at any unroll).
 template <int ACT, bool DEBUG, bool ARGMAX>
 int launch_q8_i8(const void* w, int n, int k, const void* x, float* y, int32_t* dots, uint64_t* keys,
                  hipStream_t stream, LaunchInfo* info, bool run = true) {
@@ -454,16 +455,22 @@ int launch_q8_i8(const void* w, int n, int k, const void* x, float* y, int32_t* 
     if constexpr (DEBUG || ARGMAX) {
         return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
             constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
-            auto kern = q8_i8_kernel<Wv, Sv, 4, ACT, true, DEBUG, ARGMAX>;
-            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, 4, run, stream, wp, n, k,
+            auto kern = q8_i8_kernel<Wv, Sv, 1, ACT, true, DEBUG, ARGMAX>;
+            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, 1, run, stream, wp, n, k,
                                          x, y, dots, keys);
         });
     } else {
-        return dispatch_wsu<false>(c.waves, c.split, c.unroll, [&](auto W, auto S, auto U) -> int {
+        // four-chunk items with the requantizing staging exceed 128 VGPRs
+        const int unroll = ACT == kActRequant && c.unroll > 2 ? 2 : c.unroll;
+        return dispatch_wsu<false>(c.waves, c.split, unroll, [&](auto W, auto S, auto U) -> int {
             constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value, Uv = decltype(U)::value;
-            auto kern = q8_i8_kernel<Wv, Sv, Uv, ACT, true, false, false>;
-            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, Uv, run, stream, wp, n, k,
-                                         x, y, dots, keys);
+            if constexpr (ACT == kActRequant && Uv > 2) {
+                return WSG_ERR_MODE;  // never dispatched
+            } else {
+                auto kern = q8_i8_kernel<Wv, Sv, Uv, ACT, true, false, false>;
+                return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, Uv, run, stream, wp, n,
+                                             k, x, y, dots, keys);
+            }
         });
     }
 }
@@ -499,8 +506,8 @@ int launch_bf16(const uint16_t* w, int n, int k, const float* x, float* y, uint6
     if constexpr (ARGMAX) {
         return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
             constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
-            auto kern = bf16_kernel<Wv, Sv, 2, true, true>;
-            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, 2, run, stream, w, n, k, x,
+            auto kern = bf16_kernel<Wv, Sv, 1, true, true>;
+            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, 1, run, stream, w, n, k, x,
                                          y, keys);
         });
     } else {
@@ -626,7 +633,7 @@ int wsg_tune(int knob, int value) {
             g_tune_waves.store(value);
             return WSG_OK;
         case WSG_TUNE_UNROLL:
-            if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8) return WSG_ERR_SHAPE;
+            if (value != 0 && value != 1 && value != 2 && value != 4) return WSG_ERR_SHAPE;
             g_tune_unroll.store(value);
             return WSG_OK;
         default: return WSG_ERR_MODE;

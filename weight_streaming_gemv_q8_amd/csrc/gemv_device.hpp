@@ -36,8 +36,11 @@ __host__ __device__ constexpr size_t lds_tail_bytes() {
 // consumed, and the loads of the first item before the activation staging
 // completes, so HBM sees requests from the first cycles of the launch.
 struct Sched {
-    int C, S, U, part, group, groups, n, tiles_wg, ipt;
-    __device__ Sched(int C_, int S_, int U_, int waves, int n_, int tiles) {
+    int C, S, U, part, group, groups, n, tiles_wg, ipt, grid;
+    __device__ Sched(int C_, int S_, int U_, int waves, int n_, int tiles) : Sched(C_, S_, U_, waves, n_, tiles, (int)gridDim.x) {}
+    // grid: the number of workgroups (gridDim.x), when the caller has it at hand
+    __device__ Sched(int C_, int S_, int U_, int waves, int n_, int tiles, int grid_) {
+        grid = grid_;
         C = C_;
         S = S_;
         U = U_;
@@ -46,11 +49,11 @@ struct Sched {
         group = wave / S;
         groups = waves / S;
         n = n_;
-        tiles_wg = blockIdx.x < (unsigned)tiles ? (tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+        tiles_wg = blockIdx.x < (unsigned)tiles ? (tiles - 1 - (int)blockIdx.x) / grid + 1 : 0;
         const int count = part < C ? (C - part + S - 1) / S : 0;
         ipt = (count + U - 1) / U;
     }
-    __device__ int row(int j) const { return ((int)blockIdx.x + j * (int)gridDim.x) * groups + group; }
+    __device__ int row(int j) const { return ((int)blockIdx.x + j * grid) * groups + group; }
     // chunk of slot u in item m
     __device__ int chunk(int m, int u) const { return part + S * (m * U + u); }
 };
@@ -95,45 +98,109 @@ __device__ inline void write_block_key(uint64_t best, int lane, int wave, uint64
     }
 }
 
-// The pipelined row loop shared by all paths.  `a` holds the wave's first
-// item (loaded by the caller before staging).  Items alternate between two
-// register sets, so the loads of item i+1 are in flight while item i is
-// consumed and no loaded register is ever copied (a copy would force a wait
-// for its load).  load(regs, row, m) issues an item's loads;
-// compute(regs, row, m, acc) consumes it; finish(acc, row, valid) ends a
-// tile (every wave calls it once per tile, as split-K needs).
-template <typename Regs, typename LoadF, typename ComputeF, typename FinishF>
-__device__ inline void row_loop(const Sched& sc, Regs& a, LoadF&& load, ComputeF&& compute, FinishF&& finish) {
-    if (sc.ipt == 0) {
-        for (int j = 0; j < sc.tiles_wg; ++j) finish(0.0f, sc.row(j), false);
+// Weight loads with nothing to fetch (past a wave's items, past the matrix,
+// past a row's chunks) read this small region instead, which stays in the
+// L2 cache.  So every path through a row loop issues the same loads, and the
+// compiler, which tracks loads in flight per program point, can wait for
+// exactly one ring set at a time; a load issued on some paths only would
+// make it wait for every outstanding load before each item.
+__device__ __align__(256) uint8_t g_idle[4096];
+__device__ inline gptr<uint8_t> idle_bytes() { return (gptr<uint8_t>)(const uint8_t*)g_idle; }
+
+// Item i of a wave's schedule is (tile i / ipt, item i % ipt).
+struct ItemCursor {
+    int j = 0, m = 0;
+    __device__ void next(int ipt) {
+        if (++m == ipt) {
+            m = 0;
+            ++j;
+        }
+    }
+};
+
+// The pipelined row loop shared by all paths: a ring of N register sets
+// holding items of weights.  A wave's T items are laid out at positions
+// pad .. P-1 of a sequence of P = T rounded up to a multiple of N positions
+// (the first pad = P - T positions hold nothing), position q in set q % N.
+// ring_prologue() requests positions 0 .. N-1 (the caller issues it before
+// the activation staging completes, so HBM sees requests from the first
+// cycles; the empty positions read the idle region).  Each step of the main
+// loop consumes position q and refills its set with position q + N, which
+// always exists, so every step issues one item's loads and N - 1 items stay
+// in flight while one is consumed; the last N positions are consumed
+// without refills, so no load is left in flight at the end.  No loaded
+// register is ever copied (a copy would force a wait for its load; the ring
+// is unrolled, so every set index is a constant).  load(regs, item) issues
+// an item's loads; compute(regs, row, m, acc) consumes it; finish(acc, j,
+// row, valid) ends tile j (every wave calls it once per tile, as split-K
+// needs).
+struct Ring {
+    int total, pad, groups;  // items, empty leading positions, groups of N positions
+    template <int N>
+    __device__ static Ring of(const Sched& sc) {
+        Ring r;
+        r.total = sc.ipt == 0 ? 0 : sc.tiles_wg * sc.ipt;
+        const int P = (r.total + N - 1) / N * N;
+        r.pad = P - r.total;
+        r.groups = P / N;
+        return r;
+    }
+};
+
+// The item at position q of the ring (q >= pad), or past the schedule.
+__device__ inline ItemCursor ring_item(const Sched& sc, const Ring& rg, int q) {
+    ItemCursor it;
+    const int i = q - rg.pad;
+    if (i < 0 || sc.ipt == 0) {
+        it.j = sc.tiles_wg;  // nothing: reads the idle region
+    } else {
+        it.j = i / sc.ipt;
+        it.m = i - it.j * sc.ipt;
+    }
+    return it;
+}
+
+template <int N, typename Regs, typename LoadF>
+__device__ inline void ring_prologue(const Sched& sc, Regs (&R)[N], LoadF&& load) {
+    const Ring rg = Ring::of<N>(sc);
+#pragma unroll
+    for (int s = 0; s < N; ++s) load(R[s], ring_item(sc, rg, s));
+}
+
+template <int N, typename Regs, typename LoadF, typename ComputeF, typename FinishF>
+__device__ inline void ring_loop(const Sched& sc, Regs (&R)[N], LoadF&& load, ComputeF&& compute,
+                                 FinishF&& finish) {
+    const Ring rg = Ring::of<N>(sc);
+    if (rg.total == 0) {
+        for (int j = 0; j < sc.tiles_wg; ++j) finish(0.0f, j, sc.row(j), false);
         return;
     }
-    Regs b;
+    ItemCursor cur;                             // the next item to consume
+    ItemCursor nxt = ring_item(sc, rg, N);      // the next item to request
     float acc = 0.0f;
-    int j = 0, m = 0;  // current item
-    auto step = [&](Regs& cur, Regs& nxt) {
-        const int jn = (m + 1 < sc.ipt) ? j : j + 1;
-        const int mn = (m + 1 < sc.ipt) ? m + 1 : 0;
-        if (jn < sc.tiles_wg) {
-            const int rown = sc.row(jn);
-            if (rown < sc.n) load(nxt, rown, mn);
-        }
-        const int row = sc.row(j);
+    auto consume = [&](Regs& r, int q) {
+        if (q < rg.pad) return;
+        const int row = sc.row(cur.j);
         const bool valid = row < sc.n;
-        if (valid) compute(cur, row, m, acc);
-        if (m == sc.ipt - 1) {
+        if (valid) compute(r, row, cur.m, acc);
+        if (cur.m == sc.ipt - 1) {
             if (valid) acc = wave_sum(acc);
-            finish(acc, row, valid);
+            finish(acc, cur.j, row, valid);
             acc = 0.0f;
         }
-        j = jn;
-        m = mn;
+        cur.next(sc.ipt);
     };
-    while (j < sc.tiles_wg) {
-        step(a, b);
-        if (j >= sc.tiles_wg) break;
-        step(b, a);
+    for (int g = 0; g + 1 < rg.groups; ++g) {
+#pragma unroll
+        for (int s = 0; s < N; ++s) {
+            consume(R[s], g * N + s);
+            load(R[s], nxt);
+            nxt.next(sc.ipt);
+        }
     }
+    const int q0 = (rg.groups - 1) * N;
+#pragma unroll
+    for (int s = 0; s < N; ++s) consume(R[s], q0 + s);
 }
 
 // ------------------------------------------------------ Q8_0 weight items
@@ -143,30 +210,30 @@ struct Q8Regs {
     uint16_t sc[U];
 };
 
-// P: const uint8_t* (a kernel argument, known global) or gptr<uint8_t> (a
-// pointer read from a descriptor).
-template <int U, typename P>
-__device__ inline void q8_load(Q8Regs<U>& r, P W, int64_t row_bytes, const Sched& sc, int nl, int sbl, int row,
-                               int m) {
+// Requests item `it` of the wave's schedule: U chunks of one row, 3U loads
+// whether or not the item, the row or a chunk exists (those read the idle
+// region).  Lanes past a ragged chunk's last block re-read its last block
+// (the same cache lines), so the loads are not divergent; compute skips
+// them.
+template <int U>
+__device__ inline void q8_load_item(Q8Regs<U>& r, gptr<uint8_t> W, int64_t row_bytes, const Sched& sc, int nl,
+                                    int sbl, const ItemCursor& it) {
     const int lane = threadIdx.x % kWave;
-    const P rowp = W + (int64_t)row * row_bytes;
+    const int row = it.j < sc.tiles_wg ? sc.row(it.j) : sc.n;
+    const bool has_row = row < sc.n;
+    const gptr<uint8_t> rowp = W + (int64_t)(has_row ? row : 0) * row_bytes;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int c = sc.chunk(m, u);
-        // slots past the last chunk load nothing (a wave-uniform branch);
-        // lanes past a ragged chunk's last block re-read its last block (the
-        // same cache lines), so the loads are not divergent; compute skips
-        // both
-        if (c < sc.C) {
-            const bool last = (c == sc.C - 1);
-            const int nbc = last ? nl : kChunkBlocks;
-            const int sb = last ? sbl : 2 * kChunkBlocks;
-            const int l = lane < nbc ? lane : nbc - 1;
-            const P cp = rowp + (int64_t)c * kFullChunkBytes;
-            r.sc[u] = load_u16<true>(cp + 2 * l);
-            r.a[u] = load16<true>(cp + sb + 16 * l);
-            r.b[u] = load16<true>(cp + sb + 16 * nbc + 16 * l);
-        }
+        const int c = sc.chunk(it.m, u);
+        const bool real = has_row && c < sc.C;
+        const bool last = (c == sc.C - 1);
+        const int nbc = last ? nl : kChunkBlocks;
+        const int sb = last ? sbl : 2 * kChunkBlocks;
+        const int l = lane < nbc ? lane : nbc - 1;
+        const gptr<uint8_t> cp = real ? rowp + (int64_t)c * kFullChunkBytes : idle_bytes();
+        r.sc[u] = load_u16<true>(cp + 2 * l);
+        r.a[u] = load16<true>(cp + sb + 16 * l);
+        r.b[u] = load16<true>(cp + sb + 16 * nbc + 16 * l);
     }
 }
 
@@ -355,6 +422,30 @@ template <int U>
 struct Bf16Regs {
     int4v a[U], b[U];
 };
+
+// Requests item `it`: U 1024-element chunks of one bf16 row, 2U loads
+// whether or not the item, the row or a chunk exists (those read the idle
+// region).  Lanes past the end of a ragged row re-read its last 8 elements
+// (not divergent); compute skips them.
+template <int U>
+__device__ inline void bf16_load_item(Bf16Regs<U>& r, gptr<uint16_t> W, int k, const Sched& sc,
+                                      const ItemCursor& it) {
+    const int lane = threadIdx.x % kWave;
+    const int row = it.j < sc.tiles_wg ? sc.row(it.j) : sc.n;
+    const bool has_row = row < sc.n;
+    const gptr<uint16_t> rowp = W + (int64_t)(has_row ? row : 0) * k;
+    const gptr<uint16_t> idle = (gptr<uint16_t>)idle_bytes() + 8 * lane;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = sc.chunk(it.m, u);
+        const bool real = has_row && c < sc.C;
+        const int e0 = c * 1024 + 8 * lane;
+        const int ea = e0 < k ? e0 : k - 8;
+        const int eb = e0 + 512 < k ? e0 + 512 : k - 8;
+        r.a[u] = load16<true>(real ? rowp + ea : idle);
+        r.b[u] = load16<true>(real ? rowp + eb : idle);
+    }
+}
 
 // Makes a loaded value opaque to the optimizer at its point of use, so that
 // byte or half extraction is not folded back into the (conditional) block

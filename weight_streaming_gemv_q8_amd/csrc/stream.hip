@@ -45,9 +45,8 @@ constexpr int kStreamWaves = 16;
 constexpr int kStreamUnroll = 1;
 constexpr int kStreamSets = 3;
 // Plan state, in uint32 words (each on its own 128-byte line): a 64-bit
-// launch counter, the error flag, and 4 KiB that weight loads with nothing
-// to fetch read instead (they stay in the L2 cache).
-constexpr int kStCounter = 0, kStError = 32, kStIdle = 1024, kStWords = 2048;
+// launch counter, the error flag.
+constexpr int kStCounter = 0, kStError = 32, kStWords = 64;
 // Most row tiles one workgroup takes in one op: the tiles' results wait in
 // LDS until the op's end.
 constexpr int kMaxTiles = 64;
@@ -320,92 +319,6 @@ __device__ inline Sched op_sched(const OpGeom& g) {
     return Sched(g.C, g.S, U, WAVES, g.n, (g.n + WAVES / g.S - 1) / (WAVES / g.S));
 }
 
-// Item i of this wave is (tile i / ipt, item i % ipt).
-struct ItemCursor {
-    int j = 0, m = 0;
-    __device__ void next(int ipt) {
-        if (++m == ipt) {
-            m = 0;
-            ++j;
-        }
-    }
-};
-
-// Requests item `it` into R.  Every call issues the same loads, whether or
-// not the item exists: a slot with nothing to fetch (past the op's items,
-// past the matrix, or past the row's chunks) reads the idle region instead,
-// so every path through the row loop issues the same number of loads and
-// the compiler can wait for exactly one ring set at a time.
-template <int U>
-__device__ inline void load_item(const Sched& sc, const OpGeom& g, Q8Regs<U>& R, const ItemCursor& it,
-                                 gptr<uint8_t> idle) {
-    const int lane = threadIdx.x % kWave;
-    const int row = it.j < sc.tiles_wg ? sc.row(it.j) : g.n;
-    const bool has_row = row < g.n;
-    const gptr<uint8_t> rowp = g.w + (int64_t)(has_row ? row : 0) * g.row_bytes;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = sc.chunk(it.m, u);
-        const bool real = has_row && c < sc.C;
-        const bool last = (c == sc.C - 1);
-        const int nbc = last ? g.nl : kChunkBlocks;
-        const int sb = last ? g.sbl : 2 * kChunkBlocks;
-        // lanes past a ragged chunk's last block re-read its last block (the
-        // same cache lines); compute skips them
-        const int l = lane < nbc ? lane : nbc - 1;
-        const gptr<uint8_t> cp = real ? rowp + (int64_t)c * kFullChunkBytes : idle;
-        R.sc[u] = load_u16<true>(cp + 2 * l);
-        R.a[u] = load16<true>(cp + sb + 16 * l);
-        R.b[u] = load16<true>(cp + sb + 16 * nbc + 16 * l);
-    }
-}
-
-// Requests items 0 .. N-1 into R[0 .. N-1].
-template <int N, int U>
-__device__ inline void load_first_items(const Sched& sc, const OpGeom& g, Q8Regs<U> (&R)[N], gptr<uint8_t> idle) {
-    ItemCursor it;
-#pragma unroll
-    for (int s = 0; s < N; ++s) {
-        load_item<U>(sc, g, R[s], it, idle);
-        it.next(sc.ipt == 0 ? 1 : sc.ipt);
-    }
-}
-
-// Runs this wave's items of one op with items 0 .. N-1 already requested:
-// item i is consumed from set i % N, which is then refilled with item i + N,
-// so N - 1 items stay in flight while one is consumed and no loaded register
-// is ever copied (the ring is unrolled, so every set index is a constant).
-// The loop runs a multiple of N steps and every step issues one item's
-// loads.  keep(acc, tile) runs once per tile in every wave.
-template <int N, int U, typename ComputeF, typename KeepF>
-__device__ inline void run_items(const Sched& sc, const OpGeom& g, Q8Regs<U> (&R)[N], gptr<uint8_t> idle,
-                                 ComputeF&& compute, KeepF&& keep) {
-    if (sc.ipt == 0) {
-        for (int j = 0; j < sc.tiles_wg; ++j) keep(0.0f, j);
-        return;
-    }
-    const int total = sc.tiles_wg * sc.ipt;
-    ItemCursor cur, nxt;
-    for (int s = 0; s < N; ++s) nxt.next(sc.ipt);
-    float acc = 0.0f;
-    for (int i = 0; i < total; i += N) {
-#pragma unroll
-        for (int s = 0; s < N; ++s) {
-            if (i + s < total) {
-                const int row = sc.row(cur.j);
-                if (row < g.n) compute(R[s], row, cur.m, acc);
-                if (cur.m == sc.ipt - 1) {
-                    keep(wave_sum(acc), cur.j);
-                    acc = 0.0f;
-                }
-                cur.next(sc.ipt);
-            }
-            load_item<U>(sc, g, R[s], nxt, idle);
-            nxt.next(sc.ipt);
-        }
-    }
-}
-
 template <bool F32>
 __device__ inline void stage(const OpGeom& g, uint8_t* smem, uint32_t* st, int spin_limit) {
     // one round trip for k up to 24576 (requantized) or 20480 (f32) at 16 waves
@@ -430,12 +343,14 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
     __syncthreads();
     const uint32_t parity = parity_s;
 
-    const gptr<uint8_t> idle = (gptr<uint8_t>)(const uint8_t*)(st + kStIdle);
     Q8Regs<U> R[N];
     StreamOp op = ops[0];
     OpGeom g = op_geom<WAVES>(op, parity);
     Sched sc = op_sched<WAVES, U>(g);
-    load_first_items<N, U>(sc, g, R, idle);
+    // every path issues the same loads (see q8_load_item), so the compiler
+    // waits for exactly one ring set at a time
+    auto load = [&](Q8Regs<U>& r, const ItemCursor& it) { q8_load_item<U>(r, g.w, g.row_bytes, sc, g.nl, g.sbl, it); };
+    ring_prologue(sc, R, load);
     for (int j = 0;;) {
         if (op.dep) wait_range((gcfloat)(op.dep + parity * op.dep_stride), op.dep_n, st, spin_limit);
         stage<F32>(g, smem, st, spin_limit);
@@ -453,7 +368,7 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
                 q8_i8_item<U, false>(r, sc, m, g.NB, lds_q, lds_dx, row, nullptr, acc);
             }
         };
-        run_items<N, U>(sc, g, R, idle, compute, [&](float acc, int t) { keep_tile(acc, t, lds_res); });
+        ring_loop(sc, R, load, compute, [&](float acc, int t, int, bool) { keep_tile(acc, t, lds_res); });
         __syncthreads();  // every tile's partial sums are in LDS; the activation is dead
         flush_tiles(sc.tiles_wg, g.n, g.S, lds_res, g.y, g.ynow, g.ynext);
         if (++j == n_ops) break;
@@ -461,7 +376,7 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
         op = ops[j];
         g = op_geom<WAVES>(op, parity);
         sc = op_sched<WAVES, U>(g);
-        load_first_items<N, U>(sc, g, R, idle);
+        ring_prologue(sc, R, load);
     }
 }
 
