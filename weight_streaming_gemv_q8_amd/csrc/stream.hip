@@ -4,10 +4,14 @@
 // launches).  A launch per GEMV pays a ramp (first requests in flight) and a
 // tail (last workgroups finishing) every time; here one 16-wave workgroup
 // per CU stays resident for the whole token.  When a workgroup has finished
-// its rows of one GEMV it requests the first two items of weights of the
-// next GEMV (weights do not depend on the activation) and only then waits
-// for that GEMV's activation, so the weight stream keeps HBM busy across the
-// wait and the staging of the activation.
+// its rows of one GEMV and stored them, it requests the first three items of
+// weights of the next GEMV (weights do not depend on the activation) and
+// only then waits for that GEMV's activation, so the weight stream keeps HBM
+// busy across the wait and the staging of the activation.  (Requesting them
+// earlier -- before the stores, or while the last rows are still computed --
+// measured slower: the stores and the stragglers' loads then queue behind
+// them, and the stores of the last workgroup are what every other one waits
+// for.)
 //
 // Dataflow instead of grid barriers: every GEMV output row is also written
 // into a copy that the plan owns, double-buffered by launch parity: the
@@ -44,6 +48,7 @@ namespace {
 constexpr int kStreamWaves = 16;
 constexpr int kStreamUnroll = 1;
 constexpr int kStreamSets = 3;
+constexpr int kStreamThreads = kStreamWaves * kWave;
 // Plan state, in uint32 words (each on its own 128-byte line): a 64-bit
 // launch counter, the error flag.
 constexpr int kStCounter = 0, kStError = 32, kStWords = 64;
@@ -157,7 +162,7 @@ __device__ inline void requant_unit(const float4v v0, const float4v v1, int u, i
 // sentinel, so a round costs one round trip however many are missing.
 template <int NR, int G>
 __device__ inline void issue_units(gcfloat src, int base, int units, float4v (&v)[NR][G]) {
-    const int T = blockDim.x;
+    constexpr int T = kStreamThreads;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const int u = base + threadIdx.x + i * T;
@@ -171,7 +176,7 @@ __device__ inline void issue_units(gcfloat src, int base, int units, float4v (&v
 template <int NR, int G>
 __device__ inline void await_units(gcfloat src, int base, int units, float4v (&v)[NR][G], uint32_t* st,
                                    int spin_limit, int& spins) {
-    const int T = blockDim.x;
+    constexpr int T = kStreamThreads;
     for (;;) {
         bool ok = true;
 #pragma unroll
@@ -197,7 +202,7 @@ template <int NR>
 __device__ inline void stage_requant(gcfloat src, bool produced, int k, uint32_t* st, int spin_limit,
                                      int4v* lds_q, float* lds_dx) {
     const int units = k / 8;
-    const int T = blockDim.x;
+    constexpr int T = kStreamThreads;
     int spins = 0;
     for (int base = 0; base < units; base += NR * T) {
         float4v v[NR][2];
@@ -216,7 +221,7 @@ __device__ inline void stage_requant(gcfloat src, bool produced, int k, uint32_t
 template <int NR>
 __device__ inline void stage_f32(gcfloat src, bool produced, int k, uint32_t* st, int spin_limit, float4v* lds_x) {
     const int units = k / 4;
-    const int T = blockDim.x;
+    constexpr int T = kStreamThreads;
     int spins = 0;
     for (int base = 0; base < units; base += NR * T) {
         float4v v[NR][1];
@@ -235,7 +240,7 @@ __device__ inline void stage_f32(gcfloat src, bool produced, int k, uint32_t* st
 // output would), re-reading the groups that still hold sentinels.
 __device__ inline void wait_range(gcfloat p, int n, uint32_t* st, int spin_limit) {
     const int units = n / 4;
-    const int T = blockDim.x;
+    constexpr int T = kStreamThreads;
     int spins = 0;
     for (int base = 0; base < units; base += 4 * T) {
         float4v v[4][1];
@@ -259,19 +264,19 @@ __device__ inline void wait_range(gcfloat p, int n, uint32_t* st, int spin_limit
 // compiler unable to tell how many weight loads are still in flight (it
 // would then wait for all of them before every item).
 __device__ inline void keep_tile(float acc, int j, float* lds_res) {
-    if (threadIdx.x % kWave == 0) lds_res[j * (int)(blockDim.x / kWave) + (int)(threadIdx.x / kWave)] = acc;
+    if (threadIdx.x % kWave == 0) lds_res[j * kStreamWaves + (int)(threadIdx.x / kWave)] = acc;
 }
 
 // After the op's rows (and a barrier): the split-K partials meet in part
 // order (the order of the eager kernels); every row is stored in y and in
 // this launch's copy, and the next launch's copy is reset.
-__device__ inline void flush_tiles(int tiles_wg, int n, int S, const float* lds_res, gfloat y, gfloat ynow,
-                                   gfloat ynext) {
-    const int waves = (int)(blockDim.x / kWave);
+__device__ inline void flush_tiles(int tiles_wg, int grid, int n, int S, const float* lds_res, gfloat y,
+                                   gfloat ynow, gfloat ynext) {
+    constexpr int waves = kStreamWaves;
     const int groups = waves / S;
-    for (int i = (int)threadIdx.x; i < tiles_wg * groups; i += (int)blockDim.x) {
+    for (int i = (int)threadIdx.x; i < tiles_wg * groups; i += kStreamThreads) {
         const int j = i / groups, grp = i % groups;
-        const int row = ((int)blockIdx.x + j * (int)gridDim.x) * groups + grp;
+        const int row = ((int)blockIdx.x + j * grid) * groups + grp;
         if (row < n) {
             const float* part = lds_res + j * waves + grp * S;
             float total = part[0];
@@ -315,9 +320,13 @@ __device__ inline OpGeom op_geom(const StreamOp& op, uint32_t parity) {
 }
 
 template <int WAVES, int U>
-__device__ inline Sched op_sched(const OpGeom& g) {
-    return Sched(g.C, g.S, U, WAVES, g.n, (g.n + WAVES / g.S - 1) / (WAVES / g.S));
+__device__ inline Sched op_sched(const OpGeom& g, int grid) {
+    return Sched(g.C, g.S, U, WAVES, g.n, (g.n + WAVES / g.S - 1) / (WAVES / g.S), grid);
 }
+
+// s_waitcnt immediate (gfx9 encoding): vector memory count 0, the export and
+// LDS/scalar counts at their maxima (no wait).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <bool F32>
 __device__ inline void stage(const OpGeom& g, uint8_t* smem, uint32_t* st, int spin_limit) {
@@ -342,11 +351,12 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
     }
     __syncthreads();
     const uint32_t parity = parity_s;
+    const int grid = (int)gridDim.x;
 
     Q8Regs<U> R[N];
     StreamOp op = ops[0];
     OpGeom g = op_geom<WAVES>(op, parity);
-    Sched sc = op_sched<WAVES, U>(g);
+    Sched sc = op_sched<WAVES, U>(g, grid);
     // every path issues the same loads (see q8_load_item), so the compiler
     // waits for exactly one ring set at a time
     auto load = [&](Q8Regs<U>& r, const ItemCursor& it) { q8_load_item<U>(r, g.w, g.row_bytes, sc, g.nl, g.sbl, it); };
@@ -354,6 +364,10 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
     for (int j = 0;;) {
         if (op.dep) wait_range((gcfloat)(op.dep + parity * op.dep_stride), op.dep_n, st, spin_limit);
         stage<F32>(g, smem, st, spin_limit);
+        // the staging has waited for every load before it (they complete in
+        // order); saying so lets the compiler know it on every path, so the
+        // row loop starts from a known count and its waits stay exact
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
 
         const size_t act_bytes = F32 ? lds_f32act_bytes(g.C) : lds_q8act_bytes(g.C);
@@ -370,12 +384,12 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
         };
         ring_loop(sc, R, load, compute, [&](float acc, int t, int, bool) { keep_tile(acc, t, lds_res); });
         __syncthreads();  // every tile's partial sums are in LDS; the activation is dead
-        flush_tiles(sc.tiles_wg, g.n, g.S, lds_res, g.y, g.ynow, g.ynext);
+        flush_tiles(sc.tiles_wg, grid, g.n, g.S, lds_res, g.y, g.ynow, g.ynext);
         if (++j == n_ops) break;
 
         op = ops[j];
         g = op_geom<WAVES>(op, parity);
-        sc = op_sched<WAVES, U>(g);
+        sc = op_sched<WAVES, U>(g, grid);
         ring_prologue(sc, R, load);
     }
 }
