@@ -325,15 +325,25 @@ def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, copy_fetc
     written = []
     # kernel durations
     stats = _read_csv(os.path.join(stats_dir, "run_kernel_stats.csv"))
+    # per-dispatch durations, for the median (the average includes the
+    # untimed first launches, whose weights are not yet warm in the TLBs)
+    durations = collections.defaultdict(list)
+    trace = os.path.join(stats_dir, "run_kernel_trace.csv")
+    if os.path.exists(trace):
+        for r in _read_csv(trace):
+            durations[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     path = os.path.join(PROFILES, f"kernel_stats_{workload}.txt")
     with open(path, "w") as f:
         f.write(f"# rocprofv3 kernel statistics, {workload}\n# command: {commands['stats']}\n")
-        f.write(f"# {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10} {'pct':>6}  kernel\n")
+        f.write(f"# {'calls':>6} {'avg_us':>10} {'median_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10} "
+                f"{'pct':>6}  kernel\n")
         for r in stats:
             lab = label_from_rocprof(r["Name"]) or r["Name"][:80]
-            f.write(f"  {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
-                    f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e6:10.3f} "
-                    f"{float(r['Percentage']):6.2f}  {lab}\n")
+            d = sorted(durations.get(r["Name"], []))
+            med = d[len(d) // 2] / 1e3 if d else float("nan")
+            f.write(f"  {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {med:10.2f} "
+                    f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                    f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}  {lab}\n")
     written.append(path)
 
     def per_kernel(d, counter):
