@@ -263,8 +263,10 @@ __device__ inline void wait_range(gcfloat p, int n, uint32_t* st, int spin_limit
 // loads, and a store on some paths of the loop only would leave the
 // compiler unable to tell how many weight loads are still in flight (it
 // would then wait for all of them before every item).
-__device__ inline void keep_tile(float acc, int j, float* lds_res) {
-    if (threadIdx.x % kWave == 0) lds_res[j * kStreamWaves + (int)(threadIdx.x / kWave)] = acc;
+// res[tile][group * S + part] holds the partial sum of that part of the
+// group's row of the tile.
+__device__ inline void keep_part(float acc, int j, int slot, float* lds_res) {
+    if (threadIdx.x % kWave == 0) lds_res[j * kStreamWaves + slot] = acc;
 }
 
 // After the op's rows (and a barrier): the split-K partials meet in part
@@ -324,6 +326,152 @@ __device__ inline Sched op_sched(const OpGeom& g, int grid) {
     return Sched(g.C, g.S, U, WAVES, g.n, (g.n + WAVES / g.S - 1) / (WAVES / g.S), grid);
 }
 
+// ------------------------------------------------------- rotating parts
+// With split-K (S > 1) a row's chunks are dealt to S parts (part p takes
+// chunks p, p + S, ...), and when the chunks do not divide evenly the low
+// parts take more (the 27B down projection: 3, 2, 2, 2 chunks).  A wave
+// that played part 0 in every tile would do half as much again as the
+// others and hold up the workgroup at every GEMV's end, so the wave of
+// group slot w plays part (w + tile) % S: the heavy part passes round the
+// waves.  Each part's partial sum is the same computation whichever wave
+// makes it, and the parts still meet in part order, so results equal the
+// eager kernels' bit for bit.
+struct RotSched {
+    const Sched* sc;
+    int wp;          // this wave's slot within its group (its part in tile 0)
+    int base, rem;   // part p takes base + (p < rem) chunks (S is a power of two)
+    __device__ void set(const Sched& s, int slot) {
+        sc = &s;
+        wp = slot & (s.S - 1);
+        base = s.C >> __builtin_ctz(s.S);
+        rem = s.C & (s.S - 1);
+    }
+    __device__ int part(int j) const { return (wp + j) & (sc->S - 1); }
+    __device__ int items_of(int p) const { return base + (p < rem ? 1 : 0); }
+    __device__ int items(int j) const { return items_of(part(j)); }
+    // the wave's items over all its tiles
+    __device__ int total() const {
+        int t = 0;
+        for (int p = 0; p < sc->S; ++p) {
+            const int j0 = (p - wp) & (sc->S - 1);
+            if (j0 < sc->tiles_wg) t += ((sc->tiles_wg - 1 - j0) >> __builtin_ctz(sc->S)) * items_of(p) + items_of(p);
+        }
+        return t;
+    }
+};
+
+// Walks a wave's items in order: (tile j, item m of that tile, its part p
+// and item count); j reaches tiles_wg past the last item.
+struct RotCursor {
+    int j = 0, m = 0, p = 0, ipt = 0;
+    __device__ void start(const RotSched& rs) {
+        j = 0;
+        m = 0;
+        p = rs.wp;
+        ipt = rs.items_of(p);
+        if (ipt == 0) skip_empty(rs);
+    }
+    __device__ void skip_empty(const RotSched& rs) {  // only when a part has no chunks (C < S)
+        while (j < rs.sc->tiles_wg && ipt == 0) {
+            ++j;
+            p = (p + 1) & (rs.sc->S - 1);
+            ipt = rs.items_of(p);
+        }
+    }
+    __device__ void next(const RotSched& rs) {
+        if (++m == ipt) {
+            m = 0;
+            ++j;
+            p = (p + 1) & (rs.sc->S - 1);
+            ipt = rs.items_of(p);
+            if (ipt == 0) skip_empty(rs);
+        }
+    }
+};
+
+// One item: chunk part(j) + S * m of the group's row of tile j (3 loads;
+// the idle region past the wave's items or the matrix, see q8_load_item).
+template <int U>
+__device__ inline void load_rot(Q8Regs<U>& R, const OpGeom& g, const RotSched& rs, const RotCursor& it) {
+    static_assert(U == 1, "one chunk per item");
+    const Sched& sc = *rs.sc;
+    const int lane = threadIdx.x % kWave;
+    const bool has_item = it.j < sc.tiles_wg;
+    const int row = has_item ? sc.row(it.j) : sc.n;
+    const bool has_row = row < sc.n;
+    const int c = has_item ? it.p + sc.S * it.m : sc.C;
+    const bool real = has_row && c < sc.C;
+    const bool last = (c == sc.C - 1);
+    const int nbc = last ? g.nl : kChunkBlocks;
+    const int sb = last ? g.sbl : 2 * kChunkBlocks;
+    const int l = lane < nbc ? lane : nbc - 1;
+    const gptr<uint8_t> cp = real ? g.w + (int64_t)row * g.row_bytes + (int64_t)c * kFullChunkBytes : idle_bytes();
+    R.sc[0] = load_u16<true>(cp + 2 * l);
+    R.a[0] = load16<true>(cp + sb + 16 * l);
+    R.b[0] = load16<true>(cp + sb + 16 * nbc + 16 * l);
+}
+
+// The ring over a wave's items, as ring_loop (every step issues one item's
+// loads, the padding at the front, the last N items drained without
+// refills), with rotating parts.
+template <int N>
+__device__ inline void rot_prologue(const OpGeom& g, const RotSched& rs, Q8Regs<1> (&R)[N]) {
+    const int T = rs.total();
+    const int pad = (T + N - 1) / N * N - T;
+    RotCursor it;
+    it.start(rs);
+#pragma unroll
+    for (int s = 0; s < N; ++s) {
+        if (s < pad) {
+            RotCursor none;
+            none.j = rs.sc->tiles_wg;
+            load_rot<1>(R[s], g, rs, none);
+        } else {
+            load_rot<1>(R[s], g, rs, it);
+            it.next(rs);
+        }
+    }
+}
+
+template <int N, typename ComputeF, typename KeepF>
+__device__ inline void rot_loop(const OpGeom& g, const RotSched& rs, Q8Regs<1> (&R)[N], ComputeF&& compute,
+                                KeepF&& keep) {
+    const Sched& sc = *rs.sc;
+    const int T = rs.total();
+    if (T == 0) return;
+    const int P = (T + N - 1) / N * N, pad = P - T;
+    RotCursor cur, nxt;
+    cur.start(rs);
+    nxt.start(rs);
+    for (int q = pad; q < N; ++q) nxt.next(rs);  // the items the prologue requested
+    float acc = 0.0f;
+    auto consume = [&](Q8Regs<1>& r, int q) {
+        if (q < pad) return;
+        const int row = sc.row(cur.j);
+        if (row < sc.n) {
+            Sched s1 = sc;
+            s1.part = cur.p;
+            compute(r, s1, row, cur.m, acc);
+        }
+        if (cur.m == cur.ipt - 1) {
+            keep(wave_sum(acc), cur.j, sc.group * sc.S + cur.p);
+            acc = 0.0f;
+        }
+        cur.next(rs);
+    };
+    const int groups = P / N;
+    for (int gi = 0; gi + 1 < groups; ++gi) {
+#pragma unroll
+        for (int s = 0; s < N; ++s) {
+            consume(R[s], gi * N + s);
+            load_rot<1>(R[s], g, rs, nxt);
+            nxt.next(rs);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < N; ++s) consume(R[s], (groups - 1) * N + s);
+}
+
 // s_waitcnt immediate (gfx9 encoding): vector memory count 0, the export and
 // LDS/scalar counts at their maxima (no wait).
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -357,10 +505,10 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
     StreamOp op = ops[0];
     OpGeom g = op_geom<WAVES>(op, parity);
     Sched sc = op_sched<WAVES, U>(g, grid);
-    // every path issues the same loads (see q8_load_item), so the compiler
-    // waits for exactly one ring set at a time
-    auto load = [&](Q8Regs<U>& r, const ItemCursor& it) { q8_load_item<U>(r, g.w, g.row_bytes, sc, g.nl, g.sbl, it); };
-    ring_prologue(sc, R, load);
+    const int wp = (int)(threadIdx.x / kWave);  // slot in the group: wave % S (S divides 16)
+    RotSched rs;
+    rs.set(sc, wp);
+    rot_prologue(g, rs, R);
     for (int j = 0;;) {
         if (op.dep) wait_range((gcfloat)(op.dep + parity * op.dep_stride), op.dep_n, st, spin_limit);
         stage<F32>(g, smem, st, spin_limit);
@@ -375,14 +523,19 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
         const float4v* lds_x = reinterpret_cast<const float4v*>(smem);
         const int4v* lds_q = reinterpret_cast<const int4v*>(smem);
         const float* lds_dx = reinterpret_cast<const float*>(smem + (size_t)g.C * 2 * kWave * 16);
-        auto compute = [&](const Q8Regs<U>& r, int row, int m, float& acc) {
+        auto compute = [&](const Q8Regs<U>& r, const Sched& s1, int row, int m, float& acc) {
             if constexpr (F32) {
-                q8_f32_item<U>(r, sc, m, g.NB, lds_x, acc);
+                q8_f32_item<U>(r, s1, m, g.NB, lds_x, acc);
             } else {
-                q8_i8_item<U, false>(r, sc, m, g.NB, lds_q, lds_dx, row, nullptr, acc);
+                q8_i8_item<U, false>(r, s1, m, g.NB, lds_q, lds_dx, row, nullptr, acc);
             }
         };
-        ring_loop(sc, R, load, compute, [&](float acc, int t, int, bool) { keep_tile(acc, t, lds_res); });
+        // parts this wave plays in no tile's chunks still meet as zeros
+        if (threadIdx.x % kWave < (unsigned)sc.tiles_wg) {
+            const int t = (int)(threadIdx.x % kWave);
+            if (rs.items(t) == 0) lds_res[t * kStreamWaves + sc.group * sc.S + rs.part(t)] = 0.0f;
+        }
+        rot_loop(g, rs, R, compute, [&](float acc, int t, int slot) { keep_part(acc, t, slot, lds_res); });
         __syncthreads();  // every tile's partial sums are in LDS; the activation is dead
         flush_tiles(sc.tiles_wg, grid, g.n, g.S, lds_res, g.y, g.ynow, g.ynext);
         if (++j == n_ops) break;
@@ -390,7 +543,8 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
         op = ops[j];
         g = op_geom<WAVES>(op, parity);
         sc = op_sched<WAVES, U>(g, grid);
-        ring_prologue(sc, R, load);
+        rs.set(sc, wp);
+        rot_prologue(g, rs, R);
     }
 }
 
