@@ -91,6 +91,48 @@ def test_persistent_replay_equals_eager(gpu_lib, wl_name, layers, deq):
     ts.close()
 
 
+@pytest.mark.parametrize("split", [2, 4])
+@pytest.mark.parametrize("deq", [0, 2])
+def test_persistent_forced_split_equals_eager(gpu_lib, split, deq):
+    """Forced split factors on a chain with one-chunk rows (k = 2048: some
+    parts have no chunks), a ragged last chunk (k = 2080) and ragged row
+    tiles: the persistent kernel (whose waves trade parts tile by tile)
+    still equals the eager calls bit for bit."""
+    import torch
+
+    from weight_streaming_gemv_q8_amd.stream import TokenStream
+    wsg = gpu_lib
+    shapes = [(4100, 2048, (4100,)), (3001, 4096, (3001,)), (2050, 2080, (2050,)), (2048, 2048, (2048,))]
+    seed = 0x5EED5117
+    wsg.tune(wsg.TUNE_SPLITK, split)
+    try:
+        ts = TokenStream(shapes, 2, "q8_0", deq=deq)
+
+        def fill(layer, m, part, rows, staging):
+            synth.dev_normal_f32(staging.data_ptr(), seed, W.weight_tensor_id(layer, m, part),
+                                 rows * shapes[m][1], W.WEIGHT_SIGMA, stream=torch.cuda.current_stream().cuda_stream)
+
+        ts.fill_weights(fill)
+        xs = np.stack([synth.activation(seed, W.activation_tensor_id(l), shapes[0][1], rms=True) for l in range(2)])
+        ts.set_inputs(torch.from_numpy(xs).cuda())
+        for slot in ts.slots:
+            assert wsg.gemv_config(wsg.W_Q8_0, ts.act_fmt(), slot.n, slot.k)["split"] == split
+        ts.run_eager()
+        eager = _snapshot(ts)
+        for y in ts.outputs():
+            y.fill_(np.nan)
+        plan = ts.capture(persistent=True)
+        for rep in range(2):
+            ts.launch()
+            got = _snapshot(ts)
+            assert not plan.error()
+            for i, (a, b) in enumerate(zip(eager, got)):
+                assert np.array_equal(a, b), f"replay {rep}: slot {i} differs from eager"
+        ts.close()
+    finally:
+        wsg.tune(wsg.TUNE_SPLITK, 0)
+
+
 def test_persistent_plan_rejects_unsupported_ops(gpu_lib):
     wsg = gpu_lib
     ts, _ = _stream(W.QWEN3_0P6B_BF16, 1)
