@@ -171,6 +171,109 @@ def time_plan(ts, persistent: bool, steps: int, warmup: int):
     return e0.elapsed_time(e1) / 1e3 / steps, kernels
 
 
+def _time_calls(fn, reps: int, warmup: int = 3) -> float:
+    """Seconds per call: HIP events around `reps` back-to-back calls."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def measure_configs(steps: int, warmup: int) -> list:
+    """Every workload in the way the pages run it: the single GEMV as eager
+    calls (hot: one weight copy; cold: rotating over 1024 copies, more than
+    L2 + MALL), the LM head as fused GEMV + argmax calls, the token streams
+    as graph and persistent replays.  One record per configuration and
+    mode."""
+    import numpy as np
+    import torch
+
+    import synth
+    import weight_streaming_gemv_q8_amd as wsg
+    from synth import workloads as W
+
+    out = []
+
+    def rec(wl, mode, sec, alg_bytes, **extra):
+        gbps_ = gbps(alg_bytes, sec)
+        r = {"workload": wl.name, "mode": mode, "us": round(sec * 1e6, 2), "GBps": round(gbps_, 1),
+             "frac_of_peak": round(gbps_ / HBM_PEAK_GBPS, 4), "bytes": alg_bytes, **extra}
+        log(f"{wl.name:22s} {mode:34s} {sec * 1e6:10.2f} us {gbps_:8.1f} GB/s {100 * gbps_ / HBM_PEAK_GBPS:5.1f}%")
+        out.append(r)
+
+    s = torch.cuda.current_stream().cuda_stream
+    # configs 0: one 1024x1024 Q8_0 GEMV
+    wl = W.Q8_SINGLE
+    n, k = wl.matrices[0].n, wl.matrices[0].k
+    alg = n * (k // 32) * 34
+    staging = torch.empty(n * k, dtype=torch.float32, device="cuda")
+    copies = 1024
+    wq = torch.empty((copies, wsg.q8_0_packed_bytes(n, k)), dtype=torch.uint8, device="cuda")
+    for c in range(copies):
+        synth.dev_normal_f32(staging.data_ptr(), wl.seed, 1 + c, n * k, W.WEIGHT_SIGMA, stream=s)
+        wsg.quantize_q8_0_weights(staging, n, k, wq[c])
+    x = torch.from_numpy(synth.activation(wl.seed, W.activation_tensor_id(0), k)).cuda()
+    y = torch.empty(n, dtype=torch.float32, device="cuda")
+    for deq, act in ((0, wsg.ACT_F32_REQUANT), (2, wsg.ACT_F32)):
+        for temp, pick in (("hot", lambda i: 0), ("cold", lambda i: i % copies)):
+            sec = _time_calls(lambda i: wsg.gemv_q8_0(wq[pick(i)], n, k, x, act, y), max(steps, 1) * 40)
+            rec(wl, f"eager deq{deq} {temp}", sec, alg, deq=deq)
+            # the same calls replayed from a graph of 256: the kernel without
+            # the host's launch cost
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(256):
+                    wsg.gemv_q8_0(wq[pick(i)], n, k, x, act, y)
+            sec = _time_calls(lambda i: g.replay(), max(steps, 1) // 5 + 1) / 256
+            rec(wl, f"graph of 256 calls deq{deq} {temp}", sec, alg, deq=deq)
+            del g
+    del wq, staging
+    # configs 3: the LM head, fused GEMV + two-stage argmax
+    wl = W.LM_HEAD
+    n, k = wl.matrices[0].n, wl.matrices[0].k
+    staging = torch.empty(n * k, dtype=torch.float32, device="cuda")
+    synth.dev_normal_f32(staging.data_ptr(), wl.seed, 1, n * k, W.WEIGHT_SIGMA, stream=s)
+    wb = torch.empty(n * k, dtype=torch.uint16, device="cuda")
+    wsg.convert_bf16(staging, n * k, wb)
+    wq = torch.empty(wsg.q8_0_packed_bytes(n, k), dtype=torch.uint8, device="cuda")
+    wsg.quantize_q8_0_weights(staging, n, k, wq)
+    del staging
+    x = torch.from_numpy(synth.activation(wl.seed, W.activation_tensor_id(0), k)).cuda()
+    ws = torch.empty(wsg.argmax_ws_bytes(), dtype=torch.uint8, device="cuda")
+    idx = torch.empty(1, dtype=torch.int32, device="cuda")
+    sec = _time_calls(lambda i: wsg.lm_head_argmax(wb, wsg.W_BF16, n, k, x, wsg.ACT_F32, ws, ws.numel(), idx),
+                      max(steps, 1))
+    rec(wl, "bf16 GEMV + argmax", sec, n * k * 2)
+    for deq, act in ((0, wsg.ACT_F32_REQUANT), (2, wsg.ACT_F32)):
+        sec = _time_calls(lambda i: wsg.lm_head_argmax(wq, wsg.W_Q8_0, n, k, x, act, ws, ws.numel(), idx),
+                          max(steps, 1))
+        rec(wl, f"q8_0 GEMV + argmax, deq{deq}" + (" (= deq1)" if deq == 2 else ""), sec, n * (k // 32) * 34,
+            deq=deq)
+    del wb, wq
+    torch.cuda.empty_cache()
+    # configs 1, 2, 4: token streams
+    for wl, deqs in ((W.QWEN3_0P6B_BF16, (0,)), (W.QWEN3_8B_Q8, (0,)), (W.DENSE27B_Q8, (0, 2))):
+        for deq in deqs:
+            ts = build_stream(wl, deq, "fused")
+            alg = ts.algorithmic_weight_bytes()
+            plans = ("graph",) if wl.wtype == "bf16" else ("graph", "persistent")
+            for plan in plans:
+                sec, kernels = time_plan(ts, plan == "persistent", steps, warmup)
+                rec(wl, f"{plan} deq{deq}" if wl.wtype != "bf16" else plan, sec, alg, kernels_per_token=kernels,
+                    deq=deq)
+            ts.close()
+            del ts
+            torch.cuda.empty_cache()
+    return out
+
+
 def read_ceiling(ts, reps: int = 3) -> float:
     import torch
 
@@ -405,6 +508,9 @@ def main() -> int:
                     help="only run the copy (or read) probe over --probe-bytes, 3 launches: a kernel of known "
                          "traffic for calibrating hardware byte counters")
     ap.add_argument("--probe-bytes", type=int, default=1 << 30)
+    ap.add_argument("--configs", action="store_true",
+                    help="measure every workload (single GEMV hot/cold, LM head, the three token streams) and "
+                         "print one JSON line per configuration and mode, instead of the benchmark line")
     ap.add_argument("--summarize", nargs=5, metavar=("STATS", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write profiles/ summaries from rocprofv3 output directories (no GPU needed); "
                          "the commands that made them are read from STATS/../commands.json")
@@ -427,6 +533,13 @@ def main() -> int:
 
     import weight_streaming_gemv_q8_amd as wsg
     from synth import workloads as W
+
+    if args.configs:
+        torch.cuda.set_device(0)
+        wsg.lib()
+        for r in measure_configs(args.steps, args.warmup):
+            print(json.dumps(r), flush=True)
+        return 0
 
     wl = {w.name: w for w in W.ALL}.get(args.workload)
     if wl is None or wl.wtype not in ("q8_0", "bf16") or wl.layers < 2:

@@ -70,7 +70,7 @@ q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
 
     Q8Regs<U> R[kRingSets<U>];
     if constexpr (ACT == kActRequant) {
-        StageRequant<1> st;
+        StageRequant<4> st;
         st.issue(xin, k, C);
         __builtin_amdgcn_sched_barrier(0);
         ring_prologue(sc, R, load);

@@ -284,58 +284,77 @@ struct StageQ8 {
     }
 };
 
-// f32 activation quantized with the Q8_0 rule into the same LDS layout (the
-// same device functions and bytes as quantize_act_q8_0).  A unit is one
-// 32-value block.
-__device__ inline void requant_block_to_lds(const float4v* v4, int b, int4v* lds_q, float* lds_dx) {
-    float v[32];
+// Requantized activation (the Q8_0 rule of quantize_act_q8_0) into the LDS
+// layout of the int8 path: four lanes per 32-value block, eight values each;
+// the block maximum meets in a quad reduction, every lane derives the same
+// scale and writes its eight codes (one 8-byte LDS store).
+__device__ inline void requant_unit(const float4v v0, const float4v v1, int u, int4v* lds_q, float* lds_dx) {
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        v[4 * i + 0] = v4[i].x;
-        v[4 * i + 1] = v4[i].y;
-        v[4 * i + 2] = v4[i].z;
-        v[4 * i + 3] = v4[i].w;
+    for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    const uint16_t d16 = q8_scale_bits(amax);
+    const float d = half_bits_to_float(d16);
+    uint32_t lo = 0, hi = 0;
+    if (d != 0.0f) {
+        const float r = 1.0f / d;
+        int q[8];
+        bool any_near = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            bool near;
+            q[i] = q8_code_fast(v[i], r, near);
+            any_near |= near;
+        }
+        if (__any(any_near)) {  // rare: a value within 4e-5 of a rounding boundary
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = q8_code(v[i], d, r);
+        }
+        lo = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) | ((uint32_t)(q[2] & 0xFF) << 16) |
+             ((uint32_t)q[3] << 24);
+        hi = (uint32_t)(q[4] & 0xFF) | ((uint32_t)(q[5] & 0xFF) << 8) | ((uint32_t)(q[6] & 0xFF) << 16) |
+             ((uint32_t)q[7] << 24);
     }
-    int8_t codes[32];
-    const float d = q8_quantize_block(v, codes);
-    const int c = b / kWave, l = b % kWave;
-    int4v lo, hi;
-    __builtin_memcpy(&lo, codes, 16);
-    __builtin_memcpy(&hi, codes + 16, 16);
-    lds_q[(c * 2 + 0) * kWave + l] = lo;
-    lds_q[(c * 2 + 1) * kWave + l] = hi;
-    lds_dx[b] = d;
+    const int b = u >> 2, e = u & 3;
+    const int c = b / kWave, l = b % kWave, h = e >> 1;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(lds_q + (c * 2 + h) * kWave + l) + 2 * (e & 1);
+    dst[0] = lo;
+    dst[1] = hi;
+    if (e == 0) lds_dx[b] = d;
 }
 
+// f32 activation quantized with the Q8_0 rule into the same LDS layout (the
+// codes and scales of quantize_act_q8_0): a unit is eight values, four
+// units per 32-value block (requant_unit).  units = 4 x blocks and the
+// workgroup is a whole number of waves, so the four lanes of a block are in
+// the same wave and all (in)active together.
 template <int NR>
 struct StageRequant {
-    float4v v[NR][8];
+    float4v v[NR][2];
     __device__ void issue(const void* __restrict__ xin, int k, int) {
-        const int NB = k / kBlock;
+        const int units = k / 8;
         const float4v* x4 = static_cast<const float4v*>(xin);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int b = threadIdx.x + i * blockDim.x;
-            if (b < NB) {
-#pragma unroll
-                for (int g = 0; g < 8; ++g) v[i][g] = x4[b * 8 + g];
+            const int u = threadIdx.x + i * blockDim.x;
+            if (u < units) {
+                v[i][0] = x4[2 * u];
+                v[i][1] = x4[2 * u + 1];
             }
         }
     }
     __device__ void commit(const void* __restrict__ xin, int k, int, int4v* lds_q, float* lds_dx) {
-        const int NB = k / kBlock;
+        const int units = k / 8;
         const float4v* x4 = static_cast<const float4v*>(xin);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int b = threadIdx.x + i * blockDim.x;
-            if (b < NB) requant_block_to_lds(v[i], b, lds_q, lds_dx);
+            const int u = threadIdx.x + i * blockDim.x;
+            if (u < units) requant_unit(v[i][0], v[i][1], u, lds_q, lds_dx);
         }
-        for (int b = threadIdx.x + NR * blockDim.x; b < NB; b += blockDim.x) {
-            float4v t[8];
-#pragma unroll
-            for (int g = 0; g < 8; ++g) t[g] = x4[b * 8 + g];
-            requant_block_to_lds(t, b, lds_q, lds_dx);
-        }
+        for (int u = threadIdx.x + NR * blockDim.x; u < units; u += blockDim.x)
+            requant_unit(x4[2 * u], x4[2 * u + 1], u, lds_q, lds_dx);
     }
 };
 
