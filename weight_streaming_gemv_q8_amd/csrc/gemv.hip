@@ -68,25 +68,63 @@ q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
         q8_i8_item<U, DEBUG>(r, sc, m, NB, lds_q, lds_dx, row, dots, acc);
     };
 
+    // split rows with one-chunk items: rotating parts, partials kept in LDS
+    // (rot_loop, flush_parts) while the workgroup's tiles fit
+    constexpr bool kRot = S > 1 && U == 1 && !DEBUG && !ARGMAX;
+    const int wave = threadIdx.x / kWave;
+    const bool rot = kRot && sc.tiles_wg <= kKeepTiles;
+    float* lds_res = reinterpret_cast<float*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>());
+    RotSched rs;
+    rs.set(sc, wave);
+    auto rload = [&](Q8Regs<1>& r, const RotSched& rs_, const RotCursor& it) {
+        q8_load_rot(r, Wg, row_bytes, nl, sbl, rs_, it);
+    };
+    auto prologue = [&](Q8Regs<U> (&R_)[kRingSets<U>]) {
+        if constexpr (kRot) {
+            if (rot) {
+                rot_prologue(rs, R_, rload);
+                return;
+            }
+        }
+        ring_prologue(sc, R_, load);
+    };
+
     Q8Regs<U> R[kRingSets<U>];
     if constexpr (ACT == kActRequant) {
         StageRequant<4> st;
         st.issue(xin, k, C);
         __builtin_amdgcn_sched_barrier(0);
-        ring_prologue(sc, R, load);
+        prologue(R);
         __builtin_amdgcn_sched_barrier(0);
         st.commit(xin, k, C, lds_q, lds_dx);
     } else {
         StageQ8<4> st;
         st.issue(xin, k, C);
         __builtin_amdgcn_sched_barrier(0);
-        ring_prologue(sc, R, load);
+        prologue(R);
         __builtin_amdgcn_sched_barrier(0);
         st.commit(xin, k, C, lds_q, lds_dx);
     }
     __syncthreads();
+    if constexpr (kRot) {
+        if (rot) {
+            if (threadIdx.x % kWave < (unsigned)sc.tiles_wg) {
+                const int t = (int)(threadIdx.x % kWave);
+                if (rs.items(t) == 0) lds_res[t * WAVES + sc.group * S + rs.part(t)] = 0.0f;
+            }
+            rot_loop(rs, R, rload,
+                     [&](const Q8Regs<1>& r, const Sched& s1, int row, int m, float& acc) {
+                         q8_i8_item<1, false>(r, s1, m, NB, lds_q, lds_dx, row, nullptr, acc);
+                     },
+                     [&](float acc, int t, int slot) {
+                         if (lane == 0) lds_res[t * WAVES + slot] = acc;
+                     });
+            __syncthreads();
+            flush_parts<WAVES>(sc, lds_res, y);
+            return;
+        }
+    }
     uint64_t best = 0;
-    const int wave = threadIdx.x / kWave;
     ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool) {
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
     });
@@ -115,16 +153,51 @@ q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restri
     auto load = [&](Q8Regs<U>& r, const ItemCursor& it) { q8_load_item<U>(r, Wg, row_bytes, sc, nl, sbl, it); };
     auto compute = [&](const Q8Regs<U>& r, int, int m, float& acc) { q8_f32_item<U>(r, sc, m, NB, lds_x, acc); };
 
+    constexpr bool kRot = S > 1 && U == 1 && !ARGMAX;
+    const int wave = threadIdx.x / kWave;
+    const bool rot = kRot && sc.tiles_wg <= kKeepTiles;
+    float* lds_res = reinterpret_cast<float*>(smem + lds_f32act_bytes(C) + lds_tail_bytes<WAVES>());
+    RotSched rs;
+    rs.set(sc, wave);
+    auto rload = [&](Q8Regs<1>& r, const RotSched& rs_, const RotCursor& it) {
+        q8_load_rot(r, Wg, row_bytes, nl, sbl, rs_, it);
+    };
+
     Q8Regs<U> R[kRingSets<U>];
     StageF32<4> st;
     st.issue(x, k);
     __builtin_amdgcn_sched_barrier(0);
-    ring_prologue(sc, R, load);
+    if constexpr (kRot) {
+        if (rot) {
+            rot_prologue(rs, R, rload);
+        } else {
+            ring_prologue(sc, R, load);
+        }
+    } else {
+        ring_prologue(sc, R, load);
+    }
     __builtin_amdgcn_sched_barrier(0);
     st.commit(x, k, lds_x);
     __syncthreads();
+    if constexpr (kRot) {
+        if (rot) {
+            if (threadIdx.x % kWave < (unsigned)sc.tiles_wg) {
+                const int t = (int)(threadIdx.x % kWave);
+                if (rs.items(t) == 0) lds_res[t * WAVES + sc.group * S + rs.part(t)] = 0.0f;
+            }
+            rot_loop(rs, R, rload,
+                     [&](const Q8Regs<1>& r, const Sched& s1, int, int m, float& acc) {
+                         q8_f32_item<1>(r, s1, m, NB, lds_x, acc);
+                     },
+                     [&](float acc, int t, int slot) {
+                         if (lane == 0) lds_res[t * WAVES + slot] = acc;
+                     });
+            __syncthreads();
+            flush_parts<WAVES>(sc, lds_res, y);
+            return;
+        }
+    }
     uint64_t best = 0;
-    const int wave = threadIdx.x / kWave;
     ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool) {
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
     });
@@ -446,6 +519,13 @@ int launch_kernel(K kern, size_t lds, int n, LaunchInfo* info, int unroll, bool 
 // The debug and argmax instantiations use the default one-chunk items (the
 // unroll does not change the order of additions, so their results match the
 // plain kernel at any unroll).
+// Dynamic LDS of a Q8_0 kernel: the staged activation, the tail (split-K
+// partials, argmax keys) and the kept partials of the rotating split path.
+template <int WAVES>
+size_t q8_lds_bytes(size_t lds_act) {
+    return lds_act + lds_tail_bytes<WAVES>() + lds_keep_bytes<WAVES>();
+}
+
 template <int ACT, bool DEBUG, bool ARGMAX>
 int launch_q8_i8(const void* w, int n, int k, const void* x, float* y, int32_t* dots, uint64_t* keys,
                  hipStream_t stream, LaunchInfo* info, bool run = true) {
@@ -456,7 +536,7 @@ int launch_q8_i8(const void* w, int n, int k, const void* x, float* y, int32_t* 
         return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
             constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
             auto kern = q8_i8_kernel<Wv, Sv, 1, ACT, true, DEBUG, ARGMAX>;
-            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, 1, run, stream, wp, n, k,
+            return launch_kernel<Wv, Sv>(kern, q8_lds_bytes<Wv>(lds_act), n, info, 1, run, stream, wp, n, k,
                                          x, y, dots, keys);
         });
     } else {
@@ -468,7 +548,7 @@ int launch_q8_i8(const void* w, int n, int k, const void* x, float* y, int32_t* 
                 return WSG_ERR_MODE;  // never dispatched
             } else {
                 auto kern = q8_i8_kernel<Wv, Sv, Uv, ACT, true, false, false>;
-                return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, Uv, run, stream, wp, n,
+                return launch_kernel<Wv, Sv>(kern, q8_lds_bytes<Wv>(lds_act), n, info, Uv, run, stream, wp, n,
                                              k, x, y, dots, keys);
             }
         });
@@ -485,14 +565,14 @@ int launch_q8_f32(const void* w, int n, int k, const float* x, float* y, uint64_
         return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
             constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
             auto kern = q8_f32_kernel<Wv, Sv, 1, true, true>;
-            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, 1, run, stream, wp, n, k,
+            return launch_kernel<Wv, Sv>(kern, q8_lds_bytes<Wv>(lds_act), n, info, 1, run, stream, wp, n, k,
                                          x, y, keys);
         });
     } else {
         return dispatch_wsu<true>(c.waves, c.split, c.unroll, [&](auto W, auto S, auto U) -> int {
             constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value, Uv = decltype(U)::value;
             auto kern = q8_f32_kernel<Wv, Sv, Uv, true, false>;
-            return launch_kernel<Wv, Sv>(kern, lds_act + lds_tail_bytes<Wv>(), n, info, Uv, run, stream, wp, n, k,
+            return launch_kernel<Wv, Sv>(kern, q8_lds_bytes<Wv>(lds_act), n, info, Uv, run, stream, wp, n, k,
                                          x, y, keys);
         });
     }

@@ -37,7 +37,8 @@ __host__ __device__ constexpr size_t lds_tail_bytes() {
 // completes, so HBM sees requests from the first cycles of the launch.
 struct Sched {
     int C, S, U, part, group, groups, n, tiles_wg, ipt, grid;
-    __device__ Sched(int C_, int S_, int U_, int waves, int n_, int tiles) : Sched(C_, S_, U_, waves, n_, tiles, (int)gridDim.x) {}
+    __device__ Sched(int C_, int S_, int U_, int waves, int n_, int tiles)
+        : Sched(C_, S_, U_, waves, n_, tiles, (int)gridDim.x) {}
     // grid: the number of workgroups (gridDim.x), when the caller has it at hand
     __device__ Sched(int C_, int S_, int U_, int waves, int n_, int tiles, int grid_) {
         grid = grid_;
@@ -234,6 +235,179 @@ __device__ inline void q8_load_item(Q8Regs<U>& r, gptr<uint8_t> W, int64_t row_b
         r.sc[u] = load_u16<true>(cp + 2 * l);
         r.a[u] = load16<true>(cp + sb + 16 * l);
         r.b[u] = load16<true>(cp + sb + 16 * nbc + 16 * l);
+    }
+}
+
+// ------------------------------------------------------- rotating parts
+// With split-K (S > 1) a row's chunks are dealt to S parts (part p takes
+// chunks p, p + S, ...), and when the chunks do not divide evenly the low
+// parts take more (the 27B down projection: 3, 2, 2, 2 chunks).  A wave
+// that played part 0 in every tile would do half as much again as the
+// others and hold up the workgroup at the end, so the wave of group slot w
+// plays part (w + tile) % S: the heavy part passes round the waves.  Each
+// part's partial sum is the same computation whichever wave makes it, and
+// the parts still meet in part order, so the result depends neither on the
+// rotation nor on the loop (ring_loop computes the same partials).
+// One-chunk items (U = 1).
+struct RotSched {
+    const Sched* sc;
+    int wp;          // this wave's slot within its group (its part in tile 0)
+    int base, rem;   // part p takes base + (p < rem) chunks (S is a power of two)
+    __device__ void set(const Sched& s, int slot) {
+        sc = &s;
+        wp = slot & (s.S - 1);
+        base = s.C >> __builtin_ctz(s.S);
+        rem = s.C & (s.S - 1);
+    }
+    __device__ int part(int j) const { return (wp + j) & (sc->S - 1); }
+    __device__ int items_of(int p) const { return base + (p < rem ? 1 : 0); }
+    __device__ int items(int j) const { return items_of(part(j)); }
+    // the wave's items over all its tiles
+    __device__ int total() const {
+        int t = 0;
+        for (int p = 0; p < sc->S; ++p) {
+            const int j0 = (p - wp) & (sc->S - 1);
+            if (j0 < sc->tiles_wg) t += ((sc->tiles_wg - 1 - j0) >> __builtin_ctz(sc->S)) * items_of(p) + items_of(p);
+        }
+        return t;
+    }
+};
+
+// Walks a wave's items in order: (tile j, item m of that tile, its part p
+// and item count); j reaches tiles_wg past the last item.
+struct RotCursor {
+    int j = 0, m = 0, p = 0, ipt = 0;
+    __device__ void start(const RotSched& rs) {
+        j = 0;
+        m = 0;
+        p = rs.wp;
+        ipt = rs.items_of(p);
+        if (ipt == 0) skip_empty(rs);
+    }
+    __device__ void skip_empty(const RotSched& rs) {  // only when a part has no chunks (C < S)
+        while (j < rs.sc->tiles_wg && ipt == 0) {
+            ++j;
+            p = (p + 1) & (rs.sc->S - 1);
+            ipt = rs.items_of(p);
+        }
+    }
+    __device__ void next(const RotSched& rs) {
+        if (++m == ipt) {
+            m = 0;
+            ++j;
+            p = (p + 1) & (rs.sc->S - 1);
+            ipt = rs.items_of(p);
+            if (ipt == 0) skip_empty(rs);
+        }
+    }
+};
+
+// One item: chunk part(j) + S * m of the group's row of tile j (3 loads;
+// the idle region past the wave's items or the matrix, see q8_load_item).
+__device__ inline void q8_load_rot(Q8Regs<1>& R, gptr<uint8_t> W, int64_t row_bytes, int nl, int sbl,
+                                   const RotSched& rs, const RotCursor& it) {
+    const Sched& sc = *rs.sc;
+    const int lane = threadIdx.x % kWave;
+    const bool has_item = it.j < sc.tiles_wg;
+    const int row = has_item ? sc.row(it.j) : sc.n;
+    const bool has_row = row < sc.n;
+    const int c = has_item ? it.p + sc.S * it.m : sc.C;
+    const bool real = has_row && c < sc.C;
+    const bool last = (c == sc.C - 1);
+    const int nbc = last ? nl : kChunkBlocks;
+    const int sb = last ? sbl : 2 * kChunkBlocks;
+    const int l = lane < nbc ? lane : nbc - 1;
+    const gptr<uint8_t> cp = real ? W + (int64_t)row * row_bytes + (int64_t)c * kFullChunkBytes : idle_bytes();
+    R.sc[0] = load_u16<true>(cp + 2 * l);
+    R.a[0] = load16<true>(cp + sb + 16 * l);
+    R.b[0] = load16<true>(cp + sb + 16 * nbc + 16 * l);
+}
+
+// The ring over a wave's items, as ring_loop (every step issues one item's
+// loads, the padding at the front, the last N items drained without
+// refills), with rotating parts.
+// load(regs, rs, cursor) issues one item's loads (a cursor past the
+// schedule reads the idle region).
+template <int N, typename LoadF>
+__device__ inline void rot_prologue(const RotSched& rs, Q8Regs<1> (&R)[N], LoadF&& load) {
+    const int T = rs.total();
+    const int pad = (T + N - 1) / N * N - T;
+    RotCursor it;
+    it.start(rs);
+#pragma unroll
+    for (int s = 0; s < N; ++s) {
+        if (s < pad) {
+            RotCursor none;
+            none.j = rs.sc->tiles_wg;
+            load(R[s], rs, none);
+        } else {
+            load(R[s], rs, it);
+            it.next(rs);
+        }
+    }
+}
+
+template <int N, typename LoadF, typename ComputeF, typename KeepF>
+__device__ inline void rot_loop(const RotSched& rs, Q8Regs<1> (&R)[N], LoadF&& load, ComputeF&& compute,
+                                KeepF&& keep) {
+    const Sched& sc = *rs.sc;
+    const int T = rs.total();
+    if (T == 0) return;
+    const int P = (T + N - 1) / N * N, pad = P - T;
+    RotCursor cur, nxt;
+    cur.start(rs);
+    nxt.start(rs);
+    for (int q = pad; q < N; ++q) nxt.next(rs);  // the items the prologue requested
+    float acc = 0.0f;
+    auto consume = [&](Q8Regs<1>& r, int q) {
+        if (q < pad) return;
+        const int row = sc.row(cur.j);
+        if (row < sc.n) {
+            Sched s1 = sc;
+            s1.part = cur.p;
+            compute(r, s1, row, cur.m, acc);
+        }
+        if (cur.m == cur.ipt - 1) {
+            keep(wave_sum(acc), cur.j, sc.group * sc.S + cur.p);
+            acc = 0.0f;
+        }
+        cur.next(rs);
+    };
+    const int groups = P / N;
+    for (int gi = 0; gi + 1 < groups; ++gi) {
+#pragma unroll
+        for (int s = 0; s < N; ++s) {
+            consume(R[s], gi * N + s);
+            load(R[s], rs, nxt);
+            nxt.next(rs);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < N; ++s) consume(R[s], (groups - 1) * N + s);
+}
+
+// Split-K kernels that keep each tile's partial sums in LDS (res[tile]
+// [group * S + part]) and add them once, after the row loop and one
+// barrier, rather than meeting at two barriers per tile.
+constexpr int kKeepTiles = 32;
+template <int WAVES>
+__host__ __device__ constexpr size_t lds_keep_bytes() {
+    return (size_t)kKeepTiles * WAVES * sizeof(float);
+}
+
+// After the loop and a barrier: y[row] = the row's parts added in part
+// order.
+template <int WAVES>
+__device__ inline void flush_parts(const Sched& sc, const float* res, float* y) {
+    for (int i = (int)threadIdx.x; i < sc.tiles_wg * sc.groups; i += WAVES * kWave) {
+        const int j = i / sc.groups, grp = i % sc.groups;
+        const int row = ((int)blockIdx.x + j * sc.grid) * sc.groups + grp;
+        if (row < sc.n) {
+            const float* p = res + j * WAVES + grp * sc.S;
+            float total = p[0];
+            for (int q = 1; q < sc.S; ++q) total += p[q];
+            y[row] = total;
+        }
     }
 }
 

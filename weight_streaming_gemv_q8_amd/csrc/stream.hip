@@ -74,7 +74,9 @@ typedef __attribute__((address_space(1))) float* gfloat;
 typedef const __attribute__((address_space(1))) uint64_t* gcu64;
 typedef const __attribute__((address_space(1))) uint32_t* gcu32;
 
-__device__ inline uint64_t ld_dev64(gcu64 p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline uint64_t ld_dev64(gcu64 p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // "Not written yet": a signalling NaN, which no arithmetic result can be.
 constexpr uint32_t kSentinel = kStreamSentinel;
@@ -284,151 +286,14 @@ __device__ inline Sched op_sched(const OpGeom& g, int grid) {
     return Sched(g.C, g.S, U, WAVES, g.n, (g.n + WAVES / g.S - 1) / (WAVES / g.S), grid);
 }
 
-// ------------------------------------------------------- rotating parts
-// With split-K (S > 1) a row's chunks are dealt to S parts (part p takes
-// chunks p, p + S, ...), and when the chunks do not divide evenly the low
-// parts take more (the 27B down projection: 3, 2, 2, 2 chunks).  A wave
-// that played part 0 in every tile would do half as much again as the
-// others and hold up the workgroup at every GEMV's end, so the wave of
-// group slot w plays part (w + tile) % S: the heavy part passes round the
-// waves.  Each part's partial sum is the same computation whichever wave
-// makes it, and the parts still meet in part order, so results equal the
-// eager kernels' bit for bit.
-struct RotSched {
-    const Sched* sc;
-    int wp;          // this wave's slot within its group (its part in tile 0)
-    int base, rem;   // part p takes base + (p < rem) chunks (S is a power of two)
-    __device__ void set(const Sched& s, int slot) {
-        sc = &s;
-        wp = slot & (s.S - 1);
-        base = s.C >> __builtin_ctz(s.S);
-        rem = s.C & (s.S - 1);
-    }
-    __device__ int part(int j) const { return (wp + j) & (sc->S - 1); }
-    __device__ int items_of(int p) const { return base + (p < rem ? 1 : 0); }
-    __device__ int items(int j) const { return items_of(part(j)); }
-    // the wave's items over all its tiles
-    __device__ int total() const {
-        int t = 0;
-        for (int p = 0; p < sc->S; ++p) {
-            const int j0 = (p - wp) & (sc->S - 1);
-            if (j0 < sc->tiles_wg) t += ((sc->tiles_wg - 1 - j0) >> __builtin_ctz(sc->S)) * items_of(p) + items_of(p);
-        }
-        return t;
+// A rotating-ring item of an op's matrix (see q8_load_rot).
+struct OpRotLoad {
+    const OpGeom* g;
+    template <typename Regs>
+    __device__ void operator()(Regs& R, const RotSched& rs, const RotCursor& it) const {
+        q8_load_rot(R, g->w, g->row_bytes, g->nl, g->sbl, rs, it);
     }
 };
-
-// Walks a wave's items in order: (tile j, item m of that tile, its part p
-// and item count); j reaches tiles_wg past the last item.
-struct RotCursor {
-    int j = 0, m = 0, p = 0, ipt = 0;
-    __device__ void start(const RotSched& rs) {
-        j = 0;
-        m = 0;
-        p = rs.wp;
-        ipt = rs.items_of(p);
-        if (ipt == 0) skip_empty(rs);
-    }
-    __device__ void skip_empty(const RotSched& rs) {  // only when a part has no chunks (C < S)
-        while (j < rs.sc->tiles_wg && ipt == 0) {
-            ++j;
-            p = (p + 1) & (rs.sc->S - 1);
-            ipt = rs.items_of(p);
-        }
-    }
-    __device__ void next(const RotSched& rs) {
-        if (++m == ipt) {
-            m = 0;
-            ++j;
-            p = (p + 1) & (rs.sc->S - 1);
-            ipt = rs.items_of(p);
-            if (ipt == 0) skip_empty(rs);
-        }
-    }
-};
-
-// One item: chunk part(j) + S * m of the group's row of tile j (3 loads;
-// the idle region past the wave's items or the matrix, see q8_load_item).
-template <int U>
-__device__ inline void load_rot(Q8Regs<U>& R, const OpGeom& g, const RotSched& rs, const RotCursor& it) {
-    static_assert(U == 1, "one chunk per item");
-    const Sched& sc = *rs.sc;
-    const int lane = threadIdx.x % kWave;
-    const bool has_item = it.j < sc.tiles_wg;
-    const int row = has_item ? sc.row(it.j) : sc.n;
-    const bool has_row = row < sc.n;
-    const int c = has_item ? it.p + sc.S * it.m : sc.C;
-    const bool real = has_row && c < sc.C;
-    const bool last = (c == sc.C - 1);
-    const int nbc = last ? g.nl : kChunkBlocks;
-    const int sb = last ? g.sbl : 2 * kChunkBlocks;
-    const int l = lane < nbc ? lane : nbc - 1;
-    const gptr<uint8_t> cp = real ? g.w + (int64_t)row * g.row_bytes + (int64_t)c * kFullChunkBytes : idle_bytes();
-    R.sc[0] = load_u16<true>(cp + 2 * l);
-    R.a[0] = load16<true>(cp + sb + 16 * l);
-    R.b[0] = load16<true>(cp + sb + 16 * nbc + 16 * l);
-}
-
-// The ring over a wave's items, as ring_loop (every step issues one item's
-// loads, the padding at the front, the last N items drained without
-// refills), with rotating parts.
-template <int N>
-__device__ inline void rot_prologue(const OpGeom& g, const RotSched& rs, Q8Regs<1> (&R)[N]) {
-    const int T = rs.total();
-    const int pad = (T + N - 1) / N * N - T;
-    RotCursor it;
-    it.start(rs);
-#pragma unroll
-    for (int s = 0; s < N; ++s) {
-        if (s < pad) {
-            RotCursor none;
-            none.j = rs.sc->tiles_wg;
-            load_rot<1>(R[s], g, rs, none);
-        } else {
-            load_rot<1>(R[s], g, rs, it);
-            it.next(rs);
-        }
-    }
-}
-
-template <int N, typename ComputeF, typename KeepF>
-__device__ inline void rot_loop(const OpGeom& g, const RotSched& rs, Q8Regs<1> (&R)[N], ComputeF&& compute,
-                                KeepF&& keep) {
-    const Sched& sc = *rs.sc;
-    const int T = rs.total();
-    if (T == 0) return;
-    const int P = (T + N - 1) / N * N, pad = P - T;
-    RotCursor cur, nxt;
-    cur.start(rs);
-    nxt.start(rs);
-    for (int q = pad; q < N; ++q) nxt.next(rs);  // the items the prologue requested
-    float acc = 0.0f;
-    auto consume = [&](Q8Regs<1>& r, int q) {
-        if (q < pad) return;
-        const int row = sc.row(cur.j);
-        if (row < sc.n) {
-            Sched s1 = sc;
-            s1.part = cur.p;
-            compute(r, s1, row, cur.m, acc);
-        }
-        if (cur.m == cur.ipt - 1) {
-            keep(wave_sum(acc), cur.j, sc.group * sc.S + cur.p);
-            acc = 0.0f;
-        }
-        cur.next(rs);
-    };
-    const int groups = P / N;
-    for (int gi = 0; gi + 1 < groups; ++gi) {
-#pragma unroll
-        for (int s = 0; s < N; ++s) {
-            consume(R[s], gi * N + s);
-            load_rot<1>(R[s], g, rs, nxt);
-            nxt.next(rs);
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < N; ++s) consume(R[s], (groups - 1) * N + s);
-}
 
 // s_waitcnt immediate (gfx9 encoding): vector memory count 0, the export and
 // LDS/scalar counts at their maxima (no wait).
@@ -466,7 +331,7 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
     const int wp = (int)(threadIdx.x / kWave);  // slot in the group: wave % S (S divides 16)
     RotSched rs;
     rs.set(sc, wp);
-    rot_prologue(g, rs, R);
+    rot_prologue(rs, R, OpRotLoad{&g});
     for (int j = 0;;) {
         if (op.dep) wait_range((gcfloat)(op.dep + parity * op.dep_stride), op.dep_n, st, spin_limit);
         stage<F32>(g, smem, st, spin_limit);
@@ -493,7 +358,7 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
             const int t = (int)(threadIdx.x % kWave);
             if (rs.items(t) == 0) lds_res[t * kStreamWaves + sc.group * sc.S + rs.part(t)] = 0.0f;
         }
-        rot_loop(g, rs, R, compute, [&](float acc, int t, int slot) { keep_part(acc, t, slot, lds_res); });
+        rot_loop(rs, R, OpRotLoad{&g}, compute, [&](float acc, int t, int slot) { keep_part(acc, t, slot, lds_res); });
         __syncthreads();  // every tile's partial sums are in LDS; the activation is dead
         flush_tiles(sc.tiles_wg, grid, g.n, g.S, lds_res, g.y, g.ynow, g.ynext);
         if (++j == n_ops) break;
@@ -502,7 +367,7 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
         g = op_geom<WAVES>(op, parity);
         sc = op_sched<WAVES, U>(g, grid);
         rs.set(sc, wp);
-        rot_prologue(g, rs, R);
+        rot_prologue(rs, R, OpRotLoad{&g});
     }
 }
 
