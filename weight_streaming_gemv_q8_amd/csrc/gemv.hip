@@ -39,8 +39,12 @@ namespace {
 // Register sets in each wave's ring of weight items of U chunks (one
 // consumed while the others are in flight): three one-chunk items, or two
 // items of two or more chunks.
-template <int U>
-constexpr int kRingSets = U == 1 ? 3 : 2;
+// (Measured on the 27B and 8B shapes: four one-chunk items for unsplit
+// rows, or five for split ones, stream 2-10% slower -- more requests in
+// flight only lengthen the queues; six spill.)
+constexpr int kRing1 = 3, kRingSplit = 3;
+template <int U, int S = 1>
+constexpr int kRingSets = U == 1 ? (S > 1 ? kRingSplit : kRing1) : 2;
 
 // ------------------------------------------------ Q8_0 x int8 (and requant)
 template <int WAVES, int S, int U, int ACT, bool NT, bool DEBUG, bool ARGMAX>
@@ -79,7 +83,7 @@ q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
     auto rload = [&](Q8Regs<1>& r, const RotSched& rs_, const RotCursor& it) {
         q8_load_rot(r, Wg, row_bytes, nl, sbl, rs_, it);
     };
-    auto prologue = [&](Q8Regs<U> (&R_)[kRingSets<U>]) {
+    auto prologue = [&](Q8Regs<U> (&R_)[kRingSets<U, S>]) {
         if constexpr (kRot) {
             if (rot) {
                 rot_prologue(rs, R_, rload);
@@ -89,7 +93,7 @@ q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
         ring_prologue(sc, R_, load);
     };
 
-    Q8Regs<U> R[kRingSets<U>];
+    Q8Regs<U> R[kRingSets<U, S>];
     if constexpr (ACT == kActRequant) {
         StageRequant<4> st;
         st.issue(xin, k, C);
@@ -163,7 +167,7 @@ q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restri
         q8_load_rot(r, Wg, row_bytes, nl, sbl, rs_, it);
     };
 
-    Q8Regs<U> R[kRingSets<U>];
+    Q8Regs<U> R[kRingSets<U, S>];
     StageF32<4> st;
     st.issue(x, k);
     __builtin_amdgcn_sched_barrier(0);
@@ -236,7 +240,7 @@ bf16_kernel(const uint16_t* __restrict__ W, int n, int k, const float* __restric
         }
     };
 
-    Bf16Regs<U> R[kRingSets<U>];
+    Bf16Regs<U> R[kRingSets<U, S>];
     StageBf16x<4> st;
     st.issue(x, k);
     __builtin_amdgcn_sched_barrier(0);
