@@ -117,11 +117,6 @@ __device__ inline uint16_t q8_quantize_block_bits(const float* v, int8_t* q) {
     return d16;
 }
 
-// The same, returning float(d) (0 for a zero block).
-__device__ inline float q8_quantize_block(const float* v, int8_t* q) {
-    return half_bits_to_float(q8_quantize_block_bits(v, q));
-}
-
 // ------------------------------------------------------- wave reductions
 // Butterfly sums over the 64 lanes of a wave; every lane ends with the same
 // value and the order of additions does not depend on which row is reduced.
