@@ -66,6 +66,8 @@ def lib():
         L.orc_argmax_f64.argtypes = [vp, i64]
         L.orc_argmax_f32.restype = i64
         L.orc_argmax_f32.argtypes = [vp, i64]
+        L.orc_residual_rmsnorm.restype = None
+        L.orc_residual_rmsnorm.argtypes = [vp, vp, vp, i64, ctypes.c_double, vp, vp]
         _lib = L
     return _lib
 
@@ -185,6 +187,27 @@ def argmax_f64(v) -> int:
 def argmax_f32(v) -> int:
     v = _c(v, np.float32)
     return int(lib().orc_argmax_f32(v.ctypes.data, v.size))
+
+
+# ---------------------------------------------------------------------- O9
+
+def residual_rmsnorm(h, r, g, eps: float):
+    """Residual add + RMSNorm (see oracle.c, O9): returns (h' float32[k], the
+    fp32 residual stream after the add; y float64[k]).  r may be None."""
+    h = _c(h, np.float32)
+    g = _c(g, np.float32)
+    k = h.size
+    assert h.shape == (k,) and g.shape == (k,)
+    rp = None
+    if r is not None:
+        r = _c(r, np.float32)
+        assert r.shape == (k,)
+        rp = r.ctypes.data
+    h_out = np.empty(k, dtype=np.float32)
+    y = np.empty(k, dtype=np.float64)
+    if k:
+        lib().orc_residual_rmsnorm(h.ctypes.data, rp, g.ctypes.data, k, float(eps), h_out.ctypes.data, y.ctypes.data)
+    return h_out, y
 
 
 # ------------------------------------------------------------ tolerances O7

@@ -327,3 +327,31 @@ int64_t orc_argmax_f32(const float* v, int64_t n) {
         if (v[i] == best) return i;
     return -1;
 }
+
+/* ------------------------------------------------------------------ O9 --
+ * The step either side of every GEMV: the residual add, the next RMSNorm
+ * and the activation re-quantization (emit_qwen38_generate, "Where the
+ * speed comes from", item 3, does the three in one kernel; GPU Kernel Lab,
+ * "Decode integration": RMSNorm with an FP32 reduction and residual
+ * fusion).  The pages give no formula; the readings (listed in the design
+ * notes) are
+ *   h'  = h + r, rounded once to fp32 (the residual stream after the add;
+ *         r may be absent: h' = h);
+ *   y_i = h'_i / sqrt(mean_j h'_j^2 + eps) * g_i, with eps and the
+ *         per-channel weight g given by the caller;
+ * and y is then quantized by the Q8_0 rule above (orc_quantize_q8_0 on the
+ * fp32 values the kernel produced).  Here the add is one IEEE fp32 rounding
+ * (exact in fp64, then rounded), the squares are exact in fp64, and the
+ * mean, the square root and the products are fp64.
+ */
+void orc_residual_rmsnorm(const float* h, const float* r, const float* g, int64_t k, double eps, float* h_out,
+                          double* y_out) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+        const float a = r ? (float)((double)h[i] + (double)r[i]) : h[i];
+        h_out[i] = a;
+        ss += (double)a * (double)a;
+    }
+    const double s = 1.0 / sqrt(ss / (double)k + eps);
+    for (int64_t i = 0; i < k; ++i) y_out[i] = (double)h_out[i] * s * (double)g[i];
+}
