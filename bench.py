@@ -93,7 +93,11 @@ def read_traffic(kernel_name: str):
 
 # ------------------------------------------------------------ workload
 
-def build_stream(wl, deq: int, requant: str):
+def build_stream(wl, deq: int, requant: str, norm: bool = False):
+    """The workload's token stream with its weights generated on the device.
+    norm=True chains the layers through the residual stream: a residual add
+    + RMSNorm + re-quantization call before each layer's attention input
+    (GEMV 0) and MLP input (GEMV 2)."""
     import torch
 
     import synth
@@ -101,7 +105,8 @@ def build_stream(wl, deq: int, requant: str):
     from weight_streaming_gemv_q8_amd.stream import TokenStream
 
     shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
-    ts = TokenStream(shapes, wl.layers, wl.wtype, deq=deq, requant=requant)
+    ts = TokenStream(shapes, wl.layers, wl.wtype, deq=deq, requant=requant,
+                     norm_before=(0, 2) if norm else (), eps=W.RMSNORM_EPS)
     log(f"allocated {ts.weight_bytes_alloc / 1e9:.3f} GB of weights; generating on the device")
     t0 = time.time()
 
@@ -115,6 +120,11 @@ def build_stream(wl, deq: int, requant: str):
     xs = [synth.activation(wl.seed, W.activation_tensor_id(l), k0, rms=True) for l in range(wl.layers)]
     import numpy as np
     ts.set_inputs(torch.from_numpy(np.stack(xs)).cuda())
+    if norm:
+        h0 = synth.normal_f32(wl.seed, W.RESIDUAL_TENSOR_ID, ts.hidden, 1.0)
+        gains = np.stack([np.float32(1.0) + synth.normal_f32(wl.seed, W.gain_tensor_id(i), ts.hidden, W.GAIN_SIGMA)
+                          for i in range(len(ts.norms))]).astype(np.float32)
+        ts.set_residual_input(torch.from_numpy(h0).cuda(), torch.from_numpy(gains).cuda())
     torch.cuda.synchronize()
     log(f"weights ready in {time.time() - t0:.1f} s")
     return ts
@@ -259,6 +269,31 @@ def measure_configs(steps: int, warmup: int) -> list:
             deq=deq)
     del wb, wq
     torch.cuda.empty_cache()
+    # the residual add + RMSNorm + re-quantization between GEMVs, alone, at
+    # the hidden sizes of the streams (bytes: h, r, g read; h', y written;
+    # y_q8 written)
+    for hidden in (1024, 4096, 5120):
+        h = torch.from_numpy(synth.normal_f32(0x5EED0009, 0, hidden, 1.0)).cuda()
+        r = torch.from_numpy(synth.normal_f32(0x5EED0009, 1, hidden, 0.5)).cuda()
+        g = torch.ones(hidden, dtype=torch.float32, device="cuda")
+        h_out = torch.empty_like(h)
+        yv = torch.empty_like(h)
+        yq = torch.empty(wsg.act_q8_0_bytes(hidden), dtype=torch.uint8, device="cuda")
+        nbytes = 20 * hidden + wsg.act_q8_0_bytes(hidden)
+        call = lambda i: wsg.residual_rmsnorm_q8_0(h, r, g, hidden, W.RMSNORM_EPS, h_out, yv, yq)
+        sec = _time_calls(call, max(steps, 1) * 40)
+        out.append({"workload": f"residual_rmsnorm_q8_0_k{hidden}", "mode": "eager", "us": round(sec * 1e6, 2),
+                    "bytes": nbytes})
+        log(f"residual_rmsnorm k={hidden:5d} eager {sec * 1e6:8.2f} us")
+        g_ = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_):
+            for i in range(256):
+                call(i)
+        sec = _time_calls(lambda i: g_.replay(), max(steps, 1) // 5 + 1) / 256
+        out.append({"workload": f"residual_rmsnorm_q8_0_k{hidden}", "mode": "graph of 256 calls",
+                    "us": round(sec * 1e6, 2), "bytes": nbytes})
+        log(f"residual_rmsnorm k={hidden:5d} graph {sec * 1e6:8.2f} us")
+        del g_
     # configs 1, 2, 4: token streams
     for wl, deqs in ((W.QWEN3_0P6B_BF16, (0,)), (W.QWEN3_8B_Q8, (0,)), (W.DENSE27B_Q8, (0, 2))):
         for deq in deqs:
@@ -269,6 +304,15 @@ def measure_configs(steps: int, warmup: int) -> list:
                 sec, kernels = time_plan(ts, plan == "persistent", steps, warmup)
                 rec(wl, f"{plan} deq{deq}" if wl.wtype != "bf16" else plan, sec, alg, kernels_per_token=kernels,
                     deq=deq)
+            ts.close()
+            del ts
+            torch.cuda.empty_cache()
+            # the same stream with the layers chained through the residual
+            # stream (a residual add + RMSNorm call before GEMVs 0 and 2)
+            ts = build_stream(wl, deq, "fused", norm=True)
+            sec, kernels = time_plan(ts, False, steps, warmup)
+            rec(wl, f"graph + residual/RMSNorm deq{deq}" if wl.wtype != "bf16" else "graph + residual/RMSNorm",
+                sec, alg, kernels_per_token=kernels, deq=deq)
             ts.close()
             del ts
             torch.cuda.empty_cache()

@@ -129,6 +129,28 @@ int convert_bf16(const float* in, int64_t count, uint16_t* out, hipStream_t stre
 int64_t act_q8_0_bytes(int64_t k);
 int quantize_act_q8_0(const float* x, int64_t k, void* x_q8, hipStream_t stream);
 
+/* ------------------------------------ residual add + RMSNorm + requant ---
+ * The step either side of every GEMV of a decode layer, in one kernel
+ * (emit_qwen38_generate, "Where the speed comes from", item 3: the residual
+ * add, the next RMSNorm and the activation re-quantization; GPU Kernel Lab,
+ * "Decode integration": FP32 reduction, residual fusion):
+ *     h'_i = h_i + r_i                      (one fp32 add; r NULL: h' = h)
+ *     y_i  = h'_i * s * g_i,  s = 1 / sqrt(mean_j h'_j^2 + eps)
+ *                                           (fp32; g NULL: gain 1)
+ *     y_q8 = the planar Q8_0 activation of y, exactly as quantize_act_q8_0
+ *            would write it from the f32 y (act_q8_0_bytes(k) bytes).
+ * h, r, g are f32[k]; h_out (h'), y (f32[k]) and y_q8 are outputs, each
+ * optional (NULL: not written; all three NULL: nothing is launched).  h_out
+ * may be h or r (an in-place residual update); no other buffers may overlap.
+ * k % 32 == 0, k <= WSG_MAX_K_Q8ACT; eps finite and > 0, else WSG_ERR_MODE.
+ * The mean of squares is accumulated in fp32 in a fixed order, so results
+ * repeat bit for bit.  One workgroup (the vector is small; the call is
+ * latency-bound).  Acceptance: h_out bit-exact (one IEEE add);
+ * |y - y_ref| <= 2^-16 |y_ref| against the fp64 definition;
+ * y_q8 bit-exact against the Q8_0 rule applied to the y this call computes. */
+int residual_rmsnorm_q8_0(const float* h, const float* r, const float* g, int64_t k, float eps, float* h_out,
+                          float* y, void* y_q8, hipStream_t stream);
+
 /* ------------------------------------------------------------- GEMVs ---
  * y[r] = sum_i W[r,i] x[i], f32 accumulation, r < n.  n == 0 is a no-op;
  * k == 0 writes y = 0.
@@ -195,6 +217,8 @@ enum {
     WSG_OP_GEMV_Q8_0 = 1,       /* w, n, k, x, act_fmt, y */
     WSG_OP_QUANTIZE_ACT = 2,    /* x (f32), k, y = x_q8 output (void*) */
     WSG_OP_LM_HEAD_ARGMAX = 3,  /* w, w_type, n, k, x, act_fmt, ws, ws_bytes, idx_out */
+    WSG_OP_RESIDUAL_RMSNORM = 4, /* residual_rmsnorm_q8_0: x = h, r, w = g, k, eps,
+                                    h_out, y (f32 y), y_q8 */
 };
 
 /* flags: WSG_OP_AFTER_ALL marks an op that depends on every earlier op of
@@ -217,6 +241,11 @@ typedef struct {
     size_t ws_bytes;
     int32_t* idx_out;
     int flags;
+    /* WSG_OP_RESIDUAL_RMSNORM only (zero for every other op) */
+    const void* r;
+    void* h_out;
+    void* y_q8;
+    float eps;
 } wsg_op_desc;
 
 typedef struct wsg_plan wsg_plan;

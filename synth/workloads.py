@@ -82,6 +82,18 @@ def activation_tensor_id(layer: int) -> int:
     return 1_000_000 + 4 * layer
 
 
+# Inputs of the chained token (residual stream + RMSNorm between GEMVs): the
+# residual stream entering layer 0 ~N(0,1) (an embedding row) and the gain
+# of every norm call, 1 + N(0, GAIN_SIGMA), in chain order.
+GAIN_SIGMA = 0.1
+RMSNORM_EPS = 1e-6
+RESIDUAL_TENSOR_ID = 2_000_000
+
+
+def gain_tensor_id(i: int) -> int:
+    return 2_000_002 + 2 * i
+
+
 Q8_SINGLE = Workload(
     0, "q8_single_1024x1024", "q8_0", 1,
     (Matrix("w", 1024, 1024, (1024,)),),

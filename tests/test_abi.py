@@ -90,6 +90,28 @@ def test_gemv_bf16_and_quant_argument_errors(L):
     assert L.convert_bf16(None, 10, A16, None) == wsg.ERR_NULL
 
 
+def test_residual_rmsnorm_argument_errors(L):
+    A16, BAD = 0x10000, 0x10004
+    f = L.residual_rmsnorm_q8_0
+    assert f(A16, A16, A16, 40, 1e-6, A16, A16, A16, None) == wsg.ERR_SHAPE
+    assert f(A16, A16, A16, -32, 1e-6, A16, A16, A16, None) == wsg.ERR_SHAPE
+    assert f(A16, A16, A16, wsg.MAX_K_Q8ACT + 32, 1e-6, A16, A16, A16, None) == wsg.ERR_SHAPE
+    assert f(A16, A16, A16, 64, 0.0, A16, A16, A16, None) == wsg.ERR_MODE
+    assert f(A16, A16, A16, 64, -1e-6, A16, A16, A16, None) == wsg.ERR_MODE
+    assert f(A16, A16, A16, 64, float("inf"), A16, A16, A16, None) == wsg.ERR_MODE
+    assert f(A16, A16, A16, 64, float("nan"), A16, A16, A16, None) == wsg.ERR_MODE
+    assert f(None, A16, A16, 64, 1e-6, A16, A16, A16, None) == wsg.ERR_NULL
+    assert f(BAD, A16, A16, 64, 1e-6, A16, A16, A16, None) == wsg.ERR_ALIGN
+    assert f(A16, BAD, A16, 64, 1e-6, A16, A16, A16, None) == wsg.ERR_ALIGN
+    assert f(A16, A16, BAD, 64, 1e-6, A16, A16, A16, None) == wsg.ERR_ALIGN
+    assert f(A16, A16, A16, 64, 1e-6, 0x10004, A16, A16, None) == wsg.ERR_ALIGN
+    assert f(A16, A16, A16, 64, 1e-6, A16, 0x10004, A16, None) == wsg.ERR_ALIGN
+    assert f(A16, A16, A16, 64, 1e-6, A16, A16, 0x10008, None) == wsg.ERR_ALIGN
+    # nothing to write, or an empty vector: no launch, no error
+    assert f(None, None, None, 64, 1e-6, None, None, None, None) == wsg.OK
+    assert f(None, None, None, 0, 1e-6, A16, A16, A16, None) == wsg.OK
+
+
 def test_lm_head_and_argmax_argument_errors(L):
     A16 = 0x10000
     ws = wsg.argmax_ws_bytes()

@@ -27,7 +27,7 @@ ACT_Q8_0, ACT_F32, ACT_F32_REQUANT = 0, 1, 2
 # weight types
 W_BF16, W_Q8_0 = 0, 1
 # plan ops
-OP_GEMV_BF16, OP_GEMV_Q8_0, OP_QUANTIZE_ACT, OP_LM_HEAD_ARGMAX = 0, 1, 2, 3
+OP_GEMV_BF16, OP_GEMV_Q8_0, OP_QUANTIZE_ACT, OP_LM_HEAD_ARGMAX, OP_RESIDUAL_RMSNORM = 0, 1, 2, 3, 4
 OP_AFTER_ALL = 1  # OpDesc.flags: depends on every earlier op of the plan
 
 MAX_K_Q8ACT = 57344
@@ -36,7 +36,8 @@ MAX_K_F32ACT = 36864
 # exported C symbols, in header order
 EXPORTS = (
     "wsg_status_str", "wsg_version", "q8_0_row_bytes", "q8_0_packed_bytes", "pack_q8_0",
-    "quantize_q8_0_weights", "convert_bf16", "act_q8_0_bytes", "quantize_act_q8_0", "gemv_bf16",
+    "quantize_q8_0_weights", "convert_bf16", "act_q8_0_bytes", "quantize_act_q8_0",
+    "residual_rmsnorm_q8_0", "gemv_bf16",
     "gemv_q8_0", "wsg_gemv_config", "wsg_tune", "wsg_argmax_ws_bytes", "lm_head_argmax", "argmax_f32", "wsg_plan_create",
     "wsg_plan_launch", "wsg_plan_create_persistent", "wsg_plan_error", "wsg_plan_destroy", "wsg_plan_kernel_count",
     "wsg_stream_config", "wsg_read_probe",
@@ -57,6 +58,7 @@ class OpDesc(ctypes.Structure):
         ("w", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t), ("idx_out", ctypes.c_void_p),
         ("flags", ctypes.c_int),
+        ("r", ctypes.c_void_p), ("h_out", ctypes.c_void_p), ("y_q8", ctypes.c_void_p), ("eps", ctypes.c_float),
     ]
 
 
@@ -82,6 +84,7 @@ def lib():
             "convert_bf16": (i32, [vp, i64, vp, vp]),
             "act_q8_0_bytes": (i64, [i64]),
             "quantize_act_q8_0": (i32, [vp, i64, vp, vp]),
+            "residual_rmsnorm_q8_0": (i32, [vp, vp, vp, i64, ctypes.c_float, vp, vp, vp, vp]),
             "gemv_bf16": (i32, [vp, i64, i64, vp, vp, vp]),
             "gemv_q8_0": (i32, [vp, i64, i64, vp, i32, vp, vp, vp]),
             "wsg_gemv_config": (i32, [i32, i32, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
@@ -175,6 +178,14 @@ def quantize_act_q8_0(x, k: int, x_q8, stream=None) -> None:
     _check("quantize_act_q8_0", lib().quantize_act_q8_0(_ptr(x), k, _ptr(x_q8), _stream(stream)))
 
 
+def residual_rmsnorm_q8_0(h, r, g, k: int, eps: float, h_out=None, y=None, y_q8=None, stream=None) -> None:
+    """h' = h + r, y = h' / sqrt(mean(h'^2) + eps) * g, y_q8 = Q8_0(y); r, g and
+    each output may be None."""
+    _check("residual_rmsnorm_q8_0",
+           lib().residual_rmsnorm_q8_0(_ptr(h), _ptr(r), _ptr(g), k, eps, _ptr(h_out), _ptr(y), _ptr(y_q8),
+                                       _stream(stream)))
+
+
 # ------------------------------------------------------------------ GEMV
 
 def gemv_bf16(w, n: int, k: int, x, y, stream=None) -> None:
@@ -238,6 +249,11 @@ def op_quantize_act(x, k, x_q8) -> OpDesc:
 def op_lm_head_argmax(w, w_type, n, k, x, act_fmt, ws, ws_bytes, idx_out, debug_logits=None) -> OpDesc:
     return OpDesc(op=OP_LM_HEAD_ARGMAX, w_type=w_type, act_fmt=act_fmt, n=n, k=k, w=_ptr(w), x=_ptr(x),
                   y=_ptr(debug_logits), ws=_ptr(ws), ws_bytes=ws_bytes, idx_out=_ptr(idx_out))
+
+
+def op_residual_rmsnorm(h, r, g, k, eps, h_out=None, y=None, y_q8=None) -> OpDesc:
+    return OpDesc(op=OP_RESIDUAL_RMSNORM, k=k, x=_ptr(h), r=_ptr(r), w=_ptr(g), eps=eps, h_out=_ptr(h_out),
+                  y=_ptr(y), y_q8=_ptr(y_q8))
 
 
 class Plan:

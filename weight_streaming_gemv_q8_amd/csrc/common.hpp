@@ -117,6 +117,43 @@ __device__ inline uint16_t q8_quantize_block_bits(const float* v, int8_t* q) {
     return d16;
 }
 
+// The same rule for a block spread over a quad: four consecutive lanes (all
+// active together) hold the block's 32 values, eight each, in order.  The
+// block maximum meets in a quad reduction, every lane derives the same
+// scale and packs its eight codes little-endian into lo (values 0-3) and hi
+// (values 4-7).  Returns the scale bits.
+__device__ inline uint16_t q8_quad_codes(const float (&v)[8], uint32_t& lo, uint32_t& hi) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    const uint16_t d16 = q8_scale_bits(amax);
+    const float d = half_bits_to_float(d16);
+    lo = 0;
+    hi = 0;
+    if (d != 0.0f) {
+        const float r = 1.0f / d;
+        int q[8];
+        bool any_near = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            bool near;
+            q[i] = q8_code_fast(v[i], r, near);
+            any_near |= near;
+        }
+        if (__any(any_near)) {  // rare: a value within 4e-5 of a rounding boundary
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = q8_code(v[i], d, r);
+        }
+        lo = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) | ((uint32_t)(q[2] & 0xFF) << 16) |
+             ((uint32_t)q[3] << 24);
+        hi = (uint32_t)(q[4] & 0xFF) | ((uint32_t)(q[5] & 0xFF) << 8) | ((uint32_t)(q[6] & 0xFF) << 16) |
+             ((uint32_t)q[7] << 24);
+    }
+    return d16;
+}
+
 // ------------------------------------------------------- wave reductions
 // Butterfly sums over the 64 lanes of a wave; every lane ends with the same
 // value and the order of additions does not depend on which row is reduced.

@@ -459,44 +459,18 @@ struct StageQ8 {
 };
 
 // Requantized activation (the Q8_0 rule of quantize_act_q8_0) into the LDS
-// layout of the int8 path: four lanes per 32-value block, eight values each;
-// the block maximum meets in a quad reduction, every lane derives the same
-// scale and writes its eight codes (one 8-byte LDS store).
+// layout of the int8 path: four lanes per 32-value block, eight values each
+// (q8_quad_codes); every lane writes its eight codes (one 8-byte LDS store).
 __device__ inline void requant_unit(const float4v v0, const float4v v1, int u, int4v* lds_q, float* lds_dx) {
     const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, kWave));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, kWave));
-    const uint16_t d16 = q8_scale_bits(amax);
-    const float d = half_bits_to_float(d16);
-    uint32_t lo = 0, hi = 0;
-    if (d != 0.0f) {
-        const float r = 1.0f / d;
-        int q[8];
-        bool any_near = false;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            bool near;
-            q[i] = q8_code_fast(v[i], r, near);
-            any_near |= near;
-        }
-        if (__any(any_near)) {  // rare: a value within 4e-5 of a rounding boundary
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = q8_code(v[i], d, r);
-        }
-        lo = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) | ((uint32_t)(q[2] & 0xFF) << 16) |
-             ((uint32_t)q[3] << 24);
-        hi = (uint32_t)(q[4] & 0xFF) | ((uint32_t)(q[5] & 0xFF) << 8) | ((uint32_t)(q[6] & 0xFF) << 16) |
-             ((uint32_t)q[7] << 24);
-    }
+    uint32_t lo, hi;
+    const uint16_t d16 = q8_quad_codes(v, lo, hi);
     const int b = u >> 2, e = u & 3;
     const int c = b / kWave, l = b % kWave, h = e >> 1;
     uint32_t* dst = reinterpret_cast<uint32_t*>(lds_q + (c * 2 + h) * kWave + l) + 2 * (e & 1);
     dst[0] = lo;
     dst[1] = hi;
-    if (e == 0) lds_dx[b] = d;
+    if (e == 0) lds_dx[b] = half_bits_to_float(d16);
 }
 
 // f32 activation quantized with the Q8_0 rule into the same LDS layout (the

@@ -19,6 +19,8 @@ int validate_gemv_q8(const void* w, int64_t n, int64_t k, const void* x, int act
 int validate_gemv_bf16(const void* w, int64_t n, int64_t k, const void* x, const void* y);
 int validate_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, const void* ws,
                      size_t ws_bytes, const void* idx_out);
+int validate_residual_rmsnorm(const float* h, const float* r, const float* g, int64_t k, float eps,
+                              const void* h_out, const void* y, const void* y_q8);
 }  // namespace wsg
 
 struct wsg_plan {
@@ -44,6 +46,10 @@ int validate_op(const wsg_op_desc& d) {
             return WSG_OK;
         case WSG_OP_LM_HEAD_ARGMAX:
             return wsg::validate_lm_head(d.w, d.w_type, d.n, d.k, d.x, d.act_fmt, d.ws, d.ws_bytes, d.idx_out);
+        case WSG_OP_RESIDUAL_RMSNORM:
+            return wsg::validate_residual_rmsnorm(static_cast<const float*>(d.x), static_cast<const float*>(d.r),
+                                                  static_cast<const float*>(d.w), d.k, d.eps, d.h_out, d.y,
+                                                  d.y_q8);
         default: return WSG_ERR_MODE;
     }
 }
@@ -59,6 +65,10 @@ int enqueue_op(const wsg_op_desc& d, hipStream_t s) {
         case WSG_OP_LM_HEAD_ARGMAX:
             return lm_head_argmax(d.w, d.w_type, d.n, d.k, d.x, d.act_fmt, d.ws, d.ws_bytes, d.idx_out,
                                   static_cast<float*>(d.y), s);
+        case WSG_OP_RESIDUAL_RMSNORM:
+            return residual_rmsnorm_q8_0(static_cast<const float*>(d.x), static_cast<const float*>(d.r),
+                                         static_cast<const float*>(d.w), d.k, d.eps, static_cast<float*>(d.h_out),
+                                         static_cast<float*>(d.y), d.y_q8, s);
         default: return WSG_ERR_MODE;
     }
 }

@@ -8,6 +8,15 @@ GEMV's output (the projections' data flow within a layer; the non-GEMV
 operators between them are not part of this path).  Every GEMV writes its
 own output buffer, so all intermediates stay readable after a replay.
 
+With ``norm_before`` the chain also carries the residual stream between
+the GEMVs (item 3 of the same section: the residual add, the next RMSNorm
+and the activation re-quantization in one kernel): before each listed GEMV
+a residual_rmsnorm_q8_0 call adds the previous GEMV's output (the previous
+layer's last GEMV for a layer's first) to the residual stream and feeds the
+GEMV the normalized, re-quantized result.  Each such call writes its own
+buffers, so a replay is a pure function of the token's input vector and
+the weights, and every intermediate stays readable.
+
 Weights live in one allocation; concatenated projections are filled part by
 part into consecutive row ranges.  How the weight values are produced is
 left to the caller (``fill_q8`` / ``fill_bf16`` callbacks that write f32
@@ -41,6 +50,19 @@ class GemvSlot:
     x_ptr: int = 0     # f32 input (layer input or previous output)
     xq_ptr: int = 0    # quantized-activation buffer (separate-requant mode only)
     y: torch.Tensor = None
+    norm: "NormSlot" = None  # the residual + RMSNorm call feeding this GEMV
+
+
+@dataclass(eq=False)
+class NormSlot:
+    layer: int
+    index: int              # the GEMV it feeds
+    h_in: int = 0           # residual stream before the add
+    r: int = 0              # added output (0: none)
+    g: int = 0              # gain vector
+    h_out: torch.Tensor = None
+    y: torch.Tensor = None  # f32 normalized vector
+    yq: torch.Tensor = None  # its Q8_0 activation (int8 paths)
 
 
 class TokenStream:
@@ -53,10 +75,17 @@ class TokenStream:
             layer GEMV.  BF16 chains ignore it.
     requant: "fused" (the GEMV quantizes its f32 input itself) or
             "separate" (a quantize_act_q8_0 launch before each GEMV).
+    norm_before: indices of the GEMVs of a layer that read the residual
+            stream through a residual add + RMSNorm (e.g. (0, 2): the
+            attention input and the MLP input); each such GEMV's k, and the
+            rows of the GEMV before it, are the hidden size.  Empty: every
+            layer starts from its own input vector (set_inputs).
+    eps:    the RMSNorm epsilon.
     """
 
     def __init__(self, shapes: Sequence[Tuple[int, int, Tuple[int, ...]]], layers: int, wtype: str,
-                 deq: int = 0, requant: str = "fused", device: str = "cuda"):
+                 deq: int = 0, requant: str = "fused", device: str = "cuda",
+                 norm_before: Sequence[int] = (), eps: float = 1e-6):
         if wtype not in ("q8_0", "bf16"):
             raise ValueError("wtype must be q8_0 or bf16")
         if requant not in ("fused", "separate"):
@@ -90,6 +119,13 @@ class TokenStream:
                 s.x_ptr = self.inputs[s.layer].data_ptr()
             else:
                 s.x_ptr = self.slots[i - 1].y.data_ptr()
+        self.norm_before = tuple(sorted(set(int(j) for j in norm_before)))
+        self.eps = float(eps)
+        self.norms: List[NormSlot] = []
+        self.h0 = None
+        self.gains = None
+        if self.norm_before:
+            self._lay_out_norms(device)
         self.xq = None
         if wtype == "q8_0" and requant == "separate":
             per = [_align(wsg.act_q8_0_bytes(k)) for _, k, _ in self.shapes]
@@ -99,6 +135,32 @@ class TokenStream:
                 s.xq_ptr = base
                 base += per[s.index]
         self.plan = None
+
+    def _lay_out_norms(self, device: str) -> None:
+        hidden = self.shapes[self.norm_before[0]][1]
+        nm = len(self.shapes)
+        for j in self.norm_before:
+            if not 0 <= j < nm or self.shapes[j][1] != hidden or self.shapes[j - 1][0] != hidden:
+                raise ValueError("a normalized GEMV's k and the previous GEMV's rows must be the hidden size")
+        self.hidden = hidden
+        self.h0 = torch.zeros(hidden, dtype=torch.float32, device=device)
+        count = self.layers * len(self.norm_before)
+        self.gains = torch.ones((count, hidden), dtype=torch.float32, device=device)
+        int8 = self.wtype == "q8_0" and self.act_fmt() != wsg.ACT_F32
+        h_in = self.h0.data_ptr()
+        for i, s in enumerate(self.slots):
+            if s.index not in self.norm_before:
+                continue
+            n = NormSlot(s.layer, s.index, h_in=h_in, g=self.gains[len(self.norms)].data_ptr())
+            n.r = self.slots[i - 1].y.data_ptr() if i > 0 else 0
+            n.h_out = torch.empty(hidden, dtype=torch.float32, device=device)
+            n.y = torch.empty(hidden, dtype=torch.float32, device=device)
+            if int8:
+                n.yq = torch.empty(_align(wsg.act_q8_0_bytes(hidden)), dtype=torch.uint8, device=device)
+            h_in = n.h_out.data_ptr()
+            s.norm = n
+            s.x_ptr = n.y.data_ptr()
+            self.norms.append(n)
 
     # ------------------------------------------------------------ sizes
     def algorithmic_weight_bytes(self) -> int:
@@ -142,12 +204,28 @@ class TokenStream:
     def set_inputs(self, x_rows: torch.Tensor) -> None:
         self.inputs.copy_(x_rows)
 
+    def set_residual_input(self, h0: torch.Tensor, gains: torch.Tensor = None) -> None:
+        """The residual stream entering layer 0 and (optionally) the gains of
+        every norm call, in chain order ([layers * len(norm_before), hidden])."""
+        self.h0.copy_(h0)
+        if gains is not None:
+            self.gains.copy_(gains)
+
     # ------------------------------------------------------------ calls
     def _slot_ops(self, s: GemvSlot) -> List[wsg.OpDesc]:
         w = self.weights.data_ptr() + s.w_offset
+        pre = []
+        if s.norm is not None:
+            n = s.norm
+            pre = [wsg.op_residual_rmsnorm(n.h_in, n.r or None, n.g, self.hidden, self.eps, h_out=n.h_out,
+                                           y=n.y, y_q8=n.yq)]
+            if n.yq is not None:
+                return pre + [wsg.op_gemv_q8_0(w, s.n, s.k, n.yq, wsg.ACT_Q8_0, s.y)]
         if self.wtype == "bf16":
-            return [wsg.op_gemv_bf16(w, s.n, s.k, s.x_ptr, s.y)]
+            return pre + [wsg.op_gemv_bf16(w, s.n, s.k, s.x_ptr, s.y)]
         fmt = self.act_fmt()
+        if pre:
+            return pre + [wsg.op_gemv_q8_0(w, s.n, s.k, s.x_ptr, fmt, s.y)]
         if fmt == wsg.ACT_Q8_0:
             return [wsg.op_quantize_act(s.x_ptr, s.k, s.xq_ptr),
                     wsg.op_gemv_q8_0(w, s.n, s.k, s.xq_ptr, wsg.ACT_Q8_0, s.y)]
@@ -174,6 +252,9 @@ class TokenStream:
                 wsg.gemv_bf16(op.w, op.n, op.k, op.x, op.y, stream=stream)
             elif op.op == wsg.OP_QUANTIZE_ACT:
                 wsg.quantize_act_q8_0(op.x, op.k, op.y, stream=stream)
+            elif op.op == wsg.OP_RESIDUAL_RMSNORM:
+                wsg.residual_rmsnorm_q8_0(op.x, op.r, op.w, op.k, op.eps, h_out=op.h_out, y=op.y, y_q8=op.y_q8,
+                                          stream=stream)
             else:
                 wsg.gemv_q8_0(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
 
