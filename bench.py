@@ -93,11 +93,12 @@ def read_traffic(kernel_name: str):
 
 # ------------------------------------------------------------ workload
 
-def build_stream(wl, deq: int, requant: str, norm: bool = False):
+def build_stream(wl, deq: int, requant: str, norm: bool = False, fused_norm: bool = False):
     """The workload's token stream with its weights generated on the device.
     norm=True chains the layers through the residual stream: a residual add
     + RMSNorm + re-quantization call before each layer's attention input
-    (GEMV 0) and MLP input (GEMV 2)."""
+    (GEMV 0) and MLP input (GEMV 2); fused_norm=True computes that step in
+    the GEMV's prologue instead (int8 Q8_0 streams)."""
     import torch
 
     import synth
@@ -106,7 +107,7 @@ def build_stream(wl, deq: int, requant: str, norm: bool = False):
 
     shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
     ts = TokenStream(shapes, wl.layers, wl.wtype, deq=deq, requant=requant,
-                     norm_before=(0, 2) if norm else (), eps=W.RMSNORM_EPS)
+                     norm_before=(0, 2) if norm else (), eps=W.RMSNORM_EPS, fused_norm=fused_norm)
     log(f"allocated {ts.weight_bytes_alloc / 1e9:.3f} GB of weights; generating on the device")
     t0 = time.time()
 
@@ -320,6 +321,15 @@ def measure_configs(steps: int, warmup: int) -> list:
             ts.close()
             del ts
             torch.cuda.empty_cache()
+            if wl.wtype == "q8_0" and deq == 0:
+                # the same chain with the norm step in each normalized GEMV's prologue
+                ts = build_stream(wl, deq, "fused", norm=True, fused_norm=True)
+                sec, kernels = time_plan(ts, False, steps, warmup)
+                rec(wl, f"graph + residual/RMSNorm fused into the GEMVs deq{deq}", sec, alg,
+                    kernels_per_token=kernels, deq=deq)
+                ts.close()
+                del ts
+                torch.cuda.empty_cache()
     return out
 
 

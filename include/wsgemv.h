@@ -151,6 +151,23 @@ int quantize_act_q8_0(const float* x, int64_t k, void* x_q8, hipStream_t stream)
 int residual_rmsnorm_q8_0(const float* h, const float* r, const float* g, int64_t k, float eps, float* h_out,
                           float* y, void* y_q8, hipStream_t stream);
 
+/* The int8-activation Q8_0 GEMV fed by residual_rmsnorm_q8_0, which every
+ * workgroup computes in its prologue instead of a launch of its own
+ * (emit_qwen38_generate, "Where the speed comes from", item 3):
+ *   h' = h + r (r nullable), x = h' / sqrt(mean h'^2 + eps) * g (g nullable),
+ *   y = W . Q8_0(x)  (int8 activations, as gemv_q8_0 with WSG_ACT_Q8_0),
+ * and h' is written to h_out (nullable) by one workgroup.  The mean of
+ * squares is reduced in the order residual_rmsnorm_q8_0 uses and the codes
+ * are computed with the same operations, so y equals gemv_q8_0 fed that
+ * call's y_q8, bit for bit, and h_out equals its h_out.  W in the device
+ * layout, n >= 1, 32 <= k <= WSG_MAX_K_Q8ACT, k % 32 == 0 (WSG_ERR_SHAPE);
+ * eps as for residual_rmsnorm_q8_0 (WSG_ERR_MODE); h, r, g, h_out 16-byte
+ * aligned; h_out must not overlap h, r or g, and y must overlap none of
+ * h, r, g, h_out (WSG_ERR_MODE): other workgroups still read the inputs
+ * while one writes h_out. */
+int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r, const float* g,
+                      float eps, float* h_out, float* y, hipStream_t stream);
+
 /* ------------------------------------------------------------- GEMVs ---
  * y[r] = sum_i W[r,i] x[i], f32 accumulation, r < n.  n == 0 is a no-op;
  * k == 0 writes y = 0.
@@ -219,6 +236,7 @@ enum {
     WSG_OP_LM_HEAD_ARGMAX = 3,  /* w, w_type, n, k, x, act_fmt, ws, ws_bytes, idx_out */
     WSG_OP_RESIDUAL_RMSNORM = 4, /* residual_rmsnorm_q8_0: x = h, r, w = g, k, eps,
                                     h_out, y (f32 y), y_q8 */
+    WSG_OP_GEMV_Q8_0_RMSNORM = 5, /* gemv_q8_0_rmsnorm: w, n, k, x = h, r, g, eps, h_out, y */
 };
 
 /* flags: WSG_OP_AFTER_ALL marks an op that depends on every earlier op of
@@ -241,11 +259,13 @@ typedef struct {
     size_t ws_bytes;
     int32_t* idx_out;
     int flags;
-    /* WSG_OP_RESIDUAL_RMSNORM only (zero for every other op) */
+    /* WSG_OP_RESIDUAL_RMSNORM and WSG_OP_GEMV_Q8_0_RMSNORM only (zero for
+     * every other op) */
     const void* r;
     void* h_out;
     void* y_q8;
     float eps;
+    const void* g; /* WSG_OP_GEMV_Q8_0_RMSNORM's norm weight */
 } wsg_op_desc;
 
 typedef struct wsg_plan wsg_plan;

@@ -179,3 +179,22 @@ def test_ring_plan_shape_and_rejections_before_launch(L):
     assert L.wsg_plan_create_ring(ops, 1, wsg.RING_VARIANTS, None, ctypes.byref(h)) == wsg.ERR_MODE
     assert L.wsg_plan_create_ring(ops, 1, 0, None, ctypes.byref(h)) == wsg.ERR_MODE  # not a Q8_0 GEMV
     assert not h.value
+
+
+def test_fused_norm_gemv_rejects_before_launch(L):
+    # fake, aligned device addresses: every case fails validation, so nothing
+    # is launched (no GPU needed)
+    A = 0x100000
+    h, r, g, h_out, y = A, A + 0x10000, A + 0x20000, A + 0x30000, A + 0x40000
+    f = L.gemv_q8_0_rmsnorm
+    assert f(A, 0, 1024, h, r, g, 1e-6, h_out, y, None) == wsg.ERR_SHAPE          # n = 0
+    assert f(A, 8, 0, h, r, g, 1e-6, h_out, y, None) == wsg.ERR_SHAPE             # k = 0
+    assert f(A, 8, 1000, h, r, g, 1e-6, h_out, y, None) == wsg.ERR_SHAPE          # k % 32
+    assert f(A, 8, wsg.MAX_K_Q8ACT + 32, h, r, g, 1e-6, h_out, y, None) == wsg.ERR_SHAPE
+    assert f(A, 8, 1024, h, r, g, 0.0, h_out, y, None) == wsg.ERR_MODE            # eps
+    assert f(A, 8, 1024, h, r, g, 1e-6, h, y, None) == wsg.ERR_MODE               # h_out over h
+    assert f(A, 8, 1024, h, r, g, 1e-6, r + 64, y, None) == wsg.ERR_MODE          # h_out over r
+    assert f(A, 8, 1024, h, r, g, 1e-6, h_out, g, None) == wsg.ERR_MODE           # y over g
+    assert f(A, 8, 1024, h, r, g, 1e-6, h_out, h_out + 16, None) == wsg.ERR_MODE  # y over h_out
+    assert f(A, 8, 1024, h + 4, r, g, 1e-6, h_out, y, None) == wsg.ERR_ALIGN
+    assert f(A, 8, 1024, None, r, g, 1e-6, h_out, y, None) == wsg.ERR_NULL

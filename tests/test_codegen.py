@@ -74,6 +74,14 @@ def test_stream_ring_keeps_two_items_in_flight(asm):
         assert _max_wait_before_dot(body) >= 6, name
 
 
+def test_fused_norm_gemv_keeps_two_items_in_flight(asm):
+    # the GEMVs that compute the residual add + RMSNorm in their prologue
+    ks = {n: b for n, b in _kernels(asm["gemv.hip"]).items() if "q8_i8_norm_kernel" in n}
+    assert ks
+    for name, body in ks.items():
+        assert _max_wait_before_dot(body) >= 6, name
+
+
 def test_eager_int8_ring_keeps_two_items_in_flight(asm):
     # one-chunk items (U = 1), int8 activations and the requantizing staging
     ks = {n: b for n, b in _kernels(asm["gemv.hip"]).items()

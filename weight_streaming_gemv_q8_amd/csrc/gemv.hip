@@ -47,12 +47,15 @@ template <int U, int S = 1>
 constexpr int kRingSets = U == 1 ? (S > 1 ? kRingSplit : kRing1) : 2;
 
 // ------------------------------------------------ Q8_0 x int8 (and requant)
-template <int WAVES, int S, int U, int ACT, bool NT, bool DEBUG, bool ARGMAX>
-__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
-q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict__ xin, float* __restrict__ y,
-             int32_t* __restrict__ dots, uint64_t* __restrict__ keys) {
+// The int8 path's body; `stage` fills the activation's LDS layout:
+// stage.issue() requests the input before the first weight items are
+// requested, stage.commit(lds_q, lds_dx, scratch) completes it (scratch:
+// LDS the row loop has not started to use).
+template <int WAVES, int S, int U, bool DEBUG, bool ARGMAX, typename Stage>
+__device__ __attribute__((always_inline)) inline void q8_i8_body(const uint8_t* __restrict__ W, int n, int k,
+                                                                 float* __restrict__ y, int32_t* __restrict__ dots,
+                                                                 uint64_t* __restrict__ keys, Stage& stage) {
     static_assert(WAVES % S == 0, "S must divide WAVES");
-    static_assert(NT, "the weight stream is always loaded non-temporally");
     extern __shared__ __align__(16) uint8_t smem[];
     const int C = (int)chunk_count(k);
     const int NB = k / kBlock;
@@ -94,21 +97,11 @@ q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
     };
 
     Q8Regs<U> R[kRingSets<U, S>];
-    if constexpr (ACT == kActRequant) {
-        StageRequant<4> st;
-        st.issue(xin, k, C);
-        __builtin_amdgcn_sched_barrier(0);
-        prologue(R);
-        __builtin_amdgcn_sched_barrier(0);
-        st.commit(xin, k, C, lds_q, lds_dx);
-    } else {
-        StageQ8<4> st;
-        st.issue(xin, k, C);
-        __builtin_amdgcn_sched_barrier(0);
-        prologue(R);
-        __builtin_amdgcn_sched_barrier(0);
-        st.commit(xin, k, C, lds_q, lds_dx);
-    }
+    stage.issue();
+    __builtin_amdgcn_sched_barrier(0);
+    prologue(R);
+    __builtin_amdgcn_sched_barrier(0);
+    stage.commit(lds_q, lds_dx, lds_res);
     __syncthreads();
     if constexpr (kRot) {
         if (rot) {
@@ -133,6 +126,37 @@ q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
     });
     if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
+}
+
+// Staging of the int8 path's input: a quantize_act_q8_0 output, or f32
+// requantized in the workgroup.
+template <int ACT>
+struct StageInput {
+    const void* xin;
+    int k, C;
+    typename std::conditional<ACT == kActRequant, StageRequant<4>, StageQ8<4>>::type st;
+    __device__ void issue() { st.issue(xin, k, C); }
+    __device__ void commit(int4v* lds_q, float* lds_dx, float*) { st.commit(xin, k, C, lds_q, lds_dx); }
+};
+
+template <int WAVES, int S, int U, int ACT, bool NT, bool DEBUG, bool ARGMAX>
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict__ xin, float* __restrict__ y,
+             int32_t* __restrict__ dots, uint64_t* __restrict__ keys) {
+    static_assert(NT, "the weight stream is always loaded non-temporally");
+    StageInput<ACT> stage{xin, k, (int)chunk_count(k), {}};
+    q8_i8_body<WAVES, S, U, DEBUG, ARGMAX>(W, n, k, y, dots, keys, stage);
+}
+
+// The int8 path fed by the residual add + RMSNorm + re-quantization of
+// residual_rmsnorm_q8_0, computed by every workgroup in its prologue
+// (emit_qwen38_generate, "Where the speed comes from", item 3): the same
+// codes and scales, bit for bit, with no launch of its own.
+template <int WAVES, int S, int U>
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+q8_i8_norm_kernel(const uint8_t* __restrict__ W, int n, int k, NormArgs na, float* __restrict__ y) {
+    StageNorm<WAVES * kWave> stage{na, k, {}};
+    q8_i8_body<WAVES, S, U, false, false>(W, n, k, y, nullptr, nullptr, stage);
 }
 
 template <int WAVES, int S, int U, bool NT, bool ARGMAX>
@@ -559,6 +583,21 @@ int launch_q8_i8(const void* w, int n, int k, const void* x, float* y, int32_t* 
     }
 }
 
+// The int8 path fed by the fused residual + RMSNorm staging: the waves and
+// split of the requantizing path for this shape, one-chunk items (the
+// staging's registers leave no room for deeper ones).
+int launch_q8_norm(const void* w, int n, int k, const NormArgs& na, float* y, hipStream_t stream, LaunchInfo* info,
+                   bool run = true) {
+    const Cfg c = choose_cfg(kPathI8, n, k);
+    const size_t lds_act = lds_q8act_bytes((int)chunk_count(k));
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
+        constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
+        auto kern = q8_i8_norm_kernel<Wv, Sv, 1>;
+        return launch_kernel<Wv, Sv>(kern, q8_lds_bytes<Wv>(lds_act), n, info, 1, run, stream, wp, n, k, na, y);
+    });
+}
+
 template <bool ARGMAX>
 int launch_q8_f32(const void* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
                   LaunchInfo* info, bool run = true) {
@@ -648,6 +687,31 @@ int validate_gemv_bf16(const void* w, int64_t n, int64_t k, const void* x, const
     return check_bf16_args(w, n, k, x, y);
 }
 
+int validate_residual_rmsnorm(const float* h, const float* r, const float* g, int64_t k, float eps,
+                              const void* h_out, const void* y, const void* y_q8);
+
+namespace {
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a && b && a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+}  // namespace
+
+int validate_gemv_q8_rmsnorm(const void* w, int64_t n, int64_t k, const float* h, const float* r, const float* g,
+                             float eps, const void* h_out, const void* y) {
+    int rc = check_q8_args(w, n, k, h, WSG_ACT_F32_REQUANT, y);
+    if (rc != WSG_OK) return rc;
+    if (n < 1 || k < kBlock) return WSG_ERR_SHAPE;
+    rc = validate_residual_rmsnorm(h, r, g, k, eps, h_out, y, nullptr);
+    if (rc != WSG_OK) return rc;
+    // every workgroup reads h, r and g while workgroup 0 writes h_out
+    if (overlaps(h_out, 4 * k, h, 4 * k) || overlaps(h_out, 4 * k, r, 4 * k) || overlaps(h_out, 4 * k, g, 4 * k) ||
+        overlaps(y, 4 * n, h, 4 * k) || overlaps(y, 4 * n, r, 4 * k) || overlaps(y, 4 * n, g, 4 * k) ||
+        overlaps(y, 4 * n, h_out, 4 * k))
+        return WSG_ERR_MODE;
+    return WSG_OK;
+}
+
 int validate_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, const void* ws,
                      size_t ws_bytes, const void* idx_out) {
     if (w_type != WSG_W_BF16 && w_type != WSG_W_Q8_0) return WSG_ERR_MODE;
@@ -690,6 +754,13 @@ int gemv_q8_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act
                ? launch_q8_i8<kActRequant, true, false>(w_packed, ni, ki, x, y, debug_block_dots, nullptr, stream,
                                                         nullptr)
                : launch_q8_i8<kActRequant, false, false>(w_packed, ni, ki, x, y, nullptr, nullptr, stream, nullptr);
+}
+
+int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r, const float* g,
+                      float eps, float* h_out, float* y, hipStream_t stream) {
+    const int rc = validate_gemv_q8_rmsnorm(w_packed, n, k, h, r, g, eps, h_out, y);
+    if (rc != WSG_OK) return rc;
+    return launch_q8_norm(w_packed, (int)n, (int)k, NormArgs{h, r, g, h_out, eps}, y, stream, nullptr);
 }
 
 int gemv_bf16(const uint16_t* w, int64_t n, int64_t k, const float* x, float* y, hipStream_t stream) {

@@ -506,6 +506,184 @@ struct StageRequant {
     }
 };
 
+// ------------------------------------ residual + RMSNorm + requantization
+// Arguments of residual_rmsnorm_q8_0 when a GEMV computes it in its
+// prologue: h' = h + r (r nullable), y = h' / sqrt(mean h'^2 + eps) * g (g
+// nullable), h' stored to h_out (nullable) by workgroup 0.
+struct NormArgs {
+    const float* h;
+    const float* r;
+    const float* g;
+    float* h_out;
+    float eps;
+};
+
+// Threads residual_rmsnorm_q8_0 runs for k values; thread t owns the units
+// (eight values) t, t + T, t + 2T, ...
+__host__ __device__ inline int norm_threads(int k) {
+    const int units = k / 8;
+    const int nt = (units + kWave - 1) / kWave * kWave;
+    return nt > 1024 ? 1024 : (nt < kWave ? kWave : nt);
+}
+
+// The norm step as a GEMV's input staging, by a workgroup of T threads.  The
+// mean of squares is reduced exactly as residual_rmsnorm_q8_0 reduces it:
+// this workgroup plays that kernel's threads (thread vt = tid + m T),
+// each summing its units in order with fused multiply-adds, then the same
+// butterfly per wave and the wave partials in wave order; the values are
+// then scaled and quantized with the same operations.  So the codes and
+// scales in LDS are those that kernel writes, bit for bit.  Up to four
+// units of the first pass are requested before the weight stream starts
+// (issue); the rest, the reduction and the second pass come in commit.
+// With one unit per norm thread (k <= 8192) both passes see the same units,
+// so g is requested with them and the second pass reads nothing: one round
+// trip to memory in all.
+template <int T>
+struct StageNorm {
+    static_assert(T % kWave == 0 && 1024 % T == 0, "a whole number of waves dividing 1024 threads");
+    static constexpr int MV = 1024 / T;  // most norm threads one thread plays
+    NormArgs na;
+    int k;
+    float4v hv[4][2];
+    float4v gv[4][2];  // g of the same units, when one unit per norm thread (k <= 8192)
+
+    __device__ int pairs(int& nt, int& nu, int& units) const {
+        units = k / 8;
+        nt = norm_threads(k);
+        nu = (units + nt - 1) / nt;
+        return ((nt + T - 1) / T) * nu;
+    }
+    // loads h' of pairs p0 .. p0 + 3 (pair p: norm thread tid + (p / nu) T,
+    // its (p % nu)-th unit)
+    __device__ void load4(int p0, int P, int nt, int nu, int units) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int p = p0 + q, m = p / nu, i = p - m * nu;
+            const int vt = (int)threadIdx.x + m * T, u = vt + i * nt;
+            if (p < P && vt < nt && u < units) {
+                const float4v* h4 = reinterpret_cast<const float4v*>(na.h) + 2 * u;
+                hv[q][0] = h4[0];
+                hv[q][1] = h4[1];
+                if (na.r) {
+                    const float4v* r4 = reinterpret_cast<const float4v*>(na.r) + 2 * u;
+                    hv[q][0] += r4[0];
+                    hv[q][1] += r4[1];
+                }
+            }
+        }
+    }
+    __device__ void issue() {
+        int nt, nu, units;
+        const int P = pairs(nt, nu, units);
+        load4(0, P, nt, nu, units);
+        if (nu == 1 && na.g) {  // pair q is unit tid + q T: the second pass needs only g
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int u = (int)threadIdx.x + q * T;
+                if (q < P && u < units) {
+                    const float4v* g4 = reinterpret_cast<const float4v*>(na.g) + 2 * u;
+                    gv[q][0] = g4[0];
+                    gv[q][1] = g4[1];
+                }
+            }
+        }
+    }
+    // scales h' of unit u by sc (and g), stores h' (workgroup 0) and
+    // quantizes it into LDS
+    __device__ void finish_unit(int u, float4v x0, float4v x1, bool has_g, float4v g0, float4v g1, float sc,
+                                bool store_h, int4v* lds_q, float* lds_dx) const {
+        if (store_h) {
+            float4v* o4 = reinterpret_cast<float4v*>(na.h_out) + 2 * u;
+            o4[0] = x0;
+            o4[1] = x1;
+        }
+        const float a[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        float v[8];
+        if (has_g) {
+            const float gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = (a[j] * sc) * gw[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = a[j] * sc;
+        }
+        requant_unit(float4v{v[0], v[1], v[2], v[3]}, float4v{v[4], v[5], v[6], v[7]}, u, lds_q, lds_dx);
+    }
+    __device__ void commit(int4v* lds_q, float* lds_dx, float* scratch) {
+        int nt, nu, units;
+        const int P = pairs(nt, nu, units);
+        float ss[MV];
+#pragma unroll
+        for (int mm = 0; mm < MV; ++mm) ss[mm] = 0.0f;
+        for (int p0 = 0; p0 < P; p0 += 4) {
+            if (p0 > 0) load4(p0, P, nt, nu, units);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int p = p0 + q, m = p / nu, i = p - m * nu;
+                const int vt = (int)threadIdx.x + m * T, u = vt + i * nt;
+                if (p < P && vt < nt && u < units) {
+                    const float a[8] = {hv[q][0].x, hv[q][0].y, hv[q][0].z, hv[q][0].w,
+                                        hv[q][1].x, hv[q][1].y, hv[q][1].z, hv[q][1].w};
+#pragma unroll
+                    for (int mm = 0; mm < MV; ++mm) {
+                        if (m == mm) {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) ss[mm] = __builtin_fmaf(a[j], a[j], ss[mm]);
+                        }
+                    }
+                }
+            }
+        }
+        const int lane = (int)threadIdx.x % kWave;
+#pragma unroll
+        for (int mm = 0; mm < MV; ++mm) {
+            const float w = wave_sum(ss[mm]);
+            const int vt = (int)threadIdx.x + mm * T;
+            if (lane == 0 && vt < nt) scratch[vt / kWave] = w;
+        }
+        __syncthreads();
+        float total = 0.0f;
+        for (int w = 0; w < nt / kWave; ++w) total += scratch[w];
+        const float sc = 1.0f / __builtin_sqrtf(total / (float)k + na.eps);
+        const bool store_h = na.h_out != nullptr && blockIdx.x == 0;
+        if (nu == 1) {
+            // one unit per norm thread: pair q of the first pass is unit
+            // tid + q T, still in registers with its g
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int u = (int)threadIdx.x + q * T;
+                if (q < P && u < units)
+                    finish_unit(u, hv[q][0], hv[q][1], na.g != nullptr, gv[q][0], gv[q][1], sc, store_h, lds_q,
+                                lds_dx);
+            }
+        } else {
+            second_pass(units, sc, store_h, lds_q, lds_dx);
+        }
+        // only workgroup 0 stores h': wait for every memory operation here,
+        // so that the row loop starts from the same count on every path and
+        // its waits stay exact (s_waitcnt vmcnt(0), no other counter)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    __device__ void second_pass(int units, float sc, bool store_h, int4v* lds_q, float* lds_dx) const {
+        for (int u = (int)threadIdx.x; u < units; u += T) {
+            const float4v* h4 = reinterpret_cast<const float4v*>(na.h) + 2 * u;
+            float4v x0 = h4[0], x1 = h4[1];
+            if (na.r) {
+                const float4v* r4 = reinterpret_cast<const float4v*>(na.r) + 2 * u;
+                x0 += r4[0];
+                x1 += r4[1];
+            }
+            float4v g0 = {}, g1 = {};
+            if (na.g) {
+                const float4v* g4 = reinterpret_cast<const float4v*>(na.g) + 2 * u;
+                g0 = g4[0];
+                g1 = g4[1];
+            }
+            finish_unit(u, x0, x1, na.g != nullptr, g0, g1, sc, store_h, lds_q, lds_dx);
+        }
+    }
+};
+
 // f32 activation for the dequantizing path: float4 v (values 4v..4v+3, block
 // b = v/8, group g = v%8) -> LDS float4v x[C][8][64] at (c*8+g)*64 + l.
 template <int NR>

@@ -20,6 +20,7 @@
 // thread over its units, a butterfly over the wave, then the wave partials
 // in wave order, so the result does not depend on timing.
 #include "common.hpp"
+#include "gemv_device.hpp"
 #include "internal.hpp"
 
 namespace wsg {
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kNormThreads) void residual_rmsnorm_kernel(
             a[i][0] = x0.x, a[i][1] = x0.y, a[i][2] = x0.z, a[i][3] = x0.w;
             a[i][4] = x1.x, a[i][5] = x1.y, a[i][6] = x1.z, a[i][7] = x1.w;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ss += a[i][j] * a[i][j];
+            for (int j = 0; j < 8; ++j) ss = __builtin_fmaf(a[i][j], a[i][j], ss);
         }
     }
 
@@ -130,14 +131,13 @@ void launch_norm(int threads, hipStream_t s, const float* h, const float* r, con
     hipLaunchKernelGGL(residual_rmsnorm_kernel<NU>, dim3(1), dim3(threads), 0, s, h, r, g, k, eps, h_out, y, q, d);
 }
 
-// Threads and units per thread the kernel uses for a vector of k values.
+// Threads and units per thread the kernel uses for a vector of k values
+// (norm_threads: a GEMV that computes this step in its prologue plays the
+// same threads).
 void norm_shape(int64_t k, int* threads, int* units_per_thread) {
-    const int64_t units = k / 8;
-    int64_t nt = (units + kWave - 1) / kWave * kWave;
-    if (nt > kNormThreads) nt = kNormThreads;
-    if (nt < kWave) nt = kWave;
-    *threads = (int)nt;
-    *units_per_thread = (int)((units + nt - 1) / nt);
+    const int nt = norm_threads((int)k);
+    *threads = nt;
+    *units_per_thread = (int)((k / 8 + nt - 1) / nt);
 }
 
 }  // namespace

@@ -21,6 +21,8 @@ int validate_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void
                      size_t ws_bytes, const void* idx_out);
 int validate_residual_rmsnorm(const float* h, const float* r, const float* g, int64_t k, float eps,
                               const void* h_out, const void* y, const void* y_q8);
+int validate_gemv_q8_rmsnorm(const void* w, int64_t n, int64_t k, const float* h, const float* r, const float* g,
+                             float eps, const void* h_out, const void* y);
 }  // namespace wsg
 
 struct wsg_plan {
@@ -50,6 +52,10 @@ int validate_op(const wsg_op_desc& d) {
             return wsg::validate_residual_rmsnorm(static_cast<const float*>(d.x), static_cast<const float*>(d.r),
                                                   static_cast<const float*>(d.w), d.k, d.eps, d.h_out, d.y,
                                                   d.y_q8);
+        case WSG_OP_GEMV_Q8_0_RMSNORM:
+            return wsg::validate_gemv_q8_rmsnorm(d.w, d.n, d.k, static_cast<const float*>(d.x),
+                                                 static_cast<const float*>(d.r), static_cast<const float*>(d.g),
+                                                 d.eps, d.h_out, d.y);
         default: return WSG_ERR_MODE;
     }
 }
@@ -69,6 +75,10 @@ int enqueue_op(const wsg_op_desc& d, hipStream_t s) {
             return residual_rmsnorm_q8_0(static_cast<const float*>(d.x), static_cast<const float*>(d.r),
                                          static_cast<const float*>(d.w), d.k, d.eps, static_cast<float*>(d.h_out),
                                          static_cast<float*>(d.y), d.y_q8, s);
+        case WSG_OP_GEMV_Q8_0_RMSNORM:
+            return gemv_q8_0_rmsnorm(d.w, d.n, d.k, static_cast<const float*>(d.x), static_cast<const float*>(d.r),
+                                     static_cast<const float*>(d.g), d.eps, static_cast<float*>(d.h_out),
+                                     static_cast<float*>(d.y), s);
         default: return WSG_ERR_MODE;
     }
 }

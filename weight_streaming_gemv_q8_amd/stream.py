@@ -81,11 +81,16 @@ class TokenStream:
             rows of the GEMV before it, are the hidden size.  Empty: every
             layer starts from its own input vector (set_inputs).
     eps:    the RMSNorm epsilon.
+    fused_norm: with norm_before on a Q8_0 chain with int8 activations, each
+            normalized GEMV computes the residual add + RMSNorm itself
+            (gemv_q8_0_rmsnorm) instead of after a separate norm call; the
+            results are the same bit for bit (the f32 normalized vectors
+            are then not written).
     """
 
     def __init__(self, shapes: Sequence[Tuple[int, int, Tuple[int, ...]]], layers: int, wtype: str,
                  deq: int = 0, requant: str = "fused", device: str = "cuda",
-                 norm_before: Sequence[int] = (), eps: float = 1e-6):
+                 norm_before: Sequence[int] = (), eps: float = 1e-6, fused_norm: bool = False):
         if wtype not in ("q8_0", "bf16"):
             raise ValueError("wtype must be q8_0 or bf16")
         if requant not in ("fused", "separate"):
@@ -121,6 +126,9 @@ class TokenStream:
                 s.x_ptr = self.slots[i - 1].y.data_ptr()
         self.norm_before = tuple(sorted(set(int(j) for j in norm_before)))
         self.eps = float(eps)
+        self.fused_norm = bool(fused_norm)
+        if self.fused_norm and (wtype != "q8_0" or deq == 2 or not self.norm_before):
+            raise ValueError("fused_norm needs a Q8_0 chain with int8 activations and norm_before")
         self.norms: List[NormSlot] = []
         self.h0 = None
         self.gains = None
@@ -215,6 +223,9 @@ class TokenStream:
     def _slot_ops(self, s: GemvSlot) -> List[wsg.OpDesc]:
         w = self.weights.data_ptr() + s.w_offset
         pre = []
+        if s.norm is not None and self.fused_norm:
+            n = s.norm
+            return [wsg.op_gemv_q8_0_rmsnorm(w, s.n, s.k, n.h_in, n.r or None, n.g, self.eps, s.y, h_out=n.h_out)]
         if s.norm is not None:
             n = s.norm
             pre = [wsg.op_residual_rmsnorm(n.h_in, n.r or None, n.g, self.hidden, self.eps, h_out=n.h_out,
@@ -255,6 +266,9 @@ class TokenStream:
             elif op.op == wsg.OP_RESIDUAL_RMSNORM:
                 wsg.residual_rmsnorm_q8_0(op.x, op.r, op.w, op.k, op.eps, h_out=op.h_out, y=op.y, y_q8=op.y_q8,
                                           stream=stream)
+            elif op.op == wsg.OP_GEMV_Q8_0_RMSNORM:
+                wsg.gemv_q8_0_rmsnorm(op.w, op.n, op.k, op.x, op.r, op.g, op.eps, op.y, h_out=op.h_out,
+                                      stream=stream)
             else:
                 wsg.gemv_q8_0(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
 
