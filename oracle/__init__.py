@@ -68,6 +68,8 @@ def lib():
         L.orc_argmax_f32.argtypes = [vp, i64]
         L.orc_residual_rmsnorm.restype = None
         L.orc_residual_rmsnorm.argtypes = [vp, vp, vp, i64, ctypes.c_double, vp, vp]
+        L.orc_swiglu.restype = None
+        L.orc_swiglu.argtypes = [vp, vp, i64, vp]
         _lib = L
     return _lib
 
@@ -210,7 +212,42 @@ def residual_rmsnorm(h, r, g, eps: float):
     return h_out, y
 
 
+# --------------------------------------------------------------------- O10
+
+def swiglu(g, u) -> np.ndarray:
+    """SwiGLU epilogue (see oracle.c, O10): silu(g) * u in fp64."""
+    g = _c(g, np.float64)
+    u = _c(u, np.float64)
+    assert g.shape == u.shape and g.ndim == 1
+    y = np.empty(g.size, dtype=np.float64)
+    if g.size:
+        lib().orc_swiglu(g.ctypes.data, u.ctypes.data, g.size, y.ctypes.data)
+    return y
+
+
 # ------------------------------------------------------------ tolerances O7
+
+# |silu'(x)| = |s(x) (1 + x (1 - s(x)))| (s the logistic function) peaks at
+# ~1.0998 near x = 2.4: the bound used below (pinned in the tests).
+SILU_SLOPE_MAX = 1.1
+# fp32 rounding of the epilogue itself: expf (a few ulp), one add, one
+# divide, one multiply; 2^-20 leaves ~8x margin over their sum.
+SWIGLU_REL_TOL = 2.0 ** -20
+
+
+def swiglu_tolerance(g_ref, u_ref, tol_g, tol_u) -> np.ndarray:
+    """Bound on |y - silu(g) u| for y computed in fp32 from g', u' with
+    |g' - g| <= tol_g and |u' - u| <= tol_u:
+      |silu(g)| tol_u + 1.1 tol_g (|u| + tol_u)           (input errors)
+      + 2^-20 (|silu(g)| + 1.1 tol_g)(|u| + tol_u)        (fp32 epilogue)
+      + 1e-30 (|u| + tol_u)                               (exp underflow)."""
+    g = np.asarray(g_ref, np.float64)
+    u = np.abs(np.asarray(u_ref, np.float64))
+    tg = np.asarray(tol_g, np.float64)
+    tu = np.asarray(tol_u, np.float64)
+    s = np.abs(swiglu(g, np.ones_like(g)))
+    return s * tu + SILU_SLOPE_MAX * tg * (u + tu) + SWIGLU_REL_TOL * (s + SILU_SLOPE_MAX * tg) * (u + tu) \
+        + 1e-30 * (u + tu)
 
 Q8_REL_TOL = 1e-4          # |y - y_ref| <= 1e-4 * sum_b |d_w d_x s_b| (and the f32-x analogue)
 BF16_REL_TOL = 2.0 ** -10  # |y - y_ref| <= 2^-10 * sum_i |w_i x_i|

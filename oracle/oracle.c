@@ -355,3 +355,18 @@ void orc_residual_rmsnorm(const float* h, const float* r, const float* g, int64_
     const double s = 1.0 / sqrt(ss / (double)k + eps);
     for (int64_t i = 0; i < k; ++i) y_out[i] = (double)h_out[i] * s * (double)g[i];
 }
+
+/* O10: the SwiGLU epilogue of the gate+up GEMV (GPU Kernel Lab, "What we
+ * built", "Decode integration", "Quantization experiments": a dual gate/up
+ * projection fused with SwiGLU at batch 1).  The pages give no formula; the
+ * reading (listed in the design notes) is the standard gated activation of
+ * the MLP, y_i = silu(g_i) * u_i with silu(x) = x / (1 + exp(-x)), where g
+ * is the gate half and u the up half of the concatenated gate+up output
+ * (gate rows first).  All fp64; exp(-x) overflowing to +inf for very
+ * negative x gives silu(x) = -0, the limit. */
+void orc_swiglu(const double* g, const double* u, int64_t n, double* y) {
+    for (int64_t i = 0; i < n; ++i) {
+        const double x = g[i];
+        y[i] = x / (1.0 + exp(-x)) * u[i];
+    }
+}
