@@ -93,7 +93,7 @@ def read_traffic(kernel_name: str):
 
 # ------------------------------------------------------------ workload
 
-def build_stream(wl, deq: int, requant: str, norm: bool = False, fused_norm: bool = False):
+def build_stream(wl, deq: int, requant: str, norm: bool = False, fused_norm: bool = False, swiglu: bool = False):
     """The workload's token stream with its weights generated on the device.
     norm=True chains the layers through the residual stream: a residual add
     + RMSNorm + re-quantization call before each layer's attention input
@@ -107,7 +107,8 @@ def build_stream(wl, deq: int, requant: str, norm: bool = False, fused_norm: boo
 
     shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
     ts = TokenStream(shapes, wl.layers, wl.wtype, deq=deq, requant=requant,
-                     norm_before=(0, 2) if norm else (), eps=W.RMSNORM_EPS, fused_norm=fused_norm)
+                     norm_before=(0, 2) if norm else (), eps=W.RMSNORM_EPS, fused_norm=fused_norm,
+                     swiglu_at=(2,) if swiglu else ())
     log(f"allocated {ts.weight_bytes_alloc / 1e9:.3f} GB of weights; generating on the device")
     t0 = time.time()
 
@@ -327,6 +328,13 @@ def measure_configs(steps: int, warmup: int) -> list:
                 sec, kernels = time_plan(ts, False, steps, warmup)
                 rec(wl, f"graph + residual/RMSNorm fused into the GEMVs deq{deq}", sec, alg,
                     kernels_per_token=kernels, deq=deq)
+                ts.close()
+                del ts
+                torch.cuda.empty_cache()
+                # down reading the SwiGLU of gate+up (the epilogue fused into that GEMV)
+                ts = build_stream(wl, deq, "fused", swiglu=True)
+                sec, kernels = time_plan(ts, False, steps, warmup)
+                rec(wl, f"graph + SwiGLU epilogue on gate+up deq{deq}", sec, alg, kernels_per_token=kernels, deq=deq)
                 ts.close()
                 del ts
                 torch.cuda.empty_cache()

@@ -168,6 +168,21 @@ int residual_rmsnorm_q8_0(const float* h, const float* r, const float* g, int64_
 int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r, const float* g,
                       float eps, float* h_out, float* y, hipStream_t stream);
 
+/* The gate+up GEMV with its SwiGLU epilogue (GPU Kernel Lab, "What we
+ * built", "Decode integration": the dual gate/up projection fused with
+ * SwiGLU at batch 1):
+ *   g_p = W[p] . x,  u_p = W[n_ff + p] . x,  y[p] = silu(g_p) u_p,
+ *   silu(t) = t / (1 + exp(-t)),  p < n_ff,
+ * for W in the device layout with 2 n_ff rows (the concatenated gate+up
+ * matrix, gate rows first) and int8 activations (act_fmt WSG_ACT_Q8_0 or
+ * WSG_ACT_F32_REQUANT; WSG_ERR_MODE otherwise).  Only the n_ff products are
+ * written.  g_p and u_p are reduced as gemv_q8_0 reduces an unsplit row.
+ * Acceptance: the two GEMV bounds propagated through silu(g) u (slope of
+ * silu <= 1.1) plus 2^-20 relative for the fp32 epilogue.  n_ff >= 1,
+ * 32 <= k <= WSG_MAX_K_Q8ACT, k % 32 == 0 (WSG_ERR_SHAPE). */
+int gemv_q8_0_swiglu(const void* w_packed, int64_t n_ff, int64_t k, const void* x, int act_fmt, float* y,
+                     hipStream_t stream);
+
 /* ------------------------------------------------------------- GEMVs ---
  * y[r] = sum_i W[r,i] x[i], f32 accumulation, r < n.  n == 0 is a no-op;
  * k == 0 writes y = 0.
@@ -237,6 +252,7 @@ enum {
     WSG_OP_RESIDUAL_RMSNORM = 4, /* residual_rmsnorm_q8_0: x = h, r, w = g, k, eps,
                                     h_out, y (f32 y), y_q8 */
     WSG_OP_GEMV_Q8_0_RMSNORM = 5, /* gemv_q8_0_rmsnorm: w, n, k, x = h, r, g, eps, h_out, y */
+    WSG_OP_GEMV_Q8_0_SWIGLU = 6,  /* gemv_q8_0_swiglu: w, n = n_ff, k, x, act_fmt, y */
 };
 
 /* flags: WSG_OP_AFTER_ALL marks an op that depends on every earlier op of

@@ -39,9 +39,10 @@ def asm(tmp_path_factory):
 
 
 def _kernels(text):
-    """name -> assembly of each kernel function."""
+    """name -> assembly of each kernel function (to its end label: a kernel
+    may have more than one s_endpgm)."""
     out = {}
-    for m in re.finditer(r"^(_Z\S+):[^\n]*\n(.*?)s_endpgm", text, re.S | re.M):
+    for m in re.finditer(r"^(_Z\S+):[^\n]*\n(.*?)^\.Lfunc_end", text, re.S | re.M):
         out[m.group(1)] = m.group(2)
     return out
 
@@ -74,9 +75,11 @@ def test_stream_ring_keeps_two_items_in_flight(asm):
         assert _max_wait_before_dot(body) >= 6, name
 
 
-def test_fused_norm_gemv_keeps_two_items_in_flight(asm):
-    # the GEMVs that compute the residual add + RMSNorm in their prologue
-    ks = {n: b for n, b in _kernels(asm["gemv.hip"]).items() if "q8_i8_norm_kernel" in n}
+def test_fused_norm_and_swiglu_gemvs_keep_two_items_in_flight(asm):
+    # the GEMVs that compute the residual add + RMSNorm in their prologue,
+    # and the gate+up GEMV with the SwiGLU epilogue
+    ks = {n: b for n, b in _kernels(asm["gemv.hip"]).items()
+          if "q8_i8_norm_kernel" in n or "q8_i8_swiglu_kernel" in n}
     assert ks
     for name, body in ks.items():
         assert _max_wait_before_dot(body) >= 6, name

@@ -148,6 +148,91 @@ q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
     q8_i8_body<WAVES, S, U, DEBUG, ARGMAX>(W, n, k, y, dots, keys, stage);
 }
 
+// The gate+up GEMV with the SwiGLU epilogue (GPU Kernel Lab, "What we
+// built", "Decode integration": the dual gate/up projection fused with
+// SwiGLU at batch 1): W holds 2 n_ff rows, gate rows first, and
+// y[p] = silu(g_p) u_p with g_p = row p . x and u_p = row n_ff + p . x.
+// Each wave takes one output p per tile and walks the 2C chunks of both
+// rows as one sequence (gate chunks, then up chunks), with one accumulator
+// per row, so each half is reduced exactly as the unsplit kernel reduces
+// that row (per-lane fused multiply-adds in chunk order, then the
+// butterfly) and only the n_ff products are stored.
+template <int WAVES, int ACT>
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+q8_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* __restrict__ xin,
+                    float* __restrict__ y) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int C = (int)chunk_count(k);
+    const int NB = k / kBlock;
+    const int nl = NB - (C - 1) * kChunkBlocks;
+    const int sbl = (int)scale_section_bytes(nl);
+    const int64_t row_bytes = packed_row_bytes(k);
+    int4v* lds_q = reinterpret_cast<int4v*>(smem);
+    float* lds_dx = reinterpret_cast<float*>(smem + (size_t)C * 2 * kWave * 16);
+    float* lds_res = reinterpret_cast<float*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>());
+    const int lane = threadIdx.x % kWave;
+    const Sched sc(2 * C, 1, 1, WAVES, n_ff, (n_ff + WAVES - 1) / WAVES);
+    const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
+    // item m of output p: chunk m of gate row p (m < C) or chunk m - C of up
+    // row n_ff + p; past the schedule the idle region (see q8_load_item)
+    auto load = [&](Q8Regs<1>& r, const ItemCursor& it) {
+        const int p = it.j < sc.tiles_wg ? sc.row(it.j) : sc.n;
+        const int m = sc.chunk(it.m, 0);
+        const bool up = m >= C;
+        const int c = up ? m - C : m;
+        const bool real = p < sc.n && m < 2 * C;
+        const bool last = c == C - 1;
+        const int nbc = last ? nl : kChunkBlocks;
+        const int sb = last ? sbl : 2 * kChunkBlocks;
+        const int l = lane < nbc ? lane : nbc - 1;
+        const int64_t row = real ? (int64_t)p + (up ? n_ff : 0) : 0;
+        const gptr<uint8_t> cp = real ? Wg + row * row_bytes + (int64_t)c * kFullChunkBytes : idle_bytes();
+        r.sc[0] = load_u16<true>(cp + 2 * l);
+        r.a[0] = load16<true>(cp + sb + 16 * l);
+        r.b[0] = load16<true>(cp + sb + 16 * nbc + 16 * l);
+    };
+    float acc_up = 0.0f;
+    // one block per lane, as q8_i8_item: exact int32 dot, then (d_w d_x) s
+    auto compute = [&](const Q8Regs<1>& r, int, int m, float& acc_gate) {
+        const bool up = m >= C;
+        const int c = up ? m - C : m;
+        const int blk = c * kWave + lane;
+        if (blk < NB) {
+            const int4v xa = lds_q[(c * 2 + 0) * kWave + lane];
+            const int4v xb = lds_q[(c * 2 + 1) * kWave + lane];
+            int d = 0;
+            d = __builtin_amdgcn_sdot4(r.a[0].x, xa.x, d, false);
+            d = __builtin_amdgcn_sdot4(r.a[0].y, xa.y, d, false);
+            d = __builtin_amdgcn_sdot4(r.a[0].z, xa.z, d, false);
+            d = __builtin_amdgcn_sdot4(r.a[0].w, xa.w, d, false);
+            d = __builtin_amdgcn_sdot4(r.b[0].x, xb.x, d, false);
+            d = __builtin_amdgcn_sdot4(r.b[0].y, xb.y, d, false);
+            d = __builtin_amdgcn_sdot4(r.b[0].z, xb.z, d, false);
+            d = __builtin_amdgcn_sdot4(r.b[0].w, xb.w, d, false);
+            const float t = half_bits_to_float(r.sc[0]) * lds_dx[blk];
+            if (up) {
+                acc_up = __builtin_fmaf(t, (float)d, acc_up);
+            } else {
+                acc_gate = __builtin_fmaf(t, (float)d, acc_gate);
+            }
+        }
+    };
+    Q8Regs<1> R[kRingSets<1, 1>];
+    StageInput<ACT> stage{xin, k, C, {}};
+    stage.issue();
+    __builtin_amdgcn_sched_barrier(0);
+    ring_prologue(sc, R, load);
+    __builtin_amdgcn_sched_barrier(0);
+    stage.commit(lds_q, lds_dx, lds_res);
+    __syncthreads();
+    ring_loop(sc, R, load, compute, [&](float gate, int, int p, bool valid) {
+        const float upv = wave_sum(acc_up);
+        acc_up = 0.0f;
+        // silu(g) u; exp(-g) overflowing to +inf for very negative g gives -0
+        if (valid && lane == 0) y[p] = gate / (1.0f + expf(-gate)) * upv;
+    });
+}
+
 // The int8 path fed by the residual add + RMSNorm + re-quantization of
 // residual_rmsnorm_q8_0, computed by every workgroup in its prologue
 // (emit_qwen38_generate, "Where the speed comes from", item 3): the same
@@ -598,6 +683,25 @@ int launch_q8_norm(const void* w, int n, int k, const NormArgs& na, float* y, hi
     });
 }
 
+// The gate+up GEMV with the SwiGLU epilogue: the waves the int8 path
+// uses for the whole gate+up matrix, one wave per output.
+int launch_q8_swiglu(const void* w, int n_ff, int k, const void* x, int act_fmt, float* y, hipStream_t stream,
+                     LaunchInfo* info, bool run = true) {
+    const Cfg c = choose_cfg(kPathI8, 2 * (int64_t)n_ff, k);
+    const size_t lds_act = lds_q8act_bytes((int)chunk_count(k));
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    return dispatch_ws(c.waves, 1, [&](auto W, auto) -> int {
+        constexpr int Wv = decltype(W)::value;
+        if (act_fmt == WSG_ACT_Q8_0) {
+            auto kern = q8_i8_swiglu_kernel<Wv, kActQ8>;
+            return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds_act), n_ff, info, 1, run, stream, wp, n_ff, k, x,
+                                        y);
+        }
+        auto kern = q8_i8_swiglu_kernel<Wv, kActRequant>;
+        return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds_act), n_ff, info, 1, run, stream, wp, n_ff, k, x, y);
+    });
+}
+
 template <bool ARGMAX>
 int launch_q8_f32(const void* w, int n, int k, const float* x, float* y, uint64_t* keys, hipStream_t stream,
                   LaunchInfo* info, bool run = true) {
@@ -712,6 +816,12 @@ int validate_gemv_q8_rmsnorm(const void* w, int64_t n, int64_t k, const float* h
     return WSG_OK;
 }
 
+int validate_gemv_q8_swiglu(const void* w, int64_t n_ff, int64_t k, const void* x, int act_fmt, const void* y) {
+    if (act_fmt != WSG_ACT_Q8_0 && act_fmt != WSG_ACT_F32_REQUANT) return WSG_ERR_MODE;
+    if (n_ff < 1 || k < kBlock || 2 * n_ff > kMaxDim) return WSG_ERR_SHAPE;
+    return check_q8_args(w, 2 * n_ff, k, x, act_fmt, y);
+}
+
 int validate_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, const void* ws,
                      size_t ws_bytes, const void* idx_out) {
     if (w_type != WSG_W_BF16 && w_type != WSG_W_Q8_0) return WSG_ERR_MODE;
@@ -761,6 +871,13 @@ int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h
     const int rc = validate_gemv_q8_rmsnorm(w_packed, n, k, h, r, g, eps, h_out, y);
     if (rc != WSG_OK) return rc;
     return launch_q8_norm(w_packed, (int)n, (int)k, NormArgs{h, r, g, h_out, eps}, y, stream, nullptr);
+}
+
+int gemv_q8_0_swiglu(const void* w_packed, int64_t n_ff, int64_t k, const void* x, int act_fmt, float* y,
+                     hipStream_t stream) {
+    const int rc = validate_gemv_q8_swiglu(w_packed, n_ff, k, x, act_fmt, y);
+    if (rc != WSG_OK) return rc;
+    return launch_q8_swiglu(w_packed, (int)n_ff, (int)k, x, act_fmt, y, stream, nullptr);
 }
 
 int gemv_bf16(const uint16_t* w, int64_t n, int64_t k, const float* x, float* y, hipStream_t stream) {

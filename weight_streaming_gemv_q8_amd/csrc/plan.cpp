@@ -23,6 +23,7 @@ int validate_residual_rmsnorm(const float* h, const float* r, const float* g, in
                               const void* h_out, const void* y, const void* y_q8);
 int validate_gemv_q8_rmsnorm(const void* w, int64_t n, int64_t k, const float* h, const float* r, const float* g,
                              float eps, const void* h_out, const void* y);
+int validate_gemv_q8_swiglu(const void* w, int64_t n_ff, int64_t k, const void* x, int act_fmt, const void* y);
 }  // namespace wsg
 
 struct wsg_plan {
@@ -56,6 +57,7 @@ int validate_op(const wsg_op_desc& d) {
             return wsg::validate_gemv_q8_rmsnorm(d.w, d.n, d.k, static_cast<const float*>(d.x),
                                                  static_cast<const float*>(d.r), static_cast<const float*>(d.g),
                                                  d.eps, d.h_out, d.y);
+        case WSG_OP_GEMV_Q8_0_SWIGLU: return wsg::validate_gemv_q8_swiglu(d.w, d.n, d.k, d.x, d.act_fmt, d.y);
         default: return WSG_ERR_MODE;
     }
 }
@@ -79,6 +81,8 @@ int enqueue_op(const wsg_op_desc& d, hipStream_t s) {
             return gemv_q8_0_rmsnorm(d.w, d.n, d.k, static_cast<const float*>(d.x), static_cast<const float*>(d.r),
                                      static_cast<const float*>(d.g), d.eps, static_cast<float*>(d.h_out),
                                      static_cast<float*>(d.y), s);
+        case WSG_OP_GEMV_Q8_0_SWIGLU:
+            return gemv_q8_0_swiglu(d.w, d.n, d.k, d.x, d.act_fmt, static_cast<float*>(d.y), s);
         default: return WSG_ERR_MODE;
     }
 }

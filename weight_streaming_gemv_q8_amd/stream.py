@@ -81,6 +81,11 @@ class TokenStream:
             rows of the GEMV before it, are the hidden size.  Empty: every
             layer starts from its own input vector (set_inputs).
     eps:    the RMSNorm epsilon.
+    swiglu_at: indices of the GEMVs of a layer whose output is the SwiGLU
+            of their two halves (the gate+up projection: rows 0 .. n/2 - 1
+            are the gate, the rest the up projection; gemv_q8_0_swiglu),
+            so the next GEMV reads n/2 products.  Q8_0 chains with int8
+            activations; not with fused_norm.
     fused_norm: with norm_before on a Q8_0 chain with int8 activations, each
             normalized GEMV computes the residual add + RMSNorm itself
             (gemv_q8_0_rmsnorm) instead of after a separate norm call; the
@@ -90,7 +95,8 @@ class TokenStream:
 
     def __init__(self, shapes: Sequence[Tuple[int, int, Tuple[int, ...]]], layers: int, wtype: str,
                  deq: int = 0, requant: str = "fused", device: str = "cuda",
-                 norm_before: Sequence[int] = (), eps: float = 1e-6, fused_norm: bool = False):
+                 norm_before: Sequence[int] = (), eps: float = 1e-6, fused_norm: bool = False,
+                 swiglu_at: Sequence[int] = ()):
         if wtype not in ("q8_0", "bf16"):
             raise ValueError("wtype must be q8_0 or bf16")
         if requant not in ("fused", "separate"):
@@ -101,9 +107,15 @@ class TokenStream:
         self.deq = deq
         self.requant = requant
         self.device = device
+        self.swiglu_at = tuple(sorted(set(int(j) for j in swiglu_at)))
+        for j in self.swiglu_at:
+            if not 0 <= j < len(self.shapes) or self.shapes[j][0] % 2:
+                raise ValueError("a SwiGLU GEMV needs an even number of rows (gate and up halves)")
+            if wtype != "q8_0" or deq == 2 or fused_norm:
+                raise ValueError("the SwiGLU epilogue runs on Q8_0 chains with int8 activations, without fused_norm")
         for j in range(1, len(self.shapes)):
-            if self.shapes[j][1] > self.shapes[j - 1][0]:
-                raise ValueError("a GEMV's k exceeds the previous GEMV's rows")
+            if self.shapes[j][1] > self.out_len(j - 1):
+                raise ValueError("a GEMV's k exceeds the previous GEMV's outputs")
 
         self.slots: List[GemvSlot] = []
         off = 0
@@ -117,7 +129,7 @@ class TokenStream:
         k0 = self.shapes[0][1]
         self.inputs = torch.empty((layers, k0), dtype=torch.float32, device=device)
         for s in self.slots:
-            s.y = torch.empty(s.n, dtype=torch.float32, device=device)
+            s.y = torch.empty(self.out_len(s.index), dtype=torch.float32, device=device)
         # chain the inputs
         for i, s in enumerate(self.slots):
             if s.index == 0:
@@ -169,6 +181,11 @@ class TokenStream:
             s.norm = n
             s.x_ptr = n.y.data_ptr()
             self.norms.append(n)
+
+    def out_len(self, j: int) -> int:
+        """Outputs of GEMV j of a layer: its rows, or half of them with SwiGLU."""
+        n = self.shapes[j][0]
+        return n // 2 if j in self.swiglu_at else n
 
     # ------------------------------------------------------------ sizes
     def algorithmic_weight_bytes(self) -> int:
@@ -222,6 +239,17 @@ class TokenStream:
     # ------------------------------------------------------------ calls
     def _slot_ops(self, s: GemvSlot) -> List[wsg.OpDesc]:
         w = self.weights.data_ptr() + s.w_offset
+        if s.index in self.swiglu_at:
+            nff = s.n // 2
+            if s.norm is not None:
+                n = s.norm
+                return [wsg.op_residual_rmsnorm(n.h_in, n.r or None, n.g, self.hidden, self.eps, h_out=n.h_out,
+                                                y=n.y, y_q8=n.yq),
+                        wsg.op_gemv_q8_0_swiglu(w, nff, s.k, n.yq, wsg.ACT_Q8_0, s.y)]
+            if self.act_fmt() == wsg.ACT_Q8_0:
+                return [wsg.op_quantize_act(s.x_ptr, s.k, s.xq_ptr),
+                        wsg.op_gemv_q8_0_swiglu(w, nff, s.k, s.xq_ptr, wsg.ACT_Q8_0, s.y)]
+            return [wsg.op_gemv_q8_0_swiglu(w, nff, s.k, s.x_ptr, self.act_fmt(), s.y)]
         pre = []
         if s.norm is not None and self.fused_norm:
             n = s.norm
@@ -266,6 +294,8 @@ class TokenStream:
             elif op.op == wsg.OP_RESIDUAL_RMSNORM:
                 wsg.residual_rmsnorm_q8_0(op.x, op.r, op.w, op.k, op.eps, h_out=op.h_out, y=op.y, y_q8=op.y_q8,
                                           stream=stream)
+            elif op.op == wsg.OP_GEMV_Q8_0_SWIGLU:
+                wsg.gemv_q8_0_swiglu(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
             elif op.op == wsg.OP_GEMV_Q8_0_RMSNORM:
                 wsg.gemv_q8_0_rmsnorm(op.w, op.n, op.k, op.x, op.r, op.g, op.eps, op.y, h_out=op.h_out,
                                       stream=stream)
