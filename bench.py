@@ -338,7 +338,56 @@ def measure_configs(steps: int, warmup: int) -> list:
                 ts.close()
                 del ts
                 torch.cuda.empty_cache()
+    # a whole decode step: embedding -> layers -> LM head + argmax -> advance
+    for wl in (W.QWEN3_8B_Q8, W.DENSE27B_Q8):
+        ds = build_decode(wl)
+        alg = ds.chain.algorithmic_weight_bytes() + ds.vocab * (ds.hidden // 32) * 34
+        ds.capture()
+        for _ in range(warmup):
+            ds.launch()
+        sec = _time_calls(lambda i: ds.launch(), steps, 0)
+        rec(wl, "decode step graph (embedding, norms, SwiGLU, LM head + argmax, token advance), vocab 151936",
+            sec, alg, kernels_per_token=ds.plan.kernel_count, deq=0)
+        ds.close()
+        del ds
+        torch.cuda.empty_cache()
     return out
+
+
+def build_decode(wl, vocab: int = 151936):
+    """A whole decode step on the workload's layer shapes (DecodeStep):
+    embedding gather -> the layers with the residual stream (norms fused
+    into the attention-input GEMVs, SwiGLU on gate+up) -> final norm ->
+    LM head + argmax -> token/position advance, weights generated on the
+    device."""
+    import numpy as np
+    import torch
+
+    import synth
+    from synth import workloads as W
+    from weight_streaming_gemv_q8_amd.stream import DecodeStep
+
+    shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
+    ds = DecodeStep(shapes, wl.layers, vocab, capacity=4096, eps=W.RMSNORM_EPS)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def fill(layer, m, part, rows, staging):
+        synth.dev_normal_f32(staging.data_ptr(), wl.seed, W.weight_tensor_id(layer, m, part),
+                             rows * wl.matrices[m].k, W.WEIGHT_SIGMA, stream=stream)
+
+    ds.chain.fill_weights(fill)
+    h = ds.hidden
+    ds.fill_table(ds.embedding, lambda r0, st: synth.dev_normal_f32(st.data_ptr(), wl.seed, W.EMBEDDING_TENSOR_ID,
+                                                                     st.numel(), 1.0, first=r0 * h, stream=stream))
+    ds.fill_table(ds.lm_head, lambda r0, st: synth.dev_normal_f32(st.data_ptr(), wl.seed, W.LM_HEAD_TENSOR_ID,
+                                                                   st.numel(), W.WEIGHT_SIGMA, first=r0 * h,
+                                                                   stream=stream))
+    gains = np.stack([np.float32(1.0) + synth.normal_f32(wl.seed, W.gain_tensor_id(i), h, W.GAIN_SIGMA)
+                      for i in range(len(ds.chain.norms))]).astype(np.float32)
+    ds.chain.gains.copy_(torch.from_numpy(gains))
+    ds.reset(1)
+    torch.cuda.synchronize()
+    return ds
 
 
 def read_ceiling(ts, reps: int = 3) -> float:

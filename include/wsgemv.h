@@ -183,6 +183,25 @@ int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h
 int gemv_q8_0_swiglu(const void* w_packed, int64_t n_ff, int64_t k, const void* x, int act_fmt, float* y,
                      hipStream_t stream);
 
+/* ------------------------------------------------ closing the decode loop
+ * (GPU Kernel Lab, "Decode integration": fixed token/position buffers and
+ * the LM-head GEMV + argmax + token/position update under one graph replay;
+ * emit_qwen38_generate, "Where the speed comes from", item 2: token and
+ * position advanced on the device, no host round trip per replay.)
+ *
+ * embed_gather: out[i] = row *token of the embedding table, as f32, i <
+ *   hidden.  table: w_type WSG_W_Q8_0 (device layout, vocab rows, hidden %
+ *   32 == 0; d * q is exact in f32) or WSG_W_BF16 (row-major vocab x hidden).
+ *   token is read on the device when the kernel runs (e.g. the idx_out of
+ *   lm_head_argmax); a token outside [0, vocab) gives a zero row.  Errors:
+ *   vocab or hidden < 1 (WSG_ERR_SHAPE), bad w_type (WSG_ERR_MODE), null
+ *   pointers, table not 16-byte or token/out not 4-byte aligned.
+ * token_advance: history[*pos] = *token if 0 <= *pos < capacity, then
+ *   *pos += 1 (one thread; the position keeps counting past capacity). */
+int embed_gather(const void* table, int w_type, int64_t vocab, int64_t hidden, const int32_t* token, float* out,
+                 hipStream_t stream);
+int token_advance(const int32_t* token, int32_t* history, int64_t capacity, int32_t* pos, hipStream_t stream);
+
 /* ------------------------------------------------------------- GEMVs ---
  * y[r] = sum_i W[r,i] x[i], f32 accumulation, r < n.  n == 0 is a no-op;
  * k == 0 writes y = 0.
@@ -253,6 +272,8 @@ enum {
                                     h_out, y (f32 y), y_q8 */
     WSG_OP_GEMV_Q8_0_RMSNORM = 5, /* gemv_q8_0_rmsnorm: w, n, k, x = h, r, g, eps, h_out, y */
     WSG_OP_GEMV_Q8_0_SWIGLU = 6,  /* gemv_q8_0_swiglu: w, n = n_ff, k, x, act_fmt, y */
+    WSG_OP_EMBED_GATHER = 7,      /* embed_gather: w = table, w_type, n = vocab, k = hidden, x = token, y */
+    WSG_OP_TOKEN_ADVANCE = 8,     /* token_advance: x = token, idx_out = history, n = capacity, ws = pos */
 };
 
 /* flags: WSG_OP_AFTER_ALL marks an op that depends on every earlier op of

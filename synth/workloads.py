@@ -88,6 +88,9 @@ def activation_tensor_id(layer: int) -> int:
 GAIN_SIGMA = 0.1
 RMSNORM_EPS = 1e-6
 RESIDUAL_TENSOR_ID = 2_000_000
+# embedding table and LM head of a whole decode step
+EMBEDDING_TENSOR_ID = 3_000_000
+LM_HEAD_TENSOR_ID = 3_000_001
 
 
 def gain_tensor_id(i: int) -> int:

@@ -20,7 +20,7 @@ import pytest
 
 from weight_streaming_gemv_q8_amd import build as libbuild
 
-SOURCES = ["stream.hip", "gemv.hip", "norm.hip"]
+SOURCES = ["stream.hip", "gemv.hip", "norm.hip", "decode.hip"]
 
 
 @pytest.fixture(scope="module")

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libwsgemv.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "quant.hip", "norm.hip", "gemv.hip", "stream.hip", "probe.hip", "plan.cpp"]
+SOURCES = ["api.cpp", "quant.hip", "norm.hip", "gemv.hip", "stream.hip", "decode.hip", "probe.hip", "plan.cpp"]
 
 HIP_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17",

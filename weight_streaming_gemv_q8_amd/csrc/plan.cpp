@@ -24,6 +24,9 @@ int validate_residual_rmsnorm(const float* h, const float* r, const float* g, in
 int validate_gemv_q8_rmsnorm(const void* w, int64_t n, int64_t k, const float* h, const float* r, const float* g,
                              float eps, const void* h_out, const void* y);
 int validate_gemv_q8_swiglu(const void* w, int64_t n_ff, int64_t k, const void* x, int act_fmt, const void* y);
+int validate_embed_gather(const void* table, int w_type, int64_t vocab, int64_t hidden, const int32_t* token,
+                          const float* out);
+int validate_token_advance(const int32_t* token, const int32_t* history, int64_t capacity, const int32_t* pos);
 }  // namespace wsg
 
 struct wsg_plan {
@@ -58,6 +61,12 @@ int validate_op(const wsg_op_desc& d) {
                                                  static_cast<const float*>(d.r), static_cast<const float*>(d.g),
                                                  d.eps, d.h_out, d.y);
         case WSG_OP_GEMV_Q8_0_SWIGLU: return wsg::validate_gemv_q8_swiglu(d.w, d.n, d.k, d.x, d.act_fmt, d.y);
+        case WSG_OP_EMBED_GATHER:
+            return wsg::validate_embed_gather(d.w, d.w_type, d.n, d.k, static_cast<const int32_t*>(d.x),
+                                              static_cast<const float*>(d.y));
+        case WSG_OP_TOKEN_ADVANCE:
+            return wsg::validate_token_advance(static_cast<const int32_t*>(d.x), d.idx_out, d.n,
+                                               static_cast<const int32_t*>(d.ws));
         default: return WSG_ERR_MODE;
     }
 }
@@ -83,6 +92,11 @@ int enqueue_op(const wsg_op_desc& d, hipStream_t s) {
                                      static_cast<float*>(d.y), s);
         case WSG_OP_GEMV_Q8_0_SWIGLU:
             return gemv_q8_0_swiglu(d.w, d.n, d.k, d.x, d.act_fmt, static_cast<float*>(d.y), s);
+        case WSG_OP_EMBED_GATHER:
+            return embed_gather(d.w, d.w_type, d.n, d.k, static_cast<const int32_t*>(d.x), static_cast<float*>(d.y),
+                                s);
+        case WSG_OP_TOKEN_ADVANCE:
+            return token_advance(static_cast<const int32_t*>(d.x), d.idx_out, d.n, static_cast<int32_t*>(d.ws), s);
         default: return WSG_ERR_MODE;
     }
 }

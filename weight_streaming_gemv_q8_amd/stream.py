@@ -90,7 +90,8 @@ class TokenStream:
             normalized GEMV computes the residual add + RMSNorm itself
             (gemv_q8_0_rmsnorm) instead of after a separate norm call; the
             results are the same bit for bit (the f32 normalized vectors
-            are then not written).
+            are then not written).  A normalized SwiGLU GEMV keeps its
+            separate norm call.
     """
 
     def __init__(self, shapes: Sequence[Tuple[int, int, Tuple[int, ...]]], layers: int, wtype: str,
@@ -111,8 +112,8 @@ class TokenStream:
         for j in self.swiglu_at:
             if not 0 <= j < len(self.shapes) or self.shapes[j][0] % 2:
                 raise ValueError("a SwiGLU GEMV needs an even number of rows (gate and up halves)")
-            if wtype != "q8_0" or deq == 2 or fused_norm:
-                raise ValueError("the SwiGLU epilogue runs on Q8_0 chains with int8 activations, without fused_norm")
+            if wtype != "q8_0" or deq == 2:
+                raise ValueError("the SwiGLU epilogue runs on Q8_0 chains with int8 activations")
         for j in range(1, len(self.shapes)):
             if self.shapes[j][1] > self.out_len(j - 1):
                 raise ValueError("a GEMV's k exceeds the previous GEMV's outputs")
@@ -331,3 +332,105 @@ class TokenStream:
         if self.plan is not None:
             self.plan.destroy()
             self.plan = None
+
+
+class DecodeStep:
+    """One whole batch-1 decode step on the device, captured as one graph
+    (GPU Kernel Lab, "Decode integration": fixed token/position buffers,
+    ..., the LM-head GEMV + argmax + token/position update, fixed-address
+    graph replay; emit_qwen38_generate, "Where the speed comes from",
+    item 2: the sampled token and the position advance on the device, so no
+    replay needs a host round trip):
+
+      embed_gather(token) -> residual stream h0
+      -> the layer chain (residual add + RMSNorm before the attention and
+         MLP inputs, fused into the attention-input GEMV; SwiGLU on gate+up)
+      -> residual add + final RMSNorm -> LM-head GEMV + argmax -> token
+      -> token_advance(token, history, pos)
+
+    Each replay decodes one token; history holds the tokens decoded so far.
+    Attention and the other non-GEMV operators are not part of this path:
+    the layer chain is the GEMV stream (q/k/v -> o_proj reads the first
+    rows of the qkv output)."""
+
+    def __init__(self, shapes, layers: int, vocab: int, capacity: int = 1024, device: str = "cuda",
+                 eps: float = 1e-6):
+        self.chain = TokenStream(shapes, layers, "q8_0", deq=0, device=device, norm_before=(0, 2), eps=eps,
+                                 fused_norm=True, swiglu_at=(2,))
+        self.hidden = self.chain.hidden
+        self.vocab = int(vocab)
+        self.capacity = int(capacity)
+        self.eps = float(eps)
+        rb = wsg.q8_0_packed_bytes(self.vocab, self.hidden)
+        self.embedding = torch.empty(rb, dtype=torch.uint8, device=device)
+        self.lm_head = torch.empty(rb, dtype=torch.uint8, device=device)
+        self.final_gain = torch.ones(self.hidden, dtype=torch.float32, device=device)
+        self.final_h = torch.empty(self.hidden, dtype=torch.float32, device=device)
+        self.final_y = torch.empty(self.hidden, dtype=torch.float32, device=device)
+        self.final_q8 = torch.empty(_align(wsg.act_q8_0_bytes(self.hidden)), dtype=torch.uint8, device=device)
+        self.logits = torch.empty(self.vocab, dtype=torch.float32, device=device)
+        self.ws = torch.empty(wsg.argmax_ws_bytes(), dtype=torch.uint8, device=device)
+        self.token = torch.zeros(1, dtype=torch.int32, device=device)
+        self.pos = torch.zeros(1, dtype=torch.int32, device=device)
+        self.history = torch.full((max(self.capacity, 1),), -1, dtype=torch.int32, device=device)
+        self.plan = None
+
+    def fill_table(self, table: torch.Tensor, fill_rows: Callable[[int, torch.Tensor], None],
+                   rows_per_call: int = 8192) -> None:
+        """Quantize a vocab x hidden table into `table` (embedding or LM
+        head): fill_rows(first_row, staging f32 [rows, hidden])."""
+        staging = torch.empty((rows_per_call, self.hidden), dtype=torch.float32, device=table.device)
+        row_bytes = wsg.q8_0_row_bytes(self.hidden)
+        for r0 in range(0, self.vocab, rows_per_call):
+            rows = min(rows_per_call, self.vocab - r0)
+            fill_rows(r0, staging[:rows])
+            wsg.quantize_q8_0_weights(staging[:rows], rows, self.hidden, table[r0 * row_bytes:])
+        torch.cuda.synchronize()
+
+    def reset(self, first_token: int) -> None:
+        """Start a sequence: the current token, an empty history, position 0."""
+        self.token.fill_(int(first_token))
+        self.pos.zero_()
+        self.history.fill_(-1)
+
+    def ops(self) -> List[wsg.OpDesc]:
+        chain = self.chain
+        last = chain.slots[-1]
+        h_last = chain.norms[-1].h_out
+        return ([wsg.op_embed_gather(self.embedding, wsg.W_Q8_0, self.vocab, self.hidden, self.token, chain.h0)]
+                + chain.ops()
+                + [wsg.op_residual_rmsnorm(h_last, last.y, self.final_gain, self.hidden, self.eps,
+                                           h_out=self.final_h, y=self.final_y, y_q8=self.final_q8),
+                   wsg.op_lm_head_argmax(self.lm_head, wsg.W_Q8_0, self.vocab, self.hidden, self.final_q8,
+                                         wsg.ACT_Q8_0, self.ws, self.ws.numel(), self.token,
+                                         debug_logits=self.logits),
+                   wsg.op_token_advance(self.token, self.history, self.capacity, self.pos)])
+
+    def run_eager(self, stream=None) -> None:
+        """One step through the same calls, one at a time."""
+        wsg.embed_gather(self.embedding, wsg.W_Q8_0, self.vocab, self.hidden, self.token, self.chain.h0,
+                         stream=stream)
+        self.chain.run_eager(stream)
+        last = self.chain.slots[-1]
+        wsg.residual_rmsnorm_q8_0(self.chain.norms[-1].h_out, last.y, self.final_gain, self.hidden, self.eps,
+                                  h_out=self.final_h, y=self.final_y, y_q8=self.final_q8, stream=stream)
+        wsg.lm_head_argmax(self.lm_head, wsg.W_Q8_0, self.vocab, self.hidden, self.final_q8, wsg.ACT_Q8_0,
+                           self.ws, self.ws.numel(), self.token, self.logits, stream=stream)
+        wsg.token_advance(self.token, self.history, self.capacity, self.pos, stream=stream)
+
+    def capture(self, stream=None) -> wsg.Plan:
+        if self.plan is not None:
+            self.plan.destroy()
+        self.plan = wsg.Plan(self.ops(), stream=stream)
+        return self.plan
+
+    def launch(self, stream=None) -> None:
+        if self.plan is None:
+            self.capture(stream)
+        self.plan.launch(stream)
+
+    def close(self) -> None:
+        if self.plan is not None:
+            self.plan.destroy()
+            self.plan = None
+        self.chain.close()
