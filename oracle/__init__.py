@@ -68,6 +68,8 @@ def lib():
         L.orc_argmax_f32.argtypes = [vp, i64]
         L.orc_residual_rmsnorm.restype = None
         L.orc_residual_rmsnorm.argtypes = [vp, vp, vp, i64, ctypes.c_double, vp, vp]
+        L.orc_quantize_q4_0.restype = ctypes.c_int
+        L.orc_quantize_q4_0.argtypes = [vp, i64, i64, vp, vp]
         L.orc_swiglu.restype = None
         L.orc_swiglu.argtypes = [vp, vp, i64, vp]
         _lib = L
@@ -117,6 +119,20 @@ def quantize_q8_0(x: np.ndarray):
     rc = lib().orc_quantize_q8_0(x.ctypes.data, rows, k, d.ctypes.data, q.ctypes.data)
     if rc != 0:
         raise ValueError(f"orc_quantize_q8_0 failed ({rc})")
+    return d, q
+
+
+def quantize_q4_0(x: np.ndarray):
+    """4-bit blocks (O11): x float32[..., k] -> (d fp16 bits [..., k/32], q int8 in [-7, 7] [..., k]).
+    The GEMV over these codes is gemv_q8_act_q8 (the same block-dot form)."""
+    x = _c(x, np.float32)
+    k = x.shape[-1]
+    rows = int(x.size // k) if k else 0
+    d = np.empty(x.shape[:-1] + (k // 32,), dtype=np.uint16)
+    q = np.empty(x.shape, dtype=np.int8)
+    rc = lib().orc_quantize_q4_0(x.ctypes.data, rows, k, d.ctypes.data, q.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"orc_quantize_q4_0 failed ({rc})")
     return d, q
 
 

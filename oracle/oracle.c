@@ -370,3 +370,41 @@ void orc_swiglu(const double* g, const double* u, int64_t n, double* y) {
         y[i] = x / (1.0 + exp(-x)) * u[i];
     }
 }
+
+/* O11: 4-bit weight blocks for the W4 GEMV (qwen3-8b-rtx4080-cutedsl,
+ * "W4A16 dequant-fused GEMM": group-wise 4-bit weights at ~4.6 GB for the
+ * 8B model; GPU Kernel Lab, "Quantization experiments").  The pages give
+ * no 4-bit rule; the reading (listed in the design notes) is the Q8_0 rule
+ * with 7 in place of 127: per block of 32, d = max|x| / 7 in IEEE fp32,
+ * d16 = fp16(d), q = the fp32 quotient x / d16 rounded half away from zero,
+ * clamped to [-7, 7]; an all-zero (or underflowing) block has d16 = +0 and
+ * q = 0.  The stored block is 18 bytes (fp16 d and 16 bytes of 4-bit codes
+ * q + 8), so y = sum_b d_w d_x s with s = sum_i q_w q_x is the int8 GEMV of
+ * O3 with these codes. */
+int orc_quantize_q4_0(const float* x, int64_t rows, int64_t k, uint16_t* d, int8_t* q) {
+    if (rows < 0 || k < 0 || k % 32 != 0) return -1;
+    const int64_t nb = k / 32;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float* xb = x + r * k + b * 32;
+            int8_t* qb = q + r * k + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                if (!isfinite(xb[i])) return -2;
+                const float a = fabsf(xb[i]);
+                if (a > amax) amax = a;
+            }
+            const uint16_t d16 = orc_f32_to_f16(amax / 7.0f);
+            if ((d16 & 0x7C00u) == 0x7C00u) return -2;
+            const float df = (float)orc_f16_to_f64(d16);
+            d[r * nb + b] = df == 0.0f ? 0 : d16;
+            for (int i = 0; i < 32; ++i) {
+                float c = df == 0.0f ? 0.0f : roundf(xb[i] / df);
+                if (c > 7.0f) c = 7.0f;
+                if (c < -7.0f) c = -7.0f;
+                qb[i] = (int8_t)c;
+            }
+        }
+    }
+    return 0;
+}
