@@ -168,6 +168,26 @@ int residual_rmsnorm_q8_0(const float* h, const float* r, const float* g, int64_
 int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r, const float* g,
                       float eps, float* h_out, float* y, hipStream_t stream);
 
+/* ---------------------------------------------------------- W4 weights --
+ * 4-bit blocks (qwen3-8b-rtx4080-cutedsl, "W4A16 dequant-fused GEMM"; GPU
+ * Kernel Lab, "Quantization experiments"): per 32 weights an fp16 scale
+ * d = fp16(max|w| / 7) and codes q = clamp(round(w / d), -7, 7) (the fp32
+ * quotient by the stored scale, half away from zero), stored as q + 8 in
+ * 4 bits: 18 bytes per block, 0.5625 bytes per weight.  Device layout: rows
+ * of q4_0_row_bytes(k) bytes; per 2048-weight chunk [64 fp16 scales][64 x
+ * 16 code bytes], a block's byte j holding code j (low nibble) and code
+ * j + 16 (high nibble); the last chunk's scale section is padded to 16
+ * bytes with zeros.  q4_0_*_bytes return -1 on a bad shape.
+ * gemv_q4_0: y = W x with int8 activations (act_fmt WSG_ACT_Q8_0 or
+ *   WSG_ACT_F32_REQUANT; WSG_ERR_MODE otherwise); the exact int32 block dot
+ *   s = sum q_w q_x, then y = sum_b d_w d_x s in f32.  Acceptance: as
+ *   gemv_q8_0's int8 path.  n >= 1, 32 <= k <= WSG_MAX_K_Q8ACT, k % 32 == 0
+ *   (WSG_ERR_SHAPE). */
+int64_t q4_0_row_bytes(int64_t k);
+int64_t q4_0_packed_bytes(int64_t n, int64_t k);
+int quantize_q4_0_weights(const float* w, int64_t n, int64_t k, void* w_packed, hipStream_t stream);
+int gemv_q4_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act_fmt, float* y, hipStream_t stream);
+
 /* The gate+up GEMV with its SwiGLU epilogue (GPU Kernel Lab, "What we
  * built", "Decode integration": the dual gate/up projection fused with
  * SwiGLU at batch 1):
@@ -274,6 +294,7 @@ enum {
     WSG_OP_GEMV_Q8_0_SWIGLU = 6,  /* gemv_q8_0_swiglu: w, n = n_ff, k, x, act_fmt, y */
     WSG_OP_EMBED_GATHER = 7,      /* embed_gather: w = table, w_type, n = vocab, k = hidden, x = token, y */
     WSG_OP_TOKEN_ADVANCE = 8,     /* token_advance: x = token, idx_out = history, n = capacity, ws = pos */
+    WSG_OP_GEMV_Q4_0 = 9,         /* gemv_q4_0: w, n, k, x, act_fmt, y */
 };
 
 /* flags: WSG_OP_AFTER_ALL marks an op that depends on every earlier op of

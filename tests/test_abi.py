@@ -130,7 +130,7 @@ def test_plan_rejects_bad_descriptors_before_capture(L):
     with pytest.raises(wsg.WsgError) as e:
         wsg.Plan(ops, stream=0)
     assert e.value.status == wsg.ERR_SHAPE
-    ops = [wsg.OpDesc(op=9)]
+    ops = [wsg.OpDesc(op=wsg.OP_GEMV_Q4_0 + 1)]
     with pytest.raises(wsg.WsgError) as e:
         wsg.Plan(ops, stream=0)
     assert e.value.status == wsg.ERR_MODE

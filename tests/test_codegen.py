@@ -85,6 +85,14 @@ def test_fused_norm_and_swiglu_gemvs_keep_two_items_in_flight(asm):
         assert _max_wait_before_dot(body) >= 6, name
 
 
+def test_w4_ring_keeps_two_items_in_flight(asm):
+    # 4-bit items are two loads (codes and scale): two in flight = 4
+    ks = {n: b for n, b in _kernels(asm["gemv.hip"]).items() if "q4_i8_kernel" in n}
+    assert ks
+    for name, body in ks.items():
+        assert _max_wait_before_dot(body) >= 4, name
+
+
 def test_eager_int8_ring_keeps_two_items_in_flight(asm):
     # one-chunk items (U = 1), int8 activations and the requantizing staging
     ks = {n: b for n, b in _kernels(asm["gemv.hip"]).items()

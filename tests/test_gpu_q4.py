@@ -1,0 +1,166 @@
+"""The W4 (4-bit) weight path: quantize_q4_0_weights and gemv_q4_0
+(qwen3-8b-rtx4080-cutedsl, "W4A16 dequant-fused GEMM"; GPU Kernel Lab,
+"Quantization experiments"; the format is reading R19).
+
+* the device layout decodes to the oracle's scales and codes, bit for bit,
+  and the scale sections' padding is zero, on ragged and full chunks;
+* the GEMV matches the oracle (the int8 block-dot form over the 4-bit
+  codes) on every row within the int8 path's bound, for both int8
+  activation formats, shapes spanning several chunks and ragged tails,
+  one-block and one-row cases, and 4-, 8- and 16-wave workgroups; large
+  shapes on sampled rows;
+* a 2-layer 27B-shaped 4-bit chain replays bit-identically to its eager
+  calls and matches the oracle link by link;
+* bad arguments are rejected."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import assert_within, dev, empty_u8, host
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _row_bytes(k):
+    nb = k // 32
+    c = (nb + 63) // 64
+    nl = nb - (c - 1) * 64
+    return (c - 1) * 1152 + ((2 * nl + 15) // 16) * 16 + 16 * nl
+
+
+def _decode(buf, n, k):
+    """(d fp16 bits [n, k/32], q int8 [n, k], padding bytes) of the 4-bit device layout."""
+    rb = _row_bytes(k)
+    rows = np.asarray(buf, np.uint8)[: n * rb].reshape(n, rb)
+    nb = k // 32
+    c_count = (nb + 63) // 64
+    d = np.empty((n, nb), np.uint16)
+    q = np.empty((n, nb, 32), np.int8)
+    pads = []
+    for c in range(c_count):
+        nbc = min(64, nb - 64 * c)
+        sb = ((2 * nbc + 15) // 16) * 16
+        base = c * 1152
+        d[:, 64 * c:64 * c + nbc] = rows[:, base:base + 2 * nbc].copy().view("<u2")
+        pads.append(rows[:, base + 2 * nbc:base + sb])
+        codes = rows[:, base + sb:base + sb + 16 * nbc].reshape(n, nbc, 16)
+        q[:, 64 * c:64 * c + nbc, :16] = (codes & 0xF).astype(np.int8) - 8
+        q[:, 64 * c:64 * c + nbc, 16:] = (codes >> 4).astype(np.int8) - 8
+    return d, q.reshape(n, k), np.concatenate([p.reshape(n, -1) for p in pads], axis=1)
+
+
+@pytest.mark.parametrize("n,k", [(1, 32), (3, 96), (17, 2080), (5, 4096), (2, 17408)])
+def test_quantize_q4_weights_bitexact(gpu_lib, n, k):
+    wsg = gpu_lib
+    assert wsg.q4_0_row_bytes(k) == _row_bytes(k) and wsg.q4_0_packed_bytes(n, k) == n * _row_bytes(k)
+    rng = np.random.default_rng(n * 7 + k)
+    w = (rng.normal(0, 0.02, (n, k)) * np.exp(rng.normal(0, 1, (n, 1)))).astype(np.float32)
+    w[0, :32] = 0.0  # a zero block
+    packed = empty_u8(wsg.q4_0_packed_bytes(n, k))
+    packed.fill_(0xAB)
+    wsg.quantize_q4_0_weights(dev(w), n, k, packed)
+    d, q, pad = _decode(host(packed), n, k)
+    d_ref, q_ref = oracle.quantize_q4_0(w)
+    assert np.array_equal(d, d_ref) and np.array_equal(q, q_ref)
+    assert np.all(pad == 0)
+
+
+def _problem(n, k, seed):
+    import weight_streaming_gemv_q8_amd as wsg
+    w = synth.normal_f32(seed, 1, n * k, 0.02).reshape(n, k)
+    packed = empty_u8(wsg.q4_0_packed_bytes(n, k))
+    wsg.quantize_q4_0_weights(dev(w), n, k, packed)
+    x = synth.activation(seed, 2, k, outlier_frac=0.01)
+    return w, packed, x
+
+
+@pytest.mark.parametrize("waves", [0, 4, 16])
+@pytest.mark.parametrize("act", ["requant", "q8"])
+@pytest.mark.parametrize("n,k", [(1024, 1024), (1, 32), (257, 5120), (300, 2080), (100, 17408), (4096, 4096)])
+def test_gemv_q4(gpu_lib, n, k, act, waves):
+    import torch
+    wsg = gpu_lib
+    if waves and (n, k) != (300, 2080):
+        pytest.skip("workgroup sizes are swept on one ragged shape")
+    wsg.tune(wsg.TUNE_WAVES, waves)
+    try:
+        w, packed, x = _problem(n, k, 0x5EEDC000 + n + k)
+        xd = dev(x)
+        if act == "q8":
+            xq = empty_u8(wsg.act_q8_0_bytes(k))
+            wsg.quantize_act_q8_0(xd, k, xq)
+            xin, fmt = xq, wsg.ACT_Q8_0
+        else:
+            xin, fmt = xd, wsg.ACT_F32_REQUANT
+        y = torch.full((n,), np.nan, dtype=torch.float32, device="cuda")
+        wsg.gemv_q4_0(packed, n, k, xin, fmt, y)
+        dw, qw = oracle.quantize_q4_0(w)
+        dx, qx = oracle.quantize_q8_0(x)
+        y_ref, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
+        assert_within(host(y), y_ref, oracle.q8_tolerance(den), f"W4 {n}x{k} {act}")
+    finally:
+        wsg.tune(wsg.TUNE_WAVES, 0)
+
+
+def test_gemv_q4_rejections(gpu_lib):
+    import torch
+    wsg = gpu_lib
+    _, packed, x = _problem(64, 1024, 0x5EEDC100)
+    y = torch.empty(64, dtype=torch.float32, device="cuda")
+    with pytest.raises(wsg.WsgError) as e:
+        wsg.gemv_q4_0(packed, 64, 1024, dev(x), wsg.ACT_F32, y)
+    assert e.value.status == wsg.ERR_MODE
+    for n, k in ((0, 1024), (64, 0), (64, 1000)):
+        with pytest.raises(wsg.WsgError) as e:
+            wsg.gemv_q4_0(packed, n, k, dev(x), wsg.ACT_F32_REQUANT, y)
+        assert e.value.status == wsg.ERR_SHAPE
+
+
+def test_q4_chain_27b_shapes(gpu_lib):
+    import torch
+
+    from weight_streaming_gemv_q8_amd.stream import TokenStream
+    wl = W.DENSE27B_Q8
+    layers = 2
+    shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
+    ts = TokenStream(shapes, layers, "q4_0", deq=0)
+
+    def fill(layer, m, part, rows, staging):
+        synth.dev_normal_f32(staging.data_ptr(), wl.seed, W.weight_tensor_id(layer, m, part),
+                             rows * wl.matrices[m].k, W.WEIGHT_SIGMA, stream=torch.cuda.current_stream().cuda_stream)
+
+    ts.fill_weights(fill)
+    xs = np.stack([synth.activation(wl.seed, W.activation_tensor_id(l), shapes[0][1], rms=True)
+                   for l in range(layers)])
+    ts.set_inputs(torch.from_numpy(xs).cuda())
+    ts.run_eager()
+    eager = [host(y).view(np.uint32).copy() for y in ts.outputs()]
+    for y in ts.outputs():
+        y.fill_(np.nan)
+    plan = ts.capture()
+    assert plan.kernel_count == len(ts.slots)
+    ts.launch()
+    got = [host(y).view(np.uint32).copy() for y in ts.outputs()]
+    assert all(np.array_equal(a, b) for a, b in zip(eager, got)), "replay differs from eager"
+    outs = [a.view(np.float32) for a in eager]
+    rng = np.random.default_rng(0xC4)
+    for layer in range(layers):
+        for j, m in enumerate(wl.matrices):
+            i = layer * len(wl.matrices) + j
+            x = xs[layer] if j == 0 else outs[i - 1][:m.k]
+            rows = np.array(sorted(set(int(v) for v in rng.integers(0, m.n, 40)) | {0, m.n - 1}))
+            wr = []
+            for r in rows:
+                part, base = 0, 0
+                while r >= base + m.parts[part]:
+                    base += m.parts[part]
+                    part += 1
+                wr.append(synth.normal_f32(wl.seed, W.weight_tensor_id(layer, j, part), m.k, W.WEIGHT_SIGMA,
+                                           first=(int(r) - base) * m.k))
+            dw, qw = oracle.quantize_q4_0(np.stack(wr))
+            dx, qx = oracle.quantize_q8_0(np.ascontiguousarray(x, np.float32))
+            y_ref, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
+            assert_within(outs[i][rows], y_ref, oracle.q8_tolerance(den), f"layer {layer} W4 GEMV {j}")
+    ts.close()

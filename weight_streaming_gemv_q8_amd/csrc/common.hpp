@@ -35,6 +35,19 @@ __host__ __device__ inline int64_t packed_row_bytes(int64_t k) {
     return (c - 1) * kFullChunkBytes + scale_section_bytes(nl) + 32 * nl;
 }
 
+// ------------------------------------------------------------- W4 layout
+// 4-bit blocks: per 2048-weight chunk [64 fp16 scales][64 x 16 code bytes]
+// (a block's byte j: code j in the low nibble, code j + 16 in the high one,
+// codes stored as q + 8); the last chunk's scale section padded to 16.
+constexpr int kFullChunkBytesQ4 = 2 * kChunkBlocks + kChunkWeights / 2;  // 128 + 1024
+
+__host__ __device__ inline int64_t q4_row_bytes(int64_t k) {
+    if (k <= 0) return 0;
+    const int64_t c = chunk_count(k);
+    const int64_t nl = last_chunk_blocks(k);
+    return (c - 1) * kFullChunkBytesQ4 + scale_section_bytes(nl) + 16 * nl;
+}
+
 // --------------------------------------------------------------- loads
 // Weight stream loads: 16 bytes per lane, optionally marked non-temporal so
 // the stream does not evict the (re-used) activation from L2.

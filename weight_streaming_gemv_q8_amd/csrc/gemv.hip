@@ -233,6 +233,83 @@ q8_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
     });
 }
 
+// ------------------------------------------------ 4-bit weights x int8
+// The W4 GEMV (qwen3-8b-rtx4080-cutedsl, "W4A16 dequant-fused GEMM": the
+// weights stream at 4 bits; GPU Kernel Lab, "Quantization experiments"):
+// the int8 path's schedule, staging and ring with a 4-bit item: per lane
+// one 16-byte load (its block's 32 codes) and the block's scale.  The
+// stored codes are n = q + 8 in [1, 15], so with sdot4 over the unpacked
+// nibbles s = sum n x - 8 sum x = sum q x, exact in int32; then
+// acc += (d_w d_x) s as in the int8 path.
+struct Q4Regs {
+    int4v a;
+    uint16_t sc;
+};
+
+template <int WAVES, int ACT>
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict__ xin, float* __restrict__ y) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int C = (int)chunk_count(k);
+    const int NB = k / kBlock;
+    const int nl = NB - (C - 1) * kChunkBlocks;
+    const int sbl = (int)scale_section_bytes(nl);
+    const int64_t row_bytes = q4_row_bytes(k);
+    int4v* lds_q = reinterpret_cast<int4v*>(smem);
+    float* lds_dx = reinterpret_cast<float*>(smem + (size_t)C * 2 * kWave * 16);
+    float* lds_res = reinterpret_cast<float*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>());
+    const int lane = threadIdx.x % kWave;
+    const Sched sc(C, 1, 1, WAVES, n, (n + WAVES - 1) / WAVES);
+    const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
+    // chunk m of the wave's row; past the schedule the idle region
+    auto load = [&](Q4Regs& r, const ItemCursor& it) {
+        const int row = it.j < sc.tiles_wg ? sc.row(it.j) : sc.n;
+        const int c = sc.chunk(it.m, 0);
+        const bool real = row < sc.n && c < C;
+        const bool last = c == C - 1;
+        const int nbc = last ? nl : kChunkBlocks;
+        const int sb = last ? sbl : 2 * kChunkBlocks;
+        const int l = lane < nbc ? lane : nbc - 1;
+        const gptr<uint8_t> cp = real ? Wg + (int64_t)row * row_bytes + (int64_t)c * kFullChunkBytesQ4 : idle_bytes();
+        r.sc = load_u16<true>(cp + 2 * l);
+        r.a = load16<true>(cp + sb + 16 * l);
+    };
+    auto compute = [&](const Q4Regs& r, int, int m, float& acc) {
+        const int c = sc.chunk(m, 0);
+        const int blk = c * kWave + lane;
+        if (blk < NB) {
+            const int4v xa = lds_q[(c * 2 + 0) * kWave + lane];
+            const int4v xb = lds_q[(c * 2 + 1) * kWave + lane];
+            int4v wa = r.a;
+            opaque(wa);
+            const uint32_t w4[4] = {(uint32_t)wa.x, (uint32_t)wa.y, (uint32_t)wa.z, (uint32_t)wa.w};
+            const int x4a[4] = {xa.x, xa.y, xa.z, xa.w}, x4b[4] = {xb.x, xb.y, xb.z, xb.w};
+            int dn = 0, sx = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                dn = __builtin_amdgcn_sdot4((int)(w4[q] & 0x0F0F0F0Fu), x4a[q], dn, false);
+                dn = __builtin_amdgcn_sdot4((int)((w4[q] >> 4) & 0x0F0F0F0Fu), x4b[q], dn, false);
+                sx = __builtin_amdgcn_sdot4(0x01010101, x4a[q], sx, false);
+                sx = __builtin_amdgcn_sdot4(0x01010101, x4b[q], sx, false);
+            }
+            const int s = dn - 8 * sx;
+            const float t = half_bits_to_float(r.sc) * lds_dx[blk];
+            acc = __builtin_fmaf(t, (float)s, acc);
+        }
+    };
+    Q4Regs R[kRingSets<1, 1>];
+    StageInput<ACT> stage{xin, k, C, {}};
+    stage.issue();
+    __builtin_amdgcn_sched_barrier(0);
+    ring_prologue(sc, R, load);
+    __builtin_amdgcn_sched_barrier(0);
+    stage.commit(lds_q, lds_dx, lds_res);
+    __syncthreads();
+    ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool valid) {
+        if (valid && lane == 0) y[row] = acc;
+    });
+}
+
 // The int8 path fed by the residual add + RMSNorm + re-quantization of
 // residual_rmsnorm_q8_0, computed by every workgroup in its prologue
 // (emit_qwen38_generate, "Where the speed comes from", item 3): the same
@@ -683,6 +760,23 @@ int launch_q8_norm(const void* w, int n, int k, const NormArgs& na, float* y, hi
     });
 }
 
+// The W4 GEMV: the waves the int8 path uses for the shape, unsplit rows.
+int launch_q4(const void* w, int n, int k, const void* x, int act_fmt, float* y, hipStream_t stream, LaunchInfo* info,
+              bool run = true) {
+    const Cfg c = choose_cfg(kPathI8, n, k);
+    const size_t lds_act = lds_q8act_bytes((int)chunk_count(k));
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    return dispatch_ws(c.waves, 1, [&](auto W, auto) -> int {
+        constexpr int Wv = decltype(W)::value;
+        if (act_fmt == WSG_ACT_Q8_0) {
+            auto kern = q4_i8_kernel<Wv, kActQ8>;
+            return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds_act), n, info, 1, run, stream, wp, n, k, x, y);
+        }
+        auto kern = q4_i8_kernel<Wv, kActRequant>;
+        return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds_act), n, info, 1, run, stream, wp, n, k, x, y);
+    });
+}
+
 // The gate+up GEMV with the SwiGLU epilogue: the waves the int8 path
 // uses for the whole gate+up matrix, one wave per output.
 int launch_q8_swiglu(const void* w, int n_ff, int k, const void* x, int act_fmt, float* y, hipStream_t stream,
@@ -816,6 +910,12 @@ int validate_gemv_q8_rmsnorm(const void* w, int64_t n, int64_t k, const float* h
     return WSG_OK;
 }
 
+int validate_gemv_q4(const void* w, int64_t n, int64_t k, const void* x, int act_fmt, const void* y) {
+    if (act_fmt != WSG_ACT_Q8_0 && act_fmt != WSG_ACT_F32_REQUANT) return WSG_ERR_MODE;
+    if (n < 1 || k < kBlock) return WSG_ERR_SHAPE;
+    return check_q8_args(w, n, k, x, act_fmt, y);
+}
+
 int validate_gemv_q8_swiglu(const void* w, int64_t n_ff, int64_t k, const void* x, int act_fmt, const void* y) {
     if (act_fmt != WSG_ACT_Q8_0 && act_fmt != WSG_ACT_F32_REQUANT) return WSG_ERR_MODE;
     if (n_ff < 1 || k < kBlock || 2 * n_ff > kMaxDim) return WSG_ERR_SHAPE;
@@ -871,6 +971,12 @@ int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h
     const int rc = validate_gemv_q8_rmsnorm(w_packed, n, k, h, r, g, eps, h_out, y);
     if (rc != WSG_OK) return rc;
     return launch_q8_norm(w_packed, (int)n, (int)k, NormArgs{h, r, g, h_out, eps}, y, stream, nullptr);
+}
+
+int gemv_q4_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act_fmt, float* y, hipStream_t stream) {
+    const int rc = validate_gemv_q4(w_packed, n, k, x, act_fmt, y);
+    if (rc != WSG_OK) return rc;
+    return launch_q4(w_packed, (int)n, (int)k, x, act_fmt, y, stream, nullptr);
 }
 
 int gemv_q8_0_swiglu(const void* w_packed, int64_t n_ff, int64_t k, const void* x, int act_fmt, float* y,

@@ -89,6 +89,44 @@ __global__ void quantize_weights_kernel(const float* __restrict__ w, int64_t n, 
     }
 }
 
+// 4-bit blocks (the W4 format): d16 = fp16(max|w| / 7), code = the fp32
+// quotient w / d16 rounded half away from zero, clamped to [-7, 7], stored
+// as code + 8 in the layout of q4_row_bytes; the thread of a row's last
+// block also zeroes the padding of that chunk's scale section.
+__global__ void quantize_q4_kernel(const float* __restrict__ w, int64_t n, int64_t k, uint8_t* __restrict__ out) {
+    const int64_t nb = k / kBlock;
+    const int64_t total = n * nb;
+    const int64_t row_bytes = q4_row_bytes(k);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+        const int64_t r = t / nb, b = t % nb;
+        const float* x = w + r * k + b * kBlock;
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kBlock; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+        uint16_t d16 = float_to_half_bits_rne(amax / 7.0f);
+        const float df = half_bits_to_float(d16);
+        if (df == 0.0f) d16 = 0;
+        uint8_t nib[kBlock];
+#pragma unroll
+        for (int i = 0; i < kBlock; ++i) {
+            float c = df == 0.0f ? 0.0f : roundf(x[i] / df);
+            c = c > 7.0f ? 7.0f : (c < -7.0f ? -7.0f : c);
+            nib[i] = (uint8_t)((int)c + 8);
+        }
+        const int64_t c = b / kChunkBlocks, bb = b % kChunkBlocks;
+        const int64_t nbc = c == chunk_count(k) - 1 ? last_chunk_blocks(k) : kChunkBlocks;
+        const int64_t sb = scale_section_bytes(nbc);
+        uint8_t* chunk = out + r * row_bytes + c * kFullChunkBytesQ4;
+        chunk[2 * bb] = (uint8_t)(d16 & 0xFF);
+        chunk[2 * bb + 1] = (uint8_t)(d16 >> 8);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) chunk[sb + 16 * bb + j] = (uint8_t)(nib[j] | (nib[j + 16] << 4));
+        if (bb == nbc - 1)
+            for (int64_t p = 2 * nbc; p < sb; ++p) chunk[p] = 0;
+    }
+}
+
 __global__ void pack_kernel(const uint8_t* __restrict__ aos, int64_t n, int64_t k, uint8_t* __restrict__ out) {
     const int64_t nb = k / kBlock;
     const int64_t total = n * nb;
@@ -181,6 +219,26 @@ int quantize_q8_0_weights(const float* w, int64_t n, int64_t k, void* w_packed, 
     if (!aligned(w, 16) || !aligned(w_packed, 16)) return WSG_ERR_ALIGN;
     hipLaunchKernelGGL(quantize_weights_kernel, dim3(grid_for(n * (k / kBlock), 256)), dim3(256), 0, stream, w,
                        n, k, static_cast<uint8_t*>(w_packed));
+    return launch_status();
+}
+
+int64_t q4_0_row_bytes(int64_t k) {
+    if (k < 0 || k > kMaxDim || k % kBlock) return -1;
+    return q4_row_bytes(k);
+}
+
+int64_t q4_0_packed_bytes(int64_t n, int64_t k) {
+    if (n < 0 || k < 0 || n > kMaxDim || k > kMaxDim || k % kBlock) return -1;
+    return n * q4_row_bytes(k);
+}
+
+int quantize_q4_0_weights(const float* w, int64_t n, int64_t k, void* w_packed, hipStream_t stream) {
+    if (n < 0 || k < 0 || n > kMaxDim || k > kMaxDim || k % kBlock) return WSG_ERR_SHAPE;
+    if (n == 0 || k == 0) return WSG_OK;
+    if (!w || !w_packed) return WSG_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(w_packed, 16)) return WSG_ERR_ALIGN;
+    hipLaunchKernelGGL(quantize_q4_kernel, dim3(grid_for(n * (k / kBlock), 256)), dim3(256), 0, stream, w, n, k,
+                       static_cast<uint8_t*>(w_packed));
     return launch_status();
 }
 

@@ -98,8 +98,10 @@ class TokenStream:
                  deq: int = 0, requant: str = "fused", device: str = "cuda",
                  norm_before: Sequence[int] = (), eps: float = 1e-6, fused_norm: bool = False,
                  swiglu_at: Sequence[int] = ()):
-        if wtype not in ("q8_0", "bf16"):
-            raise ValueError("wtype must be q8_0 or bf16")
+        if wtype not in ("q8_0", "q4_0", "bf16"):
+            raise ValueError("wtype must be q8_0, q4_0 or bf16")
+        if wtype == "q4_0" and (deq == 2 or requant != "fused" or norm_before or swiglu_at):
+            raise ValueError("q4_0 chains run int8 activations requantized in each GEMV")
         if requant not in ("fused", "separate"):
             raise ValueError("requant must be fused or separate")
         self.shapes = [(int(n), int(k), tuple(p)) for n, k, p in shapes]
@@ -122,7 +124,8 @@ class TokenStream:
         off = 0
         for layer in range(layers):
             for j, (n, k, _) in enumerate(self.shapes):
-                wb = wsg.q8_0_packed_bytes(n, k) if wtype == "q8_0" else n * k * 2
+                wb = (wsg.q8_0_packed_bytes(n, k) if wtype == "q8_0" else
+                      wsg.q4_0_packed_bytes(n, k) if wtype == "q4_0" else n * k * 2)
                 self.slots.append(GemvSlot(layer, j, n, k, off, wb))
                 off = _align(off + wb)
         self.weight_bytes_alloc = off
@@ -190,10 +193,10 @@ class TokenStream:
 
     # ------------------------------------------------------------ sizes
     def algorithmic_weight_bytes(self) -> int:
-        """Weight bytes per token at 34/32 (Q8_0) or 2 (BF16) bytes per weight."""
+        """Weight bytes per token at 34/32 (Q8_0), 18/32 (4-bit) or 2 (BF16) bytes per weight."""
         per = 0
         for n, k, _ in self.shapes:
-            per += n * (k // 32) * 34 if self.wtype == "q8_0" else n * k * 2
+            per += {"q8_0": n * (k // 32) * 34, "q4_0": n * (k // 32) * 18}.get(self.wtype, n * k * 2)
         return per * self.layers
 
     def act_fmt(self) -> int:
@@ -220,6 +223,9 @@ class TokenStream:
                 if self.wtype == "q8_0":
                     dst = base + s.w_offset + r0 * wsg.q8_0_row_bytes(k)
                     wsg.quantize_q8_0_weights(buf, rows, k, dst, stream)
+                elif self.wtype == "q4_0":
+                    dst = base + s.w_offset + r0 * wsg.q4_0_row_bytes(k)
+                    wsg.quantize_q4_0_weights(buf, rows, k, dst, stream)
                 else:
                     dst = base + s.w_offset + r0 * k * 2
                     wsg.convert_bf16(buf, rows * k, dst, stream)
@@ -263,6 +269,8 @@ class TokenStream:
                 return pre + [wsg.op_gemv_q8_0(w, s.n, s.k, n.yq, wsg.ACT_Q8_0, s.y)]
         if self.wtype == "bf16":
             return pre + [wsg.op_gemv_bf16(w, s.n, s.k, s.x_ptr, s.y)]
+        if self.wtype == "q4_0":
+            return [wsg.op_gemv_q4_0(w, s.n, s.k, s.x_ptr, wsg.ACT_F32_REQUANT, s.y)]
         fmt = self.act_fmt()
         if pre:
             return pre + [wsg.op_gemv_q8_0(w, s.n, s.k, s.x_ptr, fmt, s.y)]
@@ -295,6 +303,8 @@ class TokenStream:
             elif op.op == wsg.OP_RESIDUAL_RMSNORM:
                 wsg.residual_rmsnorm_q8_0(op.x, op.r, op.w, op.k, op.eps, h_out=op.h_out, y=op.y, y_q8=op.y_q8,
                                           stream=stream)
+            elif op.op == wsg.OP_GEMV_Q4_0:
+                wsg.gemv_q4_0(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
             elif op.op == wsg.OP_GEMV_Q8_0_SWIGLU:
                 wsg.gemv_q8_0_swiglu(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
             elif op.op == wsg.OP_GEMV_Q8_0_RMSNORM:
