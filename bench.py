@@ -93,12 +93,14 @@ def read_traffic(kernel_name: str):
 
 # ------------------------------------------------------------ workload
 
-def build_stream(wl, deq: int, requant: str, norm: bool = False, fused_norm: bool = False, swiglu: bool = False):
+def build_stream(wl, deq: int, requant: str, norm: bool = False, fused_norm: bool = False, swiglu: bool = False,
+                 wtype: str = None):
     """The workload's token stream with its weights generated on the device.
     norm=True chains the layers through the residual stream: a residual add
     + RMSNorm + re-quantization call before each layer's attention input
     (GEMV 0) and MLP input (GEMV 2); fused_norm=True computes that step in
-    the GEMV's prologue instead (int8 Q8_0 streams)."""
+    the GEMV's prologue instead (int8 Q8_0 streams); wtype overrides the
+    workload's weight format (\"q4_0\": the same shapes in 4 bits)."""
     import torch
 
     import synth
@@ -106,7 +108,7 @@ def build_stream(wl, deq: int, requant: str, norm: bool = False, fused_norm: boo
     from weight_streaming_gemv_q8_amd.stream import TokenStream
 
     shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
-    ts = TokenStream(shapes, wl.layers, wl.wtype, deq=deq, requant=requant,
+    ts = TokenStream(shapes, wl.layers, wtype or wl.wtype, deq=deq, requant=requant,
                      norm_before=(0, 2) if norm else (), eps=W.RMSNORM_EPS, fused_norm=fused_norm,
                      swiglu_at=(2,) if swiglu else ())
     log(f"allocated {ts.weight_bytes_alloc / 1e9:.3f} GB of weights; generating on the device")
@@ -273,7 +275,16 @@ def measure_configs(steps: int, warmup: int) -> list:
                           max(steps, 1))
         rec(wl, f"q8_0 GEMV + argmax, deq{deq}" + (" (= deq1)" if deq == 2 else ""), sec, n * (k // 32) * 34,
             deq=deq)
-    del wb, wq
+    # the same matrix with 4-bit weights (18 bytes per 32 weights)
+    staging = torch.empty(n * k, dtype=torch.float32, device="cuda")
+    synth.dev_normal_f32(staging.data_ptr(), wl.seed, 1, n * k, W.WEIGHT_SIGMA, stream=s)
+    w4 = torch.empty(wsg.q4_0_packed_bytes(n, k), dtype=torch.uint8, device="cuda")
+    wsg.quantize_q4_0_weights(staging, n, k, w4)
+    del staging
+    y4 = torch.empty(n, dtype=torch.float32, device="cuda")
+    sec = _time_calls(lambda i: wsg.gemv_q4_0(w4, n, k, x, wsg.ACT_F32_REQUANT, y4), max(steps, 1) * 4)
+    rec(wl, "q4_0 GEMV (W4), deq0", sec, n * (k // 32) * 18, deq=0)
+    del wb, wq, w4
     torch.cuda.empty_cache()
     # the residual add + RMSNorm + re-quantization between GEMVs, alone, at
     # the hidden sizes of the streams (bytes: h, r, g read; h', y written;
@@ -338,6 +349,14 @@ def measure_configs(steps: int, warmup: int) -> list:
                 ts.close()
                 del ts
                 torch.cuda.empty_cache()
+    # the 27B stream with 4-bit weights
+    ts = build_stream(W.DENSE27B_Q8, 0, "fused", wtype="q4_0")
+    sec, kernels = time_plan(ts, False, steps, warmup)
+    rec(W.DENSE27B_Q8, "graph, W4 weights (q4_0) deq0", sec, ts.algorithmic_weight_bytes(),
+        kernels_per_token=kernels, deq=0)
+    ts.close()
+    del ts
+    torch.cuda.empty_cache()
     # a whole decode step: embedding -> layers -> LM head + argmax -> advance
     for wl in (W.QWEN3_8B_Q8, W.DENSE27B_Q8):
         ds = build_decode(wl)

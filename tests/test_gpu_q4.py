@@ -7,8 +7,8 @@
 * the GEMV matches the oracle (the int8 block-dot form over the 4-bit
   codes) on every row within the int8 path's bound, for both int8
   activation formats, shapes spanning several chunks and ragged tails,
-  one-block and one-row cases, and 4-, 8- and 16-wave workgroups; large
-  shapes on sampled rows;
+  one-block and one-row cases, 4-, 8- and 16-wave workgroups and rows
+  split over 1, 2 and 4 waves;
 * a 2-layer 27B-shaped 4-bit chain replays bit-identically to its eager
   calls and matches the oracle link by link;
 * bad arguments are rejected."""
@@ -76,15 +76,16 @@ def _problem(n, k, seed):
     return w, packed, x
 
 
-@pytest.mark.parametrize("waves", [0, 4, 16])
+@pytest.mark.parametrize("waves,split", [(0, 0), (4, 1), (16, 1), (8, 2), (16, 4)])
 @pytest.mark.parametrize("act", ["requant", "q8"])
 @pytest.mark.parametrize("n,k", [(1024, 1024), (1, 32), (257, 5120), (300, 2080), (100, 17408), (4096, 4096)])
-def test_gemv_q4(gpu_lib, n, k, act, waves):
+def test_gemv_q4(gpu_lib, n, k, act, waves, split):
     import torch
     wsg = gpu_lib
-    if waves and (n, k) != (300, 2080):
-        pytest.skip("workgroup sizes are swept on one ragged shape")
+    if (waves or split) and (n, k) not in ((300, 2080), (100, 17408)):
+        pytest.skip("workgroup sizes and splits are swept on two ragged shapes")
     wsg.tune(wsg.TUNE_WAVES, waves)
+    wsg.tune(wsg.TUNE_SPLITK, split)
     try:
         w, packed, x = _problem(n, k, 0x5EEDC000 + n + k)
         xd = dev(x)
@@ -99,9 +100,10 @@ def test_gemv_q4(gpu_lib, n, k, act, waves):
         dw, qw = oracle.quantize_q4_0(w)
         dx, qx = oracle.quantize_q8_0(x)
         y_ref, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
-        assert_within(host(y), y_ref, oracle.q8_tolerance(den), f"W4 {n}x{k} {act}")
+        assert_within(host(y), y_ref, oracle.q8_tolerance(den), f"W4 {n}x{k} {act} waves {waves} split {split}")
     finally:
         wsg.tune(wsg.TUNE_WAVES, 0)
+        wsg.tune(wsg.TUNE_SPLITK, 0)
 
 
 def test_gemv_q4_rejections(gpu_lib):

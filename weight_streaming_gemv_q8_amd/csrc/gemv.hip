@@ -240,15 +240,20 @@ q8_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
 // one 16-byte load (its block's 32 codes) and the block's scale.  The
 // stored codes are n = q + 8 in [1, 15], so with sdot4 over the unpacked
 // nibbles s = sum n x - 8 sum x = sum q x, exact in int32; then
-// acc += (d_w d_x) s as in the int8 path.
+// acc += (d_w d_x) s as in the int8 path.  8 sum x depends on the
+// activation block only: each workgroup computes it once per block into
+// LDS after the staging, which halves the dot work per item.
 struct Q4Regs {
     int4v a;
     uint16_t sc;
 };
 
-template <int WAVES, int ACT>
+constexpr int kRingQ4 = 3;
+
+template <int WAVES, int S, int ACT>
 __global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict__ xin, float* __restrict__ y) {
+    static_assert(WAVES % S == 0, "S must divide WAVES");
     extern __shared__ __align__(16) uint8_t smem[];
     const int C = (int)chunk_count(k);
     const int NB = k / kBlock;
@@ -258,8 +263,12 @@ q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
     int4v* lds_q = reinterpret_cast<int4v*>(smem);
     float* lds_dx = reinterpret_cast<float*>(smem + (size_t)C * 2 * kWave * 16);
     float* lds_res = reinterpret_cast<float*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>());
+    int* lds_sx8 = reinterpret_cast<int*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>() +
+                                          lds_keep_bytes<WAVES>());
+    float* lds_part = reinterpret_cast<float*>(smem + lds_q8act_bytes(C));
     const int lane = threadIdx.x % kWave;
-    const Sched sc(C, 1, 1, WAVES, n, (n + WAVES - 1) / WAVES);
+    const int wave = threadIdx.x / kWave;
+    const Sched sc(C, S, 1, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
     const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
     // chunk m of the wave's row; past the schedule the idle region
     auto load = [&](Q4Regs& r, const ItemCursor& it) {
@@ -284,20 +293,18 @@ q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
             opaque(wa);
             const uint32_t w4[4] = {(uint32_t)wa.x, (uint32_t)wa.y, (uint32_t)wa.z, (uint32_t)wa.w};
             const int x4a[4] = {xa.x, xa.y, xa.z, xa.w}, x4b[4] = {xb.x, xb.y, xb.z, xb.w};
-            int dn = 0, sx = 0;
+            int dn = 0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 dn = __builtin_amdgcn_sdot4((int)(w4[q] & 0x0F0F0F0Fu), x4a[q], dn, false);
                 dn = __builtin_amdgcn_sdot4((int)((w4[q] >> 4) & 0x0F0F0F0Fu), x4b[q], dn, false);
-                sx = __builtin_amdgcn_sdot4(0x01010101, x4a[q], sx, false);
-                sx = __builtin_amdgcn_sdot4(0x01010101, x4b[q], sx, false);
             }
-            const int s = dn - 8 * sx;
+            const int s = dn - lds_sx8[blk];
             const float t = half_bits_to_float(r.sc) * lds_dx[blk];
             acc = __builtin_fmaf(t, (float)s, acc);
         }
     };
-    Q4Regs R[kRingSets<1, 1>];
+    Q4Regs R[kRingQ4];
     StageInput<ACT> stage{xin, k, C, {}};
     stage.issue();
     __builtin_amdgcn_sched_barrier(0);
@@ -305,8 +312,26 @@ q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
     __builtin_amdgcn_sched_barrier(0);
     stage.commit(lds_q, lds_dx, lds_res);
     __syncthreads();
-    ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool valid) {
-        if (valid && lane == 0) y[row] = acc;
+    // 8 sum x of every staged block (block c * 64 + l: words (2c) * 64 + l
+    // and (2c + 1) * 64 + l of lds_q)
+    for (int b = threadIdx.x; b < C * kWave; b += WAVES * kWave) {
+        const int4v xa = lds_q[(b / kWave * 2) * kWave + b % kWave];
+        const int4v xb = lds_q[(b / kWave * 2 + 1) * kWave + b % kWave];
+        int sx = 0;
+        sx = __builtin_amdgcn_sdot4(0x01010101, xa.x, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xa.y, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xa.z, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xa.w, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xb.x, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xb.y, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xb.z, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xb.w, sx, false);
+        lds_sx8[b] = 8 * sx;
+    }
+    __syncthreads();
+    uint64_t best = 0;
+    ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool) {
+        finish_row<WAVES, S, false>(acc, row, n, lane, wave, lds_part, y, best);
     });
 }
 
@@ -591,7 +616,7 @@ struct LaunchInfo {
     size_t lds = 0;
 };
 
-enum Path { kPathI8 = 0, kPathF32 = 1, kPathBf16 = 2 };
+enum Path { kPathI8 = 0, kPathF32 = 1, kPathBf16 = 2, kPathQ4 = 3 };
 
 // Default configuration per path and shape; tuning knobs override it.
 struct Cfg {
@@ -640,7 +665,13 @@ Cfg choose_cfg(Path path, int64_t n, int64_t k) {
     // one-chunk items, three in each wave's ring: measured fastest on every
     // workload shape once the ring's loads are pipelined
     c.unroll = 1;
-    if (path == kPathBf16) {
+    if (path == kPathQ4) {
+        // measured on the 27B-stream shapes in 4 bits: 16-wave workgroups
+        // with whole rows per wave beat every other pair on all four (the
+        // per-workgroup staging is a larger share of a 4-bit row)
+        c.waves = 16;
+        c.split = 1;
+    } else if (path == kPathBf16) {
         c.split = 1;
         if (rows_per_cu < 32 && k >= 16384) c.split = 4;
         else if (rows_per_cu < 8 && k >= 4096) c.split = 4;
@@ -760,20 +791,23 @@ int launch_q8_norm(const void* w, int n, int k, const NormArgs& na, float* y, hi
     });
 }
 
-// The W4 GEMV: the waves the int8 path uses for the shape, unsplit rows.
+// The W4 GEMV: its own waves and split choice (choose_cfg).
 int launch_q4(const void* w, int n, int k, const void* x, int act_fmt, float* y, hipStream_t stream, LaunchInfo* info,
               bool run = true) {
-    const Cfg c = choose_cfg(kPathI8, n, k);
+    const Cfg c = choose_cfg(kPathQ4, n, k);
     const size_t lds_act = lds_q8act_bytes((int)chunk_count(k));
+    const size_t lds_sx8 = chunk_count(k) * kWave * 4;  // 8 sum x per block
     const uint8_t* wp = static_cast<const uint8_t*>(w);
-    return dispatch_ws(c.waves, 1, [&](auto W, auto) -> int {
-        constexpr int Wv = decltype(W)::value;
+    return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
+        constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
         if (act_fmt == WSG_ACT_Q8_0) {
-            auto kern = q4_i8_kernel<Wv, kActQ8>;
-            return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds_act), n, info, 1, run, stream, wp, n, k, x, y);
+            auto kern = q4_i8_kernel<Wv, Sv, kActQ8>;
+            return launch_kernel<Wv, Sv>(kern, q8_lds_bytes<Wv>(lds_act) + lds_sx8, n, info, 1, run, stream, wp, n,
+                                         k, x, y);
         }
-        auto kern = q4_i8_kernel<Wv, kActRequant>;
-        return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds_act), n, info, 1, run, stream, wp, n, k, x, y);
+        auto kern = q4_i8_kernel<Wv, Sv, kActRequant>;
+        return launch_kernel<Wv, Sv>(kern, q8_lds_bytes<Wv>(lds_act) + lds_sx8, n, info, 1, run, stream, wp, n, k,
+                                     x, y);
     });
 }
 
