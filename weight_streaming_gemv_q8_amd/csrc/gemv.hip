@@ -270,10 +270,8 @@ q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
     const int wave = threadIdx.x / kWave;
     const Sched sc(C, S, 1, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
     const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
-    // chunk m of the wave's row; past the schedule the idle region
-    auto load = [&](Q4Regs& r, const ItemCursor& it) {
-        const int row = it.j < sc.tiles_wg ? sc.row(it.j) : sc.n;
-        const int c = sc.chunk(it.m, 0);
+    // chunk c of a row (row n or chunk C: the idle region)
+    auto load_rc = [&](Q4Regs& r, int row, int c) {
         const bool real = row < sc.n && c < C;
         const bool last = c == C - 1;
         const int nbc = last ? nl : kChunkBlocks;
@@ -283,8 +281,7 @@ q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
         r.sc = load_u16<true>(cp + 2 * l);
         r.a = load16<true>(cp + sb + 16 * l);
     };
-    auto compute = [&](const Q4Regs& r, int, int m, float& acc) {
-        const int c = sc.chunk(m, 0);
+    auto compute_c = [&](const Q4Regs& r, int c, float& acc) {
         const int blk = c * kWave + lane;
         if (blk < NB) {
             const int4v xa = lds_q[(c * 2 + 0) * kWave + lane];
@@ -304,11 +301,29 @@ q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
             acc = __builtin_fmaf(t, (float)s, acc);
         }
     };
+    // chunk m of the wave's row and part; past the schedule the idle region
+    auto load = [&](Q4Regs& r, const ItemCursor& it) {
+        load_rc(r, it.j < sc.tiles_wg ? sc.row(it.j) : sc.n, sc.chunk(it.m, 0));
+    };
+    auto compute = [&](const Q4Regs& r, int, int m, float& acc) { compute_c(r, sc.chunk(m, 0), acc); };
+    // split rows: rotating parts with the partials kept in LDS while the
+    // workgroup's tiles fit, as in the int8 path (rot_loop, flush_parts)
+    constexpr bool kRot = S > 1;
+    const bool rot = kRot && sc.tiles_wg <= kKeepTiles;
+    RotSched rs;
+    rs.set(sc, wave);
+    auto rload = [&](Q4Regs& r, const RotSched& rs_, const RotCursor& it) {
+        const bool has_item = it.j < rs_.sc->tiles_wg;
+        load_rc(r, has_item ? sc.row(it.j) : sc.n, has_item ? it.p + S * it.m : C);
+    };
     Q4Regs R[kRingQ4];
     StageInput<ACT> stage{xin, k, C, {}};
     stage.issue();
     __builtin_amdgcn_sched_barrier(0);
-    ring_prologue(sc, R, load);
+    if (rot)
+        rot_prologue(rs, R, rload);
+    else
+        ring_prologue(sc, R, load);
     __builtin_amdgcn_sched_barrier(0);
     stage.commit(lds_q, lds_dx, lds_res);
     __syncthreads();
@@ -329,6 +344,24 @@ q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
         lds_sx8[b] = 8 * sx;
     }
     __syncthreads();
+    if constexpr (kRot) {
+        if (rot) {
+            if (threadIdx.x % kWave < (unsigned)sc.tiles_wg) {
+                const int t = (int)(threadIdx.x % kWave);
+                if (rs.items(t) == 0) lds_res[t * WAVES + sc.group * S + rs.part(t)] = 0.0f;
+            }
+            rot_loop(rs, R, rload,
+                     [&](const Q4Regs& r, const Sched& s1, int, int m, float& acc) {
+                         compute_c(r, s1.chunk(m, 0), acc);
+                     },
+                     [&](float acc, int t, int slot) {
+                         if (lane == 0) lds_res[t * WAVES + slot] = acc;
+                     });
+            __syncthreads();
+            flush_parts<WAVES>(sc, lds_res, y);
+            return;
+        }
+    }
     uint64_t best = 0;
     ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool) {
         finish_row<WAVES, S, false>(acc, row, n, lane, wave, lds_part, y, best);
@@ -667,8 +700,9 @@ Cfg choose_cfg(Path path, int64_t n, int64_t k) {
     c.unroll = 1;
     if (path == kPathQ4) {
         // measured on the 27B-stream shapes in 4 bits: 16-wave workgroups
-        // with whole rows per wave beat every other pair on all four (the
-        // per-workgroup staging is a larger share of a 4-bit row)
+        // with whole rows per wave beat every other pair on all four, the
+        // rotating split included (the per-workgroup staging is a larger
+        // share of a 4-bit row)
         c.waves = 16;
         c.split = 1;
     } else if (path == kPathBf16) {

@@ -328,8 +328,8 @@ __device__ inline void q8_load_rot(Q8Regs<1>& R, gptr<uint8_t> W, int64_t row_by
 // refills), with rotating parts.
 // load(regs, rs, cursor) issues one item's loads (a cursor past the
 // schedule reads the idle region).
-template <int N, typename LoadF>
-__device__ inline void rot_prologue(const RotSched& rs, Q8Regs<1> (&R)[N], LoadF&& load) {
+template <int N, typename Regs, typename LoadF>
+__device__ inline void rot_prologue(const RotSched& rs, Regs (&R)[N], LoadF&& load) {
     const int T = rs.total();
     const int pad = (T + N - 1) / N * N - T;
     RotCursor it;
@@ -347,8 +347,8 @@ __device__ inline void rot_prologue(const RotSched& rs, Q8Regs<1> (&R)[N], LoadF
     }
 }
 
-template <int N, typename LoadF, typename ComputeF, typename KeepF>
-__device__ inline void rot_loop(const RotSched& rs, Q8Regs<1> (&R)[N], LoadF&& load, ComputeF&& compute,
+template <int N, typename Regs, typename LoadF, typename ComputeF, typename KeepF>
+__device__ inline void rot_loop(const RotSched& rs, Regs (&R)[N], LoadF&& load, ComputeF&& compute,
                                 KeepF&& keep) {
     const Sched& sc = *rs.sc;
     const int T = rs.total();
@@ -359,7 +359,7 @@ __device__ inline void rot_loop(const RotSched& rs, Q8Regs<1> (&R)[N], LoadF&& l
     nxt.start(rs);
     for (int q = pad; q < N; ++q) nxt.next(rs);  // the items the prologue requested
     float acc = 0.0f;
-    auto consume = [&](Q8Regs<1>& r, int q) {
+    auto consume = [&](Regs& r, int q) {
         if (q < pad) return;
         const int row = sc.row(cur.j);
         if (row < sc.n) {
