@@ -178,11 +178,14 @@ int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h
  * 16 code bytes], a block's byte j holding code j (low nibble) and code
  * j + 16 (high nibble); the last chunk's scale section is padded to 16
  * bytes with zeros.  q4_0_*_bytes return -1 on a bad shape.
- * gemv_q4_0: y = W x with int8 activations (act_fmt WSG_ACT_Q8_0 or
- *   WSG_ACT_F32_REQUANT; WSG_ERR_MODE otherwise); the exact int32 block dot
- *   s = sum q_w q_x, then y = sum_b d_w d_x s in f32.  Acceptance: as
- *   gemv_q8_0's int8 path.  n >= 1, 32 <= k <= WSG_MAX_K_Q8ACT, k % 32 == 0
- *   (WSG_ERR_SHAPE). */
+ * gemv_q4_0: y = W x.  With int8 activations (act_fmt WSG_ACT_Q8_0 or
+ *   WSG_ACT_F32_REQUANT) the exact int32 block dot s = sum q_w q_x, then
+ *   y = sum_b d_w d_x s in f32, accepted as gemv_q8_0's int8 path,
+ *   32 <= k <= WSG_MAX_K_Q8ACT.  With f32 activations (WSG_ACT_F32, the
+ *   W4A16 form of qwen3-8b-rtx4080-cutedsl, "W4A16 dequant-fused GEMM")
+ *   y = sum_b d_w sum_i q_i x_i in f32 fused multiply-adds, accepted as
+ *   gemv_q8_0's f32 path, 32 <= k <= WSG_MAX_K_F32ACT.  Other act_fmt:
+ *   WSG_ERR_MODE; n >= 1 and k % 32 == 0 else WSG_ERR_SHAPE. */
 int64_t q4_0_row_bytes(int64_t k);
 int64_t q4_0_packed_bytes(int64_t n, int64_t k);
 int quantize_q4_0_weights(const float* w, int64_t n, int64_t k, void* w_packed, hipStream_t stream);

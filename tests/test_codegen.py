@@ -93,6 +93,28 @@ def test_w4_ring_keeps_two_items_in_flight(asm):
         assert _max_wait_before_dot(body) >= 4, name
 
 
+def _max_wait_before_fma(body):
+    """Largest vmcnt of the waits that directly precede an f32 FMA."""
+    best, last = -1, None
+    for line in body.splitlines():
+        m = re.search(r"s_waitcnt\s+vmcnt\((\d+)\)", line)
+        if m:
+            last = int(m.group(1))
+        elif re.search(r"v_fmac?_f32", line) and last is not None:
+            best = max(best, last)
+            last = None
+        elif re.match(r"\.LBB|\s*s_cbranch|\s*s_branch", line):
+            last = None
+    return best
+
+
+def test_w4_f32_ring_keeps_two_items_in_flight(asm):
+    ks = {n: b for n, b in _kernels(asm["gemv.hip"]).items() if "q4_f32_kernel" in n}
+    assert len(ks) == 9
+    for name, body in ks.items():
+        assert _max_wait_before_fma(body) >= 4, name
+
+
 def test_eager_int8_ring_keeps_two_items_in_flight(asm):
     # one-chunk items (U = 1), int8 activations and the requantizing staging
     ks = {n: b for n, b in _kernels(asm["gemv.hip"]).items()

@@ -5,12 +5,13 @@
 * the device layout decodes to the oracle's scales and codes, bit for bit,
   and the scale sections' padding is zero, on ragged and full chunks;
 * the GEMV matches the oracle (the int8 block-dot form over the 4-bit
-  codes) on every row within the int8 path's bound, for both int8
-  activation formats, shapes spanning several chunks and ragged tails,
+  codes, or the f32-activation block dot of the W4A16 form) on every row
+  within the bound of the matching Q8_0 path, for all three activation
+  formats, shapes spanning several chunks and ragged tails,
   one-block and one-row cases, 4-, 8- and 16-wave workgroups and rows
   split over 1, 2 and 4 waves;
-* a 2-layer 27B-shaped 4-bit chain replays bit-identically to its eager
-  calls and matches the oracle link by link;
+* a 2-layer 27B-shaped 4-bit chain (deq 0 and deq 2) replays
+  bit-identically to its eager calls and matches the oracle link by link;
 * bad arguments are rejected."""
 import numpy as np
 import pytest
@@ -77,7 +78,7 @@ def _problem(n, k, seed):
 
 
 @pytest.mark.parametrize("waves,split", [(0, 0), (4, 1), (16, 1), (8, 2), (16, 4)])
-@pytest.mark.parametrize("act", ["requant", "q8"])
+@pytest.mark.parametrize("act", ["requant", "q8", "f32"])
 @pytest.mark.parametrize("n,k", [(1024, 1024), (1, 32), (257, 5120), (300, 2080), (100, 17408), (4096, 4096)])
 def test_gemv_q4(gpu_lib, n, k, act, waves, split):
     import torch
@@ -94,12 +95,16 @@ def test_gemv_q4(gpu_lib, n, k, act, waves, split):
             wsg.quantize_act_q8_0(xd, k, xq)
             xin, fmt = xq, wsg.ACT_Q8_0
         else:
-            xin, fmt = xd, wsg.ACT_F32_REQUANT
+            xin, fmt = xd, wsg.ACT_F32 if act == "f32" else wsg.ACT_F32_REQUANT
         y = torch.full((n,), np.nan, dtype=torch.float32, device="cuda")
         wsg.gemv_q4_0(packed, n, k, xin, fmt, y)
         dw, qw = oracle.quantize_q4_0(w)
-        dx, qx = oracle.quantize_q8_0(x)
-        y_ref, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
+        if act == "f32":
+            # the W4A16 form: the 4-bit codes against the f32 activation
+            y_ref, den = oracle.gemv_q8_act_f32(dw, qw, x)
+        else:
+            dx, qx = oracle.quantize_q8_0(x)
+            y_ref, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
         assert_within(host(y), y_ref, oracle.q8_tolerance(den), f"W4 {n}x{k} {act} waves {waves} split {split}")
     finally:
         wsg.tune(wsg.TUNE_WAVES, 0)
@@ -112,22 +117,26 @@ def test_gemv_q4_rejections(gpu_lib):
     _, packed, x = _problem(64, 1024, 0x5EEDC100)
     y = torch.empty(64, dtype=torch.float32, device="cuda")
     with pytest.raises(wsg.WsgError) as e:
-        wsg.gemv_q4_0(packed, 64, 1024, dev(x), wsg.ACT_F32, y)
+        wsg.gemv_q4_0(packed, 64, 1024, dev(x), 7, y)
     assert e.value.status == wsg.ERR_MODE
+    with pytest.raises(wsg.WsgError) as e:  # above the f32 path's k
+        wsg.gemv_q4_0(packed, 1, 40960, dev(x), wsg.ACT_F32, y)
+    assert e.value.status == wsg.ERR_SHAPE
     for n, k in ((0, 1024), (64, 0), (64, 1000)):
         with pytest.raises(wsg.WsgError) as e:
             wsg.gemv_q4_0(packed, n, k, dev(x), wsg.ACT_F32_REQUANT, y)
         assert e.value.status == wsg.ERR_SHAPE
 
 
-def test_q4_chain_27b_shapes(gpu_lib):
+@pytest.mark.parametrize("deq", [0, 2])
+def test_q4_chain_27b_shapes(gpu_lib, deq):
     import torch
 
     from weight_streaming_gemv_q8_amd.stream import TokenStream
     wl = W.DENSE27B_Q8
     layers = 2
     shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
-    ts = TokenStream(shapes, layers, "q4_0", deq=0)
+    ts = TokenStream(shapes, layers, "q4_0", deq=deq)
 
     def fill(layer, m, part, rows, staging):
         synth.dev_normal_f32(staging.data_ptr(), wl.seed, W.weight_tensor_id(layer, m, part),
@@ -162,7 +171,10 @@ def test_q4_chain_27b_shapes(gpu_lib):
                 wr.append(synth.normal_f32(wl.seed, W.weight_tensor_id(layer, j, part), m.k, W.WEIGHT_SIGMA,
                                            first=(int(r) - base) * m.k))
             dw, qw = oracle.quantize_q4_0(np.stack(wr))
-            dx, qx = oracle.quantize_q8_0(np.ascontiguousarray(x, np.float32))
-            y_ref, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
+            if deq == 2:
+                y_ref, den = oracle.gemv_q8_act_f32(dw, qw, np.ascontiguousarray(x, np.float32))
+            else:
+                dx, qx = oracle.quantize_q8_0(np.ascontiguousarray(x, np.float32))
+                y_ref, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
             assert_within(outs[i][rows], y_ref, oracle.q8_tolerance(den), f"layer {layer} W4 GEMV {j}")
     ts.close()

@@ -368,6 +368,111 @@ q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
     });
 }
 
+// The W4 GEMV with f32 activations (the W4A16 form of qwen3-8b-rtx4080-
+// cutedsl, "W4A16 dequant-fused GEMM": 4-bit weights dequantized in
+// registers against a wide activation): the f32 path's staging, ring and
+// rotating split with a 4-bit item.  Each code word is turned into the
+// int8 codes q = n - 8 exactly (per byte: set bit 7 so that subtracting 8
+// cannot borrow from the next byte, then flip bit 7 back), so the block dot
+// is the Q8_0 f32 path's, sum_i q_i x_i in f32 fused multiply-adds, then
+// acc += d_w * that.
+__device__ inline int q4_codes_i8(uint32_t nib) {
+    return (int)(((nib | 0x80808080u) - 0x08080808u) ^ 0x80808080u);
+}
+
+template <int WAVES, int S>
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+q4_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restrict__ x, float* __restrict__ y) {
+    static_assert(WAVES % S == 0, "S must divide WAVES");
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int C = (int)chunk_count(k);
+    const int NB = k / kBlock;
+    const int nl = NB - (C - 1) * kChunkBlocks;
+    const int sbl = (int)scale_section_bytes(nl);
+    const int64_t row_bytes = q4_row_bytes(k);
+    float4v* lds_x = reinterpret_cast<float4v*>(smem);
+    float* lds_part = reinterpret_cast<float*>(smem + lds_f32act_bytes(C));
+    float* lds_res = reinterpret_cast<float*>(smem + lds_f32act_bytes(C) + lds_tail_bytes<WAVES>());
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const Sched sc(C, S, 1, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
+    const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
+    // chunk c of a row (row n or chunk C: the idle region)
+    auto load_rc = [&](Q4Regs& r, int row, int c) {
+        const bool real = row < sc.n && c < C;
+        const bool last = c == C - 1;
+        const int nbc = last ? nl : kChunkBlocks;
+        const int sb = last ? sbl : 2 * kChunkBlocks;
+        const int l = lane < nbc ? lane : nbc - 1;
+        const gptr<uint8_t> cp = real ? Wg + (int64_t)row * row_bytes + (int64_t)c * kFullChunkBytesQ4 : idle_bytes();
+        r.sc = load_u16<true>(cp + 2 * l);
+        r.a = load16<true>(cp + sb + 16 * l);
+    };
+    // word q of a block's 16 bytes: low nibbles are codes 4q..4q+3 (group q
+    // of the staged activation), high nibbles codes 16+4q.. (group 4 + q)
+    auto compute_c = [&](const Q4Regs& r, int c, float& acc) {
+        if (c * kWave + lane < NB) {
+            const float4v* xv = lds_x + (size_t)c * 8 * kWave + lane;
+            int4v wa = r.a;
+            opaque(wa);
+            const uint32_t w4[4] = {(uint32_t)wa.x, (uint32_t)wa.y, (uint32_t)wa.z, (uint32_t)wa.w};
+            float bs = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bs = dot4_i8_f32(q4_codes_i8(w4[q] & 0x0F0F0F0Fu), xv[q * kWave], bs);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                bs = dot4_i8_f32(q4_codes_i8((w4[q] >> 4) & 0x0F0F0F0Fu), xv[(4 + q) * kWave], bs);
+            acc = __builtin_fmaf(half_bits_to_float(r.sc), bs, acc);
+        }
+    };
+    auto load = [&](Q4Regs& r, const ItemCursor& it) {
+        load_rc(r, it.j < sc.tiles_wg ? sc.row(it.j) : sc.n, sc.chunk(it.m, 0));
+    };
+    auto compute = [&](const Q4Regs& r, int, int m, float& acc) { compute_c(r, sc.chunk(m, 0), acc); };
+    constexpr bool kRot = S > 1;
+    const bool rot = kRot && sc.tiles_wg <= kKeepTiles;
+    RotSched rs;
+    rs.set(sc, wave);
+    auto rload = [&](Q4Regs& r, const RotSched& rs_, const RotCursor& it) {
+        const bool has_item = it.j < rs_.sc->tiles_wg;
+        load_rc(r, has_item ? sc.row(it.j) : sc.n, has_item ? it.p + S * it.m : C);
+    };
+
+    Q4Regs R[kRingQ4];
+    StageF32<4> st;
+    st.issue(x, k);
+    __builtin_amdgcn_sched_barrier(0);
+    if (rot)
+        rot_prologue(rs, R, rload);
+    else
+        ring_prologue(sc, R, load);
+    __builtin_amdgcn_sched_barrier(0);
+    st.commit(x, k, lds_x);
+    __syncthreads();
+    if constexpr (kRot) {
+        if (rot) {
+            if (threadIdx.x % kWave < (unsigned)sc.tiles_wg) {
+                const int t = (int)(threadIdx.x % kWave);
+                if (rs.items(t) == 0) lds_res[t * WAVES + sc.group * S + rs.part(t)] = 0.0f;
+            }
+            rot_loop(rs, R, rload,
+                     [&](const Q4Regs& r, const Sched& s1, int, int m, float& acc) {
+                         compute_c(r, s1.chunk(m, 0), acc);
+                     },
+                     [&](float acc, int t, int slot) {
+                         if (lane == 0) lds_res[t * WAVES + slot] = acc;
+                     });
+            __syncthreads();
+            flush_parts<WAVES>(sc, lds_res, y);
+            return;
+        }
+    }
+    uint64_t best = 0;
+    ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool) {
+        finish_row<WAVES, S, false>(acc, row, n, lane, wave, lds_part, y, best);
+    });
+}
+
 // The int8 path fed by the residual add + RMSNorm + re-quantization of
 // residual_rmsnorm_q8_0, computed by every workgroup in its prologue
 // (emit_qwen38_generate, "Where the speed comes from", item 3): the same
@@ -834,6 +939,12 @@ int launch_q4(const void* w, int n, int k, const void* x, int act_fmt, float* y,
     const uint8_t* wp = static_cast<const uint8_t*>(w);
     return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
         constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
+        if (act_fmt == WSG_ACT_F32) {
+            auto kern = q4_f32_kernel<Wv, Sv>;
+            const size_t lds = q8_lds_bytes<Wv>(lds_f32act_bytes((int)chunk_count(k)));
+            return launch_kernel<Wv, Sv>(kern, lds, n, info, 1, run, stream, wp, n, k,
+                                         static_cast<const float*>(x), y);
+        }
         if (act_fmt == WSG_ACT_Q8_0) {
             auto kern = q4_i8_kernel<Wv, Sv, kActQ8>;
             return launch_kernel<Wv, Sv>(kern, q8_lds_bytes<Wv>(lds_act) + lds_sx8, n, info, 1, run, stream, wp, n,
@@ -979,7 +1090,7 @@ int validate_gemv_q8_rmsnorm(const void* w, int64_t n, int64_t k, const float* h
 }
 
 int validate_gemv_q4(const void* w, int64_t n, int64_t k, const void* x, int act_fmt, const void* y) {
-    if (act_fmt != WSG_ACT_Q8_0 && act_fmt != WSG_ACT_F32_REQUANT) return WSG_ERR_MODE;
+    if (act_fmt != WSG_ACT_Q8_0 && act_fmt != WSG_ACT_F32_REQUANT && act_fmt != WSG_ACT_F32) return WSG_ERR_MODE;
     if (n < 1 || k < kBlock) return WSG_ERR_SHAPE;
     return check_q8_args(w, n, k, x, act_fmt, y);
 }

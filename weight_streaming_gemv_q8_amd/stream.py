@@ -100,8 +100,8 @@ class TokenStream:
                  swiglu_at: Sequence[int] = ()):
         if wtype not in ("q8_0", "q4_0", "bf16"):
             raise ValueError("wtype must be q8_0, q4_0 or bf16")
-        if wtype == "q4_0" and (deq == 2 or requant != "fused" or norm_before or swiglu_at):
-            raise ValueError("q4_0 chains run int8 activations requantized in each GEMV")
+        if wtype == "q4_0" and (requant != "fused" or norm_before or swiglu_at):
+            raise ValueError("q4_0 chains run f32 activations (deq 2) or int8 ones requantized in each GEMV")
         if requant not in ("fused", "separate"):
             raise ValueError("requant must be fused or separate")
         self.shapes = [(int(n), int(k), tuple(p)) for n, k, p in shapes]
@@ -270,7 +270,7 @@ class TokenStream:
         if self.wtype == "bf16":
             return pre + [wsg.op_gemv_bf16(w, s.n, s.k, s.x_ptr, s.y)]
         if self.wtype == "q4_0":
-            return [wsg.op_gemv_q4_0(w, s.n, s.k, s.x_ptr, wsg.ACT_F32_REQUANT, s.y)]
+            return [wsg.op_gemv_q4_0(w, s.n, s.k, s.x_ptr, wsg.ACT_F32 if self.deq == 2 else wsg.ACT_F32_REQUANT, s.y)]
         fmt = self.act_fmt()
         if pre:
             return pre + [wsg.op_gemv_q8_0(w, s.n, s.k, s.x_ptr, fmt, s.y)]
