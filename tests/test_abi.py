@@ -208,3 +208,19 @@ def test_swiglu_gemv_rejects_before_launch(L):
     assert f(A, 64, 1000, A, wsg.ACT_F32_REQUANT, A + 0x10000, None) == wsg.ERR_SHAPE
     assert f(A, 64, 1024, None, wsg.ACT_Q8_0, A + 0x10000, None) == wsg.ERR_NULL
     assert f(A + 8, 64, 1024, A, wsg.ACT_Q8_0, A + 0x10000, None) == wsg.ERR_ALIGN
+
+
+def test_w4_entry_points_reject_before_launch(L):
+    A = 0x100000
+    f = L.gemv_q4_0
+    assert f(A, 64, 1024, A, 7, A + 0x10000, None) == wsg.ERR_MODE
+    assert f(A, 0, 1024, A, wsg.ACT_F32, A + 0x10000, None) == wsg.ERR_SHAPE
+    assert f(A, 64, 1000, A, wsg.ACT_Q8_0, A + 0x10000, None) == wsg.ERR_SHAPE
+    # the f32 (W4A16) form stages the activation as f32: its smaller k limit
+    assert f(A, 64, 40960, A, wsg.ACT_F32, A + 0x10000, None) == wsg.ERR_SHAPE
+    assert f(A, 64, 57376, A, wsg.ACT_F32_REQUANT, A + 0x10000, None) == wsg.ERR_SHAPE
+    assert f(A, 64, 1024, None, wsg.ACT_F32, A + 0x10000, None) == wsg.ERR_NULL
+    assert f(A + 8, 64, 1024, A, wsg.ACT_F32, A + 0x10000, None) == wsg.ERR_ALIGN
+    assert L.q4_0_row_bytes(2048) == 1152 and L.q4_0_row_bytes(96) == 16 + 48
+    assert L.q4_0_row_bytes(1000) == -1 and L.q4_0_packed_bytes(-1, 64) == -1
+    assert L.quantize_q4_0_weights(A, 4, 1000, A, None) == wsg.ERR_SHAPE
