@@ -191,6 +191,16 @@ int64_t q4_0_packed_bytes(int64_t n, int64_t k);
 int quantize_q4_0_weights(const float* w, int64_t n, int64_t k, void* w_packed, hipStream_t stream);
 int gemv_q4_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act_fmt, float* y, hipStream_t stream);
 
+/* gemv_q4_0_rmsnorm: the 4-bit GEMV fed by the residual add + RMSNorm +
+ * re-quantization of residual_rmsnorm_q8_0 computed in its own prologue
+ * (emit_qwen38_generate, "Where the speed comes from", item 3, on 4-bit
+ * weights): y = W . Q8_0(RMSNorm(h + r) * g), bit for bit the output of
+ * residual_rmsnorm_q8_0 followed by gemv_q4_0 with WSG_ACT_Q8_0 on its
+ * codes.  Arguments, h_out, acceptance and errors as gemv_q8_0_rmsnorm,
+ * with w_packed in the 4-bit layout above. */
+int gemv_q4_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r, const float* g,
+                      float eps, float* h_out, float* y, hipStream_t stream);
+
 /* The gate+up GEMV with its SwiGLU epilogue (GPU Kernel Lab, "What we
  * built", "Decode integration": the dual gate/up projection fused with
  * SwiGLU at batch 1):
@@ -298,6 +308,7 @@ enum {
     WSG_OP_EMBED_GATHER = 7,      /* embed_gather: w = table, w_type, n = vocab, k = hidden, x = token, y */
     WSG_OP_TOKEN_ADVANCE = 8,     /* token_advance: x = token, idx_out = history, n = capacity, ws = pos */
     WSG_OP_GEMV_Q4_0 = 9,         /* gemv_q4_0: w, n, k, x, act_fmt, y */
+    WSG_OP_GEMV_Q4_0_RMSNORM = 10, /* gemv_q4_0_rmsnorm: w, n, k, x = h, r, g, eps, h_out, y */
 };
 
 /* flags: WSG_OP_AFTER_ALL marks an op that depends on every earlier op of
@@ -320,13 +331,13 @@ typedef struct {
     size_t ws_bytes;
     int32_t* idx_out;
     int flags;
-    /* WSG_OP_RESIDUAL_RMSNORM and WSG_OP_GEMV_Q8_0_RMSNORM only (zero for
-     * every other op) */
+    /* WSG_OP_RESIDUAL_RMSNORM and the fused-norm GEMVs only (zero for every
+     * other op) */
     const void* r;
     void* h_out;
     void* y_q8;
     float eps;
-    const void* g; /* WSG_OP_GEMV_Q8_0_RMSNORM's norm weight */
+    const void* g; /* the fused-norm GEMVs' norm weight */
 } wsg_op_desc;
 
 typedef struct wsg_plan wsg_plan;

@@ -130,7 +130,7 @@ def test_plan_rejects_bad_descriptors_before_capture(L):
     with pytest.raises(wsg.WsgError) as e:
         wsg.Plan(ops, stream=0)
     assert e.value.status == wsg.ERR_SHAPE
-    ops = [wsg.OpDesc(op=wsg.OP_GEMV_Q4_0 + 1)]
+    ops = [wsg.OpDesc(op=wsg.OP_GEMV_Q4_0_RMSNORM + 1)]
     with pytest.raises(wsg.WsgError) as e:
         wsg.Plan(ops, stream=0)
     assert e.value.status == wsg.ERR_MODE
@@ -224,3 +224,6 @@ def test_w4_entry_points_reject_before_launch(L):
     assert L.q4_0_row_bytes(2048) == 1152 and L.q4_0_row_bytes(96) == 16 + 48
     assert L.q4_0_row_bytes(1000) == -1 and L.q4_0_packed_bytes(-1, 64) == -1
     assert L.quantize_q4_0_weights(A, 4, 1000, A, None) == wsg.ERR_SHAPE
+    fn = L.gemv_q4_0_rmsnorm
+    assert fn(A, 64, 1000, A, None, None, 1e-6, None, A + 0x10000, None) == wsg.ERR_SHAPE
+    assert fn(A, 64, 1024, A, None, None, 0.0, None, A + 0x10000, None) == wsg.ERR_MODE

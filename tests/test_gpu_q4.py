@@ -12,6 +12,10 @@
   split over 1, 2 and 4 waves;
 * a 2-layer 27B-shaped 4-bit chain (deq 0 and deq 2) replays
   bit-identically to its eager calls and matches the oracle link by link;
+* the GEMV with the residual add + RMSNorm + re-quantization in its
+  prologue (gemv_q4_0_rmsnorm) equals the norm call followed by the GEMV,
+  bit for bit, and a 27B-shaped chain with the residual stream gives the
+  same buffers fused and unfused;
 * bad arguments are rejected."""
 import numpy as np
 import pytest
@@ -178,3 +182,96 @@ def test_q4_chain_27b_shapes(gpu_lib, deq):
                 y_ref, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
             assert_within(outs[i][rows], y_ref, oracle.q8_tolerance(den), f"layer {layer} W4 GEMV {j}")
     ts.close()
+
+
+@pytest.mark.parametrize("waves", [0, 4, 16])
+@pytest.mark.parametrize("n,k", [(300, 1024), (2051, 5120), (777, 12288), (129, 17408)])
+def test_q4_fused_norm_equals_norm_then_gemv(gpu_lib, n, k, waves):
+    """gemv_q4_0_rmsnorm: bit for bit residual_rmsnorm_q8_0 followed by
+    gemv_q4_0 on that call's codes, h_out included; the output within the
+    int8 path's bound of the oracle fed those codes."""
+    import torch
+    from gpu_util import split_act_q8
+    wsg = gpu_lib
+    eps = W.RMSNORM_EPS
+    wsg.tune(wsg.TUNE_WAVES, waves)
+    try:
+        w, packed, _ = _problem(n, k, 0x5EEDC200 + k)
+        h = synth.normal_f32(0x5EEDC200 + k, 3, k, 1.0)
+        r = synth.normal_f32(0x5EEDC200 + k, 4, k, 0.5)
+        g = (np.float32(1.0) + synth.normal_f32(0x5EEDC200 + k, 5, k, 0.1)).astype(np.float32)
+        hd, rd, gd = dev(h), dev(r), dev(g)
+        h_ref = torch.empty(k, dtype=torch.float32, device="cuda")
+        yq = empty_u8(wsg.act_q8_0_bytes(k))
+        wsg.residual_rmsnorm_q8_0(hd, rd, gd, k, eps, h_out=h_ref, y_q8=yq)
+        y_ref = torch.empty(n, dtype=torch.float32, device="cuda")
+        wsg.gemv_q4_0(packed, n, k, yq, wsg.ACT_Q8_0, y_ref)
+        y = torch.full((n,), np.nan, dtype=torch.float32, device="cuda")
+        h_out = torch.full((k,), np.nan, dtype=torch.float32, device="cuda")
+        wsg.gemv_q4_0_rmsnorm(packed, n, k, hd, rd, gd, eps, y, h_out=h_out)
+        got = host(y)
+        assert np.array_equal(got.view(np.uint32), host(y_ref).view(np.uint32)), "fused differs from norm + GEMV"
+        assert np.array_equal(host(h_out).view(np.uint32), host(h_ref).view(np.uint32)), "h' differs"
+        dx, qx = split_act_q8(host(yq), k)
+        dw, qw = oracle.quantize_q4_0(w)
+        y_or, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
+        assert_within(got, y_or, oracle.q8_tolerance(den), f"W4 fused norm {n}x{k}")
+    finally:
+        wsg.tune(wsg.TUNE_WAVES, 0)
+
+
+def test_q4_fused_norm_rejects_racy_buffers(gpu_lib):
+    import torch
+    wsg = gpu_lib
+    n, k = 256, 1024
+    _, packed, _ = _problem(n, k, 0x5EEDC300)
+    buf = torch.zeros(4 * k, dtype=torch.float32, device="cuda")
+    hd, rd, gd = buf[:k], buf[k:2 * k], buf[2 * k:3 * k]
+    y = torch.empty(n, dtype=torch.float32, device="cuda")
+    for h_out, yy in ((hd, y), (rd, y), (buf[3 * k:], hd)):
+        with pytest.raises(wsg.WsgError) as e:
+            wsg.gemv_q4_0_rmsnorm(packed, n, k, hd, rd, gd, W.RMSNORM_EPS, yy, h_out=h_out)
+        assert e.value.status == wsg.ERR_MODE
+
+
+def test_q4_fused_chain_equals_unfused_chain(gpu_lib):
+    """A 2-layer 27B-shaped 4-bit chain carrying the residual stream (norm
+    before GEMVs 0 and 2): fused and unfused give the same buffers, and
+    each graph replay equals its eager calls."""
+    import torch
+
+    from weight_streaming_gemv_q8_amd.stream import TokenStream
+    wl = W.DENSE27B_Q8
+    layers = 2
+    shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
+    got = {}
+    for fused in (False, True):
+        ts = TokenStream(shapes, layers, "q4_0", deq=0, norm_before=(0, 2), eps=W.RMSNORM_EPS, fused_norm=fused)
+
+        def fill(layer, m, part, rows, staging):
+            synth.dev_normal_f32(staging.data_ptr(), wl.seed, W.weight_tensor_id(layer, m, part),
+                                 rows * wl.matrices[m].k, W.WEIGHT_SIGMA,
+                                 stream=torch.cuda.current_stream().cuda_stream)
+
+        ts.fill_weights(fill)
+        hidden = ts.hidden
+        h0 = synth.normal_f32(wl.seed, W.RESIDUAL_TENSOR_ID, hidden, 1.0)
+        gains = np.stack([np.float32(1.0) + synth.normal_f32(wl.seed, W.gain_tensor_id(i), hidden, W.GAIN_SIGMA)
+                          for i in range(len(ts.norms))]).astype(np.float32)
+        ts.set_residual_input(torch.from_numpy(h0).cuda(), torch.from_numpy(gains).cuda())
+        bufs = [s.y for s in ts.slots] + [n.h_out for n in ts.norms]
+        ts.run_eager()
+        eager = [host(b).view(np.uint32).copy() for b in bufs]
+        for b in bufs:
+            b.fill_(np.nan)
+        plan = ts.capture()
+        assert plan.kernel_count == len(ts.slots) + (0 if fused else len(ts.norms))
+        ts.launch()
+        rep = [host(b).view(np.uint32).copy() for b in bufs]
+        assert all(np.array_equal(a, b) for a, b in zip(eager, rep)), "replay differs from eager"
+        got[fused] = eager
+        ts.close()
+        del ts
+        torch.cuda.empty_cache()
+    for i, (a, b) in enumerate(zip(got[False], got[True])):
+        assert np.array_equal(a, b), f"buffer {i}: fused chain differs from the unfused chain"

@@ -250,9 +250,12 @@ struct Q4Regs {
 
 constexpr int kRingQ4 = 3;
 
-template <int WAVES, int S, int ACT>
-__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
-q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict__ xin, float* __restrict__ y) {
+// `stage` fills the activation's LDS layout as in q8_i8_body: a staged
+// int8 input (StageInput) or the residual add + RMSNorm + re-quantization
+// (StageNorm).
+template <int WAVES, int S, typename Stage>
+__device__ __attribute__((always_inline)) inline void q4_i8_body(const uint8_t* __restrict__ W, int n, int k,
+                                                                 float* __restrict__ y, Stage& stage) {
     static_assert(WAVES % S == 0, "S must divide WAVES");
     extern __shared__ __align__(16) uint8_t smem[];
     const int C = (int)chunk_count(k);
@@ -317,7 +320,6 @@ q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
         load_rc(r, has_item ? sc.row(it.j) : sc.n, has_item ? it.p + S * it.m : C);
     };
     Q4Regs R[kRingQ4];
-    StageInput<ACT> stage{xin, k, C, {}};
     stage.issue();
     __builtin_amdgcn_sched_barrier(0);
     if (rot)
@@ -366,6 +368,24 @@ q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
     ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool) {
         finish_row<WAVES, S, false>(acc, row, n, lane, wave, lds_part, y, best);
     });
+}
+
+template <int WAVES, int S, int ACT>
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict__ xin, float* __restrict__ y) {
+    StageInput<ACT> stage{xin, k, (int)chunk_count(k), {}};
+    q4_i8_body<WAVES, S>(W, n, k, y, stage);
+}
+
+// The W4 GEMV fed by the residual add + RMSNorm + re-quantization of
+// residual_rmsnorm_q8_0, computed by every workgroup in its prologue, as
+// q8_i8_norm_kernel does for Q8_0 weights: the same codes and scales, bit
+// for bit.
+template <int WAVES, int S>
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+q4_i8_norm_kernel(const uint8_t* __restrict__ W, int n, int k, NormArgs na, float* __restrict__ y) {
+    StageNorm<WAVES * kWave> stage{na, k, {}};
+    q4_i8_body<WAVES, S>(W, n, k, y, stage);
 }
 
 // The W4 GEMV with f32 activations (the W4A16 form of qwen3-8b-rtx4080-
@@ -930,6 +950,20 @@ int launch_q8_norm(const void* w, int n, int k, const NormArgs& na, float* y, hi
     });
 }
 
+// The W4 GEMV with the norm prologue: the W4 launch choice.
+int launch_q4_norm(const void* w, int n, int k, const NormArgs& na, float* y, hipStream_t stream, LaunchInfo* info,
+                   bool run = true) {
+    const Cfg c = choose_cfg(kPathQ4, n, k);
+    const size_t lds = lds_q8act_bytes((int)chunk_count(k));
+    const size_t lds_sx8 = chunk_count(k) * kWave * 4;
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
+        constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
+        auto kern = q4_i8_norm_kernel<Wv, Sv>;
+        return launch_kernel<Wv, Sv>(kern, q8_lds_bytes<Wv>(lds) + lds_sx8, n, info, 1, run, stream, wp, n, k, na, y);
+    });
+}
+
 // The W4 GEMV: its own waves and split choice (choose_cfg).
 int launch_q4(const void* w, int n, int k, const void* x, int act_fmt, float* y, hipStream_t stream, LaunchInfo* info,
               bool run = true) {
@@ -1150,6 +1184,14 @@ int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h
     const int rc = validate_gemv_q8_rmsnorm(w_packed, n, k, h, r, g, eps, h_out, y);
     if (rc != WSG_OK) return rc;
     return launch_q8_norm(w_packed, (int)n, (int)k, NormArgs{h, r, g, h_out, eps}, y, stream, nullptr);
+}
+
+int gemv_q4_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r, const float* g,
+                      float eps, float* h_out, float* y, hipStream_t stream) {
+    // the same arguments and races as the Q8_0 form; only the weights differ
+    const int rc = validate_gemv_q8_rmsnorm(w_packed, n, k, h, r, g, eps, h_out, y);
+    if (rc != WSG_OK) return rc;
+    return launch_q4_norm(w_packed, (int)n, (int)k, NormArgs{h, r, g, h_out, eps}, y, stream, nullptr);
 }
 
 int gemv_q4_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act_fmt, float* y, hipStream_t stream) {

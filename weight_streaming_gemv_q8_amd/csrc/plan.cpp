@@ -69,6 +69,10 @@ int validate_op(const wsg_op_desc& d) {
             return wsg::validate_token_advance(static_cast<const int32_t*>(d.x), d.idx_out, d.n,
                                                static_cast<const int32_t*>(d.ws));
         case WSG_OP_GEMV_Q4_0: return wsg::validate_gemv_q4(d.w, d.n, d.k, d.x, d.act_fmt, d.y);
+        case WSG_OP_GEMV_Q4_0_RMSNORM:
+            return wsg::validate_gemv_q8_rmsnorm(d.w, d.n, d.k, static_cast<const float*>(d.x),
+                                                 static_cast<const float*>(d.r), static_cast<const float*>(d.g),
+                                                 d.eps, d.h_out, d.y);
         default: return WSG_ERR_MODE;
     }
 }
@@ -100,6 +104,10 @@ int enqueue_op(const wsg_op_desc& d, hipStream_t s) {
         case WSG_OP_TOKEN_ADVANCE:
             return token_advance(static_cast<const int32_t*>(d.x), d.idx_out, d.n, static_cast<int32_t*>(d.ws), s);
         case WSG_OP_GEMV_Q4_0: return gemv_q4_0(d.w, d.n, d.k, d.x, d.act_fmt, static_cast<float*>(d.y), s);
+        case WSG_OP_GEMV_Q4_0_RMSNORM:
+            return gemv_q4_0_rmsnorm(d.w, d.n, d.k, static_cast<const float*>(d.x), static_cast<const float*>(d.r),
+                                     static_cast<const float*>(d.g), d.eps, static_cast<float*>(d.h_out),
+                                     static_cast<float*>(d.y), s);
         default: return WSG_ERR_MODE;
     }
 }

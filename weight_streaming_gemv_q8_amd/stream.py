@@ -86,7 +86,7 @@ class TokenStream:
             are the gate, the rest the up projection; gemv_q8_0_swiglu),
             so the next GEMV reads n/2 products.  Q8_0 chains with int8
             activations; not with fused_norm.
-    fused_norm: with norm_before on a Q8_0 chain with int8 activations, each
+    fused_norm: with norm_before on a Q8_0 or q4_0 chain with int8 activations, each
             normalized GEMV computes the residual add + RMSNorm itself
             (gemv_q8_0_rmsnorm) instead of after a separate norm call; the
             results are the same bit for bit (the f32 normalized vectors
@@ -100,8 +100,9 @@ class TokenStream:
                  swiglu_at: Sequence[int] = ()):
         if wtype not in ("q8_0", "q4_0", "bf16"):
             raise ValueError("wtype must be q8_0, q4_0 or bf16")
-        if wtype == "q4_0" and (requant != "fused" or norm_before or swiglu_at):
-            raise ValueError("q4_0 chains run f32 activations (deq 2) or int8 ones requantized in each GEMV")
+        if wtype == "q4_0" and (requant != "fused" or swiglu_at or (norm_before and deq == 2)):
+            raise ValueError("q4_0 chains run f32 activations (deq 2) or int8 ones requantized in each GEMV "
+                             "or by the norm step")
         if requant not in ("fused", "separate"):
             raise ValueError("requant must be fused or separate")
         self.shapes = [(int(n), int(k), tuple(p)) for n, k, p in shapes]
@@ -143,8 +144,8 @@ class TokenStream:
         self.norm_before = tuple(sorted(set(int(j) for j in norm_before)))
         self.eps = float(eps)
         self.fused_norm = bool(fused_norm)
-        if self.fused_norm and (wtype != "q8_0" or deq == 2 or not self.norm_before):
-            raise ValueError("fused_norm needs a Q8_0 chain with int8 activations and norm_before")
+        if self.fused_norm and (wtype == "bf16" or deq == 2 or not self.norm_before):
+            raise ValueError("fused_norm needs a Q8_0 or q4_0 chain with int8 activations and norm_before")
         self.norms: List[NormSlot] = []
         self.h0 = None
         self.gains = None
@@ -170,7 +171,7 @@ class TokenStream:
         self.h0 = torch.zeros(hidden, dtype=torch.float32, device=device)
         count = self.layers * len(self.norm_before)
         self.gains = torch.ones((count, hidden), dtype=torch.float32, device=device)
-        int8 = self.wtype == "q8_0" and self.act_fmt() != wsg.ACT_F32
+        int8 = self.wtype in ("q8_0", "q4_0") and self.act_fmt() != wsg.ACT_F32
         h_in = self.h0.data_ptr()
         for i, s in enumerate(self.slots):
             if s.index not in self.norm_before:
@@ -260,13 +261,15 @@ class TokenStream:
         pre = []
         if s.norm is not None and self.fused_norm:
             n = s.norm
-            return [wsg.op_gemv_q8_0_rmsnorm(w, s.n, s.k, n.h_in, n.r or None, n.g, self.eps, s.y, h_out=n.h_out)]
+            op = wsg.op_gemv_q4_0_rmsnorm if self.wtype == "q4_0" else wsg.op_gemv_q8_0_rmsnorm
+            return [op(w, s.n, s.k, n.h_in, n.r or None, n.g, self.eps, s.y, h_out=n.h_out)]
         if s.norm is not None:
             n = s.norm
             pre = [wsg.op_residual_rmsnorm(n.h_in, n.r or None, n.g, self.hidden, self.eps, h_out=n.h_out,
                                            y=n.y, y_q8=n.yq)]
             if n.yq is not None:
-                return pre + [wsg.op_gemv_q8_0(w, s.n, s.k, n.yq, wsg.ACT_Q8_0, s.y)]
+                gemv = wsg.op_gemv_q4_0 if self.wtype == "q4_0" else wsg.op_gemv_q8_0
+                return pre + [gemv(w, s.n, s.k, n.yq, wsg.ACT_Q8_0, s.y)]
         if self.wtype == "bf16":
             return pre + [wsg.op_gemv_bf16(w, s.n, s.k, s.x_ptr, s.y)]
         if self.wtype == "q4_0":
@@ -307,9 +310,9 @@ class TokenStream:
                 wsg.gemv_q4_0(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
             elif op.op == wsg.OP_GEMV_Q8_0_SWIGLU:
                 wsg.gemv_q8_0_swiglu(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
-            elif op.op == wsg.OP_GEMV_Q8_0_RMSNORM:
-                wsg.gemv_q8_0_rmsnorm(op.w, op.n, op.k, op.x, op.r, op.g, op.eps, op.y, h_out=op.h_out,
-                                      stream=stream)
+            elif op.op in (wsg.OP_GEMV_Q8_0_RMSNORM, wsg.OP_GEMV_Q4_0_RMSNORM):
+                f = wsg.gemv_q8_0_rmsnorm if op.op == wsg.OP_GEMV_Q8_0_RMSNORM else wsg.gemv_q4_0_rmsnorm
+                f(op.w, op.n, op.k, op.x, op.r, op.g, op.eps, op.y, h_out=op.h_out, stream=stream)
             else:
                 wsg.gemv_q8_0(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
 
