@@ -201,6 +201,14 @@ int gemv_q4_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act
 int gemv_q4_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r, const float* g,
                       float eps, float* h_out, float* y, hipStream_t stream);
 
+/* gemv_q4_0_swiglu: the 4-bit gate+up GEMV with the SwiGLU epilogue (GPU
+ * Kernel Lab, "What we built", "Decode integration", on 4-bit weights):
+ * w_packed holds 2 n_ff rows in the 4-bit layout, gate rows first;
+ * y[p] = silu(g_p) u_p with g_p, u_p the int8-path outputs of rows p and
+ * n_ff + p.  Arguments, acceptance and errors as gemv_q8_0_swiglu. */
+int gemv_q4_0_swiglu(const void* w_packed, int64_t n_ff, int64_t k, const void* x, int act_fmt, float* y,
+                     hipStream_t stream);
+
 /* The gate+up GEMV with its SwiGLU epilogue (GPU Kernel Lab, "What we
  * built", "Decode integration": the dual gate/up projection fused with
  * SwiGLU at batch 1):
@@ -309,6 +317,7 @@ enum {
     WSG_OP_TOKEN_ADVANCE = 8,     /* token_advance: x = token, idx_out = history, n = capacity, ws = pos */
     WSG_OP_GEMV_Q4_0 = 9,         /* gemv_q4_0: w, n, k, x, act_fmt, y */
     WSG_OP_GEMV_Q4_0_RMSNORM = 10, /* gemv_q4_0_rmsnorm: w, n, k, x = h, r, g, eps, h_out, y */
+    WSG_OP_GEMV_Q4_0_SWIGLU = 11, /* gemv_q4_0_swiglu: w, n = n_ff, k, x, act_fmt, y */
 };
 
 /* flags: WSG_OP_AFTER_ALL marks an op that depends on every earlier op of

@@ -130,7 +130,7 @@ def test_plan_rejects_bad_descriptors_before_capture(L):
     with pytest.raises(wsg.WsgError) as e:
         wsg.Plan(ops, stream=0)
     assert e.value.status == wsg.ERR_SHAPE
-    ops = [wsg.OpDesc(op=wsg.OP_GEMV_Q4_0_RMSNORM + 1)]
+    ops = [wsg.OpDesc(op=wsg.OP_GEMV_Q4_0_SWIGLU + 1)]
     with pytest.raises(wsg.WsgError) as e:
         wsg.Plan(ops, stream=0)
     assert e.value.status == wsg.ERR_MODE
@@ -227,3 +227,7 @@ def test_w4_entry_points_reject_before_launch(L):
     fn = L.gemv_q4_0_rmsnorm
     assert fn(A, 64, 1000, A, None, None, 1e-6, None, A + 0x10000, None) == wsg.ERR_SHAPE
     assert fn(A, 64, 1024, A, None, None, 0.0, None, A + 0x10000, None) == wsg.ERR_MODE
+    fs = L.gemv_q4_0_swiglu
+    assert fs(A, 64, 1024, A, wsg.ACT_F32, A + 0x10000, None) == wsg.ERR_MODE
+    assert fs(A, 64, 1000, A, wsg.ACT_Q8_0, A + 0x10000, None) == wsg.ERR_SHAPE
+    assert fs(A, 64, 1024, None, wsg.ACT_Q8_0, A + 0x10000, None) == wsg.ERR_NULL

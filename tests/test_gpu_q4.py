@@ -16,6 +16,8 @@
   prologue (gemv_q4_0_rmsnorm) equals the norm call followed by the GEMV,
   bit for bit, and a 27B-shaped chain with the residual stream gives the
   same buffers fused and unfused;
+* the gate+up GEMV with the SwiGLU epilogue (gemv_q4_0_swiglu) matches
+  the plain GEMV's halves and the oracle, alone and in a chain;
 * bad arguments are rejected."""
 import numpy as np
 import pytest
@@ -275,3 +277,123 @@ def test_q4_fused_chain_equals_unfused_chain(gpu_lib):
         torch.cuda.empty_cache()
     for i, (a, b) in enumerate(zip(got[False], got[True])):
         assert np.array_equal(a, b), f"buffer {i}: fused chain differs from the unfused chain"
+
+
+def _w_rows(wl, layer, j, rows):
+    m = wl.matrices[j]
+    out = []
+    for r in rows:
+        part, base = 0, 0
+        while r >= base + m.parts[part]:
+            base += m.parts[part]
+            part += 1
+        out.append(synth.normal_f32(wl.seed, W.weight_tensor_id(layer, j, part), m.k, W.WEIGHT_SIGMA,
+                                    first=(int(r) - base) * m.k))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("waves", [0, 4])
+@pytest.mark.parametrize("act", ["requant", "q8"])
+@pytest.mark.parametrize("n_ff,k", [(17408, 5120), (1000, 2080), (33, 96), (1, 32)])
+def test_q4_swiglu_gemv(gpu_lib, n_ff, k, act, waves):
+    """gemv_q4_0_swiglu: silu(g) u of the plain 4-bit GEMV's own halves
+    within the epilogue's rounding, and the oracle (both halves in fp64,
+    then SwiGLU) within the two GEMV bounds carried through the product."""
+    import torch
+    wsg = gpu_lib
+    if waves and (n_ff, k) != (1000, 2080):
+        pytest.skip("workgroup sizes are swept on one ragged shape")
+    wsg.tune(wsg.TUNE_WAVES, waves)
+    try:
+        w, packed, x = _problem(2 * n_ff, k, 0x5EEDC400 + n_ff + k)
+        xd = dev(x)
+        if act == "q8":
+            xq = empty_u8(wsg.act_q8_0_bytes(k))
+            wsg.quantize_act_q8_0(xd, k, xq)
+            xin, fmt = xq, wsg.ACT_Q8_0
+        else:
+            xin, fmt = xd, wsg.ACT_F32_REQUANT
+        y = torch.full((n_ff,), np.nan, dtype=torch.float32, device="cuda")
+        wsg.gemv_q4_0_swiglu(packed, n_ff, k, xin, fmt, y)
+        full = torch.empty(2 * n_ff, dtype=torch.float32, device="cuda")
+        wsg.gemv_q4_0(packed, 2 * n_ff, k, xin, fmt, full)
+        got, gu = host(y).astype(np.float64), host(full).astype(np.float64)
+        g, u = gu[:n_ff], gu[n_ff:]
+        assert np.all(np.abs(got - oracle.swiglu(g, u)) <= oracle.swiglu_tolerance(g, u, 0.0, 0.0)), \
+            "epilogue of the plain GEMV's halves"
+        dw, qw = oracle.quantize_q4_0(w)
+        dx, qx = oracle.quantize_q8_0(x)
+        yr, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
+        t = oracle.q8_tolerance(den)
+        tol = oracle.swiglu_tolerance(yr[:n_ff], yr[n_ff:], t[:n_ff], t[n_ff:])
+        assert_within(got, oracle.swiglu(yr[:n_ff], yr[n_ff:]), tol, f"W4 swiglu {n_ff}x{k} {act}")
+    finally:
+        wsg.tune(wsg.TUNE_WAVES, 0)
+
+
+def test_q4_swiglu_rejections(gpu_lib):
+    import torch
+    wsg = gpu_lib
+    _, packed, x = _problem(128, 1024, 0x5EEDC500)
+    y = torch.empty(64, dtype=torch.float32, device="cuda")
+    with pytest.raises(wsg.WsgError) as e:
+        wsg.gemv_q4_0_swiglu(packed, 64, 1024, dev(x), wsg.ACT_F32, y)
+    assert e.value.status == wsg.ERR_MODE
+    for n_ff, k in ((0, 1024), (64, 1000)):
+        with pytest.raises(wsg.WsgError) as e:
+            wsg.gemv_q4_0_swiglu(packed, n_ff, k, dev(x), wsg.ACT_F32_REQUANT, y)
+        assert e.value.status == wsg.ERR_SHAPE
+
+
+def test_q4_swiglu_chain_27b_shapes(gpu_lib):
+    """A 2-layer 27B-shaped 4-bit chain whose down projection reads the
+    SwiGLU outputs: replays equal the eager calls; the SwiGLU link and the
+    down projection match the oracle fed the GPU's own inputs."""
+    import torch
+
+    from weight_streaming_gemv_q8_amd.stream import TokenStream
+    wl = W.DENSE27B_Q8
+    layers = 2
+    shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
+    ts = TokenStream(shapes, layers, "q4_0", deq=0, swiglu_at=(2,))
+
+    def fill(layer, m, part, rows, staging):
+        synth.dev_normal_f32(staging.data_ptr(), wl.seed, W.weight_tensor_id(layer, m, part),
+                             rows * wl.matrices[m].k, W.WEIGHT_SIGMA, stream=torch.cuda.current_stream().cuda_stream)
+
+    ts.fill_weights(fill)
+    xs = np.stack([synth.activation(wl.seed, W.activation_tensor_id(l), shapes[0][1], rms=True)
+                   for l in range(layers)])
+    ts.set_inputs(torch.from_numpy(xs).cuda())
+    ts.run_eager()
+    eager = [host(y).view(np.uint32).copy() for y in ts.outputs()]
+    for y in ts.outputs():
+        y.fill_(np.nan)
+    plan = ts.capture()
+    assert plan.kernel_count == len(ts.slots)
+    ts.launch()
+    got = [host(y).view(np.uint32).copy() for y in ts.outputs()]
+    assert all(np.array_equal(a, b) for a, b in zip(eager, got)), "replay differs from eager"
+    outs = [a.view(np.float32) for a in eager]
+    rng = np.random.default_rng(0xC5)
+    for layer in range(layers):
+        for j in (2, 3):
+            m = wl.matrices[j]
+            i = layer * len(wl.matrices) + j
+            dx, qx = oracle.quantize_q8_0(np.ascontiguousarray(outs[i - 1][:m.k], np.float32))
+            if j == 2:
+                nff = m.n // 2
+                rows = np.array(sorted(set(int(v) for v in rng.integers(0, nff, 32)) | {0, nff - 1}))
+                dw, qw = oracle.quantize_q4_0(_w_rows(wl, layer, j, np.concatenate([rows, rows + nff])))
+                yr, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
+                t = oracle.q8_tolerance(den)
+                h = len(rows)
+                tol = oracle.swiglu_tolerance(yr[:h], yr[h:], t[:h], t[h:])
+                assert_within(outs[i][rows].astype(np.float64), oracle.swiglu(yr[:h], yr[h:]), tol,
+                              f"layer {layer} W4 gate+up SwiGLU")
+            else:
+                rows = np.array(sorted(set(int(v) for v in rng.integers(0, m.n, 32)) | {0, m.n - 1}))
+                dw, qw = oracle.quantize_q4_0(_w_rows(wl, layer, j, rows))
+                yr, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
+                assert_within(outs[i][rows], yr, oracle.q8_tolerance(den), f"layer {layer} W4 down")
+    ts.close()

@@ -28,7 +28,8 @@ ACT_Q8_0, ACT_F32, ACT_F32_REQUANT = 0, 1, 2
 W_BF16, W_Q8_0 = 0, 1
 # plan ops
 (OP_GEMV_BF16, OP_GEMV_Q8_0, OP_QUANTIZE_ACT, OP_LM_HEAD_ARGMAX, OP_RESIDUAL_RMSNORM, OP_GEMV_Q8_0_RMSNORM,
- OP_GEMV_Q8_0_SWIGLU, OP_EMBED_GATHER, OP_TOKEN_ADVANCE, OP_GEMV_Q4_0, OP_GEMV_Q4_0_RMSNORM) = range(11)
+ OP_GEMV_Q8_0_SWIGLU, OP_EMBED_GATHER, OP_TOKEN_ADVANCE, OP_GEMV_Q4_0, OP_GEMV_Q4_0_RMSNORM,
+ OP_GEMV_Q4_0_SWIGLU) = range(12)
 OP_AFTER_ALL = 1  # OpDesc.flags: depends on every earlier op of the plan
 
 MAX_K_Q8ACT = 57344
@@ -39,7 +40,7 @@ EXPORTS = (
     "wsg_status_str", "wsg_version", "q8_0_row_bytes", "q8_0_packed_bytes", "pack_q8_0",
     "quantize_q8_0_weights", "convert_bf16", "act_q8_0_bytes", "quantize_act_q8_0",
     "residual_rmsnorm_q8_0", "embed_gather", "token_advance", "q4_0_row_bytes", "q4_0_packed_bytes",
-    "quantize_q4_0_weights", "gemv_q4_0", "gemv_q4_0_rmsnorm", "gemv_q8_0_rmsnorm", "gemv_q8_0_swiglu",
+    "quantize_q4_0_weights", "gemv_q4_0", "gemv_q4_0_rmsnorm", "gemv_q4_0_swiglu", "gemv_q8_0_rmsnorm", "gemv_q8_0_swiglu",
     "gemv_bf16",
     "gemv_q8_0", "wsg_gemv_config", "wsg_tune", "wsg_argmax_ws_bytes", "lm_head_argmax", "argmax_f32", "wsg_plan_create",
     "wsg_plan_launch", "wsg_plan_create_persistent", "wsg_plan_create_ring", "wsg_ring_shape", "wsg_plan_error", "wsg_plan_error_detail", "wsg_plan_destroy", "wsg_plan_kernel_count",
@@ -92,6 +93,7 @@ def lib():
             "gemv_q8_0_rmsnorm": (i32, [vp, i64, i64, vp, vp, vp, ctypes.c_float, vp, vp, vp]),
             "gemv_q4_0_rmsnorm": (i32, [vp, i64, i64, vp, vp, vp, ctypes.c_float, vp, vp, vp]),
             "gemv_q8_0_swiglu": (i32, [vp, i64, i64, vp, i32, vp, vp]),
+            "gemv_q4_0_swiglu": (i32, [vp, i64, i64, vp, i32, vp, vp]),
             "embed_gather": (i32, [vp, i32, i64, i64, vp, vp, vp]),
             "q4_0_row_bytes": (i64, [i64]),
             "q4_0_packed_bytes": (i64, [i64, i64]),
@@ -253,6 +255,12 @@ def gemv_q8_0_swiglu(w_packed, n_ff: int, k: int, x, act_fmt: int, y, stream=Non
                                                       _stream(stream)))
 
 
+def gemv_q4_0_swiglu(w_packed, n_ff: int, k: int, x, act_fmt: int, y, stream=None) -> None:
+    """gemv_q8_0_swiglu on a gate+up matrix in the 4-bit layout."""
+    _check("gemv_q4_0_swiglu", lib().gemv_q4_0_swiglu(_ptr(w_packed), n_ff, k, _ptr(x), act_fmt, _ptr(y),
+                                                      _stream(stream)))
+
+
 # ------------------------------------------------------------------ GEMV
 
 def gemv_bf16(w, n: int, k: int, x, y, stream=None) -> None:
@@ -323,6 +331,10 @@ def op_gemv_q8_0_rmsnorm(w, n, k, h, r, g, eps, y, h_out=None) -> OpDesc:
 def op_gemv_q8_0_swiglu(w, n_ff, k, x, act_fmt, y) -> OpDesc:
     return OpDesc(op=OP_GEMV_Q8_0_SWIGLU, w_type=W_Q8_0, act_fmt=act_fmt, n=n_ff, k=k, w=_ptr(w), x=_ptr(x),
                   y=_ptr(y))
+
+
+def op_gemv_q4_0_swiglu(w, n_ff, k, x, act_fmt, y) -> OpDesc:
+    return OpDesc(op=OP_GEMV_Q4_0_SWIGLU, act_fmt=act_fmt, n=n_ff, k=k, w=_ptr(w), x=_ptr(x), y=_ptr(y))
 
 
 def op_gemv_q4_0(w, n, k, x, act_fmt, y) -> OpDesc:

@@ -250,6 +250,44 @@ struct Q4Regs {
 
 constexpr int kRingQ4 = 3;
 
+// sum_i q_w,i q_x,i of block c * 64 + lane: the nibbles n = q_w + 8 dotted
+// with the staged int8 codes, less the block's 8 sum x from LDS (exact).
+__device__ inline int q4_block_dot(const Q4Regs& r, int c, int lane, const int4v* lds_q, const int* lds_sx8) {
+    const int4v xa = lds_q[(c * 2 + 0) * kWave + lane];
+    const int4v xb = lds_q[(c * 2 + 1) * kWave + lane];
+    int4v wa = r.a;
+    opaque(wa);
+    const uint32_t w4[4] = {(uint32_t)wa.x, (uint32_t)wa.y, (uint32_t)wa.z, (uint32_t)wa.w};
+    const int x4a[4] = {xa.x, xa.y, xa.z, xa.w}, x4b[4] = {xb.x, xb.y, xb.z, xb.w};
+    int dn = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        dn = __builtin_amdgcn_sdot4((int)(w4[q] & 0x0F0F0F0Fu), x4a[q], dn, false);
+        dn = __builtin_amdgcn_sdot4((int)((w4[q] >> 4) & 0x0F0F0F0Fu), x4b[q], dn, false);
+    }
+    return dn - lds_sx8[c * kWave + lane];
+}
+
+// 8 sum x of every staged block (block c * 64 + l: words (2c) * 64 + l and
+// (2c + 1) * 64 + l of lds_q), by the T threads of the workgroup.
+template <int T>
+__device__ inline void q4_block_sums(const int4v* lds_q, int* lds_sx8, int C) {
+    for (int b = threadIdx.x; b < C * kWave; b += T) {
+        const int4v xa = lds_q[(b / kWave * 2) * kWave + b % kWave];
+        const int4v xb = lds_q[(b / kWave * 2 + 1) * kWave + b % kWave];
+        int sx = 0;
+        sx = __builtin_amdgcn_sdot4(0x01010101, xa.x, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xa.y, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xa.z, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xa.w, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xb.x, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xb.y, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xb.z, sx, false);
+        sx = __builtin_amdgcn_sdot4(0x01010101, xb.w, sx, false);
+        lds_sx8[b] = 8 * sx;
+    }
+}
+
 // `stage` fills the activation's LDS layout as in q8_i8_body: a staged
 // int8 input (StageInput) or the residual add + RMSNorm + re-quantization
 // (StageNorm).
@@ -287,19 +325,7 @@ __device__ __attribute__((always_inline)) inline void q4_i8_body(const uint8_t* 
     auto compute_c = [&](const Q4Regs& r, int c, float& acc) {
         const int blk = c * kWave + lane;
         if (blk < NB) {
-            const int4v xa = lds_q[(c * 2 + 0) * kWave + lane];
-            const int4v xb = lds_q[(c * 2 + 1) * kWave + lane];
-            int4v wa = r.a;
-            opaque(wa);
-            const uint32_t w4[4] = {(uint32_t)wa.x, (uint32_t)wa.y, (uint32_t)wa.z, (uint32_t)wa.w};
-            const int x4a[4] = {xa.x, xa.y, xa.z, xa.w}, x4b[4] = {xb.x, xb.y, xb.z, xb.w};
-            int dn = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                dn = __builtin_amdgcn_sdot4((int)(w4[q] & 0x0F0F0F0Fu), x4a[q], dn, false);
-                dn = __builtin_amdgcn_sdot4((int)((w4[q] >> 4) & 0x0F0F0F0Fu), x4b[q], dn, false);
-            }
-            const int s = dn - lds_sx8[blk];
+            const int s = q4_block_dot(r, c, lane, lds_q, lds_sx8);
             const float t = half_bits_to_float(r.sc) * lds_dx[blk];
             acc = __builtin_fmaf(t, (float)s, acc);
         }
@@ -329,22 +355,7 @@ __device__ __attribute__((always_inline)) inline void q4_i8_body(const uint8_t* 
     __builtin_amdgcn_sched_barrier(0);
     stage.commit(lds_q, lds_dx, lds_res);
     __syncthreads();
-    // 8 sum x of every staged block (block c * 64 + l: words (2c) * 64 + l
-    // and (2c + 1) * 64 + l of lds_q)
-    for (int b = threadIdx.x; b < C * kWave; b += WAVES * kWave) {
-        const int4v xa = lds_q[(b / kWave * 2) * kWave + b % kWave];
-        const int4v xb = lds_q[(b / kWave * 2 + 1) * kWave + b % kWave];
-        int sx = 0;
-        sx = __builtin_amdgcn_sdot4(0x01010101, xa.x, sx, false);
-        sx = __builtin_amdgcn_sdot4(0x01010101, xa.y, sx, false);
-        sx = __builtin_amdgcn_sdot4(0x01010101, xa.z, sx, false);
-        sx = __builtin_amdgcn_sdot4(0x01010101, xa.w, sx, false);
-        sx = __builtin_amdgcn_sdot4(0x01010101, xb.x, sx, false);
-        sx = __builtin_amdgcn_sdot4(0x01010101, xb.y, sx, false);
-        sx = __builtin_amdgcn_sdot4(0x01010101, xb.z, sx, false);
-        sx = __builtin_amdgcn_sdot4(0x01010101, xb.w, sx, false);
-        lds_sx8[b] = 8 * sx;
-    }
+    q4_block_sums<WAVES * kWave>(lds_q, lds_sx8, C);
     __syncthreads();
     if constexpr (kRot) {
         if (rot) {
@@ -386,6 +397,77 @@ __global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per
 q4_i8_norm_kernel(const uint8_t* __restrict__ W, int n, int k, NormArgs na, float* __restrict__ y) {
     StageNorm<WAVES * kWave> stage{na, k, {}};
     q4_i8_body<WAVES, S>(W, n, k, y, stage);
+}
+
+// The 4-bit gate+up GEMV with the SwiGLU epilogue: q8_i8_swiglu_kernel's
+// schedule (each wave walks the gate chunks then the up chunks of one
+// output, one accumulator per half) with the 4-bit item and block dot.
+template <int WAVES, int ACT>
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+q4_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* __restrict__ xin,
+                    float* __restrict__ y) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int C = (int)chunk_count(k);
+    const int NB = k / kBlock;
+    const int nl = NB - (C - 1) * kChunkBlocks;
+    const int sbl = (int)scale_section_bytes(nl);
+    const int64_t row_bytes = q4_row_bytes(k);
+    int4v* lds_q = reinterpret_cast<int4v*>(smem);
+    float* lds_dx = reinterpret_cast<float*>(smem + (size_t)C * 2 * kWave * 16);
+    float* lds_res = reinterpret_cast<float*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>());
+    int* lds_sx8 = reinterpret_cast<int*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>() +
+                                          lds_keep_bytes<WAVES>());
+    const int lane = threadIdx.x % kWave;
+    const Sched sc(2 * C, 1, 1, WAVES, n_ff, (n_ff + WAVES - 1) / WAVES);
+    const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
+    // item m of output p: chunk m of gate row p (m < C) or chunk m - C of up
+    // row n_ff + p; past the schedule the idle region
+    auto load = [&](Q4Regs& r, const ItemCursor& it) {
+        const int p = it.j < sc.tiles_wg ? sc.row(it.j) : sc.n;
+        const int m = sc.chunk(it.m, 0);
+        const bool up = m >= C;
+        const int c = up ? m - C : m;
+        const bool real = p < sc.n && m < 2 * C;
+        const bool last = c == C - 1;
+        const int nbc = last ? nl : kChunkBlocks;
+        const int sb = last ? sbl : 2 * kChunkBlocks;
+        const int l = lane < nbc ? lane : nbc - 1;
+        const int64_t row = real ? (int64_t)p + (up ? n_ff : 0) : 0;
+        const gptr<uint8_t> cp = real ? Wg + row * row_bytes + (int64_t)c * kFullChunkBytesQ4 : idle_bytes();
+        r.sc = load_u16<true>(cp + 2 * l);
+        r.a = load16<true>(cp + sb + 16 * l);
+    };
+    float acc_up = 0.0f;
+    auto compute = [&](const Q4Regs& r, int, int m, float& acc_gate) {
+        const bool up = m >= C;
+        const int c = up ? m - C : m;
+        const int blk = c * kWave + lane;
+        if (blk < NB) {
+            const int s = q4_block_dot(r, c, lane, lds_q, lds_sx8);
+            const float t = half_bits_to_float(r.sc) * lds_dx[blk];
+            if (up) {
+                acc_up = __builtin_fmaf(t, (float)s, acc_up);
+            } else {
+                acc_gate = __builtin_fmaf(t, (float)s, acc_gate);
+            }
+        }
+    };
+    Q4Regs R[kRingQ4];
+    StageInput<ACT> stage{xin, k, C, {}};
+    stage.issue();
+    __builtin_amdgcn_sched_barrier(0);
+    ring_prologue(sc, R, load);
+    __builtin_amdgcn_sched_barrier(0);
+    stage.commit(lds_q, lds_dx, lds_res);
+    __syncthreads();
+    q4_block_sums<WAVES * kWave>(lds_q, lds_sx8, C);
+    __syncthreads();
+    ring_loop(sc, R, load, compute, [&](float gate, int, int p, bool valid) {
+        const float upv = wave_sum(acc_up);
+        acc_up = 0.0f;
+        // silu(g) u, as q8_i8_swiglu_kernel
+        if (valid && lane == 0) y[p] = gate / (1.0f + expf(-gate)) * upv;
+    });
 }
 
 // The W4 GEMV with f32 activations (the W4A16 form of qwen3-8b-rtx4080-
@@ -964,6 +1046,27 @@ int launch_q4_norm(const void* w, int n, int k, const NormArgs& na, float* y, hi
     });
 }
 
+// The 4-bit gate+up GEMV with the SwiGLU epilogue: the W4 waves, one wave
+// per output.
+int launch_q4_swiglu(const void* w, int n_ff, int k, const void* x, int act_fmt, float* y, hipStream_t stream,
+                     LaunchInfo* info, bool run = true) {
+    const Cfg c = choose_cfg(kPathQ4, 2 * (int64_t)n_ff, k);
+    const size_t lds = lds_q8act_bytes((int)chunk_count(k));
+    const size_t lds_sx8 = chunk_count(k) * kWave * 4;
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    return dispatch_ws(c.waves, 1, [&](auto W, auto) -> int {
+        constexpr int Wv = decltype(W)::value;
+        if (act_fmt == WSG_ACT_Q8_0) {
+            auto kern = q4_i8_swiglu_kernel<Wv, kActQ8>;
+            return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds) + lds_sx8, n_ff, info, 1, run, stream, wp, n_ff,
+                                        k, x, y);
+        }
+        auto kern = q4_i8_swiglu_kernel<Wv, kActRequant>;
+        return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds) + lds_sx8, n_ff, info, 1, run, stream, wp, n_ff, k,
+                                    x, y);
+    });
+}
+
 // The W4 GEMV: its own waves and split choice (choose_cfg).
 int launch_q4(const void* w, int n, int k, const void* x, int act_fmt, float* y, hipStream_t stream, LaunchInfo* info,
               bool run = true) {
@@ -1135,6 +1238,10 @@ int validate_gemv_q8_swiglu(const void* w, int64_t n_ff, int64_t k, const void* 
     return check_q8_args(w, 2 * n_ff, k, x, act_fmt, y);
 }
 
+int validate_gemv_q4_swiglu(const void* w, int64_t n_ff, int64_t k, const void* x, int act_fmt, const void* y) {
+    return validate_gemv_q8_swiglu(w, n_ff, k, x, act_fmt, y);  // the same arguments; only the layout differs
+}
+
 int validate_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, const void* ws,
                      size_t ws_bytes, const void* idx_out) {
     if (w_type != WSG_W_BF16 && w_type != WSG_W_Q8_0) return WSG_ERR_MODE;
@@ -1192,6 +1299,13 @@ int gemv_q4_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h
     const int rc = validate_gemv_q8_rmsnorm(w_packed, n, k, h, r, g, eps, h_out, y);
     if (rc != WSG_OK) return rc;
     return launch_q4_norm(w_packed, (int)n, (int)k, NormArgs{h, r, g, h_out, eps}, y, stream, nullptr);
+}
+
+int gemv_q4_0_swiglu(const void* w_packed, int64_t n_ff, int64_t k, const void* x, int act_fmt, float* y,
+                     hipStream_t stream) {
+    const int rc = validate_gemv_q4_swiglu(w_packed, n_ff, k, x, act_fmt, y);
+    if (rc != WSG_OK) return rc;
+    return launch_q4_swiglu(w_packed, (int)n_ff, (int)k, x, act_fmt, y, stream, nullptr);
 }
 
 int gemv_q4_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act_fmt, float* y, hipStream_t stream) {

@@ -28,6 +28,7 @@ int validate_embed_gather(const void* table, int w_type, int64_t vocab, int64_t 
                           const float* out);
 int validate_token_advance(const int32_t* token, const int32_t* history, int64_t capacity, const int32_t* pos);
 int validate_gemv_q4(const void* w, int64_t n, int64_t k, const void* x, int act_fmt, const void* y);
+int validate_gemv_q4_swiglu(const void* w, int64_t n_ff, int64_t k, const void* x, int act_fmt, const void* y);
 }  // namespace wsg
 
 struct wsg_plan {
@@ -69,6 +70,7 @@ int validate_op(const wsg_op_desc& d) {
             return wsg::validate_token_advance(static_cast<const int32_t*>(d.x), d.idx_out, d.n,
                                                static_cast<const int32_t*>(d.ws));
         case WSG_OP_GEMV_Q4_0: return wsg::validate_gemv_q4(d.w, d.n, d.k, d.x, d.act_fmt, d.y);
+        case WSG_OP_GEMV_Q4_0_SWIGLU: return wsg::validate_gemv_q4_swiglu(d.w, d.n, d.k, d.x, d.act_fmt, d.y);
         case WSG_OP_GEMV_Q4_0_RMSNORM:
             return wsg::validate_gemv_q8_rmsnorm(d.w, d.n, d.k, static_cast<const float*>(d.x),
                                                  static_cast<const float*>(d.r), static_cast<const float*>(d.g),
@@ -104,6 +106,8 @@ int enqueue_op(const wsg_op_desc& d, hipStream_t s) {
         case WSG_OP_TOKEN_ADVANCE:
             return token_advance(static_cast<const int32_t*>(d.x), d.idx_out, d.n, static_cast<int32_t*>(d.ws), s);
         case WSG_OP_GEMV_Q4_0: return gemv_q4_0(d.w, d.n, d.k, d.x, d.act_fmt, static_cast<float*>(d.y), s);
+        case WSG_OP_GEMV_Q4_0_SWIGLU:
+            return gemv_q4_0_swiglu(d.w, d.n, d.k, d.x, d.act_fmt, static_cast<float*>(d.y), s);
         case WSG_OP_GEMV_Q4_0_RMSNORM:
             return gemv_q4_0_rmsnorm(d.w, d.n, d.k, static_cast<const float*>(d.x), static_cast<const float*>(d.r),
                                      static_cast<const float*>(d.g), d.eps, static_cast<float*>(d.h_out),

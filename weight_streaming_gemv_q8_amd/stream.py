@@ -84,8 +84,8 @@ class TokenStream:
     swiglu_at: indices of the GEMVs of a layer whose output is the SwiGLU
             of their two halves (the gate+up projection: rows 0 .. n/2 - 1
             are the gate, the rest the up projection; gemv_q8_0_swiglu),
-            so the next GEMV reads n/2 products.  Q8_0 chains with int8
-            activations; not with fused_norm.
+            so the next GEMV reads n/2 products.  Q8_0 and q4_0 chains with
+            int8 activations; not with fused_norm.
     fused_norm: with norm_before on a Q8_0 or q4_0 chain with int8 activations, each
             normalized GEMV computes the residual add + RMSNorm itself
             (gemv_q8_0_rmsnorm) instead of after a separate norm call; the
@@ -100,7 +100,7 @@ class TokenStream:
                  swiglu_at: Sequence[int] = ()):
         if wtype not in ("q8_0", "q4_0", "bf16"):
             raise ValueError("wtype must be q8_0, q4_0 or bf16")
-        if wtype == "q4_0" and (requant != "fused" or swiglu_at or (norm_before and deq == 2)):
+        if wtype == "q4_0" and (requant != "fused" or ((norm_before or swiglu_at) and deq == 2)):
             raise ValueError("q4_0 chains run f32 activations (deq 2) or int8 ones requantized in each GEMV "
                              "or by the norm step")
         if requant not in ("fused", "separate"):
@@ -115,8 +115,8 @@ class TokenStream:
         for j in self.swiglu_at:
             if not 0 <= j < len(self.shapes) or self.shapes[j][0] % 2:
                 raise ValueError("a SwiGLU GEMV needs an even number of rows (gate and up halves)")
-            if wtype != "q8_0" or deq == 2:
-                raise ValueError("the SwiGLU epilogue runs on Q8_0 chains with int8 activations")
+            if wtype == "bf16" or deq == 2:
+                raise ValueError("the SwiGLU epilogue runs on Q8_0 and q4_0 chains with int8 activations")
         for j in range(1, len(self.shapes)):
             if self.shapes[j][1] > self.out_len(j - 1):
                 raise ValueError("a GEMV's k exceeds the previous GEMV's outputs")
@@ -249,15 +249,16 @@ class TokenStream:
         w = self.weights.data_ptr() + s.w_offset
         if s.index in self.swiglu_at:
             nff = s.n // 2
+            swiglu = wsg.op_gemv_q4_0_swiglu if self.wtype == "q4_0" else wsg.op_gemv_q8_0_swiglu
             if s.norm is not None:
                 n = s.norm
                 return [wsg.op_residual_rmsnorm(n.h_in, n.r or None, n.g, self.hidden, self.eps, h_out=n.h_out,
                                                 y=n.y, y_q8=n.yq),
-                        wsg.op_gemv_q8_0_swiglu(w, nff, s.k, n.yq, wsg.ACT_Q8_0, s.y)]
+                        swiglu(w, nff, s.k, n.yq, wsg.ACT_Q8_0, s.y)]
             if self.act_fmt() == wsg.ACT_Q8_0:
                 return [wsg.op_quantize_act(s.x_ptr, s.k, s.xq_ptr),
-                        wsg.op_gemv_q8_0_swiglu(w, nff, s.k, s.xq_ptr, wsg.ACT_Q8_0, s.y)]
-            return [wsg.op_gemv_q8_0_swiglu(w, nff, s.k, s.x_ptr, self.act_fmt(), s.y)]
+                        swiglu(w, nff, s.k, s.xq_ptr, wsg.ACT_Q8_0, s.y)]
+            return [swiglu(w, nff, s.k, s.x_ptr, self.act_fmt(), s.y)]
         pre = []
         if s.norm is not None and self.fused_norm:
             n = s.norm
@@ -310,6 +311,8 @@ class TokenStream:
                 wsg.gemv_q4_0(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
             elif op.op == wsg.OP_GEMV_Q8_0_SWIGLU:
                 wsg.gemv_q8_0_swiglu(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
+            elif op.op == wsg.OP_GEMV_Q4_0_SWIGLU:
+                wsg.gemv_q4_0_swiglu(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
             elif op.op in (wsg.OP_GEMV_Q8_0_RMSNORM, wsg.OP_GEMV_Q4_0_RMSNORM):
                 f = wsg.gemv_q8_0_rmsnorm if op.op == wsg.OP_GEMV_Q8_0_RMSNORM else wsg.gemv_q4_0_rmsnorm
                 f(op.w, op.n, op.k, op.x, op.r, op.g, op.eps, op.y, h_out=op.h_out, stream=stream)
