@@ -358,22 +358,22 @@ def measure_configs(steps: int, warmup: int) -> list:
     del ts
     torch.cuda.empty_cache()
     # a whole decode step: embedding -> layers -> LM head + argmax -> advance
-    for wl in (W.QWEN3_8B_Q8, W.DENSE27B_Q8):
-        ds = build_decode(wl)
+    for wl, wt in ((W.QWEN3_8B_Q8, "q8_0"), (W.DENSE27B_Q8, "q8_0"), (W.DENSE27B_Q8, "q4_0")):
+        ds = build_decode(wl, wtype=wt)
         alg = ds.chain.algorithmic_weight_bytes() + ds.vocab * (ds.hidden // 32) * 34
         ds.capture()
         for _ in range(warmup):
             ds.launch()
         sec = _time_calls(lambda i: ds.launch(), steps, 0)
-        rec(wl, "decode step graph (embedding, norms, SwiGLU, LM head + argmax, token advance), vocab 151936",
-            sec, alg, kernels_per_token=ds.plan.kernel_count, deq=0)
+        rec(wl, "decode step graph (embedding, norms, SwiGLU, LM head + argmax, token advance), vocab 151936"
+            + (", 4-bit layers" if wt == "q4_0" else ""), sec, alg, kernels_per_token=ds.plan.kernel_count, deq=0)
         ds.close()
         del ds
         torch.cuda.empty_cache()
     return out
 
 
-def build_decode(wl, vocab: int = 151936):
+def build_decode(wl, vocab: int = 151936, wtype: str = "q8_0"):
     """A whole decode step on the workload's layer shapes (DecodeStep):
     embedding gather -> the layers with the residual stream (norms fused
     into the attention-input GEMVs, SwiGLU on gate+up) -> final norm ->
@@ -387,7 +387,7 @@ def build_decode(wl, vocab: int = 151936):
     from weight_streaming_gemv_q8_amd.stream import DecodeStep
 
     shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
-    ds = DecodeStep(shapes, wl.layers, vocab, capacity=4096, eps=W.RMSNORM_EPS)
+    ds = DecodeStep(shapes, wl.layers, vocab, capacity=4096, eps=W.RMSNORM_EPS, wtype=wtype)
     stream = torch.cuda.current_stream().cuda_stream
 
     def fill(layer, m, part, rows, staging):

@@ -9,9 +9,10 @@ the speed comes from", item 2: token and position advanced on the device).
   outside the vocabulary;
 * token_advance appends to the history while it has room and always
   counts the position;
-* a whole decode step (embedding -> 2 layers of the 8B-shaped chain with
-  the residual stream, fused norms and SwiGLU -> final norm -> LM head +
-  argmax -> advance) replayed from one graph decodes the same tokens as
+* a whole decode step (embedding -> 2 layers of the 8B-shaped chain, in
+  Q8_0 or 4-bit weights, with the residual stream, fused norms and SwiGLU
+  -> final norm -> LM head + argmax -> advance) replayed from one graph
+  decodes the same tokens as
   its calls run one at a time; at every step the embedding is the row of
   the token consumed, the argmax is exact on the step's own logits, and
   the logits match the oracle fed the GPU's own LM-head input."""
@@ -77,13 +78,13 @@ def test_token_advance(gpu_lib):
     assert e.value.status == wsg.ERR_SHAPE
 
 
-def _decode_step(vocab, layers):
+def _decode_step(vocab, layers, wtype="q8_0"):
     import torch
 
     from weight_streaming_gemv_q8_amd.stream import DecodeStep
     wl = W.QWEN3_8B_Q8
     shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
-    ds = DecodeStep(shapes, layers, vocab, capacity=16, eps=W.RMSNORM_EPS)
+    ds = DecodeStep(shapes, layers, vocab, capacity=16, eps=W.RMSNORM_EPS, wtype=wtype)
     stream = torch.cuda.current_stream().cuda_stream
 
     def fill(layer, m, part, rows, staging):
@@ -102,9 +103,10 @@ def _decode_step(vocab, layers):
     return ds, wl.seed
 
 
-def test_decode_step_graph_equals_eager_and_oracle(gpu_lib):
+@pytest.mark.parametrize("wtype", ["q8_0", "q4_0"])
+def test_decode_step_graph_equals_eager_and_oracle(gpu_lib, wtype):
     vocab, layers, steps, first = 32000, 2, 5, 7
-    ds, seed = _decode_step(vocab, layers)
+    ds, seed = _decode_step(vocab, layers, wtype)
     hidden = ds.hidden
     rng = np.random.default_rng(0xDEC0)
     ds.reset(first)

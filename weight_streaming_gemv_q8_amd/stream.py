@@ -367,11 +367,14 @@ class DecodeStep:
     Each replay decodes one token; history holds the tokens decoded so far.
     Attention and the other non-GEMV operators are not part of this path:
     the layer chain is the GEMV stream (q/k/v -> o_proj reads the first
-    rows of the qkv output)."""
+    rows of the qkv output).  wtype is the layers' weight format ("q8_0" or
+    "q4_0"); the embedding table and the LM head stay Q8_0."""
 
     def __init__(self, shapes, layers: int, vocab: int, capacity: int = 1024, device: str = "cuda",
-                 eps: float = 1e-6):
-        self.chain = TokenStream(shapes, layers, "q8_0", deq=0, device=device, norm_before=(0, 2), eps=eps,
+                 eps: float = 1e-6, wtype: str = "q8_0"):
+        if wtype not in ("q8_0", "q4_0"):
+            raise ValueError("the decode step's layers are Q8_0 or q4_0")
+        self.chain = TokenStream(shapes, layers, wtype, deq=0, device=device, norm_before=(0, 2), eps=eps,
                                  fused_norm=True, swiglu_at=(2,))
         self.hidden = self.chain.hidden
         self.vocab = int(vocab)
