@@ -165,16 +165,15 @@ def time_per_launch(ts, reps: int = 1):
     return [a / reps for a in acc]
 
 
-def time_plan(ts, plan_kind, steps: int, warmup: int, variant: int = 0):
+def time_plan(ts, plan_kind, steps: int, warmup: int):
     """Capture the token ("graph": one node per call; "persistent": one
-    resident kernel; "ring": the LDS-ring kernel in shape `variant`, 0 = its
-    default) and time `steps` replays with HIP events on the launch stream.
-    Returns (seconds per token, kernels per token)."""
+    resident kernel) and time `steps` replays with HIP events on the launch
+    stream.  Returns (seconds per token, kernels per token)."""
     import torch
     if plan_kind is True or plan_kind is False:  # older callers: persistent or not
         plan_kind = "persistent" if plan_kind else "graph"
     persistent = plan_kind != "graph"
-    plan = ts.capture(persistent=plan_kind == "persistent", ring=variant if plan_kind == "ring" else None)
+    plan = ts.capture(persistent=persistent)
     kernels = plan.kernel_count
     for _ in range(warmup):
         ts.launch()
@@ -316,7 +315,7 @@ def measure_configs(steps: int, warmup: int) -> list:
         for deq in deqs:
             ts = build_stream(wl, deq, "fused")
             alg = ts.algorithmic_weight_bytes()
-            plans = ("graph",) if wl.wtype == "bf16" else ("graph", "persistent") + (("ring",) if deq == 0 else ())
+            plans = ("graph",) if wl.wtype == "bf16" else ("graph", "persistent")
             for plan in plans:
                 sec, kernels = time_plan(ts, plan, steps, warmup)
                 rec(wl, f"{plan} deq{deq}" if wl.wtype != "bf16" else plan, sec, alg, kernels_per_token=kernels,
@@ -531,25 +530,22 @@ def label_from_rocprof(name: str):
     """Bench label of a kernel from its demangled rocprofv3 name (template
     arguments), or None for kernels outside the GEMV stream."""
     import re
-    m = re.search(r"(q8_i8_kernel|q8_f32_kernel|bf16_kernel|stream_kernel|ring_kernel)<([^>]*)>", name)
+    m = re.search(r"(q8_i8_kernel|q8_f32_kernel|bf16_kernel|stream_kernel)<([^>]*)>", name)
     if not m:
         return None
     kind, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
-    if kind == "ring_kernel":
-        return ring_label({"waves": int(args[0]), "producers": int(args[1]), "depth": int(args[2])})
+    if kind == "stream_kernel":
+        sc = {"waves": int(args[0]), "unroll": int(args[1]), "sets": int(args[2])}
+        return stream_label(sc, args[3] == "true")
     if kind == "q8_i8_kernel":
         return f"q8_i8_kernel<waves={args[0]},split={args[1]},unroll={args[2]},{_ACT_NAMES[args[3]]}>"
     if kind in ("q8_f32_kernel", "bf16_kernel"):
         return f"{kind}<waves={args[0]},split={args[1]},unroll={args[2]},f32act>"
-    return stream_label(int(args[0]), int(args[1]), int(args[2]), args[3] == "true")
+    return None
 
 
-def stream_label(waves: int, unroll: int, sets: int, f32: bool) -> str:
-    return f"stream_kernel<waves={waves},unroll={unroll},sets={sets},{'f32act' if f32 else 'requant'}>"
-
-
-def ring_label(shape: dict) -> str:
-    return f"ring_kernel<waves={shape['waves']},producers={shape['producers']},depth={shape['depth']},requant>"
+def stream_label(sc: dict, f32: bool) -> str:
+    return f"stream_kernel<waves={sc['waves']},unroll={sc['unroll']},sets={sc['sets']},{'f32act' if f32 else 'requant'}>"
 
 
 def _read_csv(path: str):
@@ -640,11 +636,8 @@ def main() -> int:
     ap.add_argument("--workload", default="dense27b_q8_0_64L")
     ap.add_argument("--deq", type=int, default=0, choices=(0, 1, 2))
     ap.add_argument("--requant", default="fused", choices=("fused", "separate"))
-    ap.add_argument("--plan", default="graph", choices=("persistent", "graph", "ring"),
-                    help="one resident kernel per token (persistent, or ring: weights streamed through an LDS "
-                         "ring by dedicated waves), or a graph node per GEMV")
-    ap.add_argument("--ring-variant", type=int, default=0,
-                    help="shape of the ring plan's kernel (0: the library default; see wsg_ring_shape)")
+    ap.add_argument("--plan", default="graph", choices=("persistent", "graph"),
+                    help="one resident kernel per token (persistent), or a graph node per GEMV")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the deq-2 line and the read ceiling")
@@ -696,16 +689,12 @@ def main() -> int:
     ts = build_stream(wl, args.deq, args.requant)
     alg_bytes = ts.algorithmic_weight_bytes()
     act_fmt = ts.act_fmt()
-    persistent = args.plan in ("persistent", "ring")
+    persistent = args.plan == "persistent"
     if persistent and (wl.wtype != "q8_0" or args.requant != "fused"):
-        print("the persistent and ring plans run Q8_0 streams with fused requantization (or, persistent only, "
-              "f32 activations)", file=sys.stderr)
-        return 2
-    if args.plan == "ring" and args.deq == 2:
-        print("the ring plan runs deq 0 / deq 1 layer GEMVs (requantized activations) only", file=sys.stderr)
+        print("the persistent plan runs Q8_0 streams with fused requantization or f32 activations", file=sys.stderr)
         return 2
 
-    sec, kernels_per_token = time_plan(ts, args.plan, args.steps, args.warmup, args.ring_variant)
+    sec, kernels_per_token = time_plan(ts, args.plan, args.steps, args.warmup)
     value = gbps(alg_bytes, sec)
     log(f"{args.plan} plan, {kernels_per_token} kernel(s) per token: timed {args.steps} steps: "
         f"{sec * 1e6:.1f} us per token, {value:.1f} GB/s")
@@ -713,11 +702,7 @@ def main() -> int:
     wtype_code = wsg.W_Q8_0 if wl.wtype == "q8_0" else wsg.W_BF16
     if persistent:
         # one launch per token: the dominant kernel is the whole stream
-        if args.plan == "ring":
-            label = ring_label(wsg.ring_shape(args.ring_variant))
-        else:
-            sc = wsg.stream_config()
-            label = stream_label(sc["waves"], sc["unroll"], sc["sets"], act_fmt == wsg.ACT_F32)
+        label = stream_label(wsg.stream_config(), act_fmt == wsg.ACT_F32)
         roofline = {
             "bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": read_traffic(label),
@@ -756,7 +741,7 @@ def main() -> int:
     extras = {}
     if not args.no_extras:
         if wl.wtype == "q8_0" and args.requant == "fused":
-            others = [o for o in ("graph", "persistent", "ring") if o != args.plan and (o != "ring" or args.deq != 2)]
+            others = [o for o in ("graph", "persistent") if o != args.plan]
             for other in others:
                 sec_o, k_o = time_plan(ts, other, args.steps, args.warmup)
                 extras[f"{other}_plan"] = {"us_per_token": round(sec_o * 1e6, 1),
@@ -767,7 +752,7 @@ def main() -> int:
         if wl.wtype == "q8_0" and args.deq != 2:
             # the same stream with f32 activations (deq 2), same weights
             ts.deq = 2
-            sec2, _ = time_plan(ts, "graph" if args.plan == "ring" else args.plan, args.steps, args.warmup)
+            sec2, _ = time_plan(ts, args.plan, args.steps, args.warmup)
             extras["deq2"] = {"us_per_token": round(sec2 * 1e6, 1), "GBps": round(gbps(alg_bytes, sec2), 1),
                               "frac_of_peak": round(gbps(alg_bytes, sec2) / HBM_PEAK_GBPS, 4)}
             log(f"deq 2: {sec2 * 1e6:.1f} us per token")

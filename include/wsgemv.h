@@ -371,52 +371,23 @@ int wsg_plan_launch(wsg_plan* plan, hipStream_t stream);
  * reduces its rows in the same order as the eager call, so results equal
  * the eager calls' bit for bit.  An op may have at most 64 row tiles per
  * workgroup (rows <= 64 x CUs x 16 / split; 262,144 unsplit rows on 256
- * CUs), else WSG_ERR_SHAPE.  The plan owns device allocations: the
+ * CUs), else WSG_ERR_SHAPE.
+ * Unlike the hot calls, creating this plan allocates device memory (the
  * descriptor table, a launch counter, an error flag and two copies of every
- * op's output (one per launch parity).  A wait that exceeds its spin limit (about a
- * second) makes the kernel give up rather than hang, every other wait of
- * that launch stops soon after, and wsg_plan_error reports it; the plan's
- * results are then invalid and it must be destroyed.  Replays of one plan
- * must not overlap in time (launch them on one stream). */
+ * op's output, one per launch parity) and synchronizes the device; do not
+ * call it while a stream is capturing.  A wait that exceeds its spin limit
+ * (about a second) makes the kernel give up rather than hang, every other
+ * wait of that launch stops soon after, and wsg_plan_error reports it; the
+ * plan's results are then invalid and it must be destroyed.  Replays of one
+ * plan must not overlap in time (launch them on one stream). */
 int wsg_plan_create_persistent(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_plan** out);
 
-/* LDS-ring whole-token plan: the same descriptors and buffer rules as
- * wsg_plan_create_persistent, Q8_0 GEMVs with WSG_ACT_F32_REQUANT only
- * (deq 0; WSG_ERR_MODE otherwise), one workgroup per CU per replay.  The
- * weight stream is decoupled from the chain's data dependencies
- * (emit_qwen38_generate, "Where the speed comes from", items 1-2: the
- * token's ~27 GB weight stream is the time, so HBM must not idle between
- * GEMVs): some waves of each workgroup ("producers") only copy weights from
- * HBM into a ring of LDS slots in the order they are consumed, GEMV after
- * GEMV, and never wait for an activation; the other waves stage each GEMV's
- * input and compute rows from the ring.  Weights therefore keep streaming
- * while the next input is awaited.  Each row is reduced by one wave in
- * chunk order (as the eager call reduces an unsplit row), so ops that the
- * eager call does not split, fed the same input, give the eager results bit
- * for bit, and every op meets the Q8_0 bound.  `variant` picks the kernel
- * shape (0 = the default; 0 <= variant < WSG_RING_VARIANTS, else
- * WSG_ERR_MODE; wsg_ring_shape describes each).  The LDS holds two staged
- * inputs for the largest k and the weight slots; a k too large to leave
- * room for them gives WSG_ERR_SHAPE.  Ownership, the error flag
- * (wsg_plan_error, wsg_plan_error_detail) and replay rules as for the
- * persistent plan. */
-enum { WSG_RING_VARIANTS = 2 };
-int wsg_plan_create_ring(const wsg_op_desc* ops, int n_ops, int variant, hipStream_t stream, wsg_plan** out);
-/* Shape of a ring variant: waves per workgroup, producer waves among them
- * and the register sets each producer keeps (one item of weights each).
- * WSG_ERR_MODE for an unknown variant. */
-int wsg_ring_shape(int variant, int* waves, int* producers, int* depth);
-
-/* *flag = 1 if a persistent plan's barrier ever timed out (its outputs are
- * then invalid), else 0.  Synchronizes the device. */
+/* *flag = 1 if a persistent plan's wait ever timed out (its outputs are
+ * then invalid), else 0.  Synchronizes the device (not capturable). */
 int wsg_plan_error(wsg_plan* plan, int* flag);
 /* Where the first wait that gave up was (all zero if none; synchronizes the
- * device): words[0] site (1 an input or dependency of an op not written in
- * time, 2 a producer waiting for a free LDS ring slot, 3 a consumer waiting
- * for a filled slot, 4 consumer waves meeting before an op's rows),
- * words[1] workgroup, words[2] wave, words[3] op index, words[4] the value
- * awaited, words[5] the value last seen (0 for site 1).  For a persistent
- * or ring plan. */
+ * device): words[0] site (1: an input or dependency of an op not written
+ * in time), words[1] workgroup, words[2] wave, words[3..5] zero. */
 int wsg_plan_error_detail(wsg_plan* plan, int32_t* words);
 int wsg_plan_destroy(wsg_plan* plan);
 /* Number of kernel launches one replay makes. */

@@ -160,24 +160,14 @@ def test_deq_mode_mapping():
         wsg.act_fmt_for(3, False)
 
 
-def test_ring_plan_shape_and_rejections_before_launch(L):
-    # every variant is a 16-wave workgroup with at least one producer and
-    # one consumer wave, and the header declares how many there are
-    header = open(HEADER).read()
-    assert f"WSG_RING_VARIANTS = {wsg.RING_VARIANTS}" in header
-    for v in range(wsg.RING_VARIANTS):
-        s = wsg.ring_shape(v)
-        assert s["waves"] == 16 and 1 <= s["producers"] < s["waves"] and s["depth"] >= 2
-    for bad in (-1, wsg.RING_VARIANTS):
-        with pytest.raises(wsg.WsgError) as e:
-            wsg.ring_shape(bad)
-        assert e.value.status == wsg.ERR_MODE
+def test_persistent_plan_rejections_before_launch(L):
+    # validation happens before any allocation or launch (no GPU needed)
     h = ctypes.c_void_p()
     A16 = 0x10000
-    ops = (wsg.OpDesc * 1)(wsg.op_gemv_bf16(A16, 4, 32, A16, A16))
-    assert L.wsg_plan_create_ring(None, 1, 0, None, ctypes.byref(h)) == wsg.ERR_NULL
-    assert L.wsg_plan_create_ring(ops, 1, wsg.RING_VARIANTS, None, ctypes.byref(h)) == wsg.ERR_MODE
-    assert L.wsg_plan_create_ring(ops, 1, 0, None, ctypes.byref(h)) == wsg.ERR_MODE  # not a Q8_0 GEMV
+    bf16 = (wsg.OpDesc * 1)(wsg.op_gemv_bf16(A16, 4, 32, A16, A16))
+    assert L.wsg_plan_create_persistent(None, 1, None, ctypes.byref(h)) == wsg.ERR_NULL
+    assert L.wsg_plan_create_persistent(bf16, 0, None, ctypes.byref(h)) == wsg.ERR_SHAPE
+    assert L.wsg_plan_create_persistent(bf16, 1, None, ctypes.byref(h)) == wsg.ERR_MODE  # not a Q8_0 GEMV
     assert not h.value
 
 

@@ -64,30 +64,46 @@ def test_replay_equals_eager_q8(gpu_lib, deq, requant):
     ts.close()
 
 
+def _new_inputs(ts, wl, seed):
+    """Fresh seeded layer inputs (different values on every call)."""
+    import torch
+    xs = np.stack([synth.activation(seed, W.activation_tensor_id(l), ts.shapes[0][1], rms=True)
+                   for l in range(ts.layers)])
+    ts.set_inputs(torch.from_numpy(xs).cuda())
+    return xs
+
+
+def _replays_follow_inputs(ts, wl, plan, seeds):
+    """Before each replay the layer inputs change: every output of the
+    replay must equal the eager calls on those inputs, bit for bit, and no
+    wait may have timed out.  A replay that read a value left over from the
+    previous replay (a plan-owned copy of an output, a stale flag) would
+    differ here, since the previous replay saw other inputs."""
+    for rep, seed in enumerate(seeds):
+        _new_inputs(ts, wl, seed)
+        ts.run_eager()
+        eager = _snapshot(ts)
+        for y in ts.outputs():
+            y.fill_(np.nan)
+        ts.launch()
+        got = _snapshot(ts)
+        assert not plan.error(), f"replay {rep}: a wait timed out: {plan.error_detail()}"
+        for i, (a, b) in enumerate(zip(eager, got)):
+            assert np.array_equal(a, b), f"replay {rep} (seed {seed:#x}): slot {i} differs from eager"
+
+
 @pytest.mark.parametrize("wl_name,layers,deq", [("qwen3_8b_q8_0_36L", 3, 0), ("qwen3_8b_q8_0_36L", 2, 2),
                                                 ("dense27b_q8_0_64L", 2, 0), ("dense27b_q8_0_64L", 2, 2)])
 def test_persistent_replay_equals_eager(gpu_lib, wl_name, layers, deq):
     """The whole token in one resident kernel: the same rows reduced in the
-    same order as the eager calls, so every output is bit-identical, on two
-    replays, and no barrier timed out."""
+    same order as the eager calls, so every output is bit-identical, on
+    three consecutive replays whose inputs all differ, and no wait timed
+    out."""
     wl = {w.name: w for w in W.ALL}[wl_name]
     ts, _ = _stream(wl, layers, deq=deq)
-    ts.run_eager()
-    eager = _snapshot(ts)
-    for y in ts.outputs():
-        y.fill_(np.nan)
     plan = ts.capture(persistent=True)
     assert plan.kernel_count == 1
-    ts.launch()
-    first = _snapshot(ts)
-    for y in ts.outputs():
-        y.fill_(np.nan)
-    ts.launch()
-    second = _snapshot(ts)
-    assert not plan.error()
-    for i, (a, b, c) in enumerate(zip(eager, first, second)):
-        assert np.array_equal(a, b), f"slot {i}: persistent differs from eager"
-        assert np.array_equal(b, c), f"slot {i}: replays differ"
+    _replays_follow_inputs(ts, wl, plan, [0x5EED7000 + i for i in range(3)])
     ts.close()
 
 
@@ -95,9 +111,11 @@ def test_persistent_replay_equals_eager(gpu_lib, wl_name, layers, deq):
 @pytest.mark.parametrize("deq", [0, 2])
 def test_persistent_forced_split_equals_eager(gpu_lib, split, deq):
     """Forced split factors on a chain with one-chunk rows (k = 2048: some
-    parts have no chunks), a ragged last chunk (k = 2080) and ragged row
-    tiles: the persistent kernel (whose waves trade parts tile by tile)
-    still equals the eager calls bit for bit."""
+    parts have no chunks), a ragged last chunk (k = 2080) and row counts
+    that do not divide among the workgroups: the persistent kernel (whose
+    waves take (row, part) units in whatever order they get to them) still
+    equals the eager calls bit for bit, over three replays with changing
+    inputs."""
     import torch
 
     from weight_streaming_gemv_q8_amd.stream import TokenStream
@@ -113,24 +131,37 @@ def test_persistent_forced_split_equals_eager(gpu_lib, split, deq):
                                  rows * shapes[m][1], W.WEIGHT_SIGMA, stream=torch.cuda.current_stream().cuda_stream)
 
         ts.fill_weights(fill)
-        xs = np.stack([synth.activation(seed, W.activation_tensor_id(l), shapes[0][1], rms=True) for l in range(2)])
-        ts.set_inputs(torch.from_numpy(xs).cuda())
+        _new_inputs(ts, None, seed)
         for slot in ts.slots:
             assert wsg.gemv_config(wsg.W_Q8_0, ts.act_fmt(), slot.n, slot.k)["split"] == split
-        ts.run_eager()
-        eager = _snapshot(ts)
-        for y in ts.outputs():
-            y.fill_(np.nan)
         plan = ts.capture(persistent=True)
-        for rep in range(2):
-            ts.launch()
-            got = _snapshot(ts)
-            assert not plan.error()
-            for i, (a, b) in enumerate(zip(eager, got)):
-                assert np.array_equal(a, b), f"replay {rep}: slot {i} differs from eager"
+        _replays_follow_inputs(ts, None, plan, [seed + 1, seed + 2, seed + 3])
         ts.close()
     finally:
         wsg.tune(wsg.TUNE_SPLITK, 0)
+
+
+@pytest.mark.parametrize("deq", [0, 2])
+def test_persistent_small_ops_and_idle_workgroups(gpu_lib, deq):
+    """Ops with fewer rows than workgroups (some workgroups own no rows),
+    single-row ops and a one-block k: a workgroup's streaming waves may run
+    several ops ahead of its control waves; every output still equals the
+    eager calls, over three replays with changing inputs."""
+    import torch
+
+    from weight_streaming_gemv_q8_amd.stream import TokenStream
+    shapes = [(96, 1024, (96,)), (300, 64, (300,)), (40, 256, (40,)), (1, 32, (1,))]
+    seed = 0x5EED5119
+    ts = TokenStream(shapes, 3, "q8_0", deq=deq)
+
+    def fill(layer, m, part, rows, staging):
+        synth.dev_normal_f32(staging.data_ptr(), seed, W.weight_tensor_id(layer, m, part),
+                             rows * shapes[m][1], W.WEIGHT_SIGMA, stream=torch.cuda.current_stream().cuda_stream)
+
+    ts.fill_weights(fill)
+    plan = ts.capture(persistent=True)
+    _replays_follow_inputs(ts, None, plan, [seed + 1, seed + 2, seed + 3])
+    ts.close()
 
 
 def test_persistent_plan_rejects_unsupported_ops(gpu_lib):

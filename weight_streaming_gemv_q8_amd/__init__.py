@@ -43,7 +43,7 @@ EXPORTS = (
     "quantize_q4_0_weights", "gemv_q4_0", "gemv_q4_0_rmsnorm", "gemv_q4_0_swiglu", "gemv_q8_0_rmsnorm", "gemv_q8_0_swiglu",
     "gemv_bf16",
     "gemv_q8_0", "wsg_gemv_config", "wsg_tune", "wsg_argmax_ws_bytes", "lm_head_argmax", "argmax_f32", "wsg_plan_create",
-    "wsg_plan_launch", "wsg_plan_create_persistent", "wsg_plan_create_ring", "wsg_ring_shape", "wsg_plan_error", "wsg_plan_error_detail", "wsg_plan_destroy", "wsg_plan_kernel_count",
+    "wsg_plan_launch", "wsg_plan_create_persistent", "wsg_plan_error", "wsg_plan_error_detail", "wsg_plan_destroy", "wsg_plan_kernel_count",
     "wsg_stream_config", "wsg_read_probe",
     "wsg_copy_probe",
 )
@@ -111,8 +111,6 @@ def lib():
             "wsg_plan_create": (i32, [ctypes.POINTER(OpDesc), i32, vp, ctypes.POINTER(vp)]),
             "wsg_plan_launch": (i32, [vp, vp]),
             "wsg_plan_create_persistent": (i32, [ctypes.POINTER(OpDesc), i32, vp, ctypes.POINTER(vp)]),
-            "wsg_plan_create_ring": (i32, [ctypes.POINTER(OpDesc), i32, i32, vp, ctypes.POINTER(vp)]),
-            "wsg_ring_shape": (i32, [i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "wsg_plan_error": (i32, [vp, ctypes.POINTER(i32)]),
             "wsg_plan_error_detail": (i32, [vp, ctypes.POINTER(i32)]),
             "wsg_plan_destroy": (i32, [vp]),
@@ -291,16 +289,6 @@ def stream_config() -> dict:
 TUNE_SPLITK, TUNE_WG_PER_CU, TUNE_WAVES, TUNE_UNROLL = 0, 1, 2, 3
 
 
-RING_VARIANTS = 2
-
-
-def ring_shape(variant: int = 0) -> dict:
-    """Shape of an LDS-ring token kernel variant (0: the default)."""
-    w, p, d = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check("wsg_ring_shape", lib().wsg_ring_shape(variant, ctypes.byref(w), ctypes.byref(p), ctypes.byref(d)))
-    return {"variant": variant, "waves": w.value, "producers": p.value, "depth": d.value}
-
-
 def tune(knob: int, value: int) -> None:
     """Process-wide launch-configuration override for sweeps (0 = automatic)."""
     _check("wsg_tune", lib().wsg_tune(knob, value))
@@ -374,26 +362,19 @@ def op_residual_rmsnorm(h, r, g, k, eps, h_out=None, y=None, y_q8=None) -> OpDes
 
 class Plan:
     """A captured whole-token sequence of calls (hipGraph), replayed by launch().
-    persistent=True runs the whole sequence in one resident kernel launch;
-    ring=V (a variant index, or True for the default) runs it in the LDS-ring
-    kernel of that shape."""
+    persistent=True runs the whole sequence in one resident kernel launch."""
 
-    def __init__(self, ops: Sequence[OpDesc], stream=None, persistent: bool = False, ring=None):
+    def __init__(self, ops: Sequence[OpDesc], stream=None, persistent: bool = False):
         arr = (OpDesc * len(ops))(*ops)
         h = ctypes.c_void_p()
-        if ring is not None and ring is not False:
-            variant = 0 if ring is True else int(ring)
-            _check("wsg_plan_create_ring",
-                   lib().wsg_plan_create_ring(arr, len(ops), variant, _stream(stream), ctypes.byref(h)))
-        else:
-            fn = "wsg_plan_create_persistent" if persistent else "wsg_plan_create"
-            _check(fn, getattr(lib(), fn)(arr, len(ops), _stream(stream), ctypes.byref(h)))
+        fn = "wsg_plan_create_persistent" if persistent else "wsg_plan_create"
+        _check(fn, getattr(lib(), fn)(arr, len(ops), _stream(stream), ctypes.byref(h)))
         self._h = h
         self.n_ops = len(ops)
-        self.persistent = persistent or (ring is not None and ring is not False)
+        self.persistent = persistent
 
     def error(self) -> bool:
-        """True if a persistent plan's barrier timed out (outputs invalid); synchronizes."""
+        """True if a persistent plan's wait timed out (outputs invalid); synchronizes."""
         f = ctypes.c_int()
         _check("wsg_plan_error", lib().wsg_plan_error(self._h, ctypes.byref(f)))
         return bool(f.value)
@@ -402,8 +383,7 @@ class Plan:
         """Where the first wait that gave up was (site 0: none); synchronizes."""
         w = (ctypes.c_int32 * 6)()
         _check("wsg_plan_error_detail", lib().wsg_plan_error_detail(self._h, w))
-        sites = {0: "none", 1: "input or dependency", 2: "free ring slot", 3: "filled ring slot",
-                 4: "consumer meeting"}
+        sites = {0: "none", 1: "input or dependency"}
         return {"site": sites.get(w[0], str(w[0])), "workgroup": w[1], "wave": w[2], "op": w[3],
                 "awaited": w[4], "seen": w[5]}
 

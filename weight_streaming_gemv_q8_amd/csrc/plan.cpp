@@ -182,9 +182,8 @@ void release(wsg_plan* p) {
 
 namespace {
 
-// One resident kernel per replay: ring < 0 runs the persistent kernel,
-// ring >= 0 the LDS-ring kernel in that shape.
-int create_resident(const wsg_op_desc* ops, int n_ops, int ring, hipStream_t stream, wsg_plan** out) {
+// One resident kernel per replay (the whole token in one launch).
+int create_resident(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_plan** out) {
     if (!ops || !out) return WSG_ERR_NULL;
     *out = nullptr;
     if (n_ops <= 0 || n_ops > 65536) return WSG_ERR_SHAPE;
@@ -228,21 +227,13 @@ int create_resident(const wsg_op_desc* ops, int n_ops, int ring, hipStream_t str
         yc_elems += 2 * yc_stride[i];
         if (d.k > max_k) max_k = (int)d.k;
     }
-    int waves = 0, grid = 0, act_bytes = 0, slots = 0;
+    int waves = 0, grid = 0;
     size_t lds = 0;
-    int rc;
-    if (ring >= 0) {
-        if (f32) return WSG_ERR_MODE;  // the ring kernel stages requantized inputs only
-        rc = wsg::ring_config(max_k, ring, &grid, &lds, &act_bytes, &slots);
-        if (rc != WSG_OK) return rc;
-    } else {
-        rc = wsg::stream_config(max_k, f32, &waves, &grid, &lds);
-        if (rc != WSG_OK) return rc;
-        if ((int64_t)lds > wsg::device_info().max_lds) return WSG_ERR_SHAPE;
-        for (int i = 0; i < n_ops; ++i)
-            if (ops[i].n > wsg::stream_max_rows(wsg::stream_split(f32, ops[i].n, ops[i].k), grid))
-                return WSG_ERR_SHAPE;
-    }
+    int rc = wsg::stream_config(max_k, f32, &waves, &grid, &lds);
+    if (rc != WSG_OK) return rc;
+    if ((int64_t)lds > wsg::device_info().max_lds) return WSG_ERR_SHAPE;
+    for (int i = 0; i < n_ops; ++i)
+        if (ops[i].n > wsg::stream_max_rows(wsg::stream_split(f32, ops[i].n, ops[i].k), grid)) return WSG_ERR_SHAPE;
 
     const size_t state_bytes = wsg::stream_state_bytes();
     wsg_plan* p = new (std::nothrow) wsg_plan;
@@ -295,8 +286,6 @@ int create_resident(const wsg_op_desc* ops, int n_ops, int ring, hipStream_t str
     const int spin_limit = 1 << 20;
     const wsg::StreamOp* ops_dev = static_cast<const wsg::StreamOp*>(p->ops_dev);
     rc = capture_into(p, stream, [&](hipStream_t s) {
-        if (ring >= 0)
-            return wsg::ring_launch(ops_dev, n_ops, ring, p->bar_dev, grid, lds, act_bytes, slots, spin_limit, s);
         return wsg::stream_launch(ops_dev, n_ops, f32, p->bar_dev, grid, lds, spin_limit, s);
     });
     if (rc != WSG_OK) {
@@ -312,13 +301,7 @@ int create_resident(const wsg_op_desc* ops, int n_ops, int ring, hipStream_t str
 extern "C" {
 
 int wsg_plan_create_persistent(const wsg_op_desc* ops, int n_ops, hipStream_t stream, wsg_plan** out) {
-    return create_resident(ops, n_ops, -1, stream, out);
-}
-
-int wsg_plan_create_ring(const wsg_op_desc* ops, int n_ops, int variant, hipStream_t stream, wsg_plan** out) {
-    if (out) *out = nullptr;
-    if (variant < 0 || variant >= wsg::ring_variants()) return WSG_ERR_MODE;
-    return create_resident(ops, n_ops, variant, stream, out);
+    return create_resident(ops, n_ops, stream, out);
 }
 
 int wsg_plan_error(wsg_plan* plan, int* flag) {
@@ -380,15 +363,6 @@ int wsg_plan_destroy(wsg_plan* plan) {
 }
 
 int wsg_plan_kernel_count(const wsg_plan* plan) { return plan ? plan->kernels : -1; }
-
-int wsg_ring_shape(int variant, int* waves, int* producers, int* depth) {
-    int w = 0, pr = 0, d = 0;
-    if (wsg::ring_shape(variant, &w, &pr, &d) != WSG_OK) return WSG_ERR_MODE;
-    if (waves) *waves = w;
-    if (producers) *producers = pr;
-    if (depth) *depth = d;
-    return WSG_OK;
-}
 
 int wsg_stream_config(int* waves, int* unroll, int* sets) {
     int w = 0, u = 0, n = 0;

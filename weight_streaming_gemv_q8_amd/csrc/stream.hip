@@ -54,7 +54,6 @@ constexpr int kStreamThreads = kStreamWaves * kWave;
 constexpr int kStCounter = 0, kStError = 32, kStDetail = 33, kStWords = 64;
 // Sites of a wait that gave up (word kStDetail).
 constexpr int kSiteStaging = 1;  // an input or dependency not written in time
-constexpr int kSiteFreeSlot = 2, kSiteFullSlot = 3, kSiteConsumers = 4;  // the LDS-ring handshakes
 // Most row tiles one workgroup takes in one op: the tiles' results wait in
 // LDS until the op's end.
 constexpr int kMaxTiles = 64;
@@ -401,338 +400,6 @@ const void* stream_kernel_ptr() {
 }
 
 
-// ------------------------------------------------------------------------
-// LDS-ring token kernel: the weight stream decoupled from the chain's data
-// dependencies.  In the kernel above every wave both streams weights and
-// waits for its next input, and a wave's loads complete in order, so the
-// input staging at each GEMV start waits behind every weight load issued
-// before it: at most three items per wave can be requested ahead, and HBM
-// idles for the rest of each dependency wait (~4-5 us at each of the 256
-// GEMV boundaries of a 27B token).  Here each 16-wave workgroup splits into
-// P producer waves and 16 - P consumer waves.  Producers only copy weights
-// from HBM into a ring of LDS slots with gfx950's direct-to-LDS loads
-// (global_load_lds: no registers, 16 bytes per lane), one slot per item of
-// one 2048-weight chunk of one row, in the order the workgroup's rows and
-// chunks are consumed, GEMV after GEMV: they never wait for an activation,
-// only for a free slot.  Consumers stage each GEMV's input (requantized
-// into one of two LDS buffers, so staging the next input does not wait for
-// the current rows), then take the workgroup's rows in turn (rows of all
-// GEMVs dealt round-robin), read each item from its slot, free the slot
-// and store each row as soon as it is done.  While consumers wait for an
-// input, producers keep filling the ring (~120 KB, ~5 us of this CU's
-// share of HBM), so the stream runs on through the wait.
-//
-// Slot handshakes live in LDS: full[slot] = the item number a producer
-// published there, freed[slot] = the last item a consumer took out of it.
-// A producer publishes an item once the vector memory counter shows its
-// loads done (the counter counts the LDS writes of these loads; each
-// producer keeps D items in flight and waits with a constant count).  The
-// producers access the flags through inline assembly: the compiler cannot
-// tell the flags from the DMA'd slots and would otherwise wait for every
-// load in flight before each flag access.  Each wave's LDS operations
-// complete in order, which orders data before flag and read before release.
-// Each row is reduced by one wave in chunk order and a butterfly, as the
-// unsplit eager kernel reduces it.  Every wait is bounded as in the kernel
-// above.
-
-__device__ inline uint32_t lds_offset(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ inline void lds_put(uint32_t a, int v) { asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory"); }
-__device__ inline void lds_inc(uint32_t a, int v) { asm volatile("ds_add_u32 %0, %1" ::"v"(a), "v"(v) : "memory"); }
-__device__ inline int lds_get(uint32_t a) {
-    int v;
-    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
-    return v;
-}
-
-// Rows of an op this workgroup owns: blockIdx.x + i * grid.
-__device__ inline int ring_rows(int n, int grid) {
-    return (int)blockIdx.x < n ? (n - 1 - (int)blockIdx.x) / grid + 1 : 0;
-}
-
-// Item s of the workgroup's sequence (op after op; within an op, row
-// i = e / C and chunk e % C of its e-th item) is fetched by producer wave
-// s % P into its own sub-ring of NSp slots: slot ring_slot(s).  A slot is
-// the chunk's device layout reordered: [first 16 codes of 64 blocks][last
-// 16 codes][64 fp16 scales] (2176 bytes).
-template <int P>
-__device__ inline int ring_slot(int s, int NSp) {
-    return (s % P) * NSp + (s / P) % NSp;
-}
-
-// D consecutive flags of a sub-ring (16-byte aligned), in one LDS round trip.
-template <int D>
-__device__ inline void lds_get_flags(uint32_t a, int (&f)[D]) {
-    static_assert(D == 4 || D == 8 || D == 12, "flag batches of 4, 8 or 12");
-    int4v x0, x1, x2;
-    if constexpr (D == 4) {
-        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x0) : "v"(a) : "memory");
-    } else if constexpr (D == 8) {
-        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(x0), "=&v"(x1)
-                     : "v"(a)
-                     : "memory");
-    } else {
-        asm volatile(
-            "ds_read_b128 %0, %3\n\tds_read_b128 %1, %3 offset:16\n\tds_read_b128 %2, %3 offset:32\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(x0), "=&v"(x1), "=&v"(x2)
-            : "v"(a)
-            : "memory");
-    }
-    const int4v xs[3] = {x0, x1, x2};
-#pragma unroll
-    for (int b = 0; b < D; ++b) f[b] = xs[b / 4][b % 4];
-}
-
-// The op of the item a producer requests next (wave-uniform: the
-// descriptors are read with scalar loads, which do not count against the
-// vector memory counter the weight ring relies on).
-struct ProdCursor {
-    int j = -1, op_base = 0, items_j = 0, C = 1, nl = 0, sbl = 0;
-    int64_t row_bytes = 0;
-    gptr<uint8_t> w = nullptr;
-    __device__ void seek(const StreamOp* __restrict__ ops, int s, int grid) {
-        while (s - op_base >= items_j) {
-            op_base += items_j;
-            j = __builtin_amdgcn_readfirstlane(j + 1);
-            const StreamOp* op = ops + j;
-            const int kk = __builtin_amdgcn_readfirstlane(op->k);
-            C = (int)chunk_count(kk);
-            nl = kk / kBlock - (C - 1) * kChunkBlocks;
-            sbl = (int)scale_section_bytes(nl);
-            row_bytes = packed_row_bytes(kk);
-            const uint64_t wa = reinterpret_cast<uint64_t>(op->w);
-            w = (gptr<uint8_t>)((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)wa) |
-                                ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(wa >> 32)) << 32));
-            items_j = ring_rows(__builtin_amdgcn_readfirstlane(op->n), grid) * C;
-        }
-    }
-};
-
-// Producer wave p fetches its items s = k P + p (k = 0, 1, ...) through a
-// ring of R register sets, as the row loops of the other kernels do: every
-// step writes the oldest set into its LDS slot, publishes it and refills
-// the set with the item R further on (past the workgroup's items: the idle
-// region), so R - 1 items stay in flight and the compiler waits for exactly
-// one set at a time.  Before the first item of each batch of D sub-slots it
-// checks, in one LDS round trip, that the batch's slots are free (their
-// items NSp earlier consumed).
-template <int P, int R>
-__device__ __attribute__((always_inline)) inline void ring_produce(const StreamOp* __restrict__ ops, int n_ops, int grid, uint8_t* ring, int NSp,
-                                    uint32_t full_a, uint32_t freed_a, uint32_t* st, int spin_limit) {
-    constexpr int D = 4;
-    const int p = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-    const int lane = (int)threadIdx.x % kWave;
-    int total = 0;  // items of this workgroup
-    for (int j = 0; j < n_ops; ++j) total += ring_rows(ops[j].n, grid) * (int)chunk_count(ops[j].k);
-    const int mine = total > p ? (total - 1 - p) / P + 1 : 0;  // this wave's items
-    const uint32_t my_full = full_a + 4u * (uint32_t)(p * NSp);
-    const uint32_t my_freed = freed_a + 4u * (uint32_t)(p * NSp);
-    uint8_t* my_ring = ring + (size_t)(p * NSp) * kFullChunkBytes;
-
-    ProdCursor cur;
-    // requests item k of this wave (the idle region past its last item)
-    auto load = [&](Q8Regs<1>& r, int k) {
-        gptr<uint8_t> cp = idle_bytes();
-        int nbc = kChunkBlocks, sb = 2 * kChunkBlocks;
-        if (k < mine) {
-            const int s = k * P + p;
-            cur.seek(ops, s, grid);
-            const int e = s - cur.op_base;
-            const int i = e / cur.C, c = e - i * cur.C;
-            const int row = (int)blockIdx.x + i * grid;
-            const bool last = c == cur.C - 1;
-            nbc = last ? cur.nl : kChunkBlocks;
-            sb = last ? cur.sbl : 2 * kChunkBlocks;
-            cp = cur.w + (int64_t)row * cur.row_bytes + (int64_t)c * kFullChunkBytes;
-        }
-        const int l = lane < nbc ? lane : nbc - 1;  // past a ragged chunk: re-read its last block
-        r.sc[0] = load_u16<true>(cp + 2 * l);
-        r.a[0] = load16<true>(cp + sb + 16 * l);
-        r.b[0] = load16<true>(cp + sb + 16 * nbc + 16 * l);
-    };
-    bool failed = false;
-    // writes item k (landed in r) into its slot and publishes it
-    auto store = [&](const Q8Regs<1>& r, int k) {
-        if (failed || k >= mine) return;
-        const int sub = k % NSp;
-        if (k % D == 0) {  // the batch's slots must be free
-            int spins = 0;
-            for (;;) {
-                int f[D];
-                lds_get_flags<D>(my_freed + 4u * (uint32_t)sub, f);
-                int bad = -1;
-#pragma unroll
-                for (int b = 0; b < D; ++b) {
-                    const int s = (k + b) * P + p;
-                    if (k + b < mine && f[b] < s - P * NSp) bad = b;
-                }
-                if (bad < 0) break;
-                if (!poll_again(st, spin_limit, spins, kSiteFreeSlot, cur.j, (k + bad) * P + p - P * NSp, f[bad])) {
-                    failed = true;
-                    return;
-                }
-            }
-        }
-        uint8_t* it = my_ring + (size_t)sub * kFullChunkBytes;
-        reinterpret_cast<int4v*>(it)[lane] = r.a[0];
-        reinterpret_cast<int4v*>(it + 16 * kWave)[lane] = r.b[0];
-        reinterpret_cast<uint16_t*>(it + 32 * kWave)[lane] = r.sc[0];
-        if (lane == 0) lds_put(my_full + 4u * (uint32_t)sub, k * P + p);  // after the data (LDS order)
-    };
-
-    Q8Regs<1> regs[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) load(regs[r], r);
-    for (int k0 = 0; k0 < mine; k0 += R) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            store(regs[r], k0 + r);
-            load(regs[r], k0 + r + R);
-        }
-    }
-    // the last refills read the idle region: let them land before the wave ends
-#pragma unroll
-    for (int r = 0; r < R; ++r) opaque(regs[r].a[0]), opaque(regs[r].b[0]);
-}
-
-// Consumer waves: per op, stage the input into act buffer j % 2, meet at an
-// LDS counter, then take rows t_base + i (the op's i-th row of this
-// workgroup) with (t_base + i) % NC == this wave.
-template <int W, int P>
-__device__ __attribute__((always_inline)) inline void ring_consume(const StreamOp* __restrict__ ops, int n_ops, int grid, uint32_t parity,
-                                    uint8_t* smem, int act_bytes, const uint8_t* ring, int NSp, uint32_t full_a,
-                                    uint32_t freed_a, uint32_t bar_a, uint32_t* st, int spin_limit) {
-    constexpr int NC = W - P;
-    constexpr int T = NC * kWave;
-    // rounds of staging loads in flight: a 17408-value input in one round trip
-    constexpr int NR = (17408 / 8 + T - 1) / T;
-    const int tid = (int)threadIdx.x - P * kWave;
-    const int cw = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int lane = (int)threadIdx.x % kWave;
-    int s_base = 0, t_base = 0;
-    for (int j = 0; j < n_ops; ++j) {
-        const StreamOp& op = ops[j];
-        const OpGeom g = op_geom<W>(op, parity);
-        const int rows = ring_rows(g.n, grid);
-        uint8_t* act = smem + (size_t)(j & 1) * act_bytes;
-        const int4v* lds_q = reinterpret_cast<const int4v*>(act);
-        const float* lds_dx = reinterpret_cast<const float*>(act + (size_t)g.C * 2 * kWave * 16);
-        if (op.dep) wait_range<T>((gcfloat)(op.dep + parity * op.dep_stride), op.dep_n, st, spin_limit, tid);
-        stage_requant<NR, T>(g.src, g.produced, g.k, st, spin_limit, reinterpret_cast<int4v*>(act),
-                            reinterpret_cast<float*>(act + (size_t)g.C * 2 * kWave * 16), tid);
-        // every consumer wave has staged its share (and so finished op j - 1)
-        if (lane == 0) lds_inc(bar_a, 1);
-        {
-            int spins = 0;
-            int seen;
-            while ((seen = lds_get(bar_a)) < NC * (j + 1))
-                if (!poll_again(st, spin_limit, spins, kSiteConsumers, j, NC * (j + 1), seen)) return;
-        }
-        int i = cw - t_base % NC;
-        if (i < 0) i += NC;
-        for (; i < rows; i += NC) {
-            const int row = (int)blockIdx.x + i * grid;
-            int s = s_base + i * g.C;
-            float acc = 0.0f;
-            for (int c = 0; c < g.C; ++c, ++s) {
-                const int slot = ring_slot<P>(s, NSp);
-                int spins = 0;
-                int seen;
-                while ((seen = lds_get(full_a + 4 * slot)) != s)
-                    if (!poll_again(st, spin_limit, spins, kSiteFullSlot, j, s, seen)) return;
-                const uint8_t* it = ring + (size_t)slot * kFullChunkBytes;
-                const int blk = c * kWave + lane;
-                if (blk < g.NB) {
-                    const int4v wa = reinterpret_cast<const int4v*>(it)[lane];
-                    const int4v wb = reinterpret_cast<const int4v*>(it + 16 * kWave)[lane];
-                    const uint16_t sc = reinterpret_cast<const uint16_t*>(it + 32 * kWave)[lane];
-                    const int4v xa = lds_q[(c * 2 + 0) * kWave + lane];
-                    const int4v xb = lds_q[(c * 2 + 1) * kWave + lane];
-                    int d = 0;
-                    d = __builtin_amdgcn_sdot4(wa.x, xa.x, d, false);
-                    d = __builtin_amdgcn_sdot4(wa.y, xa.y, d, false);
-                    d = __builtin_amdgcn_sdot4(wa.z, xa.z, d, false);
-                    d = __builtin_amdgcn_sdot4(wa.w, xa.w, d, false);
-                    d = __builtin_amdgcn_sdot4(wb.x, xb.x, d, false);
-                    d = __builtin_amdgcn_sdot4(wb.y, xb.y, d, false);
-                    d = __builtin_amdgcn_sdot4(wb.z, xb.z, d, false);
-                    d = __builtin_amdgcn_sdot4(wb.w, xb.w, d, false);
-                    const float t = half_bits_to_float(sc) * lds_dx[blk];
-                    acc = __builtin_fmaf(t, (float)d, acc);
-                }
-                if (lane == 0) lds_put(freed_a + 4 * slot, s);  // after this wave's reads of the slot
-            }
-            acc = wave_sum(acc);
-            if (lane == 0) {
-                g.y[row] = acc;
-                __hip_atomic_store(g.ynow + row, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(g.ynext + row, __uint_as_float(kSentinel), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        s_base += rows * g.C;
-        t_base += rows;
-    }
-}
-
-// LDS: [act 0][act 1][ring NS x 2176][full NS][freed NS][barrier, parity],
-// NS = P NSp (a sub-ring of NSp slots per producer).
-template <int W, int P, int R>
-__global__ void __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(W / 4)))
-ring_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict__ st, int spin_limit, int act_bytes,
-            int NSp) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    const int NS = P * NSp;
-    uint8_t* ring = smem + 2 * (size_t)act_bytes;
-    int* full = reinterpret_cast<int*>(ring + (size_t)NS * kFullChunkBytes);
-    int* freed = full + NS;
-    int* misc = freed + NS;
-    // slot i of sub-ring q first holds item s = (i - q NSp) P + q: as if its
-    // item s - P NSp had been consumed
-    for (int i = (int)threadIdx.x; i < NS; i += W * kWave) {
-        const int q = i / NSp;
-        full[i] = -1;
-        freed[i] = (i - q * NSp) * P + q - P * NSp;
-    }
-    if (threadIdx.x == 0) {
-        misc[0] = 0;
-        const uint64_t old = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(st + kStCounter), (uint64_t)1,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        misc[1] = (int)((old / gridDim.x) & 1u);
-    }
-    __syncthreads();
-    const uint32_t parity = (uint32_t)misc[1];
-    const int grid = (int)gridDim.x;
-    if ((int)threadIdx.x < P * kWave) {
-        ring_produce<P, R>(ops, n_ops, grid, ring, NSp, lds_offset(full), lds_offset(freed), st, spin_limit);
-    } else {
-        ring_consume<W, P>(ops, n_ops, grid, parity, smem, act_bytes, ring, NSp, lds_offset(full), lds_offset(freed),
-                        lds_offset(misc), st, spin_limit);
-    }
-}
-
-// Shapes of the ring kernel: waves per workgroup (fewer waves leave more
-// registers per wave), producer waves and the register sets each keeps
-// (R - 1 items in flight).  Variant 0 is the default.
-struct RingVariant {
-    int waves, producers, depth;
-    const void* kern;
-};
-constexpr int kRingVariants = 2;
-const RingVariant* ring_variant(int variant) {
-    // (16 waves: at most 128 registers each.  Shapes of 8 and 12 waves,
-    // whose producers can hold 16-21 items, measured slower and keep
-    // their staging in scratch memory.)
-    static const RingVariant v[kRingVariants] = {
-        {16, 4, 8, reinterpret_cast<const void*>(ring_kernel<16, 4, 8>)},
-        {16, 2, 10, reinterpret_cast<const void*>(ring_kernel<16, 2, 10>)},
-    };
-    return variant >= 0 && variant < kRingVariants ? &v[variant] : nullptr;
-}
-
 }  // namespace
 
 size_t stream_state_bytes() { return (size_t)kStWords * sizeof(uint32_t); }
@@ -773,51 +440,5 @@ void stream_shape(int* waves, int* unroll, int* sets) {
 }
 
 int64_t stream_max_rows(int split, int grid) { return (int64_t)kMaxTiles * grid * (kStreamWaves / split); }
-
-int ring_config(int max_k, int variant, int* grid, size_t* lds, int* act_bytes, int* slots) {
-    const RingVariant* v = ring_variant(variant);
-    if (!v) return WSG_ERR_MODE;
-    const int C = (int)chunk_count(max_k);
-    const int act = (int)lds_q8act_bytes(C);
-    const int64_t fixed = 2 * (int64_t)act + 16;
-    // each producer's sub-ring: a whole number of 4-slot batches (a batch's
-    // slots hold items that have all been written and published before it)
-    const int64_t per = ((int64_t)device_info().max_lds - fixed) / (kFullChunkBytes + 8) / v->producers;
-    const int64_t nsp = per / 4 * 4;
-    if (nsp < 4) return WSG_ERR_SHAPE;
-    const int64_t ns = nsp * v->producers;
-    const size_t bytes = (size_t)(fixed + ns * (kFullChunkBytes + 8));
-    if (hipFuncSetAttribute(v->kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
-        return WSG_ERR_HIP;
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v->kern, v->waves * kWave, bytes) != hipSuccess ||
-        per_cu < 1)
-        return WSG_ERR_HIP;
-    *grid = device_info().cus;  // one workgroup per CU: every producer of a consumer's input is resident
-    *lds = bytes;
-    *act_bytes = act;
-    *slots = (int)nsp;
-    return WSG_OK;
-}
-
-int ring_shape(int variant, int* waves, int* producers, int* depth) {
-    const RingVariant* v = ring_variant(variant);
-    if (!v) return WSG_ERR_MODE;
-    *waves = v->waves;
-    *producers = v->producers;
-    *depth = v->depth;
-    return WSG_OK;
-}
-
-int ring_variants() { return kRingVariants; }
-
-int ring_launch(const StreamOp* ops_dev, int n_ops, int variant, uint32_t* state_dev, int grid, size_t lds,
-                int act_bytes, int slots, int spin_limit, hipStream_t stream) {
-    const RingVariant* v = ring_variant(variant);
-    if (!v) return WSG_ERR_MODE;
-    void* args[] = {&ops_dev, &n_ops, &state_dev, &spin_limit, &act_bytes, &slots};
-    (void)hipLaunchKernel(v->kern, dim3(grid), dim3(v->waves * kWave), args, lds, stream);
-    return launch_status();
-}
 
 }  // namespace wsg

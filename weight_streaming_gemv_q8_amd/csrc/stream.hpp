@@ -31,8 +31,7 @@ constexpr uint32_t kStreamSentinel = 0x7FA5A5A5u;
 size_t stream_state_bytes();
 size_t stream_error_word();
 // First of the six words describing the first wait that gave up: site
-// (1 input/dependency, 2 free ring slot, 3 filled ring slot, 4 consumer
-// meeting), workgroup, wave, op, expected value, value seen.
+// (1 input/dependency), workgroup, wave, op, expected value, value seen.
 size_t stream_detail_word();
 
 // Launch geometry of the persistent kernel for a chain whose largest k is
@@ -46,15 +45,5 @@ void stream_shape(int* waves, int* unroll, int* sets);
 // Most rows one op may have at a split factor and grid (the tiles of a
 // workgroup wait in LDS until the op's end).
 int64_t stream_max_rows(int split, int grid);
-
-// The LDS-ring kernel (deq 0 chains), in one of ring_variants() shapes
-// (waves per workgroup, producer waves, register sets per producer).
-// ring_config sizes the two activation buffers and each producer's
-// sub-ring of weight slots (`slots` per producer) for the largest k.
-int ring_config(int max_k, int variant, int* grid, size_t* lds, int* act_bytes, int* slots);
-int ring_shape(int variant, int* waves, int* producers, int* depth);
-int ring_variants();
-int ring_launch(const StreamOp* ops_dev, int n_ops, int variant, uint32_t* state_dev, int grid, size_t lds,
-                int act_bytes, int slots, int spin_limit, hipStream_t stream);
 
 }  // namespace wsg

@@ -323,14 +323,13 @@ class TokenStream:
         for i in range(len(self.slots)):
             self.run_slot(i, stream)
 
-    def capture(self, stream=None, persistent: bool = False, ring=None) -> wsg.Plan:
+    def capture(self, stream=None, persistent: bool = False) -> wsg.Plan:
         """One hipGraph per token: a node per call, or (persistent=True, Q8_0
         chains with fused requantization or f32 activations) one resident
-        kernel for the whole token, or (ring=V, Q8_0 chains with fused
-        requantization) the LDS-ring kernel in variant V (True: default)."""
+        kernel for the whole token."""
         if self.plan is not None:
             self.plan.destroy()
-        self.plan = wsg.Plan(self.ops(), stream=stream, persistent=persistent, ring=ring)
+        self.plan = wsg.Plan(self.ops(), stream=stream, persistent=persistent)
         return self.plan
 
     def launch(self, stream=None) -> None:
