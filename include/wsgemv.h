@@ -14,11 +14,16 @@
  *
  * Conventions for every entry point:
  *  - Every pointer argument is a DEVICE pointer (except the descriptor array
- *    of wsg_plan_create, which is host memory), allocated and owned by the
- *    caller.  No entry point allocates or frees device memory, and none
- *    synchronizes the host with the device, so each can be captured into a
- *    hipGraph.  Only wsg_plan_create/destroy allocate (host-side graph
- *    objects).
+ *    of the plan calls and the outputs of the size and config queries,
+ *    which are host memory), allocated and owned by the caller.
+ *  - The hot calls (quantizers, GEMVs, the norm step, the LM head, embedding
+ *    and advance, the probes) allocate no device memory, never synchronize
+ *    the host with the device and can be captured into a hipGraph.  The
+ *    exceptions, which must not be called while a stream is capturing:
+ *    wsg_plan_create (builds and instantiates a graph, host memory only),
+ *    wsg_plan_create_persistent (allocates device state and synchronizes
+ *    the device), wsg_plan_error / wsg_plan_error_detail (synchronize) and
+ *    wsg_plan_destroy (frees).
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream).
  *    The return value is a status code, decided BEFORE anything is
  *    enqueued: on any nonzero status nothing was launched.  WSG_ERR_HIP
@@ -27,9 +32,13 @@
  *  - Outputs are overwritten, never accumulated into.
  *  - Weight, activation and quantized-activation pointers must be 16-byte
  *    aligned; f32 outputs and int32 outputs 4-byte aligned.
- *  - Sizes are int64_t; n and k must each be < 2^31.
- *  - The library is stateless apart from per-device launch parameters that
- *    it looks up once; all entry points are thread-safe.
+ *  - Sizes are int64_t (signed, so that the size queries can return -1 for
+ *    a bad shape); n and k must each be < 2^31.
+ *  - State: the library looks up per-device launch parameters once per
+ *    device (the device current at the call); wsg_tune holds process-wide
+ *    tuning knobs (for measurement sweeps) that change the launch shape of
+ *    later calls from every thread.  Apart from wsg_tune, all entry points
+ *    are thread-safe.
  */
 #ifndef WSGEMV_H
 #define WSGEMV_H
@@ -185,7 +194,10 @@ int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h
  *   W4A16 form of qwen3-8b-rtx4080-cutedsl, "W4A16 dequant-fused GEMM")
  *   y = sum_b d_w sum_i q_i x_i in f32 fused multiply-adds, accepted as
  *   gemv_q8_0's f32 path, 32 <= k <= WSG_MAX_K_F32ACT.  Other act_fmt:
- *   WSG_ERR_MODE; n >= 1 and k % 32 == 0 else WSG_ERR_SHAPE. */
+ *   WSG_ERR_MODE; n >= 1 and k % 32 == 0 else WSG_ERR_SHAPE.
+ * The "q4_0" names say "4-bit, block of 32, one scale" only: these blocks
+ * are NOT llama.cpp's Q4_0 (whose scale is signed and whose codes span
+ * [-8, 7]); llama.cpp Q4_0 files cannot be loaded through them. */
 int64_t q4_0_row_bytes(int64_t k);
 int64_t q4_0_packed_bytes(int64_t n, int64_t k);
 int quantize_q4_0_weights(const float* w, int64_t n, int64_t k, void* w_packed, hipStream_t stream);
@@ -285,15 +297,19 @@ int wsg_tune(int knob, int value);
  * to one key (value, lowest index among IEEE-equal values, -0 == +0) in
  * `ws`; stage 2 (one workgroup) writes the winning row index to *idx_out
  * in device memory.  The library never reads it back.  debug_logits
- * (nullable) receives the f32 logits.  n >= 1.  ws must hold at least
- * wsg_argmax_ws_bytes() bytes (8-byte aligned). */
+ * (nullable) receives the f32 logits.  n >= 1.  ws (8-byte aligned) must
+ * hold 8 bytes per stage-1 workgroup: lm_head_argmax_ws_bytes(n, k, w_type)
+ * bytes on the current device (any activation format), at most
+ * wsg_argmax_ws_bytes() = 64 KiB for every shape (WSG_ERR_WORKSPACE if
+ * smaller).  lm_head_argmax_ws_bytes returns -1 for a bad shape or type. */
 int64_t wsg_argmax_ws_bytes(void);
+int64_t lm_head_argmax_ws_bytes(int64_t n, int64_t k, int w_type);
 int lm_head_argmax(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt,
                    void* ws, size_t ws_bytes, int32_t* idx_out, float* debug_logits,
                    hipStream_t stream);
 
 /* The same two-stage argmax over an f32 vector v[n], n >= 1 (NaN outside
- * the contract). */
+ * the contract); ws as above, at least wsg_argmax_ws_bytes() bytes. */
 int argmax_f32(const float* v, int64_t n, void* ws, size_t ws_bytes, int32_t* idx_out,
                hipStream_t stream);
 

@@ -47,6 +47,16 @@ def test_status_strings_and_sizes(L):
     assert wsg.q8_0_packed_bytes(16384, 5120) == 16384 * 5440
     assert wsg.act_q8_0_bytes(4096) == 4096 + 256
     assert wsg.argmax_ws_bytes() >= 8 * 256
+    # per-shape LM-head workspace: 8 bytes per stage-1 workgroup, never
+    # more than the all-shapes maximum; -1 for a bad shape or type
+    for n, k, wt in ((151936, 4096, wsg.W_Q8_0), (151936, 4096, wsg.W_BF16), (10, 32, wsg.W_Q8_0)):
+        b = wsg.lm_head_argmax_ws_bytes(n, k, wt)
+        assert 8 <= b <= wsg.argmax_ws_bytes() and b % 8 == 0, (n, k, wt, b)
+    lib = wsg.lib()
+    assert lib.lm_head_argmax_ws_bytes(0, 4096, wsg.W_Q8_0) == -1
+    assert lib.lm_head_argmax_ws_bytes(10, 33, wsg.W_Q8_0) == -1
+    assert lib.lm_head_argmax_ws_bytes(10, 12, wsg.W_BF16) == -1
+    assert lib.lm_head_argmax_ws_bytes(10, 32, 7) == -1
 
 
 # Every call below must fail validation, so nothing is launched (no GPU here).
@@ -117,7 +127,12 @@ def test_lm_head_and_argmax_argument_errors(L):
     ws = wsg.argmax_ws_bytes()
     assert L.lm_head_argmax(A16, 5, 10, 32, A16, 0, A16, ws, A16, None, None) == wsg.ERR_MODE
     assert L.lm_head_argmax(A16, 1, 0, 32, A16, 0, A16, ws, A16, None, None) == wsg.ERR_SHAPE
-    assert L.lm_head_argmax(A16, 1, 10, 32, A16, 0, A16, 8, A16, None, None) == wsg.ERR_WORKSPACE
+    assert L.lm_head_argmax(A16, 1, 10, 32, A16, 0, A16, 4, A16, None, None) == wsg.ERR_WORKSPACE
+    # a workspace of exactly the per-shape size is accepted by validation
+    # (the fake addresses then fail the idx_out check, so nothing launches)
+    need = wsg.lm_head_argmax_ws_bytes(151936, 4096, wsg.W_Q8_0)
+    assert L.lm_head_argmax(A16, 1, 151936, 4096, A16, 0, A16, need - 8, A16, None, None) == wsg.ERR_WORKSPACE
+    assert L.lm_head_argmax(A16, 1, 151936, 4096, A16, 0, A16, need, 0x10002, None, None) == wsg.ERR_ALIGN
     assert L.lm_head_argmax(A16, 1, 10, 32, A16, 0, A16, ws, None, None, None) == wsg.ERR_NULL
     assert L.lm_head_argmax(A16, 1, 10, 32, A16, 0, 0x10004, ws, A16, None, None) == wsg.ERR_ALIGN
     assert L.argmax_f32(A16, 0, A16, ws, A16, None) == wsg.ERR_SHAPE

@@ -42,7 +42,7 @@ EXPORTS = (
     "residual_rmsnorm_q8_0", "embed_gather", "token_advance", "q4_0_row_bytes", "q4_0_packed_bytes",
     "quantize_q4_0_weights", "gemv_q4_0", "gemv_q4_0_rmsnorm", "gemv_q4_0_swiglu", "gemv_q8_0_rmsnorm", "gemv_q8_0_swiglu",
     "gemv_bf16",
-    "gemv_q8_0", "wsg_gemv_config", "wsg_tune", "wsg_argmax_ws_bytes", "lm_head_argmax", "argmax_f32", "wsg_plan_create",
+    "gemv_q8_0", "wsg_gemv_config", "wsg_tune", "wsg_argmax_ws_bytes", "lm_head_argmax_ws_bytes", "lm_head_argmax", "argmax_f32", "wsg_plan_create",
     "wsg_plan_launch", "wsg_plan_create_persistent", "wsg_plan_error", "wsg_plan_error_detail", "wsg_plan_destroy", "wsg_plan_kernel_count",
     "wsg_stream_config", "wsg_read_probe",
     "wsg_copy_probe",
@@ -106,6 +106,7 @@ def lib():
                                        ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i64)]),
             "wsg_tune": (i32, [i32, i32]),
             "wsg_argmax_ws_bytes": (i64, []),
+            "lm_head_argmax_ws_bytes": (i64, [i64, i64, i32]),
             "lm_head_argmax": (i32, [vp, i32, i64, i64, vp, i32, vp, ctypes.c_size_t, vp, vp, vp]),
             "argmax_f32": (i32, [vp, i64, vp, ctypes.c_size_t, vp, vp]),
             "wsg_plan_create": (i32, [ctypes.POINTER(OpDesc), i32, vp, ctypes.POINTER(vp)]),
@@ -173,6 +174,14 @@ def act_q8_0_bytes(k: int) -> int:
 
 def argmax_ws_bytes() -> int:
     return int(lib().wsg_argmax_ws_bytes())
+
+
+def lm_head_argmax_ws_bytes(n: int, k: int, w_type: int) -> int:
+    """Workspace the LM-head argmax of this shape needs on the current device."""
+    v = int(lib().lm_head_argmax_ws_bytes(n, k, w_type))
+    if v < 0:
+        raise WsgError("lm_head_argmax_ws_bytes", ERR_SHAPE)
+    return v
 
 
 # --------------------------------------------------------- weight prep

@@ -30,6 +30,7 @@
 #include <cstdlib>
 #include <type_traits>
 #include <map>
+#include <tuple>
 #include <mutex>
 #include <utility>
 
@@ -747,23 +748,38 @@ __global__ void argmax_stage2_kernel(const uint64_t* __restrict__ keys, int coun
 // ------------------------------------------------------------- planning
 constexpr int kMaxGrid = 8192;  // keys in the argmax workspace
 
-std::once_flag g_info_once;
-DeviceInfo g_info;
+// Per-device facts, looked up once per device (the device current at the
+// call), so a process that drives several GPUs sizes each one's grids from
+// that GPU.
+constexpr int kMaxDevices = 64;
+std::once_flag g_info_once[kMaxDevices];
+DeviceInfo g_info[kMaxDevices];
+DeviceInfo g_info_fallback;
+
+int current_device() {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    return dev;
+}
 
 }  // namespace
 
 const DeviceInfo& device_info() {
-    std::call_once(g_info_once, [] {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
+    const int dev = current_device();
+    if (dev < 0 || dev >= kMaxDevices) {
+        g_info_fallback.cus = 256;
+        g_info_fallback.max_lds = 65536;
+        return g_info_fallback;
+    }
+    std::call_once(g_info_once[dev], [dev] {
+        DeviceInfo& d = g_info[dev];
         int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) g_info.cus = v;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess)
-            g_info.max_lds = v;
-        if (g_info.cus <= 0) g_info.cus = 256;
-        if (g_info.max_lds <= 0) g_info.max_lds = 65536;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) d.cus = v;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess) d.max_lds = v;
+        if (d.cus <= 0) d.cus = 256;
+        if (d.max_lds <= 0) d.max_lds = 65536;
     });
-    return g_info;
+    return g_info[dev];
 }
 
 namespace {
@@ -812,19 +828,20 @@ int tune_wg_per_cu() {
 }
 
 // Workgroups resident per CU for a kernel with the given dynamic LDS
-// (looked up once per kernel and LDS size).
+// (looked up once per device, kernel and LDS size).
 template <typename K>
 int resident_per_cu(K kernel, int threads, size_t lds) {
     static std::mutex mu;
-    static std::map<std::pair<const void*, size_t>, int> cache;
+    static std::map<std::tuple<int, const void*, size_t>, int> cache;
     const void* key = reinterpret_cast<const void*>(kernel);
+    const auto id = std::make_tuple(current_device(), key, lds);
     std::lock_guard<std::mutex> lock(mu);
-    auto it = cache.find({key, lds});
+    auto it = cache.find(id);
     if (it != cache.end()) return it->second;
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, key, threads, lds) != hipSuccess || blocks < 1)
         blocks = 1;
-    cache[{key, lds}] = blocks;
+    cache[id] = blocks;
     return blocks;
 }
 
@@ -1242,18 +1259,51 @@ int validate_gemv_q4_swiglu(const void* w, int64_t n_ff, int64_t k, const void* 
     return validate_gemv_q8_swiglu(w, n_ff, k, x, act_fmt, y);  // the same arguments; only the layout differs
 }
 
-int validate_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, const void* ws,
-                     size_t ws_bytes, const void* idx_out) {
+namespace {
+// Stage-1 workgroups (= argmax keys) of the LM-head launch of this shape on
+// the current device; launches nothing.  -1 for an unknown format.
+int lm_head_grid(int w_type, int act_fmt, int n, int k) {
+    LaunchInfo info;
+    int rc;
+    if (w_type == WSG_W_BF16)
+        rc = launch_bf16<true>(nullptr, n, k, nullptr, nullptr, nullptr, nullptr, &info, false);
+    else if (act_fmt == WSG_ACT_F32)
+        rc = launch_q8_f32<true>(nullptr, n, k, nullptr, nullptr, nullptr, nullptr, &info, false);
+    else if (act_fmt == WSG_ACT_Q8_0)
+        rc = launch_q8_i8<kActQ8, false, true>(nullptr, n, k, nullptr, nullptr, nullptr, nullptr, nullptr, &info,
+                                                false);
+    else if (act_fmt == WSG_ACT_F32_REQUANT)
+        rc = launch_q8_i8<kActRequant, false, true>(nullptr, n, k, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                     &info, false);
+    else
+        return -1;
+    return rc == WSG_OK ? info.grid : -1;
+}
+
+// The LM head's checks that do not involve the workspace.
+int check_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, const void* idx_out) {
     if (w_type != WSG_W_BF16 && w_type != WSG_W_Q8_0) return WSG_ERR_MODE;
     if (n < 1) return WSG_ERR_SHAPE;
-    if (!idx_out || !ws) return WSG_ERR_NULL;
-    if (!aligned(ws, 8) || !aligned(idx_out, 4)) return WSG_ERR_ALIGN;
-    if (ws_bytes < (size_t)kMaxGrid * 8) return WSG_ERR_WORKSPACE;
+    if (!idx_out) return WSG_ERR_NULL;
+    if (!aligned(idx_out, 4)) return WSG_ERR_ALIGN;
     // logits pointer is optional: validate the GEMV part with a dummy non-null output
     const int rc = w_type == WSG_W_BF16 ? check_bf16_args(w, n, k, x, idx_out)
                                         : check_q8_args(w, n, k, x, act_fmt, idx_out);
     if (rc != WSG_OK) return rc;
     if (k == 0) return WSG_ERR_SHAPE;
+    return WSG_OK;
+}
+}  // namespace
+
+int validate_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, const void* ws,
+                     size_t ws_bytes, const void* idx_out) {
+    int rc = check_lm_head(w, w_type, n, k, x, act_fmt, idx_out);
+    if (rc != WSG_OK) return rc;
+    if (!ws) return WSG_ERR_NULL;
+    if (!aligned(ws, 8)) return WSG_ERR_ALIGN;
+    const int grid = lm_head_grid(w_type, w_type == WSG_W_BF16 ? WSG_ACT_F32 : act_fmt, (int)n, (int)k);
+    if (grid < 1) return WSG_ERR_HIP;
+    if (ws_bytes < (size_t)grid * 8) return WSG_ERR_WORKSPACE;
     return WSG_OK;
 }
 
@@ -1330,6 +1380,25 @@ int gemv_bf16(const uint16_t* w, int64_t n, int64_t k, const float* x, float* y,
 }
 
 int64_t wsg_argmax_ws_bytes(void) { return (int64_t)kMaxGrid * 8; }
+
+int64_t lm_head_argmax_ws_bytes(int64_t n, int64_t k, int w_type) {
+    if (w_type != WSG_W_BF16 && w_type != WSG_W_Q8_0) return -1;
+    if (n < 1 || k < 1 || n > kMaxDim || k > kMaxDim) return -1;
+    if (w_type == WSG_W_BF16 ? (k % 8 || k > WSG_MAX_K_F32ACT) : (k % kBlock || k > WSG_MAX_K_Q8ACT)) return -1;
+    int grid = 0;
+    if (w_type == WSG_W_BF16) {
+        grid = lm_head_grid(WSG_W_BF16, WSG_ACT_F32, (int)n, (int)k);
+    } else {
+        // every activation format of the Q8_0 head (the f32 one only where k allows it)
+        for (int act : {WSG_ACT_Q8_0, WSG_ACT_F32_REQUANT, WSG_ACT_F32}) {
+            if (act == WSG_ACT_F32 && k > WSG_MAX_K_F32ACT) continue;
+            const int g = lm_head_grid(WSG_W_Q8_0, act, (int)n, (int)k);
+            if (g < 1) return -1;
+            grid = g > grid ? g : grid;
+        }
+    }
+    return grid < 1 ? -1 : (int64_t)grid * 8;
+}
 
 int wsg_tune(int knob, int value) {
     if (value < 0) return WSG_ERR_SHAPE;
