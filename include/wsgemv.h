@@ -22,8 +22,9 @@
  *    exceptions, which must not be called while a stream is capturing:
  *    wsg_plan_create (builds and instantiates a graph, host memory only),
  *    wsg_plan_create_persistent (allocates device state and synchronizes
- *    the device), wsg_plan_error / wsg_plan_error_detail (synchronize) and
- *    wsg_plan_destroy (frees).
+ *    the device), wsg_plan_error / wsg_plan_error_detail (synchronize),
+ *    wsg_plan_destroy (frees), and the first lm_head_argmax_static call on
+ *    each device (looks up its static array; later calls are capturable).
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream).
  *    The return value is a status code, decided BEFORE anything is
  *    enqueued: on any nonzero status nothing was launched.  WSG_ERR_HIP
@@ -37,8 +38,9 @@
  *  - State: the library looks up per-device launch parameters once per
  *    device (the device current at the call); wsg_tune holds process-wide
  *    tuning knobs (for measurement sweeps) that change the launch shape of
- *    later calls from every thread.  Apart from wsg_tune, all entry points
- *    are thread-safe.
+ *    later calls from every thread; lm_head_argmax_static keeps one static
+ *    array per GPU.  Apart from wsg_tune and overlapping calls of
+ *    lm_head_argmax_static on one GPU, all entry points are thread-safe.
  */
 #ifndef WSGEMV_H
 #define WSGEMV_H
@@ -307,6 +309,23 @@ int64_t lm_head_argmax_ws_bytes(int64_t n, int64_t k, int w_type);
 int lm_head_argmax(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt,
                    void* ws, size_t ws_bytes, int32_t* idx_out, float* debug_logits,
                    hipStream_t stream);
+
+/* lm_head_argmax for callers that cannot allocate device memory (code
+ * under hipGraph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, results and errors as lm_head_argmax,
+ * but the stage-1 keys go to an array in the library's static device memory
+ * instead of a caller workspace, so the call allocates nothing (no
+ * hipMalloc or allocating library routine).  The array holds 8192 keys
+ * (64 KiB) on every GPU the library runs on, until the process ends; a
+ * shape whose stage 1 would need more keys gets WSG_ERR_WORKSPACE (no shape
+ * that passes the other checks does).  Every call on one GPU uses that
+ * GPU's array, which keeps the last call's keys; each call writes every key
+ * it reads, so nothing needs clearing, but calls that overlap in time on
+ * one GPU (two streams, two threads) race and give undefined indices.  The
+ * first call on each device looks up the array's address (do it outside
+ * stream capture); later calls are capturable. */
+int lm_head_argmax_static(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt,
+                          int32_t* idx_out, float* debug_logits, hipStream_t stream);
 
 /* The same two-stage argmax over an f32 vector v[n], n >= 1 (NaN outside
  * the contract); ws as above, at least wsg_argmax_ws_bytes() bytes. */

@@ -42,7 +42,7 @@ EXPORTS = (
     "residual_rmsnorm_q8_0", "embed_gather", "token_advance", "q4_0_row_bytes", "q4_0_packed_bytes",
     "quantize_q4_0_weights", "gemv_q4_0", "gemv_q4_0_rmsnorm", "gemv_q4_0_swiglu", "gemv_q8_0_rmsnorm", "gemv_q8_0_swiglu",
     "gemv_bf16",
-    "gemv_q8_0", "wsg_gemv_config", "wsg_tune", "wsg_argmax_ws_bytes", "lm_head_argmax_ws_bytes", "lm_head_argmax", "argmax_f32", "wsg_plan_create",
+    "gemv_q8_0", "wsg_gemv_config", "wsg_tune", "wsg_argmax_ws_bytes", "lm_head_argmax_ws_bytes", "lm_head_argmax", "lm_head_argmax_static", "argmax_f32", "wsg_plan_create",
     "wsg_plan_launch", "wsg_plan_create_persistent", "wsg_plan_error", "wsg_plan_error_detail", "wsg_plan_destroy", "wsg_plan_kernel_count",
     "wsg_stream_config", "wsg_read_probe",
     "wsg_copy_probe",
@@ -108,6 +108,7 @@ def lib():
             "wsg_argmax_ws_bytes": (i64, []),
             "lm_head_argmax_ws_bytes": (i64, [i64, i64, i32]),
             "lm_head_argmax": (i32, [vp, i32, i64, i64, vp, i32, vp, ctypes.c_size_t, vp, vp, vp]),
+            "lm_head_argmax_static": (i32, [vp, i32, i64, i64, vp, i32, vp, vp, vp]),
             "argmax_f32": (i32, [vp, i64, vp, ctypes.c_size_t, vp, vp]),
             "wsg_plan_create": (i32, [ctypes.POINTER(OpDesc), i32, vp, ctypes.POINTER(vp)]),
             "wsg_plan_launch": (i32, [vp, vp]),
@@ -308,6 +309,14 @@ def lm_head_argmax(w, w_type: int, n: int, k: int, x, act_fmt: int, ws, ws_bytes
     _check("lm_head_argmax", lib().lm_head_argmax(_ptr(w), w_type, n, k, _ptr(x), act_fmt, _ptr(ws),
                                                   ws_bytes, _ptr(idx_out), _ptr(debug_logits),
                                                   _stream(stream)))
+
+
+def lm_head_argmax_static(w, w_type: int, n: int, k: int, x, act_fmt: int, idx_out, debug_logits=None,
+                          stream=None) -> None:
+    """lm_head_argmax without a workspace (keys in the library's static array)."""
+    _check("lm_head_argmax_static", lib().lm_head_argmax_static(_ptr(w), w_type, n, k, _ptr(x), act_fmt,
+                                                                _ptr(idx_out), _ptr(debug_logits),
+                                                                _stream(stream)))
 
 
 def argmax_f32(v, n: int, ws, ws_bytes: int, idx_out, stream=None) -> None:

@@ -1307,6 +1307,39 @@ int validate_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void
     return WSG_OK;
 }
 
+// ------------------------------------------- the no-allocation LM head
+// The stage-1 keys of lm_head_argmax_static: one array in the library's
+// static device memory, kMaxGrid keys (64 KiB), which every GPU the library
+// runs on holds until the process ends.  In host code `scratch` names a
+// host-side stand-in, not the device array: its device address is looked up
+// with hipGetSymbolAddress, once per device with that device current, and
+// only that address is passed to kernels.
+namespace {
+static __device__ __align__(256) uint64_t scratch[kMaxGrid];
+constexpr size_t kScratchKeys = sizeof(scratch) / sizeof(scratch[0]);
+
+std::mutex g_scratch_mu;
+uint64_t* g_scratch_dev[kMaxDevices];  // device address of `scratch` per device (nullptr: not looked up)
+
+// The current device's copy of `scratch` (looked up on the first call on
+// that device).
+int scratch_keys(uint64_t** out) {
+    const int dev = current_device();
+    if (dev < 0 || dev >= kMaxDevices) return WSG_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return WSG_ERR_HIP;
+        }
+        g_scratch_dev[dev] = static_cast<uint64_t*>(ptr);
+    }
+    *out = g_scratch_dev[dev];
+    return WSG_OK;
+}
+}  // namespace
+
 }  // namespace wsg
 
 using namespace wsg;
@@ -1453,12 +1486,11 @@ int wsg_gemv_config(int w_type, int act_fmt, int64_t n, int64_t k, int* waves, i
     return WSG_OK;
 }
 
-int lm_head_argmax(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, void* ws,
-                   size_t ws_bytes, int32_t* idx_out, float* debug_logits, hipStream_t stream) {
-    int rc = validate_lm_head(w, w_type, n, k, x, act_fmt, ws, ws_bytes, idx_out);
-    if (rc != WSG_OK) return rc;
-    if (debug_logits && !aligned(debug_logits, 4)) return WSG_ERR_ALIGN;
-    uint64_t* keys = static_cast<uint64_t*>(ws);
+namespace {
+// The LM-head GEMV with stage 1 into `keys`, then stage 2 (arguments checked).
+int launch_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, uint64_t* keys,
+                   int32_t* idx_out, float* debug_logits, hipStream_t stream) {
+    int rc;
     const int ni = (int)n, ki = (int)k;
     LaunchInfo info;
     if (w_type == WSG_W_BF16) {
@@ -1473,6 +1505,31 @@ int lm_head_argmax(const void* w, int w_type, int64_t n, int64_t k, const void* 
     }
     if (rc != WSG_OK) return rc;
     return launch_argmax_stage2(keys, info.grid, idx_out, stream);
+}
+}  // namespace
+
+int lm_head_argmax(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt, void* ws,
+                   size_t ws_bytes, int32_t* idx_out, float* debug_logits, hipStream_t stream) {
+    const int rc = validate_lm_head(w, w_type, n, k, x, act_fmt, ws, ws_bytes, idx_out);
+    if (rc != WSG_OK) return rc;
+    if (debug_logits && !aligned(debug_logits, 4)) return WSG_ERR_ALIGN;
+    return launch_lm_head(w, w_type, n, k, x, act_fmt, static_cast<uint64_t*>(ws), idx_out, debug_logits, stream);
+}
+
+int lm_head_argmax_static(const void* w, int w_type, int64_t n, int64_t k, const void* x, int act_fmt,
+                          int32_t* idx_out, float* debug_logits, hipStream_t stream) {
+    int rc = check_lm_head(w, w_type, n, k, x, act_fmt, idx_out);
+    if (rc != WSG_OK) return rc;
+    if (debug_logits && !aligned(debug_logits, 4)) return WSG_ERR_ALIGN;
+    // the stage-1 keys must fit the static array (the grid never exceeds
+    // kMaxGrid workgroups, so every valid shape does)
+    const int grid = lm_head_grid(w_type, w_type == WSG_W_BF16 ? WSG_ACT_F32 : act_fmt, (int)n, (int)k);
+    if (grid < 1) return WSG_ERR_HIP;
+    if ((size_t)grid > kScratchKeys) return WSG_ERR_WORKSPACE;
+    uint64_t* keys = nullptr;
+    rc = scratch_keys(&keys);
+    if (rc != WSG_OK) return rc;
+    return launch_lm_head(w, w_type, n, k, x, act_fmt, keys, idx_out, debug_logits, stream);
 }
 
 int argmax_f32(const float* v, int64_t n, void* ws, size_t ws_bytes, int32_t* idx_out, hipStream_t stream) {
