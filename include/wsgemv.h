@@ -179,6 +179,18 @@ int residual_rmsnorm_q8_0(const float* h, const float* r, const float* g, int64_
 int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r, const float* g,
                       float eps, float* h_out, float* y, hipStream_t stream);
 
+/* The deq 2 form of gemv_q8_0_rmsnorm: the same residual add + RMSNorm in
+ * every workgroup's prologue, then the dequantizing GEMV on the f32
+ * normalized vector (no activation quantization; emit_qwen38_generate,
+ * "Where the speed comes from", the deq paragraph):
+ *   y = W . (h' / sqrt(mean h'^2 + eps) * g),  f32 activations,
+ * bit for bit gemv_q8_0 with WSG_ACT_F32 fed the y (f32) that
+ * residual_rmsnorm_q8_0 computes, and h_out as that call's h_out.
+ * Arguments, races and errors as gemv_q8_0_rmsnorm, with
+ * 32 <= k <= WSG_MAX_K_F32ACT. */
+int gemv_q8_0_rmsnorm_f32(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r,
+                          const float* g, float eps, float* h_out, float* y, hipStream_t stream);
+
 /* ---------------------------------------------------------- W4 weights --
  * 4-bit blocks (qwen3-8b-rtx4080-cutedsl, "W4A16 dequant-fused GEMM"; GPU
  * Kernel Lab, "Quantization experiments"): per 32 weights an fp16 scale
@@ -219,7 +231,8 @@ int gemv_q4_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h
  * Kernel Lab, "What we built", "Decode integration", on 4-bit weights):
  * w_packed holds 2 n_ff rows in the 4-bit layout, gate rows first;
  * y[p] = silu(g_p) u_p with g_p, u_p the int8-path outputs of rows p and
- * n_ff + p.  Arguments, acceptance and errors as gemv_q8_0_swiglu. */
+ * n_ff + p.  Arguments, acceptance and errors as gemv_q8_0_swiglu, with
+ * int8 activations only (WSG_ACT_F32: WSG_ERR_MODE). */
 int gemv_q4_0_swiglu(const void* w_packed, int64_t n_ff, int64_t k, const void* x, int act_fmt, float* y,
                      hipStream_t stream);
 
@@ -229,12 +242,14 @@ int gemv_q4_0_swiglu(const void* w_packed, int64_t n_ff, int64_t k, const void* 
  *   g_p = W[p] . x,  u_p = W[n_ff + p] . x,  y[p] = silu(g_p) u_p,
  *   silu(t) = t / (1 + exp(-t)),  p < n_ff,
  * for W in the device layout with 2 n_ff rows (the concatenated gate+up
- * matrix, gate rows first) and int8 activations (act_fmt WSG_ACT_Q8_0 or
- * WSG_ACT_F32_REQUANT; WSG_ERR_MODE otherwise).  Only the n_ff products are
- * written.  g_p and u_p are reduced as gemv_q8_0 reduces an unsplit row.
- * Acceptance: the two GEMV bounds propagated through silu(g) u (slope of
- * silu <= 1.1) plus 2^-20 relative for the fp32 epilogue.  n_ff >= 1,
- * 32 <= k <= WSG_MAX_K_Q8ACT, k % 32 == 0 (WSG_ERR_SHAPE). */
+ * matrix, gate rows first), with int8 activations (act_fmt WSG_ACT_Q8_0 or
+ * WSG_ACT_F32_REQUANT) or f32 ones (WSG_ACT_F32: the W8A16 form of GPU
+ * Kernel Lab, "Quantization experiments"; deq 2).  Only the n_ff products
+ * are written.  g_p and u_p are reduced as gemv_q8_0 reduces an unsplit
+ * row in that activation format.  Acceptance: the two GEMV bounds (of the
+ * format) propagated through silu(g) u (slope of silu <= 1.1) plus 2^-20
+ * relative for the fp32 epilogue.  n_ff >= 1, k % 32 == 0,
+ * 32 <= k <= WSG_MAX_K_Q8ACT (WSG_MAX_K_F32ACT for f32) (WSG_ERR_SHAPE). */
 int gemv_q8_0_swiglu(const void* w_packed, int64_t n_ff, int64_t k, const void* x, int act_fmt, float* y,
                      hipStream_t stream);
 
@@ -346,7 +361,8 @@ enum {
     WSG_OP_LM_HEAD_ARGMAX = 3,  /* w, w_type, n, k, x, act_fmt, ws, ws_bytes, idx_out */
     WSG_OP_RESIDUAL_RMSNORM = 4, /* residual_rmsnorm_q8_0: x = h, r, w = g, k, eps,
                                     h_out, y (f32 y), y_q8 */
-    WSG_OP_GEMV_Q8_0_RMSNORM = 5, /* gemv_q8_0_rmsnorm: w, n, k, x = h, r, g, eps, h_out, y */
+    WSG_OP_GEMV_Q8_0_RMSNORM = 5, /* gemv_q8_0_rmsnorm (act_fmt WSG_ACT_F32: gemv_q8_0_rmsnorm_f32):
+                                     w, n, k, x = h, r, g, eps, h_out, y */
     WSG_OP_GEMV_Q8_0_SWIGLU = 6,  /* gemv_q8_0_swiglu: w, n = n_ff, k, x, act_fmt, y */
     WSG_OP_EMBED_GATHER = 7,      /* embed_gather: w = table, w_type, n = vocab, k = hidden, x = token, y */
     WSG_OP_TOKEN_ADVANCE = 8,     /* token_advance: x = token, idx_out = history, n = capacity, ws = pos */

@@ -78,13 +78,13 @@ def test_token_advance(gpu_lib):
     assert e.value.status == wsg.ERR_SHAPE
 
 
-def _decode_step(vocab, layers, wtype="q8_0"):
+def _decode_step(vocab, layers, wtype="q8_0", deq=0):
     import torch
 
     from weight_streaming_gemv_q8_amd.stream import DecodeStep
     wl = W.QWEN3_8B_Q8
     shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
-    ds = DecodeStep(shapes, layers, vocab, capacity=16, eps=W.RMSNORM_EPS, wtype=wtype)
+    ds = DecodeStep(shapes, layers, vocab, capacity=16, eps=W.RMSNORM_EPS, wtype=wtype, deq=deq)
     stream = torch.cuda.current_stream().cuda_stream
 
     def fill(layer, m, part, rows, staging):
@@ -103,10 +103,22 @@ def _decode_step(vocab, layers, wtype="q8_0"):
     return ds, wl.seed
 
 
-@pytest.mark.parametrize("wtype", ["q8_0", "q4_0"])
-def test_decode_step_graph_equals_eager_and_oracle(gpu_lib, wtype):
+@pytest.mark.parametrize("wtype,deq", [("q8_0", 0), ("q8_0", 1), ("q8_0", 2), ("q4_0", 0), ("q4_0", 1)])
+def test_decode_step_graph_equals_eager_and_oracle(gpu_lib, wtype, deq):
+    """deq (emit_qwen38_generate, the deq paragraph): 0 int8 activations
+    everywhere; 1 the LM head on the f32 final norm output; 2 (Q8_0 layers)
+    f32 activations in every GEMV: the fused norm GEMVs' f32 form, the
+    W8A16 SwiGLU GEMV, the dequantizing down projection and LM head."""
+    wsg = gpu_lib
     vocab, layers, steps, first = 32000, 2, 5, 7
-    ds, seed = _decode_step(vocab, layers, wtype)
+    ds, seed = _decode_step(vocab, layers, wtype, deq)
+    if deq == 2:
+        ops = ds.ops()
+        assert not any(o.op == wsg.OP_QUANTIZE_ACT for o in ops)
+        assert all(o.act_fmt == wsg.ACT_F32 for o in ops
+                   if o.op in (wsg.OP_GEMV_Q8_0, wsg.OP_GEMV_Q8_0_RMSNORM, wsg.OP_GEMV_Q8_0_SWIGLU,
+                               wsg.OP_LM_HEAD_ARGMAX))
+        assert all(o.y_q8 is None or not o.y_q8 for o in ops if o.op == wsg.OP_RESIDUAL_RMSNORM)
     hidden = ds.hidden
     rng = np.random.default_rng(0xDEC0)
     ds.reset(first)
@@ -123,8 +135,11 @@ def test_decode_step_graph_equals_eager_and_oracle(gpu_lib, wtype):
         assert tok == oracle.argmax_f32(logits), f"step {step}: argmax"
         rows = np.array(sorted({0, vocab - 1, tok} | set(int(v) for v in rng.integers(0, vocab, 40))))
         dw, qw = _q8_rows_host(seed, HEAD_ID, hidden, rows, W.WEIGHT_SIGMA)
-        dx, qx = split_act_q8(host(ds.final_q8), hidden)
-        y_ref, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
+        if deq == 0:
+            dx, qx = split_act_q8(host(ds.final_q8), hidden)
+            y_ref, den = oracle.gemv_q8_act_q8(dw, qw, dx, qx)
+        else:
+            y_ref, den = oracle.gemv_q8_act_f32(dw, qw, host(ds.final_y))
         assert_within(logits[rows], y_ref, oracle.q8_tolerance(den), f"step {step}: LM-head logits")
     eager = host(ds.history).copy()
     assert int(host(ds.pos)[0]) == steps and np.all(eager[:steps] >= 0) and np.all(eager[steps:] == -1)

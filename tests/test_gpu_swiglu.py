@@ -12,7 +12,8 @@ fused with SwiGLU at batch 1).
 * a 2-layer chain whose down projection reads the SwiGLU outputs replays
   bit-identically to its eager calls, and every link matches the oracle
   fed the GPU's own inputs;
-* what it does not run is rejected."""
+* what it does not run is rejected.  (The f32-activation W8A16 form is
+  tested in test_gpu_deq2.py.)"""
 import numpy as np
 import pytest
 
@@ -83,8 +84,8 @@ def test_swiglu_rejections(gpu_lib):
     wsg = gpu_lib
     _, packed, x = _problem(64, 1024, 0x5EEDA100)
     y = torch.empty(64, dtype=torch.float32, device="cuda")
-    with pytest.raises(wsg.WsgError) as e:
-        wsg.gemv_q8_0_swiglu(packed, 64, 1024, dev(x), wsg.ACT_F32, y)
+    with pytest.raises(wsg.WsgError) as e:  # not an activation format
+        wsg.gemv_q8_0_swiglu(packed, 64, 1024, dev(x), 7, y)
     assert e.value.status == wsg.ERR_MODE
     for n_ff, k in ((0, 1024), (64, 0), (64, 1000)):
         with pytest.raises(wsg.WsgError) as e:

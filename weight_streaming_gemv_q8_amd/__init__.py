@@ -40,7 +40,7 @@ EXPORTS = (
     "wsg_status_str", "wsg_version", "q8_0_row_bytes", "q8_0_packed_bytes", "pack_q8_0",
     "quantize_q8_0_weights", "convert_bf16", "act_q8_0_bytes", "quantize_act_q8_0",
     "residual_rmsnorm_q8_0", "embed_gather", "token_advance", "q4_0_row_bytes", "q4_0_packed_bytes",
-    "quantize_q4_0_weights", "gemv_q4_0", "gemv_q4_0_rmsnorm", "gemv_q4_0_swiglu", "gemv_q8_0_rmsnorm", "gemv_q8_0_swiglu",
+    "quantize_q4_0_weights", "gemv_q4_0", "gemv_q4_0_rmsnorm", "gemv_q4_0_swiglu", "gemv_q8_0_rmsnorm", "gemv_q8_0_rmsnorm_f32", "gemv_q8_0_swiglu",
     "gemv_bf16",
     "gemv_q8_0", "wsg_gemv_config", "wsg_tune", "wsg_argmax_ws_bytes", "lm_head_argmax_ws_bytes", "lm_head_argmax", "lm_head_argmax_static", "argmax_f32", "wsg_plan_create",
     "wsg_plan_launch", "wsg_plan_create_persistent", "wsg_plan_error", "wsg_plan_error_detail", "wsg_plan_destroy", "wsg_plan_kernel_count",
@@ -91,6 +91,7 @@ def lib():
             "quantize_act_q8_0": (i32, [vp, i64, vp, vp]),
             "residual_rmsnorm_q8_0": (i32, [vp, vp, vp, i64, ctypes.c_float, vp, vp, vp, vp]),
             "gemv_q8_0_rmsnorm": (i32, [vp, i64, i64, vp, vp, vp, ctypes.c_float, vp, vp, vp]),
+            "gemv_q8_0_rmsnorm_f32": (i32, [vp, i64, i64, vp, vp, vp, ctypes.c_float, vp, vp, vp]),
             "gemv_q4_0_rmsnorm": (i32, [vp, i64, i64, vp, vp, vp, ctypes.c_float, vp, vp, vp]),
             "gemv_q8_0_swiglu": (i32, [vp, i64, i64, vp, i32, vp, vp]),
             "gemv_q4_0_swiglu": (i32, [vp, i64, i64, vp, i32, vp, vp]),
@@ -220,6 +221,14 @@ def gemv_q8_0_rmsnorm(w_packed, n: int, k: int, h, r, g, eps: float, y, h_out=No
                                    _stream(stream)))
 
 
+def gemv_q8_0_rmsnorm_f32(w_packed, n: int, k: int, h, r, g, eps: float, y, h_out=None, stream=None) -> None:
+    """The deq 2 form: y = W . (RMSNorm(h + r) * g) with f32 activations, the
+    norm computed in the GEMV's prologue."""
+    _check("gemv_q8_0_rmsnorm_f32",
+           lib().gemv_q8_0_rmsnorm_f32(_ptr(w_packed), n, k, _ptr(h), _ptr(r), _ptr(g), eps, _ptr(h_out), _ptr(y),
+                                       _stream(stream)))
+
+
 def gemv_q4_0_rmsnorm(w_packed, n: int, k: int, h, r, g, eps: float, y, h_out=None, stream=None) -> None:
     """The 4-bit form of gemv_q8_0_rmsnorm: y = W . Q8_0(RMSNorm(h + r) * g)
     with W in the 4-bit layout."""
@@ -329,9 +338,10 @@ def op_gemv_q8_0(w, n, k, x, act_fmt, y) -> OpDesc:
     return OpDesc(op=OP_GEMV_Q8_0, w_type=W_Q8_0, act_fmt=act_fmt, n=n, k=k, w=_ptr(w), x=_ptr(x), y=_ptr(y))
 
 
-def op_gemv_q8_0_rmsnorm(w, n, k, h, r, g, eps, y, h_out=None) -> OpDesc:
-    return OpDesc(op=OP_GEMV_Q8_0_RMSNORM, w_type=W_Q8_0, act_fmt=ACT_F32_REQUANT, n=n, k=k, w=_ptr(w), x=_ptr(h),
-                  r=_ptr(r), g=_ptr(g), eps=eps, h_out=_ptr(h_out), y=_ptr(y))
+def op_gemv_q8_0_rmsnorm(w, n, k, h, r, g, eps, y, h_out=None, act_fmt=None) -> OpDesc:
+    """act_fmt ACT_F32 selects the dequantizing form (gemv_q8_0_rmsnorm_f32)."""
+    return OpDesc(op=OP_GEMV_Q8_0_RMSNORM, w_type=W_Q8_0, act_fmt=ACT_F32_REQUANT if act_fmt is None else act_fmt,
+                  n=n, k=k, w=_ptr(w), x=_ptr(h), r=_ptr(r), g=_ptr(g), eps=eps, h_out=_ptr(h_out), y=_ptr(y))
 
 
 def op_gemv_q8_0_swiglu(w, n_ff, k, x, act_fmt, y) -> OpDesc:

@@ -140,6 +140,18 @@ struct StageInput {
     __device__ void commit(int4v* lds_q, float* lds_dx, float*) { st.commit(xin, k, C, lds_q, lds_dx); }
 };
 
+// f32 input of the dequantizing path (the SwiGLU kernel's W8A16 form).
+template <>
+struct StageInput<kActF32> {
+    const void* xin;
+    int k, C;
+    StageF32<4> st;
+    __device__ void issue() { st.issue(static_cast<const float*>(xin), k); }
+    __device__ void commit(int4v* lds, float*, float*) {
+        st.commit(static_cast<const float*>(xin), k, reinterpret_cast<float4v*>(lds));
+    }
+};
+
 template <int WAVES, int S, int U, int ACT, bool NT, bool DEBUG, bool ARGMAX>
 __global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict__ xin, float* __restrict__ y,
@@ -157,7 +169,10 @@ q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict
 // rows as one sequence (gate chunks, then up chunks), with one accumulator
 // per row, so each half is reduced exactly as the unsplit kernel reduces
 // that row (per-lane fused multiply-adds in chunk order, then the
-// butterfly) and only the n_ff products are stored.
+// butterfly) and only the n_ff products are stored.  With f32 activations
+// (ACT = kActF32, the W8A16 form of the same page's "Quantization
+// experiments") each block is dequantized against the f32 input as in the
+// dequantizing GEMV, so each half equals that GEMV's row bit for bit.
 template <int WAVES, int ACT>
 __global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 q8_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* __restrict__ xin,
@@ -168,9 +183,12 @@ q8_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
     const int nl = NB - (C - 1) * kChunkBlocks;
     const int sbl = (int)scale_section_bytes(nl);
     const int64_t row_bytes = packed_row_bytes(k);
+    constexpr bool F32 = ACT == kActF32;
     int4v* lds_q = reinterpret_cast<int4v*>(smem);
     float* lds_dx = reinterpret_cast<float*>(smem + (size_t)C * 2 * kWave * 16);
-    float* lds_res = reinterpret_cast<float*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>());
+    const float4v* lds_x = reinterpret_cast<const float4v*>(smem);
+    const size_t act_bytes = F32 ? lds_f32act_bytes(C) : lds_q8act_bytes(C);
+    float* lds_res = reinterpret_cast<float*>(smem + act_bytes + lds_tail_bytes<WAVES>());
     const int lane = threadIdx.x % kWave;
     const Sched sc(2 * C, 1, 1, WAVES, n_ff, (n_ff + WAVES - 1) / WAVES);
     const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
@@ -199,22 +217,37 @@ q8_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
         const int c = up ? m - C : m;
         const int blk = c * kWave + lane;
         if (blk < NB) {
-            const int4v xa = lds_q[(c * 2 + 0) * kWave + lane];
-            const int4v xb = lds_q[(c * 2 + 1) * kWave + lane];
-            int d = 0;
-            d = __builtin_amdgcn_sdot4(r.a[0].x, xa.x, d, false);
-            d = __builtin_amdgcn_sdot4(r.a[0].y, xa.y, d, false);
-            d = __builtin_amdgcn_sdot4(r.a[0].z, xa.z, d, false);
-            d = __builtin_amdgcn_sdot4(r.a[0].w, xa.w, d, false);
-            d = __builtin_amdgcn_sdot4(r.b[0].x, xb.x, d, false);
-            d = __builtin_amdgcn_sdot4(r.b[0].y, xb.y, d, false);
-            d = __builtin_amdgcn_sdot4(r.b[0].z, xb.z, d, false);
-            d = __builtin_amdgcn_sdot4(r.b[0].w, xb.w, d, false);
-            const float t = half_bits_to_float(r.sc[0]) * lds_dx[blk];
-            if (up) {
-                acc_up = __builtin_fmaf(t, (float)d, acc_up);
+            float& acc = up ? acc_up : acc_gate;
+            if constexpr (F32) {
+                // as q8_f32_item: d_w times the block's f32 dot
+                const float4v* xv = lds_x + (size_t)c * 8 * kWave + lane;
+                int4v wa = r.a[0], wb = r.b[0];
+                opaque(wa);
+                opaque(wb);
+                float bs = 0.0f;
+                bs = dot4_i8_f32(wa.x, xv[0 * kWave], bs);
+                bs = dot4_i8_f32(wa.y, xv[1 * kWave], bs);
+                bs = dot4_i8_f32(wa.z, xv[2 * kWave], bs);
+                bs = dot4_i8_f32(wa.w, xv[3 * kWave], bs);
+                bs = dot4_i8_f32(wb.x, xv[4 * kWave], bs);
+                bs = dot4_i8_f32(wb.y, xv[5 * kWave], bs);
+                bs = dot4_i8_f32(wb.z, xv[6 * kWave], bs);
+                bs = dot4_i8_f32(wb.w, xv[7 * kWave], bs);
+                acc = __builtin_fmaf(half_bits_to_float(r.sc[0]), bs, acc);
             } else {
-                acc_gate = __builtin_fmaf(t, (float)d, acc_gate);
+                const int4v xa = lds_q[(c * 2 + 0) * kWave + lane];
+                const int4v xb = lds_q[(c * 2 + 1) * kWave + lane];
+                int d = 0;
+                d = __builtin_amdgcn_sdot4(r.a[0].x, xa.x, d, false);
+                d = __builtin_amdgcn_sdot4(r.a[0].y, xa.y, d, false);
+                d = __builtin_amdgcn_sdot4(r.a[0].z, xa.z, d, false);
+                d = __builtin_amdgcn_sdot4(r.a[0].w, xa.w, d, false);
+                d = __builtin_amdgcn_sdot4(r.b[0].x, xb.x, d, false);
+                d = __builtin_amdgcn_sdot4(r.b[0].y, xb.y, d, false);
+                d = __builtin_amdgcn_sdot4(r.b[0].z, xb.z, d, false);
+                d = __builtin_amdgcn_sdot4(r.b[0].w, xb.w, d, false);
+                const float t = half_bits_to_float(r.sc[0]) * lds_dx[blk];
+                acc = __builtin_fmaf(t, (float)d, acc);
             }
         }
     };
@@ -587,12 +620,14 @@ q8_i8_norm_kernel(const uint8_t* __restrict__ W, int n, int k, NormArgs na, floa
     q8_i8_body<WAVES, S, U, false, false>(W, n, k, y, nullptr, nullptr, stage);
 }
 
-template <int WAVES, int S, int U, bool NT, bool ARGMAX>
-__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
-q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restrict__ x, float* __restrict__ y,
-              uint64_t* __restrict__ keys) {
+// The dequantizing path's body; `stage` fills its f32 LDS layout
+// (stage.issue() before the first weight items are requested,
+// stage.commit(lds, unused, scratch) after).
+template <int WAVES, int S, int U, bool ARGMAX, typename Stage>
+__device__ __attribute__((always_inline)) inline void q8_f32_body(const uint8_t* __restrict__ W, int n, int k,
+                                                                  float* __restrict__ y, uint64_t* __restrict__ keys,
+                                                                  Stage& stage) {
     static_assert(WAVES % S == 0, "S must divide WAVES");
-    static_assert(NT, "the weight stream is always loaded non-temporally");
     extern __shared__ __align__(16) uint8_t smem[];
     const int C = (int)chunk_count(k);
     const int NB = k / kBlock;
@@ -620,8 +655,7 @@ q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restri
     };
 
     Q8Regs<U> R[kRingSets<U, S>];
-    StageF32<4> st;
-    st.issue(x, k);
+    stage.issue();
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kRot) {
         if (rot) {
@@ -633,7 +667,7 @@ q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restri
         ring_prologue(sc, R, load);
     }
     __builtin_amdgcn_sched_barrier(0);
-    st.commit(x, k, lds_x);
+    stage.commit(reinterpret_cast<int4v*>(lds_x), nullptr, lds_res);
     __syncthreads();
     if constexpr (kRot) {
         if (rot) {
@@ -658,6 +692,26 @@ q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restri
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
     });
     if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
+}
+
+template <int WAVES, int S, int U, bool NT, bool ARGMAX>
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restrict__ x, float* __restrict__ y,
+              uint64_t* __restrict__ keys) {
+    static_assert(NT, "the weight stream is always loaded non-temporally");
+    StageInput<kActF32> stage{x, k, (int)chunk_count(k), {}};
+    q8_f32_body<WAVES, S, U, ARGMAX>(W, n, k, y, keys, stage);
+}
+
+// The dequantizing path fed by the residual add + RMSNorm of
+// residual_rmsnorm_q8_0, computed by every workgroup in its prologue (the
+// f32 form of q8_i8_norm_kernel, for deq 2): the staged values are that
+// kernel's f32 output, bit for bit.
+template <int WAVES, int S>
+__global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+q8_f32_norm_kernel(const uint8_t* __restrict__ W, int n, int k, NormArgs na, float* __restrict__ y) {
+    StageNorm<WAVES * kWave, true> stage{na, k, {}};
+    q8_f32_body<WAVES, S, 1, false>(W, n, k, y, nullptr, stage);
 }
 
 template <int WAVES, int S, int U, bool NT, bool ARGMAX>
@@ -1049,6 +1103,20 @@ int launch_q8_norm(const void* w, int n, int k, const NormArgs& na, float* y, hi
     });
 }
 
+// The dequantizing path fed by the fused residual + RMSNorm staging (deq 2):
+// the waves and split of the f32 path for this shape.
+int launch_q8_norm_f32(const void* w, int n, int k, const NormArgs& na, float* y, hipStream_t stream,
+                       LaunchInfo* info, bool run = true) {
+    const Cfg c = choose_cfg(kPathF32, n, k);
+    const size_t lds_act = lds_f32act_bytes((int)chunk_count(k));
+    const uint8_t* wp = static_cast<const uint8_t*>(w);
+    return dispatch_ws(c.waves, c.split, [&](auto W, auto S) -> int {
+        constexpr int Wv = decltype(W)::value, Sv = decltype(S)::value;
+        auto kern = q8_f32_norm_kernel<Wv, Sv>;
+        return launch_kernel<Wv, Sv>(kern, q8_lds_bytes<Wv>(lds_act), n, info, 1, run, stream, wp, n, k, na, y);
+    });
+}
+
 // The W4 GEMV with the norm prologue: the W4 launch choice.
 int launch_q4_norm(const void* w, int n, int k, const NormArgs& na, float* y, hipStream_t stream, LaunchInfo* info,
                    bool run = true) {
@@ -1114,11 +1182,17 @@ int launch_q4(const void* w, int n, int k, const void* x, int act_fmt, float* y,
 // uses for the whole gate+up matrix, one wave per output.
 int launch_q8_swiglu(const void* w, int n_ff, int k, const void* x, int act_fmt, float* y, hipStream_t stream,
                      LaunchInfo* info, bool run = true) {
-    const Cfg c = choose_cfg(kPathI8, 2 * (int64_t)n_ff, k);
-    const size_t lds_act = lds_q8act_bytes((int)chunk_count(k));
+    const Cfg c = choose_cfg(act_fmt == WSG_ACT_F32 ? kPathF32 : kPathI8, 2 * (int64_t)n_ff, k);
+    const size_t lds_act = act_fmt == WSG_ACT_F32 ? lds_f32act_bytes((int)chunk_count(k))
+                                                  : lds_q8act_bytes((int)chunk_count(k));
     const uint8_t* wp = static_cast<const uint8_t*>(w);
     return dispatch_ws(c.waves, 1, [&](auto W, auto) -> int {
         constexpr int Wv = decltype(W)::value;
+        if (act_fmt == WSG_ACT_F32) {
+            auto kern = q8_i8_swiglu_kernel<Wv, kActF32>;
+            return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds_act), n_ff, info, 1, run, stream, wp, n_ff, k, x,
+                                        y);
+        }
         if (act_fmt == WSG_ACT_Q8_0) {
             auto kern = q8_i8_swiglu_kernel<Wv, kActQ8>;
             return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds_act), n_ff, info, 1, run, stream, wp, n_ff, k, x,
@@ -1229,8 +1303,8 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 }  // namespace
 
 int validate_gemv_q8_rmsnorm(const void* w, int64_t n, int64_t k, const float* h, const float* r, const float* g,
-                             float eps, const void* h_out, const void* y) {
-    int rc = check_q8_args(w, n, k, h, WSG_ACT_F32_REQUANT, y);
+                             float eps, const void* h_out, const void* y, int act_fmt) {
+    int rc = check_q8_args(w, n, k, h, act_fmt, y);
     if (rc != WSG_OK) return rc;
     if (n < 1 || k < kBlock) return WSG_ERR_SHAPE;
     rc = validate_residual_rmsnorm(h, r, g, k, eps, h_out, y, nullptr);
@@ -1250,13 +1324,15 @@ int validate_gemv_q4(const void* w, int64_t n, int64_t k, const void* x, int act
 }
 
 int validate_gemv_q8_swiglu(const void* w, int64_t n_ff, int64_t k, const void* x, int act_fmt, const void* y) {
-    if (act_fmt != WSG_ACT_Q8_0 && act_fmt != WSG_ACT_F32_REQUANT) return WSG_ERR_MODE;
+    if (act_fmt != WSG_ACT_Q8_0 && act_fmt != WSG_ACT_F32_REQUANT && act_fmt != WSG_ACT_F32) return WSG_ERR_MODE;
     if (n_ff < 1 || k < kBlock || 2 * n_ff > kMaxDim) return WSG_ERR_SHAPE;
     return check_q8_args(w, 2 * n_ff, k, x, act_fmt, y);
 }
 
 int validate_gemv_q4_swiglu(const void* w, int64_t n_ff, int64_t k, const void* x, int act_fmt, const void* y) {
-    return validate_gemv_q8_swiglu(w, n_ff, k, x, act_fmt, y);  // the same arguments; only the layout differs
+    // the same arguments as the Q8_0 form (only the layout differs), int8 activations only
+    if (act_fmt == WSG_ACT_F32) return WSG_ERR_MODE;
+    return validate_gemv_q8_swiglu(w, n_ff, k, x, act_fmt, y);
 }
 
 namespace {
@@ -1371,15 +1447,22 @@ int gemv_q8_0(const void* w_packed, int64_t n, int64_t k, const void* x, int act
 
 int gemv_q8_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r, const float* g,
                       float eps, float* h_out, float* y, hipStream_t stream) {
-    const int rc = validate_gemv_q8_rmsnorm(w_packed, n, k, h, r, g, eps, h_out, y);
+    const int rc = validate_gemv_q8_rmsnorm(w_packed, n, k, h, r, g, eps, h_out, y, WSG_ACT_F32_REQUANT);
     if (rc != WSG_OK) return rc;
     return launch_q8_norm(w_packed, (int)n, (int)k, NormArgs{h, r, g, h_out, eps}, y, stream, nullptr);
+}
+
+int gemv_q8_0_rmsnorm_f32(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r,
+                          const float* g, float eps, float* h_out, float* y, hipStream_t stream) {
+    const int rc = validate_gemv_q8_rmsnorm(w_packed, n, k, h, r, g, eps, h_out, y, WSG_ACT_F32);
+    if (rc != WSG_OK) return rc;
+    return launch_q8_norm_f32(w_packed, (int)n, (int)k, NormArgs{h, r, g, h_out, eps}, y, stream, nullptr);
 }
 
 int gemv_q4_0_rmsnorm(const void* w_packed, int64_t n, int64_t k, const float* h, const float* r, const float* g,
                       float eps, float* h_out, float* y, hipStream_t stream) {
     // the same arguments and races as the Q8_0 form; only the weights differ
-    const int rc = validate_gemv_q8_rmsnorm(w_packed, n, k, h, r, g, eps, h_out, y);
+    const int rc = validate_gemv_q8_rmsnorm(w_packed, n, k, h, r, g, eps, h_out, y, WSG_ACT_F32_REQUANT);
     if (rc != WSG_OK) return rc;
     return launch_q4_norm(w_packed, (int)n, (int)k, NormArgs{h, r, g, h_out, eps}, y, stream, nullptr);
 }

@@ -506,6 +506,14 @@ struct StageRequant {
     }
 };
 
+// LDS slot of the f32 staging layout of the dequantizing path for float4
+// unit u (values 4u .. 4u+3): block b = u / 8 (= 64 c + l), group g = u % 8
+// -> float4 (c * 8 + g) * 64 + l.
+__device__ inline int f32_slot(int u) {
+    const int b = u >> 3, g = u & 7, c = b / kWave, l = b % kWave;
+    return (c * 8 + g) * kWave + l;
+}
+
 // ------------------------------------ residual + RMSNorm + requantization
 // Arguments of residual_rmsnorm_q8_0 when a GEMV computes it in its
 // prologue: h' = h + r (r nullable), y = h' / sqrt(mean h'^2 + eps) * g (g
@@ -532,13 +540,16 @@ __host__ __device__ inline int norm_threads(int k) {
 // each summing its units in order with fused multiply-adds, then the same
 // butterfly per wave and the wave partials in wave order; the values are
 // then scaled and quantized with the same operations.  So the codes and
-// scales in LDS are those that kernel writes, bit for bit.  Up to four
+// scales in LDS are those that kernel writes, bit for bit.  With F32OUT the
+// normalized values themselves are staged instead, in the f32 layout the
+// dequantizing GEMV reads: they are that kernel's f32 output y, bit for
+// bit.  Up to four
 // units of the first pass are requested before the weight stream starts
 // (issue); the rest, the reduction and the second pass come in commit.
 // With one unit per norm thread (k <= 8192) both passes see the same units,
 // so g is requested with them and the second pass reads nothing: one round
 // trip to memory in all.
-template <int T>
+template <int T, bool F32OUT = false>
 struct StageNorm {
     static_assert(T % kWave == 0 && 1024 % T == 0, "a whole number of waves dividing 1024 threads");
     static constexpr int MV = 1024 / T;  // most norm threads one thread plays
@@ -607,7 +618,14 @@ struct StageNorm {
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = a[j] * sc;
         }
-        requant_unit(float4v{v[0], v[1], v[2], v[3]}, float4v{v[4], v[5], v[6], v[7]}, u, lds_q, lds_dx);
+        if constexpr (F32OUT) {
+            float4v* lds_x = reinterpret_cast<float4v*>(lds_q);
+            lds_x[f32_slot(2 * u)] = float4v{v[0], v[1], v[2], v[3]};
+            lds_x[f32_slot(2 * u + 1)] = float4v{v[4], v[5], v[6], v[7]};
+            (void)lds_dx;
+        } else {
+            requant_unit(float4v{v[0], v[1], v[2], v[3]}, float4v{v[4], v[5], v[6], v[7]}, u, lds_q, lds_dx);
+        }
     }
     __device__ void commit(int4v* lds_q, float* lds_dx, float* scratch) {
         int nt, nu, units;
@@ -689,10 +707,7 @@ struct StageNorm {
 template <int NR>
 struct StageF32 {
     float4v v[NR];
-    __device__ static int slot(int u) {
-        const int b = u >> 3, g = u & 7, c = b / kWave, l = b % kWave;
-        return (c * 8 + g) * kWave + l;
-    }
+    __device__ static int slot(int u) { return f32_slot(u); }
     __device__ void issue(const float* __restrict__ x, int k) {
         const float4v* x4 = reinterpret_cast<const float4v*>(x);
 #pragma unroll

@@ -22,7 +22,7 @@ int validate_lm_head(const void* w, int w_type, int64_t n, int64_t k, const void
 int validate_residual_rmsnorm(const float* h, const float* r, const float* g, int64_t k, float eps,
                               const void* h_out, const void* y, const void* y_q8);
 int validate_gemv_q8_rmsnorm(const void* w, int64_t n, int64_t k, const float* h, const float* r, const float* g,
-                             float eps, const void* h_out, const void* y);
+                             float eps, const void* h_out, const void* y, int act_fmt);
 int validate_gemv_q8_swiglu(const void* w, int64_t n_ff, int64_t k, const void* x, int act_fmt, const void* y);
 int validate_embed_gather(const void* table, int w_type, int64_t vocab, int64_t hidden, const int32_t* token,
                           const float* out);
@@ -59,9 +59,11 @@ int validate_op(const wsg_op_desc& d) {
                                                   static_cast<const float*>(d.w), d.k, d.eps, d.h_out, d.y,
                                                   d.y_q8);
         case WSG_OP_GEMV_Q8_0_RMSNORM:
+            // act_fmt WSG_ACT_F32 selects the dequantizing (deq 2) form
             return wsg::validate_gemv_q8_rmsnorm(d.w, d.n, d.k, static_cast<const float*>(d.x),
                                                  static_cast<const float*>(d.r), static_cast<const float*>(d.g),
-                                                 d.eps, d.h_out, d.y);
+                                                 d.eps, d.h_out, d.y,
+                                                 d.act_fmt == WSG_ACT_F32 ? WSG_ACT_F32 : WSG_ACT_F32_REQUANT);
         case WSG_OP_GEMV_Q8_0_SWIGLU: return wsg::validate_gemv_q8_swiglu(d.w, d.n, d.k, d.x, d.act_fmt, d.y);
         case WSG_OP_EMBED_GATHER:
             return wsg::validate_embed_gather(d.w, d.w_type, d.n, d.k, static_cast<const int32_t*>(d.x),
@@ -74,7 +76,7 @@ int validate_op(const wsg_op_desc& d) {
         case WSG_OP_GEMV_Q4_0_RMSNORM:
             return wsg::validate_gemv_q8_rmsnorm(d.w, d.n, d.k, static_cast<const float*>(d.x),
                                                  static_cast<const float*>(d.r), static_cast<const float*>(d.g),
-                                                 d.eps, d.h_out, d.y);
+                                                 d.eps, d.h_out, d.y, WSG_ACT_F32_REQUANT);
         default: return WSG_ERR_MODE;
     }
 }
@@ -95,9 +97,9 @@ int enqueue_op(const wsg_op_desc& d, hipStream_t s) {
                                          static_cast<const float*>(d.w), d.k, d.eps, static_cast<float*>(d.h_out),
                                          static_cast<float*>(d.y), d.y_q8, s);
         case WSG_OP_GEMV_Q8_0_RMSNORM:
-            return gemv_q8_0_rmsnorm(d.w, d.n, d.k, static_cast<const float*>(d.x), static_cast<const float*>(d.r),
-                                     static_cast<const float*>(d.g), d.eps, static_cast<float*>(d.h_out),
-                                     static_cast<float*>(d.y), s);
+            return (d.act_fmt == WSG_ACT_F32 ? gemv_q8_0_rmsnorm_f32 : gemv_q8_0_rmsnorm)(
+                d.w, d.n, d.k, static_cast<const float*>(d.x), static_cast<const float*>(d.r),
+                static_cast<const float*>(d.g), d.eps, static_cast<float*>(d.h_out), static_cast<float*>(d.y), s);
         case WSG_OP_GEMV_Q8_0_SWIGLU:
             return gemv_q8_0_swiglu(d.w, d.n, d.k, d.x, d.act_fmt, static_cast<float*>(d.y), s);
         case WSG_OP_EMBED_GATHER:

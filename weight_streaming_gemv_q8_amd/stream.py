@@ -84,14 +84,14 @@ class TokenStream:
     swiglu_at: indices of the GEMVs of a layer whose output is the SwiGLU
             of their two halves (the gate+up projection: rows 0 .. n/2 - 1
             are the gate, the rest the up projection; gemv_q8_0_swiglu),
-            so the next GEMV reads n/2 products.  Q8_0 and q4_0 chains with
-            int8 activations; not with fused_norm.
-    fused_norm: with norm_before on a Q8_0 or q4_0 chain with int8 activations, each
-            normalized GEMV computes the residual add + RMSNorm itself
-            (gemv_q8_0_rmsnorm) instead of after a separate norm call; the
-            results are the same bit for bit (the f32 normalized vectors
-            are then not written).  A normalized SwiGLU GEMV keeps its
-            separate norm call.
+            so the next GEMV reads n/2 products.  Q8_0 chains (the W8A16
+            form at deq 2) and q4_0 chains with int8 activations.
+    fused_norm: with norm_before on a Q8_0 chain or a q4_0 chain with int8
+            activations, each normalized GEMV computes the residual add +
+            RMSNorm itself (gemv_q8_0_rmsnorm, or gemv_q8_0_rmsnorm_f32 at
+            deq 2) instead of after a separate norm call; the results are
+            the same bit for bit (the f32 normalized vectors are then not
+            written).  A normalized SwiGLU GEMV keeps its separate norm call.
     """
 
     def __init__(self, shapes: Sequence[Tuple[int, int, Tuple[int, ...]]], layers: int, wtype: str,
@@ -115,8 +115,8 @@ class TokenStream:
         for j in self.swiglu_at:
             if not 0 <= j < len(self.shapes) or self.shapes[j][0] % 2:
                 raise ValueError("a SwiGLU GEMV needs an even number of rows (gate and up halves)")
-            if wtype == "bf16" or deq == 2:
-                raise ValueError("the SwiGLU epilogue runs on Q8_0 and q4_0 chains with int8 activations")
+            if wtype == "bf16" or (wtype == "q4_0" and deq == 2):
+                raise ValueError("the SwiGLU epilogue runs on Q8_0 chains and on q4_0 chains with int8 activations")
         for j in range(1, len(self.shapes)):
             if self.shapes[j][1] > self.out_len(j - 1):
                 raise ValueError("a GEMV's k exceeds the previous GEMV's outputs")
@@ -144,8 +144,8 @@ class TokenStream:
         self.norm_before = tuple(sorted(set(int(j) for j in norm_before)))
         self.eps = float(eps)
         self.fused_norm = bool(fused_norm)
-        if self.fused_norm and (wtype == "bf16" or deq == 2 or not self.norm_before):
-            raise ValueError("fused_norm needs a Q8_0 or q4_0 chain with int8 activations and norm_before")
+        if self.fused_norm and (wtype == "bf16" or (wtype == "q4_0" and deq == 2) or not self.norm_before):
+            raise ValueError("fused_norm needs norm_before and a Q8_0 chain, or a q4_0 chain with int8 activations")
         self.norms: List[NormSlot] = []
         self.h0 = None
         self.gains = None
@@ -252,9 +252,11 @@ class TokenStream:
             swiglu = wsg.op_gemv_q4_0_swiglu if self.wtype == "q4_0" else wsg.op_gemv_q8_0_swiglu
             if s.norm is not None:
                 n = s.norm
-                return [wsg.op_residual_rmsnorm(n.h_in, n.r or None, n.g, self.hidden, self.eps, h_out=n.h_out,
-                                                y=n.y, y_q8=n.yq),
-                        swiglu(w, nff, s.k, n.yq, wsg.ACT_Q8_0, s.y)]
+                norm = wsg.op_residual_rmsnorm(n.h_in, n.r or None, n.g, self.hidden, self.eps, h_out=n.h_out,
+                                               y=n.y, y_q8=n.yq)
+                if n.yq is None:  # f32 activations (deq 2): the W8A16 SwiGLU GEMV reads y
+                    return [norm, swiglu(w, nff, s.k, n.y, wsg.ACT_F32, s.y)]
+                return [norm, swiglu(w, nff, s.k, n.yq, wsg.ACT_Q8_0, s.y)]
             if self.act_fmt() == wsg.ACT_Q8_0:
                 return [wsg.op_quantize_act(s.x_ptr, s.k, s.xq_ptr),
                         swiglu(w, nff, s.k, s.xq_ptr, wsg.ACT_Q8_0, s.y)]
@@ -262,8 +264,11 @@ class TokenStream:
         pre = []
         if s.norm is not None and self.fused_norm:
             n = s.norm
-            op = wsg.op_gemv_q4_0_rmsnorm if self.wtype == "q4_0" else wsg.op_gemv_q8_0_rmsnorm
-            return [op(w, s.n, s.k, n.h_in, n.r or None, n.g, self.eps, s.y, h_out=n.h_out)]
+            if self.wtype == "q4_0":
+                return [wsg.op_gemv_q4_0_rmsnorm(w, s.n, s.k, n.h_in, n.r or None, n.g, self.eps, s.y,
+                                                 h_out=n.h_out)]
+            return [wsg.op_gemv_q8_0_rmsnorm(w, s.n, s.k, n.h_in, n.r or None, n.g, self.eps, s.y, h_out=n.h_out,
+                                             act_fmt=wsg.ACT_F32 if self.act_fmt() == wsg.ACT_F32 else None)]
         if s.norm is not None:
             n = s.norm
             pre = [wsg.op_residual_rmsnorm(n.h_in, n.r or None, n.g, self.hidden, self.eps, h_out=n.h_out,
@@ -314,7 +319,8 @@ class TokenStream:
             elif op.op == wsg.OP_GEMV_Q4_0_SWIGLU:
                 wsg.gemv_q4_0_swiglu(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
             elif op.op in (wsg.OP_GEMV_Q8_0_RMSNORM, wsg.OP_GEMV_Q4_0_RMSNORM):
-                f = wsg.gemv_q8_0_rmsnorm if op.op == wsg.OP_GEMV_Q8_0_RMSNORM else wsg.gemv_q4_0_rmsnorm
+                f = (wsg.gemv_q4_0_rmsnorm if op.op == wsg.OP_GEMV_Q4_0_RMSNORM else
+                     wsg.gemv_q8_0_rmsnorm_f32 if op.act_fmt == wsg.ACT_F32 else wsg.gemv_q8_0_rmsnorm)
                 f(op.w, op.n, op.k, op.x, op.r, op.g, op.eps, op.y, h_out=op.h_out, stream=stream)
             else:
                 wsg.gemv_q8_0(op.w, op.n, op.k, op.x, op.act_fmt, op.y, stream=stream)
@@ -367,14 +373,26 @@ class DecodeStep:
     Attention and the other non-GEMV operators are not part of this path:
     the layer chain is the GEMV stream (q/k/v -> o_proj reads the first
     rows of the qkv output).  wtype is the layers' weight format ("q8_0" or
-    "q4_0"); the embedding table and the LM head stay Q8_0."""
+    "q4_0"); the embedding table and the LM head stay Q8_0.
+
+    deq (emit_qwen38_generate, "Where the speed comes from", the deq
+    paragraph) picks where activations are quantized: 0 = every GEMV takes
+    int8 activations; 1 = the layers do, the LM head takes the f32 final
+    normalized vector; 2 = every Q8_0 GEMV takes f32 activations (the fused
+    norm GEMVs' f32 form, the W8A16 SwiGLU GEMV, the dequantizing down
+    projection and LM head), so no activation is quantized anywhere.  q4_0
+    layers run deq 0 or 1."""
 
     def __init__(self, shapes, layers: int, vocab: int, capacity: int = 1024, device: str = "cuda",
-                 eps: float = 1e-6, wtype: str = "q8_0"):
+                 eps: float = 1e-6, wtype: str = "q8_0", deq: int = 0):
         if wtype not in ("q8_0", "q4_0"):
             raise ValueError("the decode step's layers are Q8_0 or q4_0")
-        self.chain = TokenStream(shapes, layers, wtype, deq=0, device=device, norm_before=(0, 2), eps=eps,
-                                 fused_norm=True, swiglu_at=(2,))
+        if deq not in (0, 1, 2) or (wtype == "q4_0" and deq == 2):
+            raise ValueError("deq is 0, 1 or 2 (q4_0 layers: 0 or 1)")
+        self.deq = deq
+        self.head_act = wsg.ACT_Q8_0 if deq == 0 else wsg.ACT_F32
+        self.chain = TokenStream(shapes, layers, wtype, deq=2 if deq == 2 else 0, device=device,
+                                 norm_before=(0, 2), eps=eps, fused_norm=True, swiglu_at=(2,))
         self.hidden = self.chain.hidden
         self.vocab = int(vocab)
         self.capacity = int(capacity)
@@ -405,6 +423,15 @@ class DecodeStep:
             wsg.quantize_q8_0_weights(staging[:rows], rows, self.hidden, table[r0 * row_bytes:])
         torch.cuda.synchronize()
 
+    def final_q8_or_none(self):
+        """The final norm's Q8_0 output, written only when the LM head reads it."""
+        return self.final_q8 if self.head_act == wsg.ACT_Q8_0 else None
+
+    def head_input(self) -> torch.Tensor:
+        """The LM head's activation: the final norm's Q8_0 codes (deq 0) or
+        its f32 output (deq 1 and 2)."""
+        return self.final_q8 if self.head_act == wsg.ACT_Q8_0 else self.final_y
+
     def reset(self, first_token: int) -> None:
         """Start a sequence: the current token, an empty history, position 0."""
         self.token.fill_(int(first_token))
@@ -418,9 +445,9 @@ class DecodeStep:
         return ([wsg.op_embed_gather(self.embedding, wsg.W_Q8_0, self.vocab, self.hidden, self.token, chain.h0)]
                 + chain.ops()
                 + [wsg.op_residual_rmsnorm(h_last, last.y, self.final_gain, self.hidden, self.eps,
-                                           h_out=self.final_h, y=self.final_y, y_q8=self.final_q8),
-                   wsg.op_lm_head_argmax(self.lm_head, wsg.W_Q8_0, self.vocab, self.hidden, self.final_q8,
-                                         wsg.ACT_Q8_0, self.ws, self.ws.numel(), self.token,
+                                           h_out=self.final_h, y=self.final_y, y_q8=self.final_q8_or_none()),
+                   wsg.op_lm_head_argmax(self.lm_head, wsg.W_Q8_0, self.vocab, self.hidden, self.head_input(),
+                                         self.head_act, self.ws, self.ws.numel(), self.token,
                                          debug_logits=self.logits),
                    wsg.op_token_advance(self.token, self.history, self.capacity, self.pos)])
 
@@ -431,8 +458,8 @@ class DecodeStep:
         self.chain.run_eager(stream)
         last = self.chain.slots[-1]
         wsg.residual_rmsnorm_q8_0(self.chain.norms[-1].h_out, last.y, self.final_gain, self.hidden, self.eps,
-                                  h_out=self.final_h, y=self.final_y, y_q8=self.final_q8, stream=stream)
-        wsg.lm_head_argmax(self.lm_head, wsg.W_Q8_0, self.vocab, self.hidden, self.final_q8, wsg.ACT_Q8_0,
+                                  h_out=self.final_h, y=self.final_y, y_q8=self.final_q8_or_none(), stream=stream)
+        wsg.lm_head_argmax(self.lm_head, wsg.W_Q8_0, self.vocab, self.hidden, self.head_input(), self.head_act,
                            self.ws, self.ws.numel(), self.token, self.logits, stream=stream)
         wsg.token_advance(self.token, self.history, self.capacity, self.pos, stream=stream)
 
