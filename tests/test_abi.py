@@ -203,12 +203,18 @@ def test_fused_norm_gemv_rejects_before_launch(L):
     assert f(A, 8, 1024, h, r, g, 1e-6, h_out, h_out + 16, None) == wsg.ERR_MODE  # y over h_out
     assert f(A, 8, 1024, h + 4, r, g, 1e-6, h_out, y, None) == wsg.ERR_ALIGN
     assert f(A, 8, 1024, None, r, g, 1e-6, h_out, y, None) == wsg.ERR_NULL
+    f32 = L.gemv_q8_0_rmsnorm_f32  # the deq 2 form: the same checks, the f32 staging limit
+    assert f32(A, 8, wsg.MAX_K_F32ACT + 32, h, r, g, 1e-6, h_out, y, None) == wsg.ERR_SHAPE
+    assert f32(A, 8, 1024, h, r, g, 1e-6, h, y, None) == wsg.ERR_MODE
+    assert f32(A, 8, 1024, h, r, g, -1.0, h_out, y, None) == wsg.ERR_MODE
 
 
 def test_swiglu_gemv_rejects_before_launch(L):
     A = 0x100000
     f = L.gemv_q8_0_swiglu
-    assert f(A, 64, 1024, A, wsg.ACT_F32, A + 0x10000, None) == wsg.ERR_MODE     # f32 activations
+    assert f(A, 64, 1024, A, 7, A + 0x10000, None) == wsg.ERR_MODE                # not a format
+    assert L.gemv_q4_0_swiglu(A, 64, 1024, A, wsg.ACT_F32, A + 0x10000, None) == wsg.ERR_MODE  # 4-bit: int8 only
+    assert f(A, 64, wsg.MAX_K_F32ACT + 32, A, wsg.ACT_F32, A + 0x10000, None) == wsg.ERR_SHAPE  # f32 staging limit
     assert f(A, 0, 1024, A, wsg.ACT_F32_REQUANT, A + 0x10000, None) == wsg.ERR_SHAPE
     assert f(A, 64, 1000, A, wsg.ACT_F32_REQUANT, A + 0x10000, None) == wsg.ERR_SHAPE
     assert f(A, 64, 1024, None, wsg.ACT_Q8_0, A + 0x10000, None) == wsg.ERR_NULL
