@@ -146,29 +146,12 @@ def kernel_label(wtype: str, act_fmt: int, cfg: dict) -> str:
     return f"{base}<waves={cfg['waves']},split={cfg['split']},unroll={cfg['unroll']},{act}>"
 
 
-def time_per_launch(ts, reps: int = 1):
-    """HIP events around every GEMV launch of the chain (eager, on the
-    current stream); returns per-slot mean seconds."""
-    import torch
-    n = len(ts.slots)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    acc = [0.0] * n
-    for _ in range(reps):
-        torch.cuda.synchronize()
-        for i in range(n):
-            ev[i][0].record()
-            ts.run_slot(i)
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        for i in range(n):
-            acc[i] += ev[i][0].elapsed_time(ev[i][1]) / 1e3
-    return [a / reps for a in acc]
-
-
-def time_plan(ts, plan_kind, steps: int, warmup: int):
+def time_plan(ts, plan_kind, steps: int, warmup: int, stats: dict = None):
     """Capture the token ("graph": one node per call; "persistent": one
     resident kernel) and time `steps` replays with HIP events on the launch
-    stream.  Returns (seconds per token, kernels per token)."""
+    stream (an event between consecutive replays, so each replay's time is
+    known too: stats, if given, receives their median and min in
+    seconds).  Returns (mean seconds per token, kernels per token)."""
     import torch
     if plan_kind is True or plan_kind is False:  # older callers: persistent or not
         plan_kind = "persistent" if plan_kind else "graph"
@@ -178,15 +161,57 @@ def time_plan(ts, plan_kind, steps: int, warmup: int):
     for _ in range(warmup):
         ts.launch()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         ts.launch()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     if persistent and plan.error():
         raise RuntimeError(f"a wait of the {plan_kind} token kernel timed out: results invalid")
-    return e0.elapsed_time(e1) / 1e3 / steps, kernels
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(steps))
+    if stats is not None:
+        stats["median_s"] = per[len(per) // 2]
+        stats["min_s"] = per[0]
+        stats["replays"] = steps
+    return ev[0].elapsed_time(ev[steps]) / 1e3 / steps, kernels
+
+
+def time_per_shape(ts, wtype_code: int, act_fmt: int, reps: int):
+    """Every GEMV shape of the layer as it runs in the token: a graph of the
+    L launches of that matrix (one per layer: that layer's weights and
+    input buffers, the same kernel and launch shape as in the token),
+    replayed `reps` times with HIP events on the launch stream.  Returns one
+    record per shape: kernel label, n, k, algorithmic bytes and seconds per
+    launch."""
+    import torch
+
+    import weight_streaming_gemv_q8_amd as wsg
+    out = []
+    per_layer = len(ts.slots) // ts.layers
+    for j in range(per_layer):
+        slots = [s for s in ts.slots if s.index == j]
+        ops = []
+        for s in slots:
+            ops.extend(ts._slot_ops(s))
+        plan = wsg.Plan(ops)
+        for _ in range(2):
+            plan.launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            plan.launch()
+        e1.record()
+        torch.cuda.synchronize()
+        plan.destroy()
+        sec = e0.elapsed_time(e1) / 1e3 / (reps * len(slots))
+        n, k = slots[0].n, slots[0].k
+        cfg = wsg.gemv_config(wtype_code, act_fmt, n, k)
+        bpl = {"q8_0": n * (k // 32) * 34, "q4_0": n * (k // 32) * 18}.get(ts.wtype, n * k * 2)
+        out.append({"matrix": j, "n": n, "k": k, "label": kernel_label(ts.wtype, act_fmt, cfg), "grid": cfg["grid"],
+                    "bytes": bpl, "us": sec * 1e6, "launches_per_token": len(slots), "kernels_per_launch": len(ops) // len(slots)})
+    return out
 
 
 def _time_calls(fn, reps: int, warmup: int = 3) -> float:
@@ -427,66 +452,97 @@ def read_ceiling(ts, reps: int = 3) -> float:
 
 # ------------------------------------------------------------ CPU baseline
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, deq: int, budget_s: float) -> dict:
-    """The oracle as it stands, single-threaded, on a bounded sample: the
-    first layer(s) of the same stream, weights generated and quantized on the
-    host beforehand (untimed, as on the GPU), then the chain of GEMVs (with
-    per-call activation quantization at deq 0) repeated until the budget is
-    used.  GB/s of weight stream."""
+    """The oracle as it stands on a bounded sample: layer 0 of the same
+    stream (weights generated and quantized on the host beforehand,
+    untimed, as on the GPU), its chain of GEMVs (with per-call activation
+    quantization at deq 0) repeated for about budget_s / 2 seconds on one
+    thread, then for as long again with the rows of every GEMV split over
+    every core in sched_getaffinity (one oracle call per row range; the
+    oracle's C calls release the interpreter lock).  GB/s of weight stream;
+    value = the multi-threaded rate; the whole-token time is that layer's
+    time x layers (extrapolated, and so labelled)."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     import oracle
     import synth
     from synth import workloads as W
 
-    layers = []
     t_setup = time.time()
-    n_layers = 1
-    for l in range(n_layers):
-        mats = []
-        for j, m in enumerate(wl.matrices):
-            w = np.concatenate([synth.normal_f32(wl.seed, W.weight_tensor_id(l, j, p), r * m.k, W.WEIGHT_SIGMA)
-                                .reshape(r, m.k) for p, r in enumerate(m.parts)])
-            if wl.wtype == "q8_0":
-                mats.append(oracle.quantize_q8_0(w))
-            else:
-                mats.append(oracle.f32_to_bf16_rows(w))
-            del w
-        layers.append(mats)
-    xs = [synth.activation(wl.seed, W.activation_tensor_id(l), wl.matrices[0].k, rms=True)
-          for l in range(n_layers)]
-    log(f"cpu baseline: sample of {n_layers} layer(s) prepared in {time.time() - t_setup:.1f} s")
+    mats = []
+    for j, m in enumerate(wl.matrices):
+        w = np.concatenate([synth.normal_f32(wl.seed, W.weight_tensor_id(0, j, p), r * m.k, W.WEIGHT_SIGMA)
+                            .reshape(r, m.k) for p, r in enumerate(m.parts)])
+        mats.append(oracle.quantize_q8_0(w) if wl.wtype == "q8_0" else oracle.f32_to_bf16_rows(w))
+        del w
+    x0 = synth.activation(wl.seed, W.activation_tensor_id(0), wl.matrices[0].k, rms=True)
+    log(f"cpu baseline: layer 0 prepared in {time.time() - t_setup:.1f} s")
+    threads = len(os.sched_getaffinity(0))
 
-    per_layer_bytes = wl.weight_bytes_per_layer()
-    done_bytes = 0
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        for l, mats in enumerate(layers):
-            x = xs[l]
-            for j, m in enumerate(wl.matrices):
-                xin = x[:m.k].astype(np.float32)
-                if wl.wtype == "bf16":
-                    y, _ = oracle.gemv_bf16(mats[j], xin)
-                elif deq == 2:
-                    y, _ = oracle.gemv_q8_act_f32(mats[j][0], mats[j][1], xin)
-                else:
-                    dx, qx = oracle.quantize_q8_0(xin)
-                    y, _ = oracle.gemv_q8_act_q8(mats[j][0], mats[j][1], dx, qx)
-                x = y
-            done_bytes += per_layer_bytes
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+    def gemv(j, xin, rows):
+        r0, r1 = rows
+        if wl.wtype == "bf16":
+            return oracle.gemv_bf16(mats[j][r0:r1], xin)[0]
+        if deq == 2:
+            return oracle.gemv_q8_act_f32(mats[j][0][r0:r1], mats[j][1][r0:r1], xin)[0]
+        dx, qx = xin
+        return oracle.gemv_q8_act_q8(mats[j][0][r0:r1], mats[j][1][r0:r1], dx, qx)[0]
+
+    def layer_pass(pool, nthreads):
+        x = x0
+        for j, m in enumerate(wl.matrices):
+            xin = np.ascontiguousarray(x[:m.k], np.float32)
+            if wl.wtype == "q8_0" and deq != 2:
+                xin = oracle.quantize_q8_0(xin)
+            cuts = np.linspace(0, m.n, nthreads + 1).astype(int)
+            ranges = [(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+            if pool is None:
+                x = np.concatenate([gemv(j, xin, r) for r in ranges])
+            else:
+                x = np.concatenate(list(pool.map(lambda r: gemv(j, xin, r), ranges)))
+        return x
+
+    def timed(pool, nthreads):
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            layer_pass(pool, nthreads)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s / 2:
+                return el / passes, passes
+
+    per_layer = wl.weight_bytes_per_layer()
+    t1, p1 = timed(None, 1)
+    with cf.ThreadPoolExecutor(max_workers=threads) as pool:
+        tn, pn = timed(pool, threads)
+    quant = ", with per-call activation quantization" if wl.wtype == "q8_0" and deq != 2 else ""
     return {
-        "value": round(gbps(done_bytes, el), 4),
+        "value": round(gbps(per_layer, tn), 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"layer 0 of {wl.name} ({per_layer_bytes / 1e6:.1f} MB of weights, "
-                   f"{len(wl.matrices)} GEMVs{', with per-call activation quantization' if wl.wtype == 'q8_0' and deq != 2 else ''}), "
-                   f"{passes} pass(es) in {el:.1f} s, single-threaded fp64 C oracle"),
+        "sample": (f"layer 0 of {wl.name} ({per_layer / 1e6:.1f} MB of weights, {len(wl.matrices)} GEMVs{quant}); "
+                   f"{pn} passes on {threads} threads (rows split over sched_getaffinity), and {p1} single-threaded; "
+                   f"fp64 C oracle"),
+        "cpu_model": cpu_model(),
+        "single_thread": {"value": round(gbps(per_layer, t1), 4), "unit": "GB/s", "cores": 1},
+        "us_per_token_extrapolated": {"threads": round(tn * wl.layers * 1e6, 1),
+                                      "single_thread": round(t1 * wl.layers * 1e6, 1),
+                                      "note": f"one layer's time x {wl.layers} layers (extrapolated)"},
     }
 
 
@@ -528,7 +584,7 @@ _ACT_NAMES = {"0": "q8act", "1": "f32act", "2": "requant"}
 
 def label_from_rocprof(name: str):
     """Bench label of a kernel from its demangled rocprofv3 name (template
-    arguments), or None for kernels outside the GEMV stream."""
+    arguments), or None for kernels outside the library's GEMV stream."""
     import re
     m = re.search(r"(q8_i8_kernel|q8_f32_kernel|bf16_kernel|stream_kernel)<([^>]*)>", name)
     if not m:
@@ -538,10 +594,32 @@ def label_from_rocprof(name: str):
         sc = {"waves": int(args[0]), "unroll": int(args[1]), "sets": int(args[2])}
         return stream_label(sc, args[3] == "true")
     if kind == "q8_i8_kernel":
-        return f"q8_i8_kernel<waves={args[0]},split={args[1]},unroll={args[2]},{_ACT_NAMES[args[3]]}>"
-    if kind in ("q8_f32_kernel", "bf16_kernel"):
-        return f"{kind}<waves={args[0]},split={args[1]},unroll={args[2]},f32act>"
-    return None
+        extra = (",debug" if args[5] == "true" else "") + (",argmax" if args[6] == "true" else "")
+        return f"q8_i8_kernel<waves={args[0]},split={args[1]},unroll={args[2]},{_ACT_NAMES[args[3]]}{extra}>"
+    extra = ",argmax" if args[4] == "true" else ""
+    return f"{kind}<waves={args[0]},split={args[1]},unroll={args[2]},f32act{extra}>"
+
+
+def short_kernel_name(name: str) -> str:
+    """A kernel's label for the summaries: the bench label for the GEMV
+    kernels, else its name with template arguments and no namespaces or
+    parameter list."""
+    import re
+    lab = label_from_rocprof(name)
+    if lab:
+        return lab
+    s = re.sub(r"^void ", "", name)
+    s = re.sub(r"\b\w+::|\(anonymous namespace\)::", "", s)
+    depth, out = 0, []
+    for ch in s:  # drop the parameter list (the first '(' outside template brackets)
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            break
+        out.append(ch)
+    return "".join(out).strip()[:90]
 
 
 def stream_label(sc: dict, f32: bool) -> str:
@@ -556,45 +634,46 @@ def _read_csv(path: str):
 
 def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
                        workload: str, commands: dict) -> list:
-    """Writes profiles/kernel_stats_<workload>.txt from a --kernel-trace --stats
-    run and profiles/traffic_<kernel>_<workload>.txt per GEMV kernel from two
-    --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter
-    reads for the copy probe of known size.  Returns the files written."""
+    """Writes profiles/kernel_stats_<workload>.txt from a --kernel-trace
+    --stats run (per kernel and grid size: calls, mean, median, min, max
+    and total duration) and, when counter runs are given (not "-"),
+    profiles/traffic_<kernel>_<workload>.txt per library kernel from two
+    --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same
+    counter reads for the copy probe of known size.  Returns the files
+    written."""
     import collections
     os.makedirs(PROFILES, exist_ok=True)
     written = []
-    # kernel durations
-    stats = _read_csv(os.path.join(stats_dir, "run_kernel_stats.csv"))
-    # per-dispatch durations, for the median (the average includes the
-    # untimed first launches, whose weights are not yet warm in the TLBs)
-    durations = collections.defaultdict(list)
-    trace = os.path.join(stats_dir, "run_kernel_trace.csv")
-    if os.path.exists(trace):
-        for r in _read_csv(trace):
-            durations[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    # per-dispatch durations from the trace, grouped by (kernel, grid size)
+    groups = collections.defaultdict(list)
+    for r in _read_csv(os.path.join(stats_dir, "run_kernel_trace.csv")):
+        key = (short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1))
+        groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total_all = sum(sum(v) for v in groups.values())
     path = os.path.join(PROFILES, f"kernel_stats_{workload}.txt")
     with open(path, "w") as f:
-        f.write(f"# rocprofv3 kernel statistics, {workload}\n# command: {commands['stats']}\n")
-        f.write(f"# {'calls':>6} {'avg_us':>10} {'median_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10} "
-                f"{'pct':>6}  kernel\n")
-        for r in stats:
-            lab = label_from_rocprof(r["Name"]) or r["Name"][:80]
-            d = sorted(durations.get(r["Name"], []))
-            med = d[len(d) // 2] / 1e3 if d else float("nan")
-            f.write(f"  {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {med:10.2f} "
-                    f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
-                    f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}  {lab}\n")
+        f.write(f"# rocprofv3 kernel statistics, {workload}, per kernel and grid (workgroups)\n")
+        f.write(f"# command: {commands['stats']}\n")
+        f.write(f"# {'calls':>6} {'grid':>6} {'avg_us':>10} {'median_us':>10} {'min_us':>10} {'max_us':>10} "
+                f"{'total_ms':>10} {'pct':>6}  kernel\n")
+        for (lab, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            d = sorted(d)
+            f.write(f"  {len(d):6d} {grid:6d} {sum(d) / len(d):10.2f} {d[len(d) // 2]:10.2f} {d[0]:10.2f} "
+                    f"{d[-1]:10.2f} {sum(d) / 1e3:10.3f} {100 * sum(d) / total_all:6.2f}  {lab}\n")
     written.append(path)
+    if fetch_dir == "-" or write_dir == "-":
+        return written
 
     def per_kernel(d, counter):
         agg = collections.defaultdict(list)
         for r in _read_csv(os.path.join(d, "run_counter_collection.csv")):
             if r["Counter_Name"] == counter:
-                agg[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)  # KiB -> bytes
+                wg = max(int(r["Workgroup_Size"]), 1)
+                agg[(r["Kernel_Name"], int(r["Grid_Size"]) // wg)].append(float(r["Counter_Value"]) * 1024.0)
         return agg
 
     def copy_factor(d, counter, true_bytes):
-        vals = [v for k, v in per_kernel(d, counter).items() if "copy_probe_kernel" in k]
+        vals = [v for (k, _), v in per_kernel(d, counter).items() if "copy_probe_kernel" in k]
         if not vals:
             raise RuntimeError(f"no copy_probe_kernel rows in {d}")
         got = sum(vals[0]) / len(vals[0])
@@ -604,14 +683,16 @@ def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, copy_fetc
     rf, rgot = copy_factor(copy_fetch_dir, "FETCH_SIZE", probe_bytes)
     wf, wgot = copy_factor(copy_write_dir, "WRITE_SIZE", probe_bytes)
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    by_label = collections.defaultdict(list)
+    for (name, grid), vals in fetch.items():
+        if (name, grid) in write and ("wsg::" in name or label_from_rocprof(name)):
+            by_label[short_kernel_name(name)].append((name, grid, vals, write[(name, grid)]))
     digest = source_digest()
-    for name, vals in fetch.items():
-        lab = label_from_rocprof(name)
-        if lab is None or name not in write:
-            continue
-        fb = sum(vals) / len(vals) * rf
-        wb = sum(write[name]) / len(write[name]) * wf
-        safe = lab.replace("<", "_").replace(">", "").replace(",", "_").replace("=", "")
+    for lab, items in sorted(by_label.items()):
+        fv = [v for it in items for v in it[2]]
+        wv = [v for it in items for v in it[3]]
+        fb, wb = sum(fv) / len(fv) * rf, sum(wv) / len(wv) * wf
+        safe = "".join(c if c.isalnum() else "_" for c in lab).strip("_")
         path = os.path.join(PROFILES, f"traffic_{safe}_{workload}.txt")
         with open(path, "w") as f:
             f.write(f"# HBM traffic per launch from rocprofv3 counters, {workload}\n")
@@ -620,8 +701,11 @@ def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, copy_fetc
             f.write(f"# calibration: copy probe of {probe_bytes} B read / {probe_bytes} B written per launch; "
                     f"FETCH_SIZE reads {rgot:.0f} B (factor {rf:.4f}), WRITE_SIZE reads {wgot:.0f} B "
                     f"(factor {wf:.4f})\n")
-            f.write(f"kernel: {lab}\nrocprof_name: {name}\nsource_sha256: {digest}\n")
-            f.write(f"launches: {len(vals)}\nfetch_bytes_per_launch: {fb:.0f}\nwrite_bytes_per_launch: {wb:.0f}\n")
+            f.write(f"kernel: {lab}\nrocprof_name: {items[0][0]}\nsource_sha256: {digest}\n")
+            f.write(f"launches: {len(fv)}\nfetch_bytes_per_launch: {fb:.0f}\nwrite_bytes_per_launch: {wb:.0f}\n")
+            for name, grid, fvals, wvals in sorted(items, key=lambda it: it[1]):
+                f.write(f"grid {grid}: launches {len(fvals)}, fetch_bytes_per_launch {sum(fvals) / len(fvals) * rf:.0f}, "
+                        f"write_bytes_per_launch {sum(wvals) / len(wvals) * wf:.0f}\n")
         written.append(path)
     return written
 
@@ -694,10 +778,12 @@ def main() -> int:
         print("the persistent plan runs Q8_0 streams with fused requantization or f32 activations", file=sys.stderr)
         return 2
 
-    sec, kernels_per_token = time_plan(ts, args.plan, args.steps, args.warmup)
+    rstats = {}
+    sec, kernels_per_token = time_plan(ts, args.plan, args.steps, args.warmup, rstats)
     value = gbps(alg_bytes, sec)
     log(f"{args.plan} plan, {kernels_per_token} kernel(s) per token: timed {args.steps} steps: "
-        f"{sec * 1e6:.1f} us per token, {value:.1f} GB/s")
+        f"{sec * 1e6:.1f} us per token (median {rstats['median_s'] * 1e6:.1f}, min {rstats['min_s'] * 1e6:.1f}), "
+        f"{value:.1f} GB/s")
 
     wtype_code = wsg.W_Q8_0 if wl.wtype == "q8_0" else wsg.W_BF16
     if persistent:
@@ -708,24 +794,20 @@ def main() -> int:
             "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": read_traffic(label),
             "kernel": label + " (the whole token in one launch)",
             "launches_per_token": 1, "bytes_per_launch": alg_bytes, "us_per_launch": round(sec * 1e6, 1),
+            "timing": "HIP events around the token replays",
         }
     else:
-        # group the launches by kernel instantiation.  HIP events around each
-        # eager launch also count the command processor's dispatch of it
-        # (~2 us); the shares they give are scaled to the measured replay
-        # time of the whole graph, so the launches add up to the token.
-        per = time_per_launch(ts, reps=3)
-        scale = sec / sum(per)
-        per = [t * scale for t in per]
+        # each matrix of the layer as it runs in the token (its L launches in
+        # one graph, HIP events around the replays), grouped by kernel
+        # instantiation; the dominant one takes the most time per token
+        shapes = time_per_shape(ts, wtype_code, act_fmt, reps=max(5, args.steps // 5))
         groups = {}
-        for slot, t in zip(ts.slots, per):
-            cfg = wsg.gemv_config(wtype_code, act_fmt, slot.n, slot.k)
-            label = kernel_label(wl.wtype, act_fmt, cfg)
-            bpl = slot.n * (slot.k // 32) * 34 if wl.wtype == "q8_0" else slot.n * slot.k * 2
-            g = groups.setdefault(label, {"t": 0.0, "bytes": 0, "launches": 0})
-            g["t"] += t
-            g["bytes"] += bpl
-            g["launches"] += 1
+        for r in shapes:
+            g = groups.setdefault(r["label"], {"t": 0.0, "bytes": 0, "launches": 0, "shapes": []})
+            g["t"] += r["us"] * 1e-6 * r["launches_per_token"]
+            g["bytes"] += r["bytes"] * r["launches_per_token"]
+            g["launches"] += r["launches_per_token"]
+            g["shapes"].append(r)
         dom = max(groups, key=lambda kk: groups[kk]["t"])
         g = groups[dom]
         achieved = gbps(g["bytes"] / g["launches"], g["t"] / g["launches"])
@@ -734,7 +816,19 @@ def main() -> int:
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": read_traffic(dom), "kernel": dom,
             "launches_per_token": g["launches"], "bytes_per_launch": g["bytes"] // g["launches"],
             "us_per_launch": round(g["t"] / g["launches"] * 1e6, 2),
+            "timing": ("HIP events around graphs of each matrix's launches of the token (one per layer, "
+                       "in token order); bytes and time summed over the kernel's shapes"),
+            "shapes": [{"n": r["n"], "k": r["k"], "grid": r["grid"], "bytes_per_launch": r["bytes"],
+                        "us_per_launch": round(r["us"], 2), "GBps": round(gbps(r["bytes"], r["us"] * 1e-6), 1),
+                        "frac": round(gbps(r["bytes"], r["us"] * 1e-6) / HBM_PEAK_GBPS, 4)} for r in g["shapes"]],
+            "other_kernels": {lab: {"launches_per_token": o["launches"],
+                                    "us_per_launch": round(o["t"] / o["launches"] * 1e6, 2),
+                                    "GBps": round(gbps(o["bytes"] / o["launches"], o["t"] / o["launches"]), 1)}
+                              for lab, o in groups.items() if lab != dom},
         }
+        for r in shapes:
+            log(f"  {r['label']} n={r['n']} k={r['k']}: {r['us']:.2f} us/launch, "
+                f"{gbps(r['bytes'], r['us'] * 1e-6):.1f} GB/s")
     log(f"dominant kernel {roofline['kernel']}: {roofline['us_per_launch']} us/launch, "
         f"{roofline['achieved']} GB/s")
 
@@ -795,6 +889,9 @@ def main() -> int:
             "plan": args.plan,
         },
         "us_per_token": round(sec * 1e6, 1),
+        "us_per_token_median": round(rstats["median_s"] * 1e6, 1),
+        "us_per_token_min": round(rstats["min_s"] * 1e6, 1),
+        "timed_replays": rstats["replays"],
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "tok_per_s_equiv": round(1.0 / sec, 1),
         "roofline": roofline,

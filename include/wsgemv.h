@@ -450,9 +450,10 @@ int wsg_stream_config(int* waves, int* unroll, int* sets);
 
 /* --------------------------------------------------- measurement tools ---
  * wsg_read_probe: reads `bytes` (multiple of 16) from buf with the same
- * load width and cache policy as the GEMV weight stream and writes one
- * float per workgroup to sink[blocks] so the reads are not elided; blocks
- * <= 0 picks the GEMV's grid size.  wsg_copy_probe: dst[i] = src[i] for
+ * load width and cache policy as the GEMV weight stream (each wave one
+ * contiguous span, eight 1 KB wave loads in flight) and writes one float
+ * per 256-thread workgroup to sink[blocks] so the reads are not elided;
+ * blocks <= 0 picks four workgroups per CU.  wsg_copy_probe: dst[i] = src[i] for
  * `bytes` (multiple of 16): a kernel of exactly known traffic for
  * calibrating hardware byte counters. */
 int wsg_read_probe(const void* buf, int64_t bytes, float* sink, int blocks, hipStream_t stream);
