@@ -68,9 +68,10 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
-def read_traffic(kernel_name: str):
+def read_traffic(kernel_name: str, workload: str):
     """HBM bytes per launch measured by rocprofv3 counters for this kernel
-    (profiles/traffic_*.txt), or None if absent or taken on other sources."""
+    in this workload (profiles/traffic_*.txt), or None if absent or taken
+    on other sources."""
     if not os.path.isdir(PROFILES):
         return None
     digest = source_digest()
@@ -83,12 +84,22 @@ def read_traffic(kernel_name: str):
                 if ":" in line and not line.startswith("#"):
                     a, b = line.split(":", 1)
                     kv[a.strip()] = b.strip()
-        if kv.get("kernel") == kernel_name and kv.get("source_sha256") == digest:
+        if kv.get("kernel") == kernel_name and kv.get("workload") == workload and kv.get("source_sha256") == digest:
             try:
-                return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+                return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]), fn
             except (KeyError, ValueError):
                 return None
     return None
+
+
+def profile_refs(kernel_name: str, workload: str):
+    """The roofline's traffic figure and the committed rocprofv3 summaries
+    behind it (kernel statistics, counters) for this kernel and workload."""
+    t = read_traffic(kernel_name, workload)
+    stats = f"kernel_stats_{workload}.txt"
+    refs = {"stats": f"profiles/{stats}" if os.path.exists(os.path.join(PROFILES, stats)) else None,
+            "traffic": f"profiles/{t[1]}" if t else None}
+    return (round(t[0]) if t else None), refs
 
 
 # ------------------------------------------------------------ workload
@@ -586,10 +597,19 @@ def label_from_rocprof(name: str):
     """Bench label of a kernel from its demangled rocprofv3 name (template
     arguments), or None for kernels outside the library's GEMV stream."""
     import re
-    m = re.search(r"(q8_i8_kernel|q8_f32_kernel|bf16_kernel|stream_kernel)<([^>]*)>", name)
+    m = re.search(r"\b(q8_i8_kernel|q8_f32_kernel|bf16_kernel|stream_kernel|q8_i8_norm_kernel|q8_f32_norm_kernel|"
+                  r"q8_i8_swiglu_kernel|q4_i8_kernel|q4_i8_norm_kernel|q4_i8_swiglu_kernel|q4_f32_kernel)<([^>]*)>", name)
     if not m:
         return None
     kind, args = m.group(1), [a.strip() for a in m.group(2).split(",")]
+    if kind in ("q8_i8_swiglu_kernel", "q4_i8_swiglu_kernel"):
+        return f"{kind}<waves={args[0]},{_ACT_NAMES[args[1]]}>"
+    if kind == "q4_i8_kernel":
+        return f"{kind}<waves={args[0]},split={args[1]},{_ACT_NAMES[args[2]]}>"
+    if kind == "q8_i8_norm_kernel":
+        return f"{kind}<waves={args[0]},split={args[1]},unroll={args[2]}>"
+    if kind in ("q8_f32_norm_kernel", "q4_i8_norm_kernel", "q4_f32_kernel"):
+        return f"{kind}<waves={args[0]},split={args[1]}>"
     if kind == "stream_kernel":
         sc = {"waves": int(args[0]), "unroll": int(args[1]), "sets": int(args[2])}
         return stream_label(sc, args[3] == "true")
@@ -701,7 +721,7 @@ def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, copy_fetc
             f.write(f"# calibration: copy probe of {probe_bytes} B read / {probe_bytes} B written per launch; "
                     f"FETCH_SIZE reads {rgot:.0f} B (factor {rf:.4f}), WRITE_SIZE reads {wgot:.0f} B "
                     f"(factor {wf:.4f})\n")
-            f.write(f"kernel: {lab}\nrocprof_name: {items[0][0]}\nsource_sha256: {digest}\n")
+            f.write(f"kernel: {lab}\nworkload: {workload}\nrocprof_name: {items[0][0]}\nsource_sha256: {digest}\n")
             f.write(f"launches: {len(fv)}\nfetch_bytes_per_launch: {fb:.0f}\nwrite_bytes_per_launch: {wb:.0f}\n")
             for name, grid, fvals, wvals in sorted(items, key=lambda it: it[1]):
                 f.write(f"grid {grid}: launches {len(fvals)}, fetch_bytes_per_launch {sum(fvals) / len(fvals) * rf:.0f}, "
@@ -734,7 +754,7 @@ def main() -> int:
                          "print one JSON line per configuration and mode, instead of the benchmark line")
     ap.add_argument("--summarize", nargs=5, metavar=("STATS", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write profiles/ summaries from rocprofv3 output directories (no GPU needed); "
-                         "the commands that made them are read from STATS/../commands.json")
+                         "the commands that made them are read from STATS/commands.json")
     args = ap.parse_args()
     if args.probe:
         return run_probe(args.probe, args.probe_bytes)
@@ -786,12 +806,14 @@ def main() -> int:
         f"{value:.1f} GB/s")
 
     wtype_code = wsg.W_Q8_0 if wl.wtype == "q8_0" else wsg.W_BF16
+    prof_workload = f"{wl.name}_{args.plan}" + ("_deq2" if args.deq == 2 else "")
     if persistent:
         # one launch per token: the dominant kernel is the whole stream
         label = stream_label(wsg.stream_config(), act_fmt == wsg.ACT_F32)
+        traffic, refs = profile_refs(label, prof_workload)
         roofline = {
             "bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": read_traffic(label),
+            "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": traffic, "profiles": refs,
             "kernel": label + " (the whole token in one launch)",
             "launches_per_token": 1, "bytes_per_launch": alg_bytes, "us_per_launch": round(sec * 1e6, 1),
             "timing": "HIP events around the token replays",
@@ -811,9 +833,10 @@ def main() -> int:
         dom = max(groups, key=lambda kk: groups[kk]["t"])
         g = groups[dom]
         achieved = gbps(g["bytes"] / g["launches"], g["t"] / g["launches"])
+        traffic, refs = profile_refs(dom, prof_workload)
         roofline = {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": read_traffic(dom), "kernel": dom,
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "profiles": refs, "kernel": dom,
             "launches_per_token": g["launches"], "bytes_per_launch": g["bytes"] // g["launches"],
             "us_per_launch": round(g["t"] / g["launches"] * 1e6, 2),
             "timing": ("HIP events around graphs of each matrix's launches of the token (one per layer, "

@@ -64,3 +64,68 @@ def test_gbps_and_multi_gpu_refusal(capsys):
     finally:
         sys.argv = argv
     assert "one GPU" in capsys.readouterr().err
+
+
+def _write_csv(path, header, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=header)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_kernel_labels_from_rocprof_names():
+    ns = "void wsg::(anonymous namespace)::"
+    cases = {
+        "q8_i8_kernel<8, 1, 1, 2, true, false, false>(unsigned char const*)": "q8_i8_kernel<waves=8,split=1,unroll=1,requant>",
+        "q8_i8_kernel<8, 1, 1, 0, true, false, true>(unsigned char const*)": "q8_i8_kernel<waves=8,split=1,unroll=1,q8act,argmax>",
+        "q8_f32_kernel<16, 4, 1, true, false>(unsigned char const*)": "q8_f32_kernel<waves=16,split=4,unroll=1,f32act>",
+        "q8_f32_norm_kernel<8, 1>(unsigned char const*)": "q8_f32_norm_kernel<waves=8,split=1>",
+        "q8_i8_swiglu_kernel<8, 1>(unsigned char const*)": "q8_i8_swiglu_kernel<waves=8,f32act>",
+        "q4_i8_kernel<16, 1, 2>(unsigned char const*)": "q4_i8_kernel<waves=16,split=1,requant>",
+        "stream_kernel<16, 1, 3, false>(wsg::StreamOp const*, int, unsigned int*, int)": "stream_kernel<waves=16,unroll=1,sets=3,requant>",
+    }
+    for raw, lab in cases.items():
+        assert bench.label_from_rocprof(ns + raw) == lab
+        assert bench.short_kernel_name(ns + raw) == lab
+    assert bench.label_from_rocprof(ns + "argmax_stage2_kernel(unsigned long const*, int, int*)") is None
+    assert bench.short_kernel_name(ns + "argmax_stage2_kernel(unsigned long const*, int, int*)") == "argmax_stage2_kernel"
+
+
+def test_profile_summary_groups_by_grid_and_calibrates(tmp_path, monkeypatch):
+    """Per-(kernel, grid) statistics from a kernel trace, and per-launch
+    bytes from counter runs scaled by the copy probe's known traffic."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    k = "void wsg::(anonymous namespace)::q8_i8_kernel<8, 1, 1, 2, true, false, false>(unsigned char const*)"
+    copy = "wsg::(anonymous namespace)::copy_probe_kernel(int4v const*, int4v*, long)"
+    th = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"]
+    trace = [{"Kernel_Name": k, "Grid_Size_X": 512 * 512, "Workgroup_Size_X": 512, "Start_Timestamp": 0,
+              "End_Timestamp": d} for d in (16000, 17000, 15000)]
+    trace += [{"Kernel_Name": k, "Grid_Size_X": 484 * 512, "Workgroup_Size_X": 512, "Start_Timestamp": 0,
+               "End_Timestamp": 32000}]
+    _write_csv(str(tmp_path / "s" / "run_kernel_trace.csv"), th, trace)
+    ch = ["Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name", "Counter_Value"]
+
+    def counters(d, name, vals):
+        _write_csv(str(tmp_path / d / "run_counter_collection.csv"), ch,
+                   [{"Kernel_Name": kn, "Grid_Size": g * 512, "Workgroup_Size": 512, "Counter_Name": name,
+                     "Counter_Value": v} for kn, g, v in vals])
+
+    counters("f", "FETCH_SIZE", [(k, 512, 1000.0), (k, 512, 1200.0), (k, 484, 3000.0)])
+    counters("w", "WRITE_SIZE", [(k, 512, 10.0), (k, 512, 10.0), (k, 484, 20.0)])
+    counters("cf", "FETCH_SIZE", [(copy, 2048, 512.0)])    # 1 MiB copy read, counter shows half
+    counters("cw", "WRITE_SIZE", [(copy, 2048, 1024.0)])
+    cmds = {"stats": "S", "fetch": "F", "write": "W", "copy_fetch": "CF", "copy_write": "CW", "probe_bytes": 1 << 20}
+    out = bench.summarize_profiles(*(str(tmp_path / d) for d in ("s", "f", "w", "cf", "cw")),
+                                   workload="wl", commands=cmds)
+    stats = open(out[0]).read().splitlines()
+    rows = [l.split() for l in stats if not l.startswith("#")]
+    assert [(r[0], r[1], r[2]) for r in rows] == [("3", "512", "16.00"), ("1", "484", "32.00")]
+    lab = "q8_i8_kernel<waves=8,split=1,unroll=1,requant>"
+    got, refs = bench.profile_refs(lab, "wl")
+    # fetch factor 2 (the counter read half the copy's bytes), write factor 1; KiB -> bytes
+    assert got == round((1000 + 1200 + 3000) / 3 * 2 * 1024 + (10 + 10 + 20) / 3 * 1024)
+    assert refs["stats"] == "profiles/kernel_stats_wl.txt" and refs["traffic"].endswith("_wl.txt")
+    assert bench.profile_refs(lab, "other") == (None, {"stats": None, "traffic": None})
