@@ -368,7 +368,7 @@ def measure_configs(steps: int, warmup: int) -> list:
             ts.close()
             del ts
             torch.cuda.empty_cache()
-            if wl.wtype == "q8_0" and deq == 0:
+            if wl.wtype == "q8_0":
                 # the same chain with the norm step in each normalized GEMV's prologue
                 ts = build_stream(wl, deq, "fused", norm=True, fused_norm=True)
                 sec, kernels = time_plan(ts, False, steps, warmup)
@@ -393,22 +393,24 @@ def measure_configs(steps: int, warmup: int) -> list:
     del ts
     torch.cuda.empty_cache()
     # a whole decode step: embedding -> layers -> LM head + argmax -> advance
-    for wl, wt in ((W.QWEN3_8B_Q8, "q8_0"), (W.DENSE27B_Q8, "q8_0"), (W.DENSE27B_Q8, "q4_0")):
-        ds = build_decode(wl, wtype=wt)
+    for wl, wt, deq in ((W.QWEN3_8B_Q8, "q8_0", 0), (W.DENSE27B_Q8, "q8_0", 0), (W.DENSE27B_Q8, "q8_0", 2),
+                        (W.DENSE27B_Q8, "q4_0", 0)):
+        ds = build_decode(wl, wtype=wt, deq=deq)
         alg = ds.chain.algorithmic_weight_bytes() + ds.vocab * (ds.hidden // 32) * 34
         ds.capture()
         for _ in range(warmup):
             ds.launch()
         sec = _time_calls(lambda i: ds.launch(), steps, 0)
         rec(wl, "decode step graph (embedding, norms, SwiGLU, LM head + argmax, token advance), vocab 151936"
-            + (", 4-bit layers" if wt == "q4_0" else ""), sec, alg, kernels_per_token=ds.plan.kernel_count, deq=0)
+            + (", 4-bit layers" if wt == "q4_0" else "") + f", deq{deq}", sec, alg,
+            kernels_per_token=ds.plan.kernel_count, deq=deq)
         ds.close()
         del ds
         torch.cuda.empty_cache()
     return out
 
 
-def build_decode(wl, vocab: int = 151936, wtype: str = "q8_0"):
+def build_decode(wl, vocab: int = 151936, wtype: str = "q8_0", deq: int = 0):
     """A whole decode step on the workload's layer shapes (DecodeStep):
     embedding gather -> the layers with the residual stream (norms fused
     into the attention-input GEMVs, SwiGLU on gate+up) -> final norm ->
@@ -422,7 +424,7 @@ def build_decode(wl, vocab: int = 151936, wtype: str = "q8_0"):
     from weight_streaming_gemv_q8_amd.stream import DecodeStep
 
     shapes = [(m.n, m.k, m.parts) for m in wl.matrices]
-    ds = DecodeStep(shapes, wl.layers, vocab, capacity=4096, eps=W.RMSNORM_EPS, wtype=wtype)
+    ds = DecodeStep(shapes, wl.layers, vocab, capacity=4096, eps=W.RMSNORM_EPS, wtype=wtype, deq=deq)
     stream = torch.cuda.current_stream().cuda_stream
 
     def fill(layer, m, part, rows, staging):

@@ -131,21 +131,21 @@ __device__ __attribute__((always_inline)) inline void q8_i8_body(const uint8_t* 
 
 // Staging of the int8 path's input: a quantize_act_q8_0 output, or f32
 // requantized in the workgroup.
-template <int ACT>
+template <int ACT, int T>
 struct StageInput {
     const void* xin;
     int k, C;
-    typename std::conditional<ACT == kActRequant, StageRequant<4>, StageQ8<4>>::type st;
+    typename std::conditional<ACT == kActRequant, StageRequant<4, T>, StageQ8<4, T>>::type st;
     __device__ void issue() { st.issue(xin, k, C); }
     __device__ void commit(int4v* lds_q, float* lds_dx, float*) { st.commit(xin, k, C, lds_q, lds_dx); }
 };
 
 // f32 input of the dequantizing path (the SwiGLU kernel's W8A16 form).
-template <>
-struct StageInput<kActF32> {
+template <int T>
+struct StageInput<kActF32, T> {
     const void* xin;
     int k, C;
-    StageF32<4> st;
+    StageF32<4, T> st;
     __device__ void issue() { st.issue(static_cast<const float*>(xin), k); }
     __device__ void commit(int4v* lds, float*, float*) {
         st.commit(static_cast<const float*>(xin), k, reinterpret_cast<float4v*>(lds));
@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per
 q8_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict__ xin, float* __restrict__ y,
              int32_t* __restrict__ dots, uint64_t* __restrict__ keys) {
     static_assert(NT, "the weight stream is always loaded non-temporally");
-    StageInput<ACT> stage{xin, k, (int)chunk_count(k), {}};
+    StageInput<ACT, WAVES * kWave> stage{xin, k, (int)chunk_count(k), {}};
     q8_i8_body<WAVES, S, U, DEBUG, ARGMAX>(W, n, k, y, dots, keys, stage);
 }
 
@@ -252,7 +252,7 @@ q8_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
         }
     };
     Q8Regs<1> R[kRingSets<1, 1>];
-    StageInput<ACT> stage{xin, k, C, {}};
+    StageInput<ACT, WAVES * kWave> stage{xin, k, C, {}};
     stage.issue();
     __builtin_amdgcn_sched_barrier(0);
     ring_prologue(sc, R, load);
@@ -418,7 +418,7 @@ __device__ __attribute__((always_inline)) inline void q4_i8_body(const uint8_t* 
 template <int WAVES, int S, int ACT>
 __global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 q4_i8_kernel(const uint8_t* __restrict__ W, int n, int k, const void* __restrict__ xin, float* __restrict__ y) {
-    StageInput<ACT> stage{xin, k, (int)chunk_count(k), {}};
+    StageInput<ACT, WAVES * kWave> stage{xin, k, (int)chunk_count(k), {}};
     q4_i8_body<WAVES, S>(W, n, k, y, stage);
 }
 
@@ -487,7 +487,7 @@ q4_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
         }
     };
     Q4Regs R[kRingQ4];
-    StageInput<ACT> stage{xin, k, C, {}};
+    StageInput<ACT, WAVES * kWave> stage{xin, k, C, {}};
     stage.issue();
     __builtin_amdgcn_sched_barrier(0);
     ring_prologue(sc, R, load);
@@ -575,7 +575,7 @@ q4_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restri
     };
 
     Q4Regs R[kRingQ4];
-    StageF32<4> st;
+    StageF32<4, WAVES * kWave> st;
     st.issue(x, k);
     __builtin_amdgcn_sched_barrier(0);
     if (rot)
@@ -699,7 +699,7 @@ __global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per
 q8_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restrict__ x, float* __restrict__ y,
               uint64_t* __restrict__ keys) {
     static_assert(NT, "the weight stream is always loaded non-temporally");
-    StageInput<kActF32> stage{x, k, (int)chunk_count(k), {}};
+    StageInput<kActF32, WAVES * kWave> stage{x, k, (int)chunk_count(k), {}};
     q8_f32_body<WAVES, S, U, ARGMAX>(W, n, k, y, keys, stage);
 }
 
@@ -747,7 +747,7 @@ bf16_kernel(const uint16_t* __restrict__ W, int n, int k, const float* __restric
     };
 
     Bf16Regs<U> R[kRingSets<U, S>];
-    StageBf16x<4> st;
+    StageBf16x<4, WAVES * kWave> st;
     st.issue(x, k);
     __builtin_amdgcn_sched_barrier(0);
     ring_prologue(sc, R, load);
@@ -763,13 +763,18 @@ bf16_kernel(const uint16_t* __restrict__ W, int n, int k, const float* __restric
 }
 
 // ---------------------------------------------------------------- argmax
-__global__ void argmax_stage1_kernel(const float* __restrict__ v, int64_t n, uint64_t* __restrict__ keys) {
+// Block sizes of the two argmax stages (compile-time, so no index waits
+// for a load of the block size).
+constexpr int kArgmax1Threads = 256, kArgmax2Threads = 1024;
+
+__global__ void __launch_bounds__(kArgmax1Threads) argmax_stage1_kernel(const float* __restrict__ v, int64_t n,
+                                                                         uint64_t* __restrict__ keys) {
     __shared__ uint64_t lds_key[16];
     const int64_t per = (n + gridDim.x - 1) / gridDim.x;
     const int64_t begin = (int64_t)blockIdx.x * per;
     const int64_t end = begin + per < n ? begin + per : n;
     uint64_t best = 0;
-    for (int64_t i = begin + threadIdx.x; i < end; i += blockDim.x) {
+    for (int64_t i = begin + threadIdx.x; i < end; i += kArgmax1Threads) {
         const uint64_t key = argmax_key(v[i], (uint32_t)i);
         best = key > best ? key : best;
     }
@@ -779,22 +784,23 @@ __global__ void argmax_stage1_kernel(const float* __restrict__ v, int64_t n, uin
     __syncthreads();
     if (threadIdx.x == 0) {
         uint64_t m = lds_key[0];
-        for (int w = 1; w < (int)(blockDim.x / kWave); ++w) m = lds_key[w] > m ? lds_key[w] : m;
+        for (int w = 1; w < kArgmax1Threads / kWave; ++w) m = lds_key[w] > m ? lds_key[w] : m;
         keys[blockIdx.x] = m;
     }
 }
 
-__global__ void argmax_stage2_kernel(const uint64_t* __restrict__ keys, int count, int32_t* __restrict__ idx_out) {
+__global__ void __launch_bounds__(kArgmax2Threads) argmax_stage2_kernel(const uint64_t* __restrict__ keys, int count,
+                                                                         int32_t* __restrict__ idx_out) {
     __shared__ uint64_t lds_key[16];
     uint64_t best = 0;
-    for (int i = threadIdx.x; i < count; i += blockDim.x) best = keys[i] > best ? keys[i] : best;
+    for (int i = threadIdx.x; i < count; i += kArgmax2Threads) best = keys[i] > best ? keys[i] : best;
     best = wave_max_u64(best);
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     if (lane == 0) lds_key[wave] = best;
     __syncthreads();
     if (threadIdx.x == 0) {
         uint64_t m = lds_key[0];
-        for (int w = 1; w < (int)(blockDim.x / kWave); ++w) m = lds_key[w] > m ? lds_key[w] : m;
+        for (int w = 1; w < kArgmax2Threads / kWave; ++w) m = lds_key[w] > m ? lds_key[w] : m;
         idx_out[0] = (int32_t)argmax_key_index(m);
     }
 }
@@ -1249,7 +1255,7 @@ int launch_bf16(const uint16_t* w, int n, int k, const float* x, float* y, uint6
 }
 
 int launch_argmax_stage2(const uint64_t* keys, int count, int32_t* idx_out, hipStream_t stream) {
-    hipLaunchKernelGGL(argmax_stage2_kernel, dim3(1), dim3(1024), 0, stream, keys, count, idx_out);
+    hipLaunchKernelGGL(argmax_stage2_kernel, dim3(1), dim3(kArgmax2Threads), 0, stream, keys, count, idx_out);
     return launch_status();
 }
 
@@ -1626,7 +1632,7 @@ int argmax_f32(const float* v, int64_t n, void* ws, size_t ws_bytes, int32_t* id
     if (g > kMaxGrid) g = kMaxGrid;
     if (g < 1) g = 1;
     uint64_t* keys = static_cast<uint64_t*>(ws);
-    hipLaunchKernelGGL(argmax_stage1_kernel, dim3((unsigned)g), dim3(256), 0, stream, v, n, keys);
+    hipLaunchKernelGGL(argmax_stage1_kernel, dim3((unsigned)g), dim3(kArgmax1Threads), 0, stream, v, n, keys);
     int rc = launch_status();
     if (rc != WSG_OK) return rc;
     return launch_argmax_stage2(keys, (int)g, idx_out, stream);

@@ -415,11 +415,15 @@ __device__ inline void flush_parts(const Sched& sc, const float* res, float* y) 
 // Each path stages the activation in LDS in two steps: issue() puts this
 // thread's first NR units in registers (before the weight prefetch, so
 // waiting for them does not wait for the weights), commit() writes them and
-// any remaining units to LDS.
+// any remaining units to LDS.  The workgroup's thread count T is a template
+// argument, not blockDim.x: on this target the block size is read from the
+// dispatch's implicit arguments with a 16-bit vector load, and an address
+// computed from it makes the wave wait for every load issued before it, so
+// the weight prefetch would start one memory round trip late.
 
 // Planar Q8_0 activation (q[k] then fp16 d[k/32]) -> LDS int4v q[C][2][64]
 // (half h of block 64c+l) and float dx[C*64].
-template <int NR>
+template <int NR, int T>
 struct StageQ8 {
     int4v q[NR];
     uint16_t d[NR];
@@ -429,11 +433,11 @@ struct StageQ8 {
         const uint16_t* dx = reinterpret_cast<const uint16_t*>(qx + k);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int u = threadIdx.x + i * blockDim.x;
+            const int u = threadIdx.x + i * T;
             const int l = u % kWave, ch = u / kWave, h = ch & 1, c = ch >> 1;
             const int b = c * kWave + l;
             if (u < C * 2 * kWave && b < NB) q[i] = *reinterpret_cast<const int4v*>(qx + (int64_t)b * kBlock + 16 * h);
-            const int bd = threadIdx.x + i * blockDim.x;
+            const int bd = threadIdx.x + i * T;
             if (bd < NB) d[i] = dx[bd];
         }
     }
@@ -443,18 +447,18 @@ struct StageQ8 {
         const uint16_t* dx = reinterpret_cast<const uint16_t*>(qx + k);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int u = threadIdx.x + i * blockDim.x;
+            const int u = threadIdx.x + i * T;
             const int l = u % kWave, c = (u / kWave) >> 1;
             if (u < C * 2 * kWave && c * kWave + l < NB) lds_q[u] = q[i];
-            const int bd = threadIdx.x + i * blockDim.x;
+            const int bd = threadIdx.x + i * T;
             if (bd < NB) lds_dx[bd] = half_bits_to_float(d[i]);
         }
-        for (int u = threadIdx.x + NR * blockDim.x; u < C * 2 * kWave; u += blockDim.x) {
+        for (int u = threadIdx.x + NR * T; u < C * 2 * kWave; u += T) {
             const int l = u % kWave, ch = u / kWave, h = ch & 1, c = ch >> 1;
             const int b = c * kWave + l;
             if (b < NB) lds_q[u] = *reinterpret_cast<const int4v*>(qx + (int64_t)b * kBlock + 16 * h);
         }
-        for (int b = threadIdx.x + NR * blockDim.x; b < NB; b += blockDim.x) lds_dx[b] = half_bits_to_float(dx[b]);
+        for (int b = threadIdx.x + NR * T; b < NB; b += T) lds_dx[b] = half_bits_to_float(dx[b]);
     }
 };
 
@@ -478,7 +482,7 @@ __device__ inline void requant_unit(const float4v v0, const float4v v1, int u, i
 // units per 32-value block (requant_unit).  units = 4 x blocks and the
 // workgroup is a whole number of waves, so the four lanes of a block are in
 // the same wave and all (in)active together.
-template <int NR>
+template <int NR, int T>
 struct StageRequant {
     float4v v[NR][2];
     __device__ void issue(const void* __restrict__ xin, int k, int) {
@@ -486,7 +490,7 @@ struct StageRequant {
         const float4v* x4 = static_cast<const float4v*>(xin);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int u = threadIdx.x + i * blockDim.x;
+            const int u = threadIdx.x + i * T;
             if (u < units) {
                 v[i][0] = x4[2 * u];
                 v[i][1] = x4[2 * u + 1];
@@ -498,10 +502,10 @@ struct StageRequant {
         const float4v* x4 = static_cast<const float4v*>(xin);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int u = threadIdx.x + i * blockDim.x;
+            const int u = threadIdx.x + i * T;
             if (u < units) requant_unit(v[i][0], v[i][1], u, lds_q, lds_dx);
         }
-        for (int u = threadIdx.x + NR * blockDim.x; u < units; u += blockDim.x)
+        for (int u = threadIdx.x + NR * T; u < units; u += T)
             requant_unit(x4[2 * u], x4[2 * u + 1], u, lds_q, lds_dx);
     }
 };
@@ -704,7 +708,7 @@ struct StageNorm {
 
 // f32 activation for the dequantizing path: float4 v (values 4v..4v+3, block
 // b = v/8, group g = v%8) -> LDS float4v x[C][8][64] at (c*8+g)*64 + l.
-template <int NR>
+template <int NR, int T>
 struct StageF32 {
     float4v v[NR];
     __device__ static int slot(int u) { return f32_slot(u); }
@@ -712,7 +716,7 @@ struct StageF32 {
         const float4v* x4 = reinterpret_cast<const float4v*>(x);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int u = threadIdx.x + i * blockDim.x;
+            const int u = threadIdx.x + i * T;
             if (u < k / 4) v[i] = x4[u];
         }
     }
@@ -720,16 +724,16 @@ struct StageF32 {
         const float4v* x4 = reinterpret_cast<const float4v*>(x);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int u = threadIdx.x + i * blockDim.x;
+            const int u = threadIdx.x + i * T;
             if (u < k / 4) lds_x[slot(u)] = v[i];
         }
-        for (int u = threadIdx.x + NR * blockDim.x; u < k / 4; u += blockDim.x) lds_x[slot(u)] = x4[u];
+        for (int u = threadIdx.x + NR * T; u < k / 4; u += T) lds_x[slot(u)] = x4[u];
     }
 };
 
 // f32 activation for the bf16 path: element e = 1024c + 512h + 8l + 4j ->
 // LDS float4v x[C'][2][2][64] at ((c*2+h)*2+j)*64 + l.
-template <int NR>
+template <int NR, int T>
 struct StageBf16x {
     float4v v[NR];
     __device__ static int slot(int u) {
@@ -741,7 +745,7 @@ struct StageBf16x {
         const float4v* x4 = reinterpret_cast<const float4v*>(x);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int u = threadIdx.x + i * blockDim.x;
+            const int u = threadIdx.x + i * T;
             if (u < k / 4) v[i] = x4[u];
         }
     }
@@ -749,10 +753,10 @@ struct StageBf16x {
         const float4v* x4 = reinterpret_cast<const float4v*>(x);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const int u = threadIdx.x + i * blockDim.x;
+            const int u = threadIdx.x + i * T;
             if (u < k / 4) lds_x[slot(u)] = v[i];
         }
-        for (int u = threadIdx.x + NR * blockDim.x; u < k / 4; u += blockDim.x) lds_x[slot(u)] = x4[u];
+        for (int u = threadIdx.x + NR * T; u < k / 4; u += T) lds_x[slot(u)] = x4[u];
     }
 };
 

@@ -37,13 +37,14 @@ static_assert(kNormMaxUnits * 8 * kNormThreads == WSG_MAX_K_Q8ACT, "k limit is a
 template <int NU>
 __global__ __launch_bounds__(kNormThreads) void residual_rmsnorm_kernel(
     const float* h, const float* r, const float* __restrict__ g, int k, float eps, float* h_out,
-    float* __restrict__ y, int8_t* __restrict__ q, uint16_t* __restrict__ d) {
+    float* __restrict__ y, int8_t* __restrict__ q, uint16_t* __restrict__ d, int nt) {
     // g is loaded with h and r while it fits in registers beside h'.
     constexpr bool kEarlyG = NU <= 4;
     __shared__ float wave_part[kNormWaves];
     const int units = k >> 3;
+    // nt = the block size, passed as an argument: reading blockDim.x is a
+    // vector load on this target, and the first unit's address would wait for it
     const int t = threadIdx.x;
-    const int nt = blockDim.x;
 
     float a[NU][8];
     float gv[kEarlyG ? NU : 1][8];
@@ -128,7 +129,8 @@ __global__ __launch_bounds__(kNormThreads) void residual_rmsnorm_kernel(
 template <int NU>
 void launch_norm(int threads, hipStream_t s, const float* h, const float* r, const float* g, int k, float eps,
                  float* h_out, float* y, int8_t* q, uint16_t* d) {
-    hipLaunchKernelGGL(residual_rmsnorm_kernel<NU>, dim3(1), dim3(threads), 0, s, h, r, g, k, eps, h_out, y, q, d);
+    hipLaunchKernelGGL(residual_rmsnorm_kernel<NU>, dim3(1), dim3(threads), 0, s, h, r, g, k, eps, h_out, y, q, d,
+                       threads);
 }
 
 // Threads and units per thread the kernel uses for a vector of k values

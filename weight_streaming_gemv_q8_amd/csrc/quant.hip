@@ -26,9 +26,13 @@ __device__ inline uint16_t quantize_block32(const float* __restrict__ src, int8_
     return q8_quantize_block_bits(v, q);
 }
 
-__global__ void quantize_act_kernel(const float* __restrict__ x, int nb, int8_t* __restrict__ q,
-                                    uint16_t* __restrict__ d) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+// Block sizes are compile-time constants: reading blockDim.x is a vector load
+// on this target, and every index computed from it would wait for that load.
+constexpr int kActThreads = 64, kPrepThreads = 256;
+
+__global__ void __launch_bounds__(kActThreads) quantize_act_kernel(const float* __restrict__ x, int nb,
+                                                                   int8_t* __restrict__ q, uint16_t* __restrict__ d) {
+    const int b = blockIdx.x * kActThreads + threadIdx.x;
     if (b >= nb) return;
     int8_t codes[32];
     const uint16_t d16 = quantize_block32(x + (int64_t)b * kBlock, codes);
@@ -80,8 +84,8 @@ __global__ void quantize_weights_kernel(const float* __restrict__ w, int64_t n, 
     const int64_t nb = k / kBlock;
     const int64_t total = n * nb;
     const int64_t row_bytes = packed_row_bytes(k);
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int64_t stride = (int64_t)gridDim.x * kPrepThreads;
+    for (int64_t t = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x; t < total; t += stride) {
         const int64_t r = t / nb, b = t % nb;
         int8_t codes[32];
         const uint16_t d16 = quantize_block32(w + r * k + b * kBlock, codes);
@@ -97,8 +101,8 @@ __global__ void quantize_q4_kernel(const float* __restrict__ w, int64_t n, int64
     const int64_t nb = k / kBlock;
     const int64_t total = n * nb;
     const int64_t row_bytes = q4_row_bytes(k);
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int64_t stride = (int64_t)gridDim.x * kPrepThreads;
+    for (int64_t t = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x; t < total; t += stride) {
         const int64_t r = t / nb, b = t % nb;
         const float* x = w + r * k + b * kBlock;
         float amax = 0.0f;
@@ -131,8 +135,8 @@ __global__ void pack_kernel(const uint8_t* __restrict__ aos, int64_t n, int64_t 
     const int64_t nb = k / kBlock;
     const int64_t total = n * nb;
     const int64_t row_bytes = packed_row_bytes(k);
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int64_t stride = (int64_t)gridDim.x * kPrepThreads;
+    for (int64_t t = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x; t < total; t += stride) {
         const int64_t r = t / nb, b = t % nb;
         const uint8_t* src = aos + t * 34;
         const uint16_t d16 = (uint16_t)(src[0] | (src[1] << 8));
@@ -144,8 +148,8 @@ __global__ void pack_kernel(const uint8_t* __restrict__ aos, int64_t n, int64_t 
 }
 
 __global__ void convert_bf16_kernel(const float* __restrict__ in, int64_t count, uint16_t* __restrict__ out) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+    const int64_t stride = (int64_t)gridDim.x * kPrepThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x; i < count; i += stride) {
         const uint32_t b = __float_as_uint(in[i]);
         uint16_t r;
         if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu)) {
@@ -160,8 +164,8 @@ __global__ void convert_bf16_kernel(const float* __restrict__ in, int64_t count,
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ y, int64_t n) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) y[i] = 0.0f;
+    const int64_t stride = (int64_t)gridDim.x * kPrepThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x; i < n; i += stride) y[i] = 0.0f;
 }
 
 unsigned grid_for(int64_t items, int block) {
@@ -175,7 +179,7 @@ unsigned grid_for(int64_t items, int block) {
 
 int fill_zero_f32(float* y, int64_t n, hipStream_t stream) {
     if (n <= 0) return WSG_OK;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, y, n);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n, kPrepThreads)), dim3(kPrepThreads), 0, stream, y, n);
     return launch_status();
 }
 
@@ -208,7 +212,7 @@ int quantize_act_q8_0(const float* x, int64_t k, void* x_q8, hipStream_t stream)
     const int nb = (int)(k / kBlock);
     int8_t* q = static_cast<int8_t*>(x_q8);
     uint16_t* d = reinterpret_cast<uint16_t*>(q + k);
-    hipLaunchKernelGGL(quantize_act_kernel, dim3(grid_for(nb, 64)), dim3(64), 0, stream, x, nb, q, d);
+    hipLaunchKernelGGL(quantize_act_kernel, dim3(grid_for(nb, kActThreads)), dim3(kActThreads), 0, stream, x, nb, q, d);
     return launch_status();
 }
 
@@ -217,8 +221,8 @@ int quantize_q8_0_weights(const float* w, int64_t n, int64_t k, void* w_packed, 
     if (n == 0 || k == 0) return WSG_OK;
     if (!w || !w_packed) return WSG_ERR_NULL;
     if (!aligned(w, 16) || !aligned(w_packed, 16)) return WSG_ERR_ALIGN;
-    hipLaunchKernelGGL(quantize_weights_kernel, dim3(grid_for(n * (k / kBlock), 256)), dim3(256), 0, stream, w,
-                       n, k, static_cast<uint8_t*>(w_packed));
+    hipLaunchKernelGGL(quantize_weights_kernel, dim3(grid_for(n * (k / kBlock), kPrepThreads)), dim3(kPrepThreads), 0,
+                       stream, w, n, k, static_cast<uint8_t*>(w_packed));
     return launch_status();
 }
 
@@ -237,8 +241,8 @@ int quantize_q4_0_weights(const float* w, int64_t n, int64_t k, void* w_packed, 
     if (n == 0 || k == 0) return WSG_OK;
     if (!w || !w_packed) return WSG_ERR_NULL;
     if (!aligned(w, 16) || !aligned(w_packed, 16)) return WSG_ERR_ALIGN;
-    hipLaunchKernelGGL(quantize_q4_kernel, dim3(grid_for(n * (k / kBlock), 256)), dim3(256), 0, stream, w, n, k,
-                       static_cast<uint8_t*>(w_packed));
+    hipLaunchKernelGGL(quantize_q4_kernel, dim3(grid_for(n * (k / kBlock), kPrepThreads)), dim3(kPrepThreads), 0,
+                       stream, w, n, k, static_cast<uint8_t*>(w_packed));
     return launch_status();
 }
 
@@ -247,7 +251,7 @@ int pack_q8_0(const void* blocks_aos, int64_t n, int64_t k, void* w_packed, hipS
     if (n == 0 || k == 0) return WSG_OK;
     if (!blocks_aos || !w_packed) return WSG_ERR_NULL;
     if (!aligned(w_packed, 16)) return WSG_ERR_ALIGN;
-    hipLaunchKernelGGL(pack_kernel, dim3(grid_for(n * (k / kBlock), 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(pack_kernel, dim3(grid_for(n * (k / kBlock), kPrepThreads)), dim3(kPrepThreads), 0, stream,
                        static_cast<const uint8_t*>(blocks_aos), n, k, static_cast<uint8_t*>(w_packed));
     return launch_status();
 }
@@ -257,7 +261,8 @@ int convert_bf16(const float* in, int64_t count, uint16_t* out, hipStream_t stre
     if (count == 0) return WSG_OK;
     if (!in || !out) return WSG_ERR_NULL;
     if (!aligned(in, 4) || !aligned(out, 2)) return WSG_ERR_ALIGN;
-    hipLaunchKernelGGL(convert_bf16_kernel, dim3(grid_for(count, 256)), dim3(256), 0, stream, in, count, out);
+    hipLaunchKernelGGL(convert_bf16_kernel, dim3(grid_for(count, kPrepThreads)), dim3(kPrepThreads), 0, stream, in,
+                       count, out);
     return launch_status();
 }
 

@@ -213,7 +213,7 @@ __device__ inline void stage_f32(gcfloat src, bool produced, int k, uint32_t* st
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int u = base + tid + i * T;
-            if (u < units) lds_x[StageF32<1>::slot(u)] = v[i][0];
+            if (u < units) lds_x[f32_slot(u)] = v[i][0];
         }
     }
 }
