@@ -331,6 +331,37 @@ def test_q4_swiglu_gemv(gpu_lib, n_ff, k, act, waves):
         wsg.tune(wsg.TUNE_WAVES, 0)
 
 
+def test_q4_swiglu_pair_paths(gpu_lib):
+    """The two ways the wave pairs of gemv_q4_0_swiglu meet (halves kept in
+    LDS until after the row loop, or a meeting at the end of every tile when
+    a workgroup has more tiles than LDS keeps: forced here with 4-wave
+    workgroups, one per CU) give the same outputs bit for bit, equal to the
+    epilogue applied to the plain GEMV's halves."""
+    import torch
+    wsg = gpu_lib
+    n_ff, k = 17408, 5120
+    w, packed, x = _problem(2 * n_ff, k, 0x5EEDC600)
+    xd = dev(x)
+    outs = []
+    try:
+        for waves, wgpc in ((0, 0), (4, 1)):
+            wsg.tune(wsg.TUNE_WAVES, waves)
+            wsg.tune(wsg.TUNE_WG_PER_CU, wgpc)
+            y = torch.full((n_ff,), np.nan, dtype=torch.float32, device="cuda")
+            wsg.gemv_q4_0_swiglu(packed, n_ff, k, xd, wsg.ACT_F32_REQUANT, y)
+            outs.append(host(y).view(np.uint32).copy())
+        full = torch.empty(2 * n_ff, dtype=torch.float32, device="cuda")
+        wsg.gemv_q4_0(packed, 2 * n_ff, k, xd, wsg.ACT_F32_REQUANT, full)
+    finally:
+        wsg.tune(wsg.TUNE_WAVES, 0)
+        wsg.tune(wsg.TUNE_WG_PER_CU, 0)
+    assert np.array_equal(outs[0], outs[1]), "kept halves vs per-tile meeting"
+    gu = host(full).astype(np.float64)
+    got = outs[0].view(np.float32).astype(np.float64)
+    g, u = gu[:n_ff], gu[n_ff:]
+    assert np.all(np.abs(got - oracle.swiglu(g, u)) <= oracle.swiglu_tolerance(g, u, 0.0, 0.0))
+
+
 def test_q4_swiglu_rejections(gpu_lib):
     import torch
     wsg = gpu_lib

@@ -433,13 +433,21 @@ q4_i8_norm_kernel(const uint8_t* __restrict__ W, int n, int k, NormArgs na, floa
     q4_i8_body<WAVES, S>(W, n, k, y, stage);
 }
 
-// The 4-bit gate+up GEMV with the SwiGLU epilogue: q8_i8_swiglu_kernel's
-// schedule (each wave walks the gate chunks then the up chunks of one
-// output, one accumulator per half) with the 4-bit item and block dot.
+// The 4-bit gate+up GEMV with the SwiGLU epilogue, two waves per output:
+// the waves of a workgroup pair up (2g, 2g + 1) and each pair takes one
+// output p per tile, the even wave gate row p and the odd wave up row
+// n_ff + p, each walking all C chunks of its row as the plain W4 kernel
+// walks a row (so each half is reduced exactly as that kernel reduces the
+// row).  Every wave streams one row at a time, as in the plain kernel,
+// instead of one wave walking both rows of an output.  The halves wait in
+// LDS (up to kKeepTiles tiles per workgroup) and meet after the row loop,
+// so the stream has no workgroup barrier; with more tiles the pair meets
+// at the end of each tile.
 template <int WAVES, int ACT>
 __global__ void __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 q4_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* __restrict__ xin,
                     float* __restrict__ y) {
+    static_assert(WAVES % 2 == 0, "waves pair up");
     extern __shared__ __align__(16) uint8_t smem[];
     const int C = (int)chunk_count(k);
     const int NB = k / kBlock;
@@ -448,20 +456,22 @@ q4_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
     const int64_t row_bytes = q4_row_bytes(k);
     int4v* lds_q = reinterpret_cast<int4v*>(smem);
     float* lds_dx = reinterpret_cast<float*>(smem + (size_t)C * 2 * kWave * 16);
+    float* lds_part = reinterpret_cast<float*>(smem + lds_q8act_bytes(C));
     float* lds_res = reinterpret_cast<float*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>());
     int* lds_sx8 = reinterpret_cast<int*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>() +
                                           lds_keep_bytes<WAVES>());
     const int lane = threadIdx.x % kWave;
-    const Sched sc(2 * C, 1, 1, WAVES, n_ff, (n_ff + WAVES - 1) / WAVES);
+    const int wave = threadIdx.x / kWave;
+    // a schedule of 2C chunks in two parts has C items per wave and part =
+    // wave % 2; item m of either part is chunk m of that part's row
+    const Sched sc(2 * C, 2, 1, WAVES, n_ff, (n_ff + WAVES / 2 - 1) / (WAVES / 2));
+    const bool up = sc.part == 1;
     const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
-    // item m of output p: chunk m of gate row p (m < C) or chunk m - C of up
-    // row n_ff + p; past the schedule the idle region
+    // chunk m of the wave's row of output p; past the schedule the idle region
     auto load = [&](Q4Regs& r, const ItemCursor& it) {
         const int p = it.j < sc.tiles_wg ? sc.row(it.j) : sc.n;
-        const int m = sc.chunk(it.m, 0);
-        const bool up = m >= C;
-        const int c = up ? m - C : m;
-        const bool real = p < sc.n && m < 2 * C;
+        const int c = it.m;
+        const bool real = p < sc.n && c < C;
         const bool last = c == C - 1;
         const int nbc = last ? nl : kChunkBlocks;
         const int sb = last ? sbl : 2 * kChunkBlocks;
@@ -471,19 +481,12 @@ q4_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
         r.sc = load_u16<true>(cp + 2 * l);
         r.a = load16<true>(cp + sb + 16 * l);
     };
-    float acc_up = 0.0f;
-    auto compute = [&](const Q4Regs& r, int, int m, float& acc_gate) {
-        const bool up = m >= C;
-        const int c = up ? m - C : m;
-        const int blk = c * kWave + lane;
+    auto compute = [&](const Q4Regs& r, int, int m, float& acc) {
+        const int blk = m * kWave + lane;
         if (blk < NB) {
-            const int s = q4_block_dot(r, c, lane, lds_q, lds_sx8);
+            const int s = q4_block_dot(r, m, lane, lds_q, lds_sx8);
             const float t = half_bits_to_float(r.sc) * lds_dx[blk];
-            if (up) {
-                acc_up = __builtin_fmaf(t, (float)s, acc_up);
-            } else {
-                acc_gate = __builtin_fmaf(t, (float)s, acc_gate);
-            }
+            acc = __builtin_fmaf(t, (float)s, acc);
         }
     };
     Q4Regs R[kRingQ4];
@@ -496,11 +499,33 @@ q4_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
     __syncthreads();
     q4_block_sums<WAVES * kWave>(lds_q, lds_sx8, C);
     __syncthreads();
-    ring_loop(sc, R, load, compute, [&](float gate, int, int p, bool valid) {
-        const float upv = wave_sum(acc_up);
-        acc_up = 0.0f;
-        // silu(g) u, as q8_i8_swiglu_kernel
-        if (valid && lane == 0) y[p] = gate / (1.0f + expf(-gate)) * upv;
+    if (sc.tiles_wg <= kKeepTiles) {
+        // each wave keeps its row results in LDS and the pairs meet once,
+        // after the row loop: no workgroup barrier inside the stream
+        ring_loop(sc, R, load, compute, [&](float acc, int j, int, bool) {
+            if (lane == 0) lds_res[j * WAVES + wave] = acc;
+        });
+        __syncthreads();
+        for (int i = (int)threadIdx.x; i < sc.tiles_wg * sc.groups; i += WAVES * kWave) {
+            const int j = i / sc.groups, grp = i % sc.groups;
+            const int p = ((int)blockIdx.x + j * sc.grid) * sc.groups + grp;
+            if (p < n_ff) {
+                const float gate = lds_res[j * WAVES + 2 * grp], upv = lds_res[j * WAVES + 2 * grp + 1];
+                // silu(g) u, as q8_i8_swiglu_kernel
+                y[p] = gate / (1.0f + expf(-gate)) * upv;
+            }
+        }
+        return;
+    }
+    ring_loop(sc, R, load, compute, [&](float acc, int, int p, bool valid) {
+        // every wave ends each tile once: the pair meets in LDS
+        if (lane == 0) lds_part[wave] = acc;
+        __syncthreads();
+        if (!up && valid && lane == 0) {
+            const float gate = lds_part[wave], upv = lds_part[wave + 1];
+            y[p] = gate / (1.0f + expf(-gate)) * upv;
+        }
+        __syncthreads();
     });
 }
 
@@ -1137,8 +1162,8 @@ int launch_q4_norm(const void* w, int n, int k, const NormArgs& na, float* y, hi
     });
 }
 
-// The 4-bit gate+up GEMV with the SwiGLU epilogue: the W4 waves, one wave
-// per output.
+// The 4-bit gate+up GEMV with the SwiGLU epilogue: the W4 waves, two per
+// output (WAVES / 2 outputs per tile).
 int launch_q4_swiglu(const void* w, int n_ff, int k, const void* x, int act_fmt, float* y, hipStream_t stream,
                      LaunchInfo* info, bool run = true) {
     const Cfg c = choose_cfg(kPathQ4, 2 * (int64_t)n_ff, k);
@@ -1149,11 +1174,11 @@ int launch_q4_swiglu(const void* w, int n_ff, int k, const void* x, int act_fmt,
         constexpr int Wv = decltype(W)::value;
         if (act_fmt == WSG_ACT_Q8_0) {
             auto kern = q4_i8_swiglu_kernel<Wv, kActQ8>;
-            return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds) + lds_sx8, n_ff, info, 1, run, stream, wp, n_ff,
+            return launch_kernel<Wv, 2>(kern, q8_lds_bytes<Wv>(lds) + lds_sx8, n_ff, info, 1, run, stream, wp, n_ff,
                                         k, x, y);
         }
         auto kern = q4_i8_swiglu_kernel<Wv, kActRequant>;
-        return launch_kernel<Wv, 1>(kern, q8_lds_bytes<Wv>(lds) + lds_sx8, n_ff, info, 1, run, stream, wp, n_ff, k,
+        return launch_kernel<Wv, 2>(kern, q8_lds_bytes<Wv>(lds) + lds_sx8, n_ff, info, 1, run, stream, wp, n_ff, k,
                                     x, y);
     });
 }
