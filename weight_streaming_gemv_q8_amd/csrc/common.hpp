@@ -167,6 +167,12 @@ __device__ inline uint16_t q8_quad_codes(const float (&v)[8], uint32_t& lo, uint
     return d16;
 }
 
+// The wave's index in its workgroup, as a wave-uniform (scalar) value: the
+// compiler cannot tell that threadIdx.x / 64 is the same in every lane, and
+// without this everything derived from it (rows, chunk addresses, loop
+// bounds) would be computed per lane in vector registers.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)); }
+
 // ------------------------------------------------------- wave reductions
 // Butterfly sums over the 64 lanes of a wave; every lane ends with the same
 // value and the order of additions does not depend on which row is reduced.

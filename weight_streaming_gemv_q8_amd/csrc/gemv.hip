@@ -79,7 +79,7 @@ __device__ __attribute__((always_inline)) inline void q8_i8_body(const uint8_t* 
     // split rows with one-chunk items: rotating parts, partials kept in LDS
     // (rot_loop, flush_parts) while the workgroup's tiles fit
     constexpr bool kRot = S > 1 && U == 1 && !DEBUG && !ARGMAX;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     const bool rot = kRot && sc.tiles_wg <= kKeepTiles;
     float* lds_res = reinterpret_cast<float*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>());
     RotSched rs;
@@ -206,9 +206,9 @@ q8_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
         const int l = lane < nbc ? lane : nbc - 1;
         const int64_t row = real ? (int64_t)p + (up ? n_ff : 0) : 0;
         const gptr<uint8_t> cp = real ? Wg + row * row_bytes + (int64_t)c * kFullChunkBytes : idle_bytes();
-        r.sc[0] = load_u16<true>(cp + 2 * l);
-        r.a[0] = load16<true>(cp + sb + 16 * l);
-        r.b[0] = load16<true>(cp + sb + 16 * nbc + 16 * l);
+        r.sc[0] = load_u16<true>(cp + 2u * (uint32_t)l);
+        r.a[0] = load16<true>(cp + ((uint32_t)sb + 16u * (uint32_t)l));
+        r.b[0] = load16<true>(cp + ((uint32_t)(sb + 16 * nbc) + 16u * (uint32_t)l));
     };
     float acc_up = 0.0f;
     // one block per lane, as q8_i8_item: exact int32 dot, then (d_w d_x) s
@@ -342,7 +342,7 @@ __device__ __attribute__((always_inline)) inline void q4_i8_body(const uint8_t* 
                                           lds_keep_bytes<WAVES>());
     float* lds_part = reinterpret_cast<float*>(smem + lds_q8act_bytes(C));
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     const Sched sc(C, S, 1, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
     const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
     // chunk c of a row (row n or chunk C: the idle region)
@@ -353,8 +353,8 @@ __device__ __attribute__((always_inline)) inline void q4_i8_body(const uint8_t* 
         const int sb = last ? sbl : 2 * kChunkBlocks;
         const int l = lane < nbc ? lane : nbc - 1;
         const gptr<uint8_t> cp = real ? Wg + (int64_t)row * row_bytes + (int64_t)c * kFullChunkBytesQ4 : idle_bytes();
-        r.sc = load_u16<true>(cp + 2 * l);
-        r.a = load16<true>(cp + sb + 16 * l);
+        r.sc = load_u16<true>(cp + 2u * (uint32_t)l);
+        r.a = load16<true>(cp + ((uint32_t)sb + 16u * (uint32_t)l));
     };
     auto compute_c = [&](const Q4Regs& r, int c, float& acc) {
         const int blk = c * kWave + lane;
@@ -461,7 +461,7 @@ q4_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
     int* lds_sx8 = reinterpret_cast<int*>(smem + lds_q8act_bytes(C) + lds_tail_bytes<WAVES>() +
                                           lds_keep_bytes<WAVES>());
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     // a schedule of 2C chunks in two parts has C items per wave and part =
     // wave % 2; item m of either part is chunk m of that part's row
     const Sched sc(2 * C, 2, 1, WAVES, n_ff, (n_ff + WAVES / 2 - 1) / (WAVES / 2));
@@ -478,8 +478,8 @@ q4_i8_swiglu_kernel(const uint8_t* __restrict__ W, int n_ff, int k, const void* 
         const int l = lane < nbc ? lane : nbc - 1;
         const int64_t row = real ? (int64_t)p + (up ? n_ff : 0) : 0;
         const gptr<uint8_t> cp = real ? Wg + row * row_bytes + (int64_t)c * kFullChunkBytesQ4 : idle_bytes();
-        r.sc = load_u16<true>(cp + 2 * l);
-        r.a = load16<true>(cp + sb + 16 * l);
+        r.sc = load_u16<true>(cp + 2u * (uint32_t)l);
+        r.a = load16<true>(cp + ((uint32_t)sb + 16u * (uint32_t)l));
     };
     auto compute = [&](const Q4Regs& r, int, int m, float& acc) {
         const int blk = m * kWave + lane;
@@ -555,7 +555,7 @@ q4_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restri
     float* lds_part = reinterpret_cast<float*>(smem + lds_f32act_bytes(C));
     float* lds_res = reinterpret_cast<float*>(smem + lds_f32act_bytes(C) + lds_tail_bytes<WAVES>());
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     const Sched sc(C, S, 1, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
     const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
     // chunk c of a row (row n or chunk C: the idle region)
@@ -566,8 +566,8 @@ q4_f32_kernel(const uint8_t* __restrict__ W, int n, int k, const float* __restri
         const int sb = last ? sbl : 2 * kChunkBlocks;
         const int l = lane < nbc ? lane : nbc - 1;
         const gptr<uint8_t> cp = real ? Wg + (int64_t)row * row_bytes + (int64_t)c * kFullChunkBytesQ4 : idle_bytes();
-        r.sc = load_u16<true>(cp + 2 * l);
-        r.a = load16<true>(cp + sb + 16 * l);
+        r.sc = load_u16<true>(cp + 2u * (uint32_t)l);
+        r.a = load16<true>(cp + ((uint32_t)sb + 16u * (uint32_t)l));
     };
     // word q of a block's 16 bytes: low nibbles are codes 4q..4q+3 (group q
     // of the staged activation), high nibbles codes 16+4q.. (group 4 + q)
@@ -670,7 +670,7 @@ __device__ __attribute__((always_inline)) inline void q8_f32_body(const uint8_t*
     auto compute = [&](const Q8Regs<U>& r, int, int m, float& acc) { q8_f32_item<U>(r, sc, m, NB, lds_x, acc); };
 
     constexpr bool kRot = S > 1 && U == 1 && !ARGMAX;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     const bool rot = kRot && sc.tiles_wg <= kKeepTiles;
     float* lds_res = reinterpret_cast<float*>(smem + lds_f32act_bytes(C) + lds_tail_bytes<WAVES>());
     RotSched rs;
@@ -780,7 +780,7 @@ bf16_kernel(const uint16_t* __restrict__ W, int n, int k, const float* __restric
     st.commit(x, k, lds_x);
     __syncthreads();
     uint64_t best = 0;
-    const int wave = threadIdx.x / kWave;
+    const int wave = wave_id();
     ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool) {
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
     });
@@ -804,7 +804,7 @@ __global__ void __launch_bounds__(kArgmax1Threads) argmax_stage1_kernel(const fl
         best = key > best ? key : best;
     }
     best = wave_max_u64(best);
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave, wave = wave_id();
     if (lane == 0) lds_key[wave] = best;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -820,7 +820,7 @@ __global__ void __launch_bounds__(kArgmax2Threads) argmax_stage2_kernel(const ui
     uint64_t best = 0;
     for (int i = threadIdx.x; i < count; i += kArgmax2Threads) best = keys[i] > best ? keys[i] : best;
     best = wave_max_u64(best);
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave, wave = wave_id();
     if (lane == 0) lds_key[wave] = best;
     __syncthreads();
     if (threadIdx.x == 0) {

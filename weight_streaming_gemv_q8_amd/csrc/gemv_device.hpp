@@ -45,7 +45,7 @@ struct Sched {
         C = C_;
         S = S_;
         U = U_;
-        const int wave = threadIdx.x / kWave;
+        const int wave = wave_id();
         part = wave % S;
         group = wave / S;
         groups = waves / S;
@@ -230,11 +230,13 @@ __device__ inline void q8_load_item(Q8Regs<U>& r, gptr<uint8_t> W, int64_t row_b
         const bool last = (c == sc.C - 1);
         const int nbc = last ? nl : kChunkBlocks;
         const int sb = last ? sbl : 2 * kChunkBlocks;
-        const int l = lane < nbc ? lane : nbc - 1;
+        // a wave-uniform item base plus a 32-bit per-lane offset: a scalar
+        // base register and a vector offset in each load
+        const uint32_t l = (uint32_t)(lane < nbc ? lane : nbc - 1);
         const gptr<uint8_t> cp = real ? rowp + (int64_t)c * kFullChunkBytes : idle_bytes();
-        r.sc[u] = load_u16<true>(cp + 2 * l);
-        r.a[u] = load16<true>(cp + sb + 16 * l);
-        r.b[u] = load16<true>(cp + sb + 16 * nbc + 16 * l);
+        r.sc[u] = load_u16<true>(cp + 2u * l);
+        r.a[u] = load16<true>(cp + ((uint32_t)sb + 16u * l));
+        r.b[u] = load16<true>(cp + ((uint32_t)(sb + 16 * nbc) + 16u * l));
     }
 }
 
@@ -318,9 +320,9 @@ __device__ inline void q8_load_rot(Q8Regs<1>& R, gptr<uint8_t> W, int64_t row_by
     const int sb = last ? sbl : 2 * kChunkBlocks;
     const int l = lane < nbc ? lane : nbc - 1;
     const gptr<uint8_t> cp = real ? W + (int64_t)row * row_bytes + (int64_t)c * kFullChunkBytes : idle_bytes();
-    R.sc[0] = load_u16<true>(cp + 2 * l);
-    R.a[0] = load16<true>(cp + sb + 16 * l);
-    R.b[0] = load16<true>(cp + sb + 16 * nbc + 16 * l);
+    R.sc[0] = load_u16<true>(cp + 2u * (uint32_t)l);
+    R.a[0] = load16<true>(cp + ((uint32_t)sb + 16u * (uint32_t)l));
+    R.b[0] = load16<true>(cp + ((uint32_t)(sb + 16 * nbc) + 16u * (uint32_t)l));
 }
 
 // The ring over a wave's items, as ring_loop (every step issues one item's
@@ -797,8 +799,7 @@ __device__ inline void bf16_load_item(Bf16Regs<U>& r, gptr<uint16_t> W, int k, c
     const int lane = threadIdx.x % kWave;
     const int row = it.j < sc.tiles_wg ? sc.row(it.j) : sc.n;
     const bool has_row = row < sc.n;
-    const gptr<uint16_t> rowp = W + (int64_t)(has_row ? row : 0) * k;
-    const gptr<uint16_t> idle = (gptr<uint16_t>)idle_bytes() + 8 * lane;
+    const gptr<uint8_t> rowp = (gptr<uint8_t>)(W + (int64_t)(has_row ? row : 0) * k);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int c = sc.chunk(it.m, u);
@@ -806,8 +807,11 @@ __device__ inline void bf16_load_item(Bf16Regs<U>& r, gptr<uint16_t> W, int k, c
         const int e0 = c * 1024 + 8 * lane;
         const int ea = e0 < k ? e0 : k - 8;
         const int eb = e0 + 512 < k ? e0 + 512 : k - 8;
-        r.a[u] = load16<true>(real ? rowp + ea : idle);
-        r.b[u] = load16<true>(real ? rowp + eb : idle);
+        // a wave-uniform base (the row or the idle region) plus a 32-bit
+        // per-lane byte offset: a scalar base register in each load
+        const gptr<uint8_t> base = real ? rowp : idle_bytes();
+        r.a[u] = load16<true>(base + (real ? 2u * (uint32_t)ea : 16u * (uint32_t)lane));
+        r.b[u] = load16<true>(base + (real ? 2u * (uint32_t)eb : 16u * (uint32_t)lane));
     }
 }
 

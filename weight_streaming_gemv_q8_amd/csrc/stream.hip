@@ -351,7 +351,7 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
     StreamOp op = ops[0];
     OpGeom g = op_geom<WAVES>(op, parity);
     Sched sc = op_sched<WAVES, U>(g, grid);
-    const int wp = (int)(threadIdx.x / kWave);  // slot in the group: wave % S (S divides 16)
+    const int wp = wave_id();  // slot in the group: wave % S (S divides 16)
     RotSched rs;
     rs.set(sc, wp);
     rot_prologue(rs, R, OpRotLoad{&g});
