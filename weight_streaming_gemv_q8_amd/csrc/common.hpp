@@ -17,6 +17,21 @@ constexpr int kFullChunkBytes = 2 * kChunkBlocks + kChunkWeights;  // 128 scale 
 typedef int int4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
+// ------------------------------------------------------------- DPP moves
+// Cross-lane moves within rows of 16 lanes (data-parallel primitives of the
+// vector ALU): quad_perm [1,0,3,2] (lane ^ 1) and [2,3,0,1] (lane ^ 2),
+// row_half_mirror (lane 7 - i within 8), row_mirror (lane 15 - i within 16)
+// and row_bcast:15 (lane 15 of each row into the next row, for the rows the
+// row mask enables; the others keep `old`).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140,
+              kDppRowBcast15 = 0x142;
+template <int CTRL, int ROWS = 0xF>
+__device__ inline float dpp_f32(float v, float old = 0.0f) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                   __builtin_bit_cast(int, v), CTRL, ROWS, 0xF,
+                                                                   false));
+}
+
 // ------------------------------------------------------------- Q8_0 layout
 // Bytes of a chunk's scale section: 2 bytes per block, padded to 16.
 __host__ __device__ inline int64_t scale_section_bytes(int64_t nb) { return (2 * nb + 15) & ~int64_t(15); }
@@ -139,8 +154,8 @@ __device__ inline uint16_t q8_quad_codes(const float (&v)[8], uint32_t& lo, uint
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, kWave));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    amax = __builtin_fmaxf(amax, dpp_f32<kDppXor1>(amax));
+    amax = __builtin_fmaxf(amax, dpp_f32<kDppXor2>(amax));
     const uint16_t d16 = q8_scale_bits(amax);
     const float d = half_bits_to_float(d16);
     lo = 0;
@@ -174,12 +189,22 @@ __device__ inline uint16_t q8_quad_codes(const float (&v)[8], uint32_t& lo, uint
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)); }
 
 // ------------------------------------------------------- wave reductions
-// Butterfly sums over the 64 lanes of a wave; every lane ends with the same
-// value and the order of additions does not depend on which row is reduced.
+// A sum over the 64 lanes of a wave as a fixed binary tree: lanes pair up
+// with lane ^ 1, then quads with their neighbour quad (every lane of a quad
+// holds the same value by then), then 8-lane groups, all as DPP moves within
+// rows of 16 lanes (no LDS round trip); lane 15 of rows 0 and 2 is added
+// into rows 1 and 3, and the result is row sums (0 + 1) + (2 + 3), read from
+// lanes 31 and 63 into a wave-uniform value.  The order of additions does
+// not depend on the data or on which row is reduced.
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    v += dpp_f32<kDppMirror>(v);
+    v += dpp_f32<kDppRowBcast15, 0xA>(v);
+    const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+    const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    return lo + hi;
 }
 
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
