@@ -74,10 +74,13 @@ def lib():
     """The loaded C library; raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+        # WSG_LIBRARY names another build of the same library (the diagnostic
+        # timeline build, see timeline.py)
+        path = os.environ.get("WSG_LIBRARY") or LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
                                "(there is no fallback path)")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         sig = {
             "wsg_status_str": (ctypes.c_char_p, [i32]),

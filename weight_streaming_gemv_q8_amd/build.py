@@ -17,6 +17,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libwsgemv.so")
 OBJ_DIR = os.path.join(PKG, "_build")
+# the diagnostic build: the same library with per-workgroup timestamps in the
+# int8 GEMV (csrc/timeline.hpp, read by timeline.py)
+TIMELINE_LIB = os.path.join(PKG, "libwsgemv_timeline.so")
+TIMELINE_OBJ_DIR = os.path.join(PKG, "_build_timeline")
 
 SOURCES = ["api.cpp", "quant.hip", "norm.hip", "gemv.hip", "stream.hip", "decode.hip", "probe.hip", "plan.cpp"]
 
@@ -28,10 +32,11 @@ HIP_FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, verbose: bool, timeline: bool = False) -> str:
+    obj = os.path.join(TIMELINE_OBJ_DIR if timeline else OBJ_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = ["hipcc", *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = ["-DWSG_TIMELINE"] if timeline else []
+    cmd = ["hipcc", *HIP_FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,17 +46,20 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    """Builds libwsgemv.so (or, with timeline=True, the diagnostic
+    libwsgemv_timeline.so) and returns its path."""
+    lib = TIMELINE_LIB if timeline else LIB
+    os.makedirs(TIMELINE_OBJ_DIR if timeline else OBJ_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+        objs = list(ex.map(lambda s: _compile(s, verbose, timeline), SOURCES))
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, timeline="--timeline" in sys.argv)

@@ -25,6 +25,7 @@
 #include "common.hpp"
 #include "gemv_device.hpp"
 #include "internal.hpp"
+#include "timeline.hpp"
 
 #include <atomic>
 #include <cstdlib>
@@ -69,6 +70,7 @@ __device__ __attribute__((always_inline)) inline void q8_i8_body(const uint8_t* 
     uint64_t* lds_key = reinterpret_cast<uint64_t*>(smem + ((lds_q8act_bytes(C) + WAVES * 4 + 15) & ~size_t(15)));
     const int lane = threadIdx.x % kWave;
 
+    WSG_TL_BEGIN();
     const Sched sc(C, S, U, WAVES, n, (n + WAVES / S - 1) / (WAVES / S));
     const gptr<uint8_t> Wg = (gptr<uint8_t>)W;
     auto load = [&](Q8Regs<U>& r, const ItemCursor& it) { q8_load_item<U>(r, Wg, row_bytes, sc, nl, sbl, it); };
@@ -104,6 +106,7 @@ __device__ __attribute__((always_inline)) inline void q8_i8_body(const uint8_t* 
     __builtin_amdgcn_sched_barrier(0);
     stage.commit(lds_q, lds_dx, lds_res);
     __syncthreads();
+    WSG_TL_STAGED();
     if constexpr (kRot) {
         if (rot) {
             if (threadIdx.x % kWave < (unsigned)sc.tiles_wg) {
@@ -117,8 +120,10 @@ __device__ __attribute__((always_inline)) inline void q8_i8_body(const uint8_t* 
                      [&](float acc, int t, int slot) {
                          if (lane == 0) lds_res[t * WAVES + slot] = acc;
                      });
+            WSG_TL_LOOP_END();
             __syncthreads();
             flush_parts<WAVES>(sc, lds_res, y);
+            WSG_TL_END(y);
             return;
         }
     }
@@ -126,7 +131,9 @@ __device__ __attribute__((always_inline)) inline void q8_i8_body(const uint8_t* 
     ring_loop(sc, R, load, compute, [&](float acc, int, int row, bool) {
         finish_row<WAVES, S, ARGMAX>(acc, row, n, lane, wave, lds_part, y, best);
     });
+    WSG_TL_LOOP_END();
     if constexpr (ARGMAX) write_block_key<WAVES>(best, lane, wave, lds_key, keys);
+    WSG_TL_END(y);
 }
 
 // Staging of the int8 path's input: a quantize_act_q8_0 output, or f32
@@ -1664,3 +1671,20 @@ int argmax_f32(const float* v, int64_t n, void* ws, size_t ws_bytes, int32_t* id
 }
 
 }  // extern "C"
+
+#ifdef WSG_TIMELINE
+namespace wsg {
+__device__ uint64_t* g_timeline;
+__device__ uint32_t g_timeline_mod;
+}  // namespace wsg
+
+// Diagnostic build only: where the int8 GEMV's workgroups record their
+// timestamps (timeline.hpp); buf = nullptr stops recording.
+extern "C" __attribute__((visibility("default"))) int wsg_timeline_set(void* buf, uint32_t modulus) {
+    uint64_t* b = static_cast<uint64_t*>(buf);
+    if (hipMemcpyToSymbol(HIP_SYMBOL(wsg::g_timeline), &b, sizeof(b)) != hipSuccess) return WSG_ERR_HIP;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(wsg::g_timeline_mod), &modulus, sizeof(modulus)) != hipSuccess)
+        return WSG_ERR_HIP;
+    return WSG_OK;
+}
+#endif
