@@ -1673,18 +1673,10 @@ int argmax_f32(const float* v, int64_t n, void* ws, size_t ws_bytes, int32_t* id
 }  // extern "C"
 
 #ifdef WSG_TIMELINE
-namespace wsg {
-__device__ uint64_t* g_timeline;
-__device__ uint32_t g_timeline_mod;
-}  // namespace wsg
-
-// Diagnostic build only: where the int8 GEMV's workgroups record their
+// Diagnostic build only: where the GEMV kernels' workgroups record their
 // timestamps (timeline.hpp); buf = nullptr stops recording.
 extern "C" __attribute__((visibility("default"))) int wsg_timeline_set(void* buf, uint32_t modulus) {
-    uint64_t* b = static_cast<uint64_t*>(buf);
-    if (hipMemcpyToSymbol(HIP_SYMBOL(wsg::g_timeline), &b, sizeof(b)) != hipSuccess) return WSG_ERR_HIP;
-    if (hipMemcpyToSymbol(HIP_SYMBOL(wsg::g_timeline_mod), &modulus, sizeof(modulus)) != hipSuccess)
-        return WSG_ERR_HIP;
+    if (wsg::tl_set_here(buf, modulus) != 0 || wsg::stream_timeline_set(buf, modulus) != 0) return WSG_ERR_HIP;
     return WSG_OK;
 }
 #endif

@@ -34,6 +34,7 @@
 #include "gemv_device.hpp"
 #include "internal.hpp"
 #include "stream.hpp"
+#include "timeline.hpp"
 
 namespace wsg {
 namespace {
@@ -354,6 +355,7 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
     const int wp = wave_id();  // slot in the group: wave % S (S divides 16)
     RotSched rs;
     rs.set(sc, wp);
+    WSG_TL_OP(0, 2);
     rot_prologue(rs, R, OpRotLoad{&g});
     for (int j = 0;;) {
         if (op.dep) wait_range((gcfloat)(op.dep + parity * op.dep_stride), op.dep_n, st, spin_limit);
@@ -363,6 +365,7 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
         // row loop starts from a known count and its waits stay exact
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
+        WSG_TL_OP(j, 3);
 
         const size_t act_bytes = F32 ? lds_f32act_bytes(g.C) : lds_q8act_bytes(g.C);
         float* lds_res = reinterpret_cast<float*>(smem + act_bytes);
@@ -383,13 +386,16 @@ stream_kernel(const StreamOp* __restrict__ ops, int n_ops, uint32_t* __restrict_
         }
         rot_loop(rs, R, OpRotLoad{&g}, compute, [&](float acc, int t, int slot) { keep_part(acc, t, slot, lds_res); });
         __syncthreads();  // every tile's partial sums are in LDS; the activation is dead
+        WSG_TL_OP(j, 4);
         flush_tiles(sc.tiles_wg, grid, g.n, g.S, lds_res, g.y, g.ynow, g.ynext);
+        WSG_TL_OP(j, 5);
         if (++j == n_ops) break;
 
         op = ops[j];
         g = op_geom<WAVES>(op, parity);
         sc = op_sched<WAVES, U>(g, grid);
         rs.set(sc, wp);
+        WSG_TL_OP(j, 2);
         rot_prologue(rs, R, OpRotLoad{&g});
     }
 }
@@ -440,5 +446,9 @@ void stream_shape(int* waves, int* unroll, int* sets) {
 }
 
 int64_t stream_max_rows(int split, int grid) { return (int64_t)kMaxTiles * grid * (kStreamWaves / split); }
+
+#ifdef WSG_TIMELINE
+int stream_timeline_set(void* buf, uint32_t modulus) { return tl_set_here(buf, modulus); }
+#endif
 
 }  // namespace wsg

@@ -1,4 +1,5 @@
-// Per-workgroup timestamps of the int8 GEMV kernel, for the diagnostic
+// Per-workgroup timestamps of the int8 GEMV kernel and of the persistent
+// token kernel (per op: see tl_op), for the diagnostic
 // build only (build.py --timeline defines WSG_TIMELINE and writes
 // libwsgemv_timeline.so; the library proper compiles every macro here to
 // nothing).  Each workgroup of each launch records, from the GPU's
@@ -21,8 +22,18 @@ namespace wsg {
 constexpr int kTimelineFields = 10;
 constexpr unsigned kTimelineWorkgroups = 512;
 
-extern __device__ uint64_t* g_timeline;
-extern __device__ uint32_t g_timeline_mod;
+// Each source file that records has its own copy (the library is built
+// without relocatable device code); wsg_timeline_set sets all of them.
+static __device__ uint64_t* g_timeline;
+static __device__ uint32_t g_timeline_mod;
+
+static inline int tl_set_here(void* buf, uint32_t modulus) {
+    uint64_t* b = static_cast<uint64_t*>(buf);
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_timeline), &b, sizeof(b)) != hipSuccess) return -1;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_timeline_mod), &modulus, sizeof(modulus)) != hipSuccess) return -1;
+    return 0;
+}
+int stream_timeline_set(void* buf, uint32_t modulus);  // stream.hip's copy
 
 __device__ inline uint64_t tl_now() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -65,8 +76,28 @@ __device__ inline void tl_end(uint64_t t_entry, uint64_t t_staged, const void* y
     r[9] = last_entry;
 }
 
+// The persistent token kernel records one slot per op and workgroup: slot
+// op * 512 + b (the caller sizes the buffer for every op; the modulus is not
+// used).  Fields: 0 the op index, 1 blk | grid << 32, 2 when the op's first
+// weight requests were issued (the previous op's results stored, or the
+// kernel's entry), 3 the op's input staged, 4 the row loop ended (every
+// wave: after the barrier), 5 the op's results stored (thread 0's share),
+// 7 HW_ID, 8 XCC_ID.
+__device__ inline void tl_op(int op, int field, uint64_t t) {
+    if (threadIdx.x != 0 || g_timeline == nullptr || blockIdx.x >= kTimelineWorkgroups) return;
+    uint64_t* r = g_timeline + ((uint64_t)op * kTimelineWorkgroups + blockIdx.x) * kTimelineFields;
+    if (field == 2) {
+        r[0] = (uint64_t)op;
+        r[1] = blockIdx.x | ((uint64_t)gridDim.x << 32);
+        r[7] = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+        r[8] = __builtin_amdgcn_s_getreg((31 << 11) | 20);
+    }
+    r[field] = t;
+}
+
 }  // namespace wsg
 
+#define WSG_TL_OP(op, field) wsg::tl_op((op), (field), wsg::tl_now())
 #define WSG_TL_BEGIN()                          \
     const uint64_t tl_t_entry = wsg::tl_now(); \
     wsg::tl_wave(0, tl_t_entry)
@@ -76,6 +107,7 @@ __device__ inline void tl_end(uint64_t t_entry, uint64_t t_staged, const void* y
 
 #else
 
+#define WSG_TL_OP(op, field) (void)0
 #define WSG_TL_BEGIN() (void)0
 #define WSG_TL_STAGED() (void)0
 #define WSG_TL_LOOP_END() (void)0
