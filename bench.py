@@ -384,14 +384,19 @@ def measure_configs(steps: int, warmup: int) -> list:
                 ts.close()
                 del ts
                 torch.cuda.empty_cache()
-    # the 27B stream with 4-bit weights
-    ts = build_stream(W.DENSE27B_Q8, 0, "fused", wtype="q4_0")
-    sec, kernels = time_plan(ts, False, steps, warmup)
-    rec(W.DENSE27B_Q8, "graph, W4 weights (q4_0) deq0", sec, ts.algorithmic_weight_bytes(),
-        kernels_per_token=kernels, deq=0)
-    ts.close()
-    del ts
-    torch.cuda.empty_cache()
+    # the 27B stream with 4-bit weights: int8 activations (deq 0) and f32
+    # ones (deq 2, W4A16); at deq 0 also with the norm prologue and the
+    # SwiGLU epilogue
+    for deq, extra, kw in ((0, "", {}), (2, " (W4A16)", {}),
+                           (0, " + residual/RMSNorm fused into the GEMVs", {"norm": True, "fused_norm": True}),
+                           (0, " + SwiGLU epilogue on gate+up", {"swiglu": True})):
+        ts = build_stream(W.DENSE27B_Q8, deq, "fused", wtype="q4_0", **kw)
+        sec, kernels = time_plan(ts, False, steps, warmup)
+        rec(W.DENSE27B_Q8, f"graph, W4 weights (q4_0){extra} deq{deq}", sec, ts.algorithmic_weight_bytes(),
+            kernels_per_token=kernels, deq=deq)
+        ts.close()
+        del ts
+        torch.cuda.empty_cache()
     # a whole decode step: embedding -> layers -> LM head + argmax -> advance
     for wl, wt, deq in ((W.QWEN3_8B_Q8, "q8_0", 0), (W.DENSE27B_Q8, "q8_0", 0), (W.DENSE27B_Q8, "q8_0", 2),
                         (W.DENSE27B_Q8, "q4_0", 0)):

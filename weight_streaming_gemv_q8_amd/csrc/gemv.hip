@@ -965,7 +965,7 @@ struct LaunchInfo {
     size_t lds = 0;
 };
 
-enum Path { kPathI8 = 0, kPathF32 = 1, kPathBf16 = 2, kPathQ4 = 3 };
+enum Path { kPathI8 = 0, kPathF32 = 1, kPathBf16 = 2, kPathQ4 = 3, kPathQ4F32 = 4 };
 
 // Default configuration per path and shape; tuning knobs override it.
 struct Cfg {
@@ -1021,6 +1021,14 @@ Cfg choose_cfg(Path path, int64_t n, int64_t k) {
         // share of a 4-bit row)
         c.waves = 16;
         c.split = 1;
+    } else if (path == kPathQ4F32) {
+        // measured on the same shapes with f32 activations (W4A16), where
+        // the dequantizing arithmetic weighs more than the staging: 8-wave
+        // workgroups, whole rows except long rows few per CU (down: split
+        // 4); within 1% of the best of 4/8/16 waves x split 1/2/4 on all
+        // four, up to 11% faster than 16 waves with whole rows
+        c.waves = 8;
+        c.split = (rows_per_cu < 32 && k >= 16384) ? 4 : 1;
     } else if (path == kPathBf16) {
         c.split = 1;
         if (rows_per_cu < 32 && k >= 16384) c.split = 4;
@@ -1028,6 +1036,10 @@ Cfg choose_cfg(Path path, int64_t n, int64_t k) {
         else if (rows_per_cu < 8 && k >= 2048) c.split = 2;
     } else {
         c.split = balanced_split(n, k);
+        // f32 activations (deq 2): 16-wave workgroups on every shape; on the
+        // tall 27B matrices they beat two 8-wave ones (qkvz 16.6 against
+        // 18.3 us, gate+up 32.5 against 33.4), the LM head runs the same
+        if (path == kPathF32) c.waves = 16;
     }
     const int tw = tune_waves(), ts = tune_splitk(), tu = tune_unroll();
     if (tw == 4 || tw == 8 || tw == 16) c.waves = tw;
@@ -1193,7 +1205,7 @@ int launch_q4_swiglu(const void* w, int n_ff, int k, const void* x, int act_fmt,
 // The W4 GEMV: its own waves and split choice (choose_cfg).
 int launch_q4(const void* w, int n, int k, const void* x, int act_fmt, float* y, hipStream_t stream, LaunchInfo* info,
               bool run = true) {
-    const Cfg c = choose_cfg(kPathQ4, n, k);
+    const Cfg c = choose_cfg(act_fmt == WSG_ACT_F32 ? kPathQ4F32 : kPathQ4, n, k);
     const size_t lds_act = lds_q8act_bytes((int)chunk_count(k));
     const size_t lds_sx8 = chunk_count(k) * kWave * 4;  // 8 sum x per block
     const uint8_t* wp = static_cast<const uint8_t*>(w);
