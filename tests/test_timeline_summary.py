@@ -11,9 +11,10 @@ NM, LAYERS = 4, 3  # matrices per layer, layers: GEMVs 4..7 are summarized
 
 
 def _graph_records(grid):
-    """GEMV j starts at 2000 j; workgroup b enters at +b, stages 300 ticks
-    later, its waves end 1000 and 1000 + 20 b ticks after entry (b < 8 ends
-    100 ticks before b >= 8), and it exits 10 ticks after its last wave."""
+    """GEMV j starts at 2000 j; workgroup b enters at +b and stages 300
+    ticks later; its first wave ends 1000 ticks after entry and its last
+    one at the same time (b < 8) or 100 ticks later (b >= 8); it exits 10
+    ticks after its last wave."""
     by = {}
     for j in range(NM * LAYERS):
         e = np.zeros((grid, tl.NF), dtype=np.int64)
