@@ -240,12 +240,66 @@ def _time_calls(fn, reps: int, warmup: int = 3) -> float:
     return e0.elapsed_time(e1) / 1e3 / reps
 
 
-def measure_configs(steps: int, warmup: int) -> list:
+def _stream_configs(W):
+    return ((W.QWEN3_0P6B_BF16, (0,)), (W.QWEN3_8B_Q8, (0,)), (W.DENSE27B_Q8, (0, 2)))
+
+
+# the 27B stream with 4-bit weights: int8 activations (deq 0) and f32 ones
+# (deq 2, W4A16); at deq 0 also with the norm prologue and the SwiGLU epilogue
+_W4_CONFIGS = ((0, "", {}), (2, " (W4A16)", {}),
+               (0, " + residual/RMSNorm fused into the GEMVs", {"norm": True, "fused_norm": True}),
+               (0, " + SwiGLU epilogue on gate+up", {"swiglu": True}))
+
+
+def _decode_configs(W):
+    return ((W.QWEN3_8B_Q8, "q8_0", 0), (W.DENSE27B_Q8, "q8_0", 0), (W.DENSE27B_Q8, "q8_0", 2),
+            (W.DENSE27B_Q8, "q4_0", 0))
+
+
+def config_part_names() -> list:
+    """The parts of the configs run, in order (no GPU needed): the small
+    workloads together, then each token stream, 4-bit stream and decode
+    step on its own."""
+    from synth import workloads as W
+    names = ["small"]
+    for wl, deqs in _stream_configs(W):
+        for deq in deqs:
+            variants = ("plain", "norm") + (("fused_norm", "swiglu") if wl.wtype == "q8_0" else ())
+            names += [f"stream:{wl.name}:deq{deq}:{v}" for v in variants]
+    names += [f"w4:{i}" for i in range(len(_W4_CONFIGS))]
+    names += [f"decode:{i}" for i in range(len(_decode_configs(W)))]
+    return names
+
+
+def run_configs_in_children(steps: int, warmup: int) -> int:
+    """The configs run with each part in a child process of its own, one
+    after another.  A token stream's speed depends on the state its weights
+    are allocated in: the first 26.7 GB allocation of a process streams ~3.5%
+    faster than one made after another stream was freed (27B stream: 4783
+    against 4974 us per token in one process).  A fresh process per part
+    measures each the way a server allocates its weights once, at start-up.
+    This process never touches the GPU."""
+    import subprocess
+    for name in config_part_names():
+        cmd = [sys.executable, os.path.abspath(__file__), "--configs", "--configs-part", name,
+               "--steps", str(steps), "--warmup", str(warmup)]
+        p = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+        for line in p.stdout.splitlines():
+            if line.startswith("{"):
+                print(line, flush=True)
+        if p.returncode != 0:
+            print(f"configs part {name} failed with status {p.returncode}", file=sys.stderr)
+            return p.returncode
+    return 0
+
+
+def measure_configs(steps: int, warmup: int, part: str = None) -> list:
     """Every workload in the way the pages run it: the single GEMV as eager
     calls (hot: one weight copy; cold: rotating over 1024 copies, more than
     L2 + MALL), the LM head as fused GEMV + argmax calls, the token streams
     as graph and persistent replays.  One record per configuration and
-    mode."""
+    mode.  part: one of config_part_names() (None: all of them, in this
+    process)."""
     import numpy as np
     import torch
 
@@ -254,6 +308,7 @@ def measure_configs(steps: int, warmup: int) -> list:
     from synth import workloads as W
 
     out = []
+    want = lambda name: part is None or part == name
 
     def rec(wl, mode, sec, alg_bytes, **extra):
         gbps_ = gbps(alg_bytes, sec)
@@ -262,134 +317,143 @@ def measure_configs(steps: int, warmup: int) -> list:
         log(f"{wl.name:22s} {mode:34s} {sec * 1e6:10.2f} us {gbps_:8.1f} GB/s {100 * gbps_ / HBM_PEAK_GBPS:5.1f}%")
         out.append(r)
 
-    s = torch.cuda.current_stream().cuda_stream
-    # configs 0: one 1024x1024 Q8_0 GEMV
-    wl = W.Q8_SINGLE
-    n, k = wl.matrices[0].n, wl.matrices[0].k
-    alg = n * (k // 32) * 34
-    staging = torch.empty(n * k, dtype=torch.float32, device="cuda")
-    copies = 1024
-    wq = torch.empty((copies, wsg.q8_0_packed_bytes(n, k)), dtype=torch.uint8, device="cuda")
-    for c in range(copies):
-        synth.dev_normal_f32(staging.data_ptr(), wl.seed, 1 + c, n * k, W.WEIGHT_SIGMA, stream=s)
-        wsg.quantize_q8_0_weights(staging, n, k, wq[c])
-    x = torch.from_numpy(synth.activation(wl.seed, W.activation_tensor_id(0), k)).cuda()
-    y = torch.empty(n, dtype=torch.float32, device="cuda")
-    for deq, act in ((0, wsg.ACT_F32_REQUANT), (2, wsg.ACT_F32)):
-        for temp, pick in (("hot", lambda i: 0), ("cold", lambda i: i % copies)):
-            sec = _time_calls(lambda i: wsg.gemv_q8_0(wq[pick(i)], n, k, x, act, y), max(steps, 1) * 40)
-            rec(wl, f"eager deq{deq} {temp}", sec, alg, deq=deq)
-            # the same calls replayed from a graph of 256: the kernel without
-            # the host's launch cost
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(256):
-                    wsg.gemv_q8_0(wq[pick(i)], n, k, x, act, y)
-            sec = _time_calls(lambda i: g.replay(), max(steps, 1) // 5 + 1) / 256
-            rec(wl, f"graph of 256 calls deq{deq} {temp}", sec, alg, deq=deq)
-            del g
-    del wq, staging
-    # configs 3: the LM head, fused GEMV + two-stage argmax
-    wl = W.LM_HEAD
-    n, k = wl.matrices[0].n, wl.matrices[0].k
-    staging = torch.empty(n * k, dtype=torch.float32, device="cuda")
-    synth.dev_normal_f32(staging.data_ptr(), wl.seed, 1, n * k, W.WEIGHT_SIGMA, stream=s)
-    wb = torch.empty(n * k, dtype=torch.uint16, device="cuda")
-    wsg.convert_bf16(staging, n * k, wb)
-    wq = torch.empty(wsg.q8_0_packed_bytes(n, k), dtype=torch.uint8, device="cuda")
-    wsg.quantize_q8_0_weights(staging, n, k, wq)
-    del staging
-    x = torch.from_numpy(synth.activation(wl.seed, W.activation_tensor_id(0), k)).cuda()
-    ws = torch.empty(wsg.argmax_ws_bytes(), dtype=torch.uint8, device="cuda")
-    idx = torch.empty(1, dtype=torch.int32, device="cuda")
-    sec = _time_calls(lambda i: wsg.lm_head_argmax(wb, wsg.W_BF16, n, k, x, wsg.ACT_F32, ws, ws.numel(), idx),
-                      max(steps, 1))
-    rec(wl, "bf16 GEMV + argmax", sec, n * k * 2)
-    for deq, act in ((0, wsg.ACT_F32_REQUANT), (2, wsg.ACT_F32)):
-        sec = _time_calls(lambda i: wsg.lm_head_argmax(wq, wsg.W_Q8_0, n, k, x, act, ws, ws.numel(), idx),
+    def small_workloads(steps, rec, s):
+        # configs 0: one 1024x1024 Q8_0 GEMV
+        wl = W.Q8_SINGLE
+        n, k = wl.matrices[0].n, wl.matrices[0].k
+        alg = n * (k // 32) * 34
+        staging = torch.empty(n * k, dtype=torch.float32, device="cuda")
+        copies = 1024
+        wq = torch.empty((copies, wsg.q8_0_packed_bytes(n, k)), dtype=torch.uint8, device="cuda")
+        for c in range(copies):
+            synth.dev_normal_f32(staging.data_ptr(), wl.seed, 1 + c, n * k, W.WEIGHT_SIGMA, stream=s)
+            wsg.quantize_q8_0_weights(staging, n, k, wq[c])
+        x = torch.from_numpy(synth.activation(wl.seed, W.activation_tensor_id(0), k)).cuda()
+        y = torch.empty(n, dtype=torch.float32, device="cuda")
+        for deq, act in ((0, wsg.ACT_F32_REQUANT), (2, wsg.ACT_F32)):
+            for temp, pick in (("hot", lambda i: 0), ("cold", lambda i: i % copies)):
+                sec = _time_calls(lambda i: wsg.gemv_q8_0(wq[pick(i)], n, k, x, act, y), max(steps, 1) * 40)
+                rec(wl, f"eager deq{deq} {temp}", sec, alg, deq=deq)
+                # the same calls replayed from a graph of 256: the kernel without
+                # the host's launch cost
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(256):
+                        wsg.gemv_q8_0(wq[pick(i)], n, k, x, act, y)
+                sec = _time_calls(lambda i: g.replay(), max(steps, 1) // 5 + 1) / 256
+                rec(wl, f"graph of 256 calls deq{deq} {temp}", sec, alg, deq=deq)
+                del g
+        del wq, staging
+        # configs 3: the LM head, fused GEMV + two-stage argmax
+        wl = W.LM_HEAD
+        n, k = wl.matrices[0].n, wl.matrices[0].k
+        staging = torch.empty(n * k, dtype=torch.float32, device="cuda")
+        synth.dev_normal_f32(staging.data_ptr(), wl.seed, 1, n * k, W.WEIGHT_SIGMA, stream=s)
+        wb = torch.empty(n * k, dtype=torch.uint16, device="cuda")
+        wsg.convert_bf16(staging, n * k, wb)
+        wq = torch.empty(wsg.q8_0_packed_bytes(n, k), dtype=torch.uint8, device="cuda")
+        wsg.quantize_q8_0_weights(staging, n, k, wq)
+        del staging
+        x = torch.from_numpy(synth.activation(wl.seed, W.activation_tensor_id(0), k)).cuda()
+        ws = torch.empty(wsg.argmax_ws_bytes(), dtype=torch.uint8, device="cuda")
+        idx = torch.empty(1, dtype=torch.int32, device="cuda")
+        sec = _time_calls(lambda i: wsg.lm_head_argmax(wb, wsg.W_BF16, n, k, x, wsg.ACT_F32, ws, ws.numel(), idx),
                           max(steps, 1))
-        rec(wl, f"q8_0 GEMV + argmax, deq{deq}" + (" (= deq1)" if deq == 2 else ""), sec, n * (k // 32) * 34,
-            deq=deq)
-    # the same matrix with 4-bit weights (18 bytes per 32 weights)
-    staging = torch.empty(n * k, dtype=torch.float32, device="cuda")
-    synth.dev_normal_f32(staging.data_ptr(), wl.seed, 1, n * k, W.WEIGHT_SIGMA, stream=s)
-    w4 = torch.empty(wsg.q4_0_packed_bytes(n, k), dtype=torch.uint8, device="cuda")
-    wsg.quantize_q4_0_weights(staging, n, k, w4)
-    del staging
-    y4 = torch.empty(n, dtype=torch.float32, device="cuda")
-    sec = _time_calls(lambda i: wsg.gemv_q4_0(w4, n, k, x, wsg.ACT_F32_REQUANT, y4), max(steps, 1) * 4)
-    rec(wl, "q4_0 GEMV (W4), deq0", sec, n * (k // 32) * 18, deq=0)
-    del wb, wq, w4
-    torch.cuda.empty_cache()
-    # the residual add + RMSNorm + re-quantization between GEMVs, alone, at
-    # the hidden sizes of the streams (bytes: h, r, g read; h', y written;
-    # y_q8 written)
-    for hidden in (1024, 4096, 5120):
-        h = torch.from_numpy(synth.normal_f32(0x5EED0009, 0, hidden, 1.0)).cuda()
-        r = torch.from_numpy(synth.normal_f32(0x5EED0009, 1, hidden, 0.5)).cuda()
-        g = torch.ones(hidden, dtype=torch.float32, device="cuda")
-        h_out = torch.empty_like(h)
-        yv = torch.empty_like(h)
-        yq = torch.empty(wsg.act_q8_0_bytes(hidden), dtype=torch.uint8, device="cuda")
-        nbytes = 20 * hidden + wsg.act_q8_0_bytes(hidden)
-        call = lambda i: wsg.residual_rmsnorm_q8_0(h, r, g, hidden, W.RMSNORM_EPS, h_out, yv, yq)
-        sec = _time_calls(call, max(steps, 1) * 40)
-        out.append({"workload": f"residual_rmsnorm_q8_0_k{hidden}", "mode": "eager", "us": round(sec * 1e6, 2),
-                    "bytes": nbytes})
-        log(f"residual_rmsnorm k={hidden:5d} eager {sec * 1e6:8.2f} us")
-        g_ = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_):
-            for i in range(256):
-                call(i)
-        sec = _time_calls(lambda i: g_.replay(), max(steps, 1) // 5 + 1) / 256
-        out.append({"workload": f"residual_rmsnorm_q8_0_k{hidden}", "mode": "graph of 256 calls",
-                    "us": round(sec * 1e6, 2), "bytes": nbytes})
-        log(f"residual_rmsnorm k={hidden:5d} graph {sec * 1e6:8.2f} us")
-        del g_
+        rec(wl, "bf16 GEMV + argmax", sec, n * k * 2)
+        for deq, act in ((0, wsg.ACT_F32_REQUANT), (2, wsg.ACT_F32)):
+            sec = _time_calls(lambda i: wsg.lm_head_argmax(wq, wsg.W_Q8_0, n, k, x, act, ws, ws.numel(), idx),
+                              max(steps, 1))
+            rec(wl, f"q8_0 GEMV + argmax, deq{deq}" + (" (= deq1)" if deq == 2 else ""), sec, n * (k // 32) * 34,
+                deq=deq)
+        # the same matrix with 4-bit weights (18 bytes per 32 weights)
+        staging = torch.empty(n * k, dtype=torch.float32, device="cuda")
+        synth.dev_normal_f32(staging.data_ptr(), wl.seed, 1, n * k, W.WEIGHT_SIGMA, stream=s)
+        w4 = torch.empty(wsg.q4_0_packed_bytes(n, k), dtype=torch.uint8, device="cuda")
+        wsg.quantize_q4_0_weights(staging, n, k, w4)
+        del staging
+        y4 = torch.empty(n, dtype=torch.float32, device="cuda")
+        sec = _time_calls(lambda i: wsg.gemv_q4_0(w4, n, k, x, wsg.ACT_F32_REQUANT, y4), max(steps, 1) * 4)
+        rec(wl, "q4_0 GEMV (W4), deq0", sec, n * (k // 32) * 18, deq=0)
+        del wb, wq, w4
+        torch.cuda.empty_cache()
+        # the residual add + RMSNorm + re-quantization between GEMVs, alone, at
+        # the hidden sizes of the streams (bytes: h, r, g read; h', y written;
+        # y_q8 written)
+        for hidden in (1024, 4096, 5120):
+            h = torch.from_numpy(synth.normal_f32(0x5EED0009, 0, hidden, 1.0)).cuda()
+            r = torch.from_numpy(synth.normal_f32(0x5EED0009, 1, hidden, 0.5)).cuda()
+            g = torch.ones(hidden, dtype=torch.float32, device="cuda")
+            h_out = torch.empty_like(h)
+            yv = torch.empty_like(h)
+            yq = torch.empty(wsg.act_q8_0_bytes(hidden), dtype=torch.uint8, device="cuda")
+            nbytes = 20 * hidden + wsg.act_q8_0_bytes(hidden)
+            call = lambda i: wsg.residual_rmsnorm_q8_0(h, r, g, hidden, W.RMSNORM_EPS, h_out, yv, yq)
+            sec = _time_calls(call, max(steps, 1) * 40)
+            out.append({"workload": f"residual_rmsnorm_q8_0_k{hidden}", "mode": "eager", "us": round(sec * 1e6, 2),
+                        "bytes": nbytes})
+            log(f"residual_rmsnorm k={hidden:5d} eager {sec * 1e6:8.2f} us")
+            g_ = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_):
+                for i in range(256):
+                    call(i)
+            sec = _time_calls(lambda i: g_.replay(), max(steps, 1) // 5 + 1) / 256
+            out.append({"workload": f"residual_rmsnorm_q8_0_k{hidden}", "mode": "graph of 256 calls",
+                        "us": round(sec * 1e6, 2), "bytes": nbytes})
+            log(f"residual_rmsnorm k={hidden:5d} graph {sec * 1e6:8.2f} us")
+            del g_
+
+    s = torch.cuda.current_stream().cuda_stream
+    if want("small"):
+        small_workloads(steps, rec, s)
     # configs 1, 2, 4: token streams
-    for wl, deqs in ((W.QWEN3_0P6B_BF16, (0,)), (W.QWEN3_8B_Q8, (0,)), (W.DENSE27B_Q8, (0, 2))):
+    for wl, deqs in _stream_configs(W):
         for deq in deqs:
-            ts = build_stream(wl, deq, "fused")
-            alg = ts.algorithmic_weight_bytes()
-            plans = ("graph",) if wl.wtype == "bf16" else ("graph", "persistent")
-            for plan in plans:
-                sec, kernels = time_plan(ts, plan, steps, warmup)
-                rec(wl, f"{plan} deq{deq}" if wl.wtype != "bf16" else plan, sec, alg, kernels_per_token=kernels,
-                    deq=deq)
-            ts.close()
-            del ts
-            torch.cuda.empty_cache()
+            name = f"stream:{wl.name}:deq{deq}"
+            alg = None
+            if want(f"{name}:plain"):
+                ts = build_stream(wl, deq, "fused")
+                alg = ts.algorithmic_weight_bytes()
+                plans = ("graph",) if wl.wtype == "bf16" else ("graph", "persistent")
+                for plan in plans:
+                    sec, kernels = time_plan(ts, plan, steps, warmup)
+                    rec(wl, f"{plan} deq{deq}" if wl.wtype != "bf16" else plan, sec, alg, kernels_per_token=kernels,
+                        deq=deq)
+                ts.close()
+                del ts
+                torch.cuda.empty_cache()
             # the same stream with the layers chained through the residual
             # stream (a residual add + RMSNorm call before GEMVs 0 and 2)
-            ts = build_stream(wl, deq, "fused", norm=True)
-            sec, kernels = time_plan(ts, False, steps, warmup)
-            rec(wl, f"graph + residual/RMSNorm deq{deq}" if wl.wtype != "bf16" else "graph + residual/RMSNorm",
-                sec, alg, kernels_per_token=kernels, deq=deq)
-            ts.close()
-            del ts
-            torch.cuda.empty_cache()
-            if wl.wtype == "q8_0":
-                # the same chain with the norm step in each normalized GEMV's prologue
+            if want(f"{name}:norm"):
+                ts = build_stream(wl, deq, "fused", norm=True)
+                sec, kernels = time_plan(ts, False, steps, warmup)
+                rec(wl, f"graph + residual/RMSNorm deq{deq}" if wl.wtype != "bf16" else "graph + residual/RMSNorm",
+                    sec, ts.algorithmic_weight_bytes(), kernels_per_token=kernels, deq=deq)
+                ts.close()
+                del ts
+                torch.cuda.empty_cache()
+            if wl.wtype != "q8_0":
+                continue
+            # the same chain with the norm step in each normalized GEMV's prologue
+            if want(f"{name}:fused_norm"):
                 ts = build_stream(wl, deq, "fused", norm=True, fused_norm=True)
                 sec, kernels = time_plan(ts, False, steps, warmup)
-                rec(wl, f"graph + residual/RMSNorm fused into the GEMVs deq{deq}", sec, alg,
+                rec(wl, f"graph + residual/RMSNorm fused into the GEMVs deq{deq}", sec, ts.algorithmic_weight_bytes(),
                     kernels_per_token=kernels, deq=deq)
                 ts.close()
                 del ts
                 torch.cuda.empty_cache()
-                # down reading the SwiGLU of gate+up (the epilogue fused into that GEMV)
+            # down reading the SwiGLU of gate+up (the epilogue fused into that GEMV)
+            if want(f"{name}:swiglu"):
                 ts = build_stream(wl, deq, "fused", swiglu=True)
                 sec, kernels = time_plan(ts, False, steps, warmup)
-                rec(wl, f"graph + SwiGLU epilogue on gate+up deq{deq}", sec, alg, kernels_per_token=kernels, deq=deq)
+                rec(wl, f"graph + SwiGLU epilogue on gate+up deq{deq}", sec, ts.algorithmic_weight_bytes(),
+                    kernels_per_token=kernels, deq=deq)
                 ts.close()
                 del ts
                 torch.cuda.empty_cache()
-    # the 27B stream with 4-bit weights: int8 activations (deq 0) and f32
-    # ones (deq 2, W4A16); at deq 0 also with the norm prologue and the
-    # SwiGLU epilogue
-    for deq, extra, kw in ((0, "", {}), (2, " (W4A16)", {}),
-                           (0, " + residual/RMSNorm fused into the GEMVs", {"norm": True, "fused_norm": True}),
-                           (0, " + SwiGLU epilogue on gate+up", {"swiglu": True})):
+    for i, (deq, extra, kw) in enumerate(_W4_CONFIGS):
+        if not want(f"w4:{i}"):
+            continue
         ts = build_stream(W.DENSE27B_Q8, deq, "fused", wtype="q4_0", **kw)
         sec, kernels = time_plan(ts, False, steps, warmup)
         rec(W.DENSE27B_Q8, f"graph, W4 weights (q4_0){extra} deq{deq}", sec, ts.algorithmic_weight_bytes(),
@@ -398,8 +462,9 @@ def measure_configs(steps: int, warmup: int) -> list:
         del ts
         torch.cuda.empty_cache()
     # a whole decode step: embedding -> layers -> LM head + argmax -> advance
-    for wl, wt, deq in ((W.QWEN3_8B_Q8, "q8_0", 0), (W.DENSE27B_Q8, "q8_0", 0), (W.DENSE27B_Q8, "q8_0", 2),
-                        (W.DENSE27B_Q8, "q4_0", 0)):
+    for i, (wl, wt, deq) in enumerate(_decode_configs(W)):
+        if not want(f"decode:{i}"):
+            continue
         ds = build_decode(wl, wtype=wt, deq=deq)
         alg = ds.chain.algorithmic_weight_bytes() + ds.vocab * (ds.hidden // 32) * 34
         ds.capture()
@@ -759,6 +824,11 @@ def main() -> int:
     ap.add_argument("--configs", action="store_true",
                     help="measure every workload (single GEMV hot/cold, LM head, the three token streams) and "
                          "print one JSON line per configuration and mode, instead of the benchmark line")
+    ap.add_argument("--configs-part", default=None, metavar="NAME",
+                    help="with --configs: measure one part (see config_part_names) in this process")
+    ap.add_argument("--configs-one-process", action="store_true",
+                    help="with --configs: measure every part in this process (for profilers; later streams "
+                         "then run on re-used allocations, ~3.5%% slower)")
     ap.add_argument("--summarize", nargs=5, metavar=("STATS", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write profiles/ summaries from rocprofv3 output directories (no GPU needed); "
                          "the commands that made them are read from STATS/commands.json")
@@ -777,6 +847,12 @@ def main() -> int:
               "sharding by output rows); run it with --gpus 1", file=sys.stderr)
         return 2
 
+    if args.configs and args.configs_part is None and not args.configs_one_process:
+        return run_configs_in_children(args.steps, args.warmup)
+    if args.configs_part is not None and args.configs_part not in config_part_names():
+        print(f"unknown configs part {args.configs_part}; choose one of {config_part_names()}", file=sys.stderr)
+        return 2
+
     import torch
 
     import weight_streaming_gemv_q8_amd as wsg
@@ -785,7 +861,7 @@ def main() -> int:
     if args.configs:
         torch.cuda.set_device(0)
         wsg.lib()
-        for r in measure_configs(args.steps, args.warmup):
+        for r in measure_configs(args.steps, args.warmup, args.configs_part):
             print(json.dumps(r), flush=True)
         return 0
 

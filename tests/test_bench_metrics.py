@@ -129,3 +129,23 @@ def test_profile_summary_groups_by_grid_and_calibrates(tmp_path, monkeypatch):
     assert got == round((1000 + 1200 + 3000) / 3 * 2 * 1024 + (10 + 10 + 20) / 3 * 1024)
     assert refs["stats"] == "profiles/kernel_stats_wl.txt" and refs["traffic"].endswith("_wl.txt")
     assert bench.profile_refs(lab, "other") == (None, {"stats": None, "traffic": None})
+
+
+def test_config_parts_cover_every_workload_once():
+    names = bench.config_part_names()
+    assert names[0] == "small" and len(set(names)) == len(names)
+    streams = [n for n in names if n.startswith("stream:")]
+    # BF16 chains have no fused norm or SwiGLU form; Q8_0 ones have all four
+    assert {n.rsplit(":", 1)[1] for n in streams if "bf16" in n} == {"plain", "norm"}
+    assert {n.rsplit(":", 1)[1] for n in streams if "q8_0" in n} == {"plain", "norm", "fused_norm", "swiglu"}
+    assert any(n.startswith("stream:dense27b_q8_0_64L:deq2:") for n in names)
+    assert [n for n in names if n.startswith("w4:")] == ["w4:0", "w4:1", "w4:2", "w4:3"]
+    assert [n for n in names if n.startswith("decode:")] == ["decode:0", "decode:1", "decode:2", "decode:3"]
+
+
+def test_unknown_configs_part_is_refused_before_the_gpu():
+    import subprocess
+    import sys
+    p = subprocess.run([sys.executable, bench.__file__, "--configs", "--configs-part", "nope"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2 and "unknown configs part" in p.stderr
