@@ -1017,12 +1017,12 @@ Cfg choose_cfg(Path path, int64_t n, int64_t k) {
     // workload shape once the ring's loads are pipelined
     c.unroll = 1;
     if (path == kPathQ4) {
-        // measured on the 27B-stream shapes in 4 bits: 16-wave workgroups
-        // with whole rows per wave beat every other pair on all four, the
-        // rotating split included (the per-workgroup staging is a larger
-        // share of a 4-bit row)
+        // measured on the 27B-stream shapes in 4 bits: 16-wave workgroups,
+        // whole rows per wave (the per-workgroup staging is a larger share
+        // of a 4-bit row) except long rows few per CU, which split in 4
+        // (down: 13.6 against 14.8 us; qkvz, gate+up and out keep whole rows)
         c.waves = 16;
-        c.split = 1;
+        c.split = (rows_per_cu < 32 && k >= 16384) ? 4 : 1;
     } else if (path == kPathQ4F32) {
         // measured on the same shapes with f32 activations (W4A16), where
         // the dequantizing arithmetic weighs more than the staging: 8-wave
