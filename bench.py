@@ -847,6 +847,8 @@ def main() -> int:
               "sharding by output rows); run it with --gpus 1", file=sys.stderr)
         return 2
 
+    if args.configs_part is not None:
+        args.configs = True
     if args.configs and args.configs_part is None and not args.configs_one_process:
         return run_configs_in_children(args.steps, args.warmup)
     if args.configs_part is not None and args.configs_part not in config_part_names():
