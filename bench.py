@@ -950,6 +950,9 @@ def main() -> int:
                                            "GBps": round(gbps(alg_bytes, sec_o), 1), "kernels_per_token": k_o}
                 log(f"{other} plan: {sec_o * 1e6:.1f} us per token")
         extras["read_ceiling_GBps"] = round(read_ceiling(ts), 1)
+        # the token's and the dominant kernel's rates against that ceiling
+        extras["frac_of_read_ceiling"] = round(value / extras["read_ceiling_GBps"], 4)
+        extras["roofline_frac_of_read_ceiling"] = round(roofline["achieved"] / extras["read_ceiling_GBps"], 4)
         log(f"read ceiling {extras['read_ceiling_GBps']} GB/s")
         if wl.wtype == "q8_0" and args.deq != 2:
             # the same stream with f32 activations (deq 2), same weights
