@@ -965,9 +965,9 @@ struct LaunchInfo {
     size_t lds = 0;
 };
 
-// kPathF32Gemv: the plain f32-activation GEMV (and LM head); the fused
-// norm and SwiGLU forms with f32 activations take kPathF32.
-enum Path { kPathI8 = 0, kPathF32 = 1, kPathBf16 = 2, kPathQ4 = 3, kPathQ4F32 = 4, kPathF32Gemv = 5 };
+// kPathI8Gemv / kPathF32Gemv: the plain GEMV (and LM head) with int8 or f32
+// activations; the fused norm and SwiGLU forms take kPathI8 / kPathF32.
+enum Path { kPathI8 = 0, kPathF32 = 1, kPathBf16 = 2, kPathQ4 = 3, kPathQ4F32 = 4, kPathF32Gemv = 5, kPathI8Gemv = 6 };
 
 // Default configuration per path and shape; tuning knobs override it.
 struct Cfg {
@@ -1038,12 +1038,13 @@ Cfg choose_cfg(Path path, int64_t n, int64_t k) {
         else if (rows_per_cu < 8 && k >= 2048) c.split = 2;
     } else {
         c.split = balanced_split(n, k);
-        // the plain GEMV with f32 activations (deq 2): 16-wave workgroups on
-        // every shape; on the tall 27B matrices they beat two 8-wave ones
-        // (gate+up 32.5 against 33.7 us, qkvz 18.0 against 18.3), the LM
-        // head runs the same.  Not the fused norm and SwiGLU forms, whose
-        // prologue and epilogue run slower at 16 waves.
-        if (path == kPathF32Gemv) c.waves = 16;
+        // the plain GEMV: 16-wave workgroups on every shape.  On the tall
+        // 27B matrices they beat two 8-wave ones, with f32 activations
+        // (deq 2: gate+up 32.5 against 33.7 us, qkvz 18.0 against 18.3) and
+        // by less with int8 ones (the 27B token 4770 against 4792 us); the
+        // LM head runs the same.  Not the fused norm and SwiGLU forms,
+        // whose prologue and epilogue run slower at 16 waves.
+        if (path == kPathF32Gemv || path == kPathI8Gemv) c.waves = 16;
     }
     const int tw = tune_waves(), ts = tune_splitk(), tu = tune_unroll();
     if (tw == 4 || tw == 8 || tw == 16) c.waves = tw;
@@ -1116,7 +1117,7 @@ size_t q8_lds_bytes(size_t lds_act) {
 template <int ACT, bool DEBUG, bool ARGMAX>
 int launch_q8_i8(const void* w, int n, int k, const void* x, float* y, int32_t* dots, uint64_t* keys,
                  hipStream_t stream, LaunchInfo* info, bool run = true) {
-    const Cfg c = choose_cfg(kPathI8, n, k);
+    const Cfg c = choose_cfg(kPathI8Gemv, n, k);
     const size_t lds_act = lds_q8act_bytes((int)chunk_count(k));
     const uint8_t* wp = static_cast<const uint8_t*>(w);
     if constexpr (DEBUG || ARGMAX) {
