@@ -5,7 +5,8 @@
 // nothing).  Each workgroup of each launch records, from the GPU's
 // constant 100 MHz clock (s_memrealtime): its entry, the end of its
 // activation staging, the first and the last of its waves to finish the
-// row loop, its end, its CU and XCD, and the latest wave entry.  A launch
+// row loop (and which waves they were), its end, its CU and XCD, and the
+// latest wave entry.  A launch
 // is told apart by its output pointer: the record of workgroup b of the
 // launch writing y goes to slot ((y >> 2) % modulus) * 512 + b of the
 // buffer set by wsg_timeline_set (the caller picks a modulus under which
@@ -57,9 +58,16 @@ __device__ inline void tl_end(uint64_t t_entry, uint64_t t_staged, const void* y
     const int nw = (int)(blockDim.x / kWave) < 16 ? (int)(blockDim.x / kWave) : 16;
     const TlWaves& w = tl_waves();
     uint64_t first_end = ~0ull, last_end = 0, last_entry = 0;
+    uint64_t first_wave = 0, last_wave = 0;
     for (int i = 0; i < nw; ++i) {
-        first_end = w.t[i][1] < first_end ? w.t[i][1] : first_end;
-        last_end = w.t[i][1] > last_end ? w.t[i][1] : last_end;
+        if (w.t[i][1] < first_end) {
+            first_end = w.t[i][1];
+            first_wave = (uint64_t)i;
+        }
+        if (w.t[i][1] > last_end) {
+            last_end = w.t[i][1];
+            last_wave = (uint64_t)i;
+        }
         last_entry = w.t[i][0] > last_entry ? w.t[i][0] : last_entry;
     }
     const uint64_t key = ((uint64_t)y >> 2) % g_timeline_mod;
@@ -72,7 +80,8 @@ __device__ inline void tl_end(uint64_t t_entry, uint64_t t_staged, const void* y
     r[5] = last_end;
     r[6] = t_end;
     r[7] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID: CU, SE
-    r[8] = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
+    // XCC_ID, and the waves that ended the row loop first and last
+    r[8] = __builtin_amdgcn_s_getreg((31 << 11) | 20) | (first_wave << 32) | (last_wave << 40);
     r[9] = last_entry;
 }
 

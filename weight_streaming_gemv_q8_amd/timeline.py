@@ -17,7 +17,9 @@ Graph plan (one launch per GEMV, the int8 GEMV kernel):
   boundary itself: completion, cache write-back, the next dispatch);
 * wave spread: within a workgroup, the first to the last wave to finish its
   row loop (median over workgroups);
-* the two workgroups sharing a CU (b and b + CUs): median end of each.
+* the two workgroups sharing a CU (b and b + CUs): median end of each;
+* the index of the wave that ends its row loop first, and last (median
+  over workgroups).
 
 Persistent plan (one resident kernel per token; per op and workgroup):
 
@@ -87,7 +89,8 @@ def _persistent_records(h, n_ops, r):
 
 
 def _graph_summary(np, by, replays, nm, n, cus):
-    keys = ("period", "entry", "staging", "body", "tail", "gap", "waves", "first_wg", "second_wg")
+    keys = ("period", "entry", "staging", "body", "tail", "gap", "waves", "first_wg", "second_wg", "first_w",
+            "last_w")
     per = {q: {k: [] for k in keys} for q in range(nm)}
     for r in range(replays):
         for j in range(nm, n - nm):  # layers 1 .. L-2
@@ -103,11 +106,15 @@ def _graph_summary(np, by, replays, nm, n, cus):
             d["tail"].append((ends.max() - float(np.median(ends))) * US)
             d["gap"].append((e2[:, 2].min() - ends.max()) * US)
             d["waves"].append(float(np.median(e[:, 5] - e[:, 4])) * US)
+            # which wave of the workgroup ended its row loop first / last
+            d["first_w"].append(float(np.median((e[:, 8] >> 32) & 0xFF)))
+            d["last_w"].append(float(np.median((e[:, 8] >> 40) & 0xFF)))
             if grid > cus:
                 b = np.arange(len(e))
                 d["first_wg"].append(float(np.median(ends[b < cus] - t0)) * US)
                 d["second_wg"].append(float(np.median(ends[(b >= cus) & (b < 2 * cus)] - t0)) * US)
-    heads = ("period", "entry", "staging", "body", "tail", "gap", "waves", "1st WG", "2nd WG")
+    heads = ("period", "entry", "staging", "body", "tail", "gap", "waves", "1st WG", "2nd WG", "1st wave",
+             "last wave")
     return per, keys, heads, ("period", "staging", "tail", "gap")
 
 
@@ -220,6 +227,15 @@ def main() -> int:
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+    if not persistent:
+        # how often each wave index ends the row loop first / last
+        for q in range(nm):
+            f8 = np.concatenate([by[(r, j)][1][:, 8] for r in range(args.replays) for j in range(nm, n - nm)
+                                 if j % nm == q])
+            first = np.bincount(((f8 >> 32) & 0xFF).astype(np.int64), minlength=16)
+            last = np.bincount(((f8 >> 40) & 0xFF).astype(np.int64), minlength=16)
+            print(f"  {names[q]:8s} first-ending wave counts {first.tolist()}")
+            print(f"  {names[q]:8s} last-ending wave counts  {last.tolist()}")
     print(out)
     return 0
 
