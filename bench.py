@@ -724,6 +724,44 @@ def _read_csv(path: str):
         return list(csv.DictReader(f))
 
 
+def _summarize_boundaries(stats_dir: str, workload: str, commands: dict) -> str:
+    """profiles/boundaries_<workload>.txt: the GEMV boundaries of the token
+    replays as the rocprofv3 kernel trace sees them.  Consecutive library
+    GEMV dispatches whose kernel or grid differ (a token's chain; the
+    per-shape graphs repeat one shape) give, per boundary (this kernel and
+    grid -> the next): the traced duration, the period to the next
+    dispatch's start and the gap between this end and that start."""
+    import collections
+    rows = [r for r in _read_csv(os.path.join(stats_dir, "run_kernel_trace.csv"))
+            if "wsg::" in r["Kernel_Name"] and "_kernel<" in short_kernel_name(r["Kernel_Name"])
+            and "quantize" not in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    key = lambda r: (short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1))
+    agg = collections.defaultdict(lambda: ([], [], []))
+    for a, b in zip(rows, rows[1:]):
+        if key(a) == key(b):
+            continue
+        sa, ea, sb = int(a["Start_Timestamp"]), int(a["End_Timestamp"]), int(b["Start_Timestamp"])
+        if sb - sa > 1_000_000:  # not back to back (host work between replays)
+            continue
+        d, per, gap = agg[(key(a), key(b))]
+        d.append((ea - sa) / 1e3)
+        per.append((sb - sa) / 1e3)
+        gap.append((sb - ea) / 1e3)
+    med = lambda v: sorted(v)[len(v) // 2]
+    path = os.path.join(PROFILES, f"boundaries_{workload}.txt")
+    with open(path, "w") as f:
+        f.write(f"# GEMV boundaries of the token replays in the rocprofv3 kernel trace, {workload}\n")
+        f.write(f"# command: {commands['stats']}\n")
+        f.write("# medians over consecutive dispatches of different kernels or grids; us.  The trace stamps a\n"
+                "# kernel's start at the previous kernel's end, so the boundary cost is inside the durations:\n"
+                "# the per-workgroup timeline (python -m weight_streaming_gemv_q8_amd.timeline) splits it.\n")
+        f.write(f"# {'dispatches':>10} {'duration':>9} {'period':>9} {'gap':>7}  boundary (kernel, grid -> next)\n")
+        for ((la, ga), (lb, gb)), (d, per, gap) in sorted(agg.items(), key=lambda kv: -sum(kv[1][0])):
+            f.write(f"  {len(d):10d} {med(d):9.2f} {med(per):9.2f} {med(gap):7.2f}  {la} grid {ga} -> {lb} grid {gb}\n")
+    return path
+
+
 def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
                        workload: str, commands: dict) -> list:
     """Writes profiles/kernel_stats_<workload>.txt from a --kernel-trace
@@ -753,6 +791,8 @@ def summarize_profiles(stats_dir: str, fetch_dir: str, write_dir: str, copy_fetc
             f.write(f"  {len(d):6d} {grid:6d} {sum(d) / len(d):10.2f} {d[len(d) // 2]:10.2f} {d[0]:10.2f} "
                     f"{d[-1]:10.2f} {sum(d) / 1e3:10.3f} {100 * sum(d) / total_all:6.2f}  {lab}\n")
     written.append(path)
+    if workload.endswith("_graph") or workload.endswith("_graph_deq2"):
+        written.append(_summarize_boundaries(stats_dir, workload, commands))
     if fetch_dir == "-" or write_dir == "-":
         return written
 

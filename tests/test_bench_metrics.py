@@ -149,3 +149,38 @@ def test_unknown_configs_part_is_refused_before_the_gpu():
     p = subprocess.run([sys.executable, bench.__file__, "--configs", "--configs-part", "nope"],
                        capture_output=True, text=True, timeout=120)
     assert p.returncode == 2 and "unknown configs part" in p.stderr
+
+
+def test_boundary_summary_pairs_consecutive_kernels(tmp_path, monkeypatch):
+    """Graph-plan runs also get profiles/boundaries_<workload>.txt: per
+    boundary (kernel, grid -> next), the traced duration, the period to the
+    next start and the gap; repeated shapes (per-shape graphs) and
+    dispatches far apart (host work between replays) are not boundaries."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    a = "void wsg::(anonymous namespace)::q8_i8_kernel<16, 1, 1, 2, true, false, false>(unsigned char const*)"
+    b = "void wsg::(anonymous namespace)::q8_i8_kernel<16, 4, 1, 2, true, false, false>(unsigned char const*)"
+    th = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"]
+    trace, t = [], 0
+    for _ in range(3):  # a token of two GEMVs, three replays back to back: a 20 us then b 10 us, 1 us gaps
+        trace.append({"Kernel_Name": a, "Grid_Size_X": 256 * 1024, "Workgroup_Size_X": 1024,
+                      "Start_Timestamp": t, "End_Timestamp": t + 20000})
+        trace.append({"Kernel_Name": b, "Grid_Size_X": 256 * 1024, "Workgroup_Size_X": 1024,
+                      "Start_Timestamp": t + 21000, "End_Timestamp": t + 31000})
+        t += 32000
+    t += 5_000_000  # a per-shape graph later: the same kernel repeated
+    for _ in range(4):
+        trace.append({"Kernel_Name": a, "Grid_Size_X": 256 * 1024, "Workgroup_Size_X": 1024,
+                      "Start_Timestamp": t, "End_Timestamp": t + 20000})
+        t += 20000
+    _write_csv(str(tmp_path / "s" / "run_kernel_trace.csv"), th, trace)
+    out = bench.summarize_profiles(str(tmp_path / "s"), "-", "-", "-", "-", workload="wl_graph",
+                                   commands={"stats": "S"})
+    bpath = [p for p in out if "boundaries_wl_graph" in p]
+    assert len(bpath) == 1
+    rows = [l.split() for l in open(bpath[0]) if not l.startswith("#")]
+    got = {(r[4], r[8]): (int(r[0]), float(r[1]), float(r[2]), float(r[3])) for r in rows}
+    sa = "q8_i8_kernel<waves=16,split=1,unroll=1,requant>"
+    sb = "q8_i8_kernel<waves=16,split=4,unroll=1,requant>"
+    assert got[(sa, sb)] == (3, 20.0, 21.0, 1.0)
+    assert got[(sb, sa)] == (2, 10.0, 11.0, 1.0)  # the third b is followed by the far-away graph
+    assert len(got) == 2
